@@ -1,0 +1,215 @@
+/*
+ * ssb.h — C ABI of the MI355X self-speculative block-decoding round engine.
+ *
+ * The engine runs greedy self-speculative decoding of a shared
+ * autoregressive / block-diffusion decoder on one gfx950 GPU. One decoder
+ * and one LM head serve both modes; the only extra parameter is the [M]
+ * (mask) embedding row (GravityOCR review, section 3.1 "AR-to-Diffusion
+ * Conversion").
+ *
+ * A round (GravityOCR review, section 3.2 and Appendix B.2; velog review,
+ * round description):
+ *   - draft: [x0, [M] x B] at positions p..p+B. The boundary row is causal;
+ *     the mask rows see the cache and the whole window. Gives a0, d1..dB.
+ *   - verify: [a0, d1..dB] at positions p+1..p+B+1, causal. Overwrites the
+ *     mask KV slots with causal state. Gives a1..a(B+1).
+ *   - accept: A = longest prefix with d_j == a_j. Commits a0, d1..dA, a(A+1)
+ *     (2..B+2 tokens) and rolls back to length p+A+2. a(A+1) becomes the
+ *     next boundary.
+ *
+ * Conventions for every call:
+ *   - Return 0 (SSB_OK) or a negative SSB_E* code. ssb_last_error() gives a
+ *     thread-local message. No C++ exception crosses this boundary.
+ *   - Pointers named *_dev are device pointers. Others are host pointers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Calls that return host results synchronize that stream first.
+ *   - On error, committed state (sequence length, boundary token) is
+ *     unchanged.
+ *   - One model with its pools and KV caches is used from one host thread
+ *     at a time; there is no internal locking.
+ */
+#ifndef SSB_H
+#define SSB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSB_OK 0
+#define SSB_EINVAL (-1)  /* bad argument or configuration */
+#define SSB_ENOKV (-2)   /* KV capacity or pool pages exhausted */
+#define SSB_EHIP (-3)    /* a HIP runtime call failed (message has the HIP error) */
+#define SSB_ESTATE (-4)  /* call not valid in the current state (e.g. round before prefill) */
+#define SSB_ENOMEM (-5)  /* device allocation at init failed */
+
+#define SSB_F32 0
+#define SSB_BF16 1
+
+#define SSB_MAX_BATCH 16 /* requests per ssb_round_batch call */
+#define SSB_MAX_BLOCK 64 /* largest block size B */
+
+/* Decoder shape. Pre-norm Llama-style block: RMSNorm, RoPE (rotate-half
+ * pairing), grouped-query attention, SwiGLU MLP, no biases, untied LM head.
+ * Constraints:
+ *   - hidden, n_heads*head_dim and ffn are multiples of 128. The reduction
+ *     lengths hidden, n_heads*head_dim and ffn are 128 times a power of two.
+ *   - head_dim is 32 or 64.
+ *   - n_heads/n_kv_heads is 1 or 4.
+ *   - page_tokens == 16.
+ *   - block_B <= SSB_MAX_BLOCK. */
+typedef struct ssb_config {
+  int n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  int mask_id;        /* id of the [M] embedding row; never produced as output */
+  int eos_id;         /* end of sequence; committed, then decoding stops */
+  int block_B;        /* largest block size rounds will use */
+  int page_tokens;    /* KV page size in tokens (16) */
+  int max_rows;       /* rows per forward pass: prefill chunk, batched windows */
+  int max_positions;  /* largest position + 1 any sequence reaches */
+  float rms_eps, rope_theta;
+  int dtype;          /* SSB_BF16 or SSB_F32: weights, KV cache and GEMM inputs */
+} ssb_config;
+
+/* Weights: device pointers, row-major [out_features][in_features] in the
+ * config dtype (bf16 as raw uint16 bits); norm gains are float32 [hidden].
+ * The per-layer arrays are host arrays of n_layers device pointers.
+ * ssb_init_model copies the weights into its own layout, so the caller may
+ * free them once it returns. */
+typedef struct ssb_weights {
+  const void* embed;              /* [vocab][hidden], row mask_id is the [M] embedding */
+  const void* lm_head;            /* [vocab][hidden] */
+  const float* final_norm;        /* [hidden] */
+  const float* const* attn_norm;  /* [n_layers] -> [hidden] */
+  const float* const* mlp_norm;   /* [n_layers] -> [hidden] */
+  const void* const* wq;          /* [n_layers] -> [n_heads*head_dim][hidden] */
+  const void* const* wk;          /* [n_layers] -> [n_kv_heads*head_dim][hidden] */
+  const void* const* wv;          /* [n_layers] -> [n_kv_heads*head_dim][hidden] */
+  const void* const* wo;          /* [n_layers] -> [hidden][n_heads*head_dim] */
+  const void* const* wg;          /* [n_layers] -> [ffn][hidden] */
+  const void* const* wu;          /* [n_layers] -> [ffn][hidden] */
+  const void* const* wd;          /* [n_layers] -> [hidden][ffn] */
+} ssb_weights;
+
+typedef struct ssb_model ssb_model;
+typedef struct ssb_pool ssb_pool;
+typedef struct ssb_kv ssb_kv;
+
+/* Per-decode statistics (ssb_decode / ssb_decode_ar). Accept counts exclude
+ * a0 and a(A+1) (GravityOCR review, section 4.1). Forwards count draft and
+ * verify passes, not prefill. */
+typedef struct ssb_stats {
+  int rounds;            /* rounds run (AR: steps) */
+  int forwards;          /* decode forwards: 2 per round, 1 per AR step */
+  int tokens;            /* output tokens, y1 from prefill included */
+  int accepted;          /* sum of A over rounds */
+  double decode_us;      /* wall time of the decode loop, prefill excluded */
+  double prefill_us;     /* wall time of prefill */
+} ssb_stats;
+
+const char* ssb_last_error(void);
+
+/* Validates a configuration without touching the GPU: 0 or SSB_EINVAL. */
+int ssb_check_config(const ssb_config* cfg);
+
+/* Builds a model on the current device. Packs the weights and allocates
+ * the engine's fixed workspace; nothing on the round path allocates
+ * afterwards. *out is owned by the caller; release it with ssb_free_model. */
+int ssb_init_model(const ssb_config* cfg, const ssb_weights* w, void* stream, ssb_model** out);
+void ssb_free_model(ssb_model* m);
+
+/* KV page pool, in caller-owned device memory. ssb_pool_bytes returns the
+ * size of n_pages pages: each page holds page_tokens positions of K and V
+ * for every layer and KV head. The layout is [layer][page][K|V][kv_head]
+ * [token][head_dim]. */
+int ssb_pool_bytes(const ssb_model* m, int n_pages, size_t* bytes);
+int ssb_pool_init(ssb_model* m, void* dev_buf, size_t bytes, int n_pages, ssb_pool** out);
+void ssb_pool_free(ssb_pool* p);
+int ssb_pool_free_pages(const ssb_pool* p, int* n_free);
+
+/* One sequence's KV cache. Pages come from the pool on demand. After a
+ * round, pages wholly past what the next window can reach go back to the
+ * pool. ssb_kv_create allocates a small device page table.
+ * ssb_kv_reset releases all pages: length 0, no boundary. */
+int ssb_kv_create(ssb_pool* p, int max_tokens, ssb_kv** out);
+void ssb_kv_free(ssb_kv* kv);
+int ssb_kv_reset(ssb_kv* kv);
+/* State query: committed length n (positions with KV), boundary token x0
+ * (-1 before prefill) and pages held. */
+int ssb_kv_state(const ssb_kv* kv, int* seq_len, int32_t* x0, int* pages_held);
+
+/* Rewinds the kv to an earlier committed state: length n <= the current
+ * length, boundary token x0 (the token committed at position n, which the
+ * caller must supply). KV at positions < n is causal state of the committed
+ * prefix and stays valid. Pages past the next window are returned to the
+ * pool. Used to repeat a round from the same state. */
+int ssb_kv_rewind(ssb_kv* kv, int n, int32_t x0);
+
+/* Prefill (GravityOCR review, section 4.1 counts it outside TPF). Runs a
+ * causal forward over P prefix embeddings (device [P][hidden], config
+ * dtype) and writes KV for positions 0..P-1. *first_token (host) gets
+ * y1 = argmax of row P-1, which becomes the boundary x0. The kv must be
+ * empty. */
+int ssb_prefill(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int32_t* first_token,
+                void* stream);
+
+/* One self-speculative round from the kv's state (length p, boundary x0).
+ *   B: block size, 0..block_B.
+ *   max_commit: output budget, >= 1. Tokens past it are not committed.
+ *   planted_dev: nullable device [B] of token ids, -1 = keep the draft's own
+ *     token. It replaces drafts before verification. Test/benchmark hook;
+ *     it does not change the rule.
+ *   committed (host, capacity B+2): the committed tokens, cut after the
+ *     first EOS (inclusive) and at max_commit.
+ *   *n_committed, *accept_len: count and A.
+ * Afterwards the kv has length p+A+2 and boundary a(A+1).
+ * draft_logits_dev / verify_logits_dev (nullable, device fp32
+ * [B+1][vocab]) receive the scaled logits of the two forwards. */
+int ssb_round(ssb_model* m, ssb_kv* kv, int B, int max_commit, const int32_t* planted_dev,
+              int32_t* committed, int32_t* n_committed, int32_t* accept_len, float* draft_logits_dev,
+              float* verify_logits_dev, void* stream);
+
+/* One AR step: feed x0 at position p causally. *token gets the argmax,
+ * which becomes the new boundary. Length becomes p+1. logits_dev is
+ * nullable, fp32 [vocab]. */
+int ssb_ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits_dev, void* stream);
+
+/* Greedy self-speculative decode: prefill, then rounds until EOS or max_len
+ * output tokens. out (host, capacity max_len) gets y1..yN, N <= max_len,
+ * the first EOS included. The kv must be empty.
+ * Optional planting (benchmark hook):
+ *   - cont_dev (device [cont_len]) is the AR greedy continuation y1...
+ *   - astar (host [n_astar]) gives the planted accept length per round.
+ *   - Round k plants d_j = y_{c+1+j} for j <= astar[k], and a token other
+ *     than y_{c+astar+2} at j = astar+1 (c = tokens output so far).
+ *   - Rounds past n_astar are not planted. */
+int ssb_decode(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int B, int max_len,
+               const int32_t* cont_dev, int cont_len, const int32_t* astar, int n_astar, int32_t* out,
+               int32_t* n_out, ssb_stats* stats, void* stream);
+
+/* Greedy AR decode with the same kernels (window of one row). */
+int ssb_decode_ar(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int max_len, int32_t* out,
+                  int32_t* n_out, ssb_stats* stats, void* stream);
+
+/* R <= SSB_MAX_BATCH concurrent requests, one launch per stage. Each
+ * request has its own kv, state, budget and page table. Every kv needs a
+ * boundary token (prefilled). planted_dev: nullable device [R][B].
+ * committed: host [R][B+2]. n_committed, accept_len: host [R]. */
+int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_t* max_commit,
+                    const int32_t* planted_dev, int32_t* committed, int32_t* n_committed,
+                    int32_t* accept_len, void* stream);
+
+/* Teacher-forced causal forward over tokens (host [M], M <= max_rows) at
+ * positions p..p+M-1 of the kv. Writes their KV but does not change the
+ * kv's committed length. logits_dev: nullable device fp32 [M][vocab].
+ * argmax (host [M]) gets the greedy token of every row. top1/top2 (host
+ * [M], nullable) get the two largest logits. Used to judge decoded
+ * sequences position by position. */
+int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, int p, float* logits_dev,
+                       int32_t* argmax, float* top1, float* top2, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSB_H */

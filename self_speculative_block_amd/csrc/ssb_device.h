@@ -1,0 +1,152 @@
+// Shared device-side definitions of the self-speculative round engine (gfx950).
+//
+// Numerics contract (holds for every kernel here): the value computed for one
+// row never depends on how many rows share the launch, on the row's slot in
+// the window, or on how work is split across workgroups.  Reductions run in a
+// fixed order over fixed absolute structures (128-wide K chunks in GEMMs,
+// 64-key position chunks in attention, vocabulary groups in the argmax); no
+// floating-point atomics are used.  Consequently the verify rows of a round
+// reproduce an AR step at the same position bit for bit, which is what makes
+// greedy self-speculative output identical to greedy AR output on the GPU as
+// it is in exact arithmetic (GravityOCR review, Appendix B.3).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssb {
+
+typedef uint16_t bf16_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;      // 4 waves per workgroup
+constexpr int kChunkK = 128;       // fixed K chunk of every GEMM reduction
+constexpr int kKeyChunk = 64;      // fixed key chunk of attention (absolute positions)
+constexpr int kPage = 16;          // tokens per KV page
+constexpr int kNormGroup = 64;     // columns per sum-of-squares partial of the residual
+constexpr int kMaxReq = 16;        // requests per batched launch
+constexpr int kMaxTasks = 64;      // attention row tasks per launch
+constexpr int kTaskRows = 48;      // rows per attention task (3 MFMA row tiles)
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                               // round to nearest even
+  return (bf16_t)(u >> 16);
+}
+
+// Storage-type traits.  A "fragment" is the 16 bytes one lane feeds to the
+// matrix core per step: 8 bf16 or 4 f32 values along K.
+template <typename T> struct Ty;
+template <> struct Ty<bf16_t> {
+  static constexpr int kStepK = 32;   // K covered by one 16-byte-per-lane step
+  static constexpr int kPerFrag = 8;
+  static __device__ __forceinline__ float to_f(bf16_t v) { return bf2f(v); }
+  static __device__ __forceinline__ bf16_t from_f(float v) { return f2bf(v); }
+};
+template <> struct Ty<float> {
+  static constexpr int kStepK = 16;
+  static constexpr int kPerFrag = 4;
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+
+// One 16x16 output tile step: acc[n][m] += sum_k A[n][k] * B[k][m].
+// Lane l supplies A row (l % 16) and B column (l % 16), and the K values
+// [kStepK/4 * (l/16), kStepK/4 * (l/16 + 1)) of the step; A and B use the
+// same lane->K map, so any fixed K permutation inside a step is harmless.
+// Result layout: lane l, element i holds acc[4*(l/16) + i][l % 16].
+__device__ __forceinline__ void mma_step(f32x4_t& acc, uint4 a, uint4 b, bf16_t) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_step(f32x4_t& acc, uint4 a, uint4 b, float) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+
+// Per-request launch arguments (passed by value).
+struct ReqArgs {
+  int n;                              // requests in this launch
+  int B;                              // block size (mask tokens per window)
+  int p[kMaxReq];                     // position of the boundary token x0 (= cache length)
+  int x0[kMaxReq];                    // boundary token
+  int row0[kMaxReq];                  // first row of this request's window
+  int max_commit[kMaxReq];            // remaining output budget
+  const int32_t* pt[kMaxReq];         // device page table of the request
+  const int32_t* planted[kMaxReq];    // nullable device [B]: -1 keeps the draft's own token
+  const int32_t* cont[kMaxReq];       // nullable device AR continuation for planting
+  int cont_len[kMaxReq];
+  int cont_c[kMaxReq];                // output tokens committed before this round
+  int astar[kMaxReq];                 // planted accept length (continuation mode)
+};
+
+struct AttnTask { int req, row0, nrows; };
+struct AttnTasks { int n; AttnTask t[kMaxTasks]; };
+
+
+enum PrepMode { PREP_PREFILL = 0, PREP_DRAFT = 1, PREP_VERIFY = 2, PREP_TOKENS = 3 };
+
+struct PrepArgs {
+  int mode;
+  int M, hidden, vocab, mask_id;
+  int pos0;                    // PREFILL / TOKENS: position of row 0
+  const void* prefix;          // PREFILL: [*][hidden] of T, row pos0 + m
+  const int32_t* tokens;       // TOKENS: device [M]
+  const int32_t* am_prev;      // VERIFY: argmax rows of the draft forward
+  const void* embed;           // [vocab][hidden] of T
+  int32_t* row_tok; int32_t* row_pos; int32_t* row_lim; int32_t* row_req;
+  float* h; float* ssq; int ssq_ld;
+  ReqArgs req;
+};
+
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+struct GemmArgs {
+  const uint4* W; int K; int n_groups; int M; int S;
+  const float* h; const float* gain;           // RMSNorm input (QKV, SWIGLU, LOGITS)
+  const void* x; int ldx;                       // plain input (RESID)
+  float* part; int* counters;                   // split-K sums and tickets
+  const float* ssq; int ssq_ld; int n_ssq; float eps; int hidden;
+  float* h_out; float* ssq_out;                 // RESID
+  void* y; int ldy;                             // SWIGLU act / QKV q
+  int n_heads, n_kv, head_dim, layer, n_pages;  // QKV
+  void* kv_pool; const float2* rope;
+  const int32_t* row_pos; const int32_t* row_req;
+  const int32_t* pt[kMaxReq];
+  float* logits; int vocab; int mask_id;        // LOGITS
+  float* am_v1; int32_t* am_i1; float* am_v2; int am_ld;
+};
+
+struct AttnArgs {
+  const void* q; int q_ld;                 // [rows][n_heads*hd]
+  const void* kv_pool; int layer; int n_pages; int n_heads; int n_kv;
+  const int32_t* pt[kMaxReq];
+  const int32_t* row_lim;
+  float* part; int max_chunks;             // records [row][head][chunk][hd+4]
+  void* out; int out_ld;                   // fold: [rows][n_heads*hd]
+  int fold;
+  float scale;
+  AttnTasks tasks;
+};
+
+// Launchers (defined in ssb_kernels.hip).
+template <typename T>
+hipError_t launch_pack(uint4* dst, int n_tiles, int K, int mode, const void* s0, const void* s1, const void* s2,
+                       int n0, int n1, hipStream_t st);
+template <typename T> hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
+template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, int nt, hipStream_t st);
+hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, int n_groups, int ld, int M,
+                         int32_t* tok, float* top1, float* top2, hipStream_t st);
+template <typename T> hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipStream_t st);
+template <typename T>
+hipError_t launch_attn_combine(const float* part, int max_chunks, int n_heads, int head_dim, const int32_t* row_lim,
+                               int M, void* out, int out_ld, hipStream_t st);
+hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs& ra, int eos_id, int32_t* out,
+                         int out_stride, hipStream_t st);
+
+}  // namespace ssb

@@ -1,0 +1,885 @@
+// Host engine and C ABI of the self-speculative round (see include/ssb.h).
+//
+// The engine owns: the packed weights, a fixed workspace (allocated once at
+// init), the KV page allocator and the orchestration of forwards.  Every
+// forward is a fixed sequence of kernel launches on the caller's stream:
+//   prep+embed, then per layer [QKV+RoPE+KV write, attention (+combine),
+//   O + residual, gate|up + SwiGLU, down + residual], then LM head + argmax.
+// A round is draft forward, verify forward, accept, then one device->host
+// copy of the committed tokens (GravityOCR review, section 3.2).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/ssb.h"
+#include "ssb_device.h"
+
+
+using namespace ssb;
+
+namespace {
+
+thread_local std::string g_err;
+
+struct Error {
+  int code;
+  std::string msg;
+};
+
+[[noreturn]] void fail(int code, const std::string& msg) { throw Error{code, msg}; }
+
+void hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) fail(SSB_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <typename F>
+int guard(F&& f) {
+  try {
+    f();
+    return SSB_OK;
+  } catch (const Error& e) {
+    g_err = e.msg;
+    return e.code;
+  } catch (const std::bad_alloc&) {
+    g_err = "host allocation failed";
+    return SSB_ENOMEM;
+  } catch (...) {
+    g_err = "unexpected internal error";
+    return SSB_EINVAL;
+  }
+}
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+constexpr int kOutStride = 4 + SSB_MAX_BLOCK + 2;  // accept record per request
+
+}  // namespace
+
+struct ssb_pool {
+  ssb_model* m;
+  char* base;
+  int n_pages;
+  std::vector<int> free_pages;  // stack of free page ids
+};
+
+struct ssb_kv {
+  ssb_pool* pool;
+  int max_tokens;
+  int max_pages;
+  std::vector<int32_t> pages;   // logical page -> pool page
+  int32_t* pt_dev;              // device page table [max_pages]
+  int32_t* pt_host;             // pinned mirror
+  int seq_len;
+  int32_t x0;
+};
+
+struct GemmShape {
+  const uint4* W;
+  int K, n_groups, S, nt;
+};
+
+struct ssb_model {
+  ssb_config c;
+  int device;
+  int elem;
+  // packed weights
+  void* wmem;
+  const void* embed;
+  const float* final_norm;
+  std::vector<const float*> attn_norm, mlp_norm;
+  std::vector<GemmShape> qkv, o, gu, d;
+  GemmShape lm;
+  float2* rope;
+  // workspace
+  void* ws;
+  float* h;
+  float* ssq;
+  void* q;
+  void* attn;
+  void* act;
+  int32_t *row_tok, *row_pos, *row_lim, *row_req;
+  int32_t* am_tok;
+  float *am_top1, *am_top2;
+  float *amv1, *amv2;
+  int32_t* ami1;
+  float* gpart;
+  int* counters;
+  float* apart;
+  int max_chunks;
+  int max_decode_rows;
+  int32_t* accept_dev;
+  int32_t* tok_dev;
+  // pinned host staging
+  int32_t* pin_i32;   // [max_rows + kMaxReq*kOutStride]
+  float* pin_f32;     // [2*max_rows]
+};
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int split_for(int n_groups, int nchunks) {
+  int target = std::max(1, 256 / n_groups);
+  int s = 1;
+  while (s * 2 <= std::min(target, nchunks)) s *= 2;
+  return s;
+}
+
+void check_config(const ssb_config* c) {
+  if (!c) fail(SSB_EINVAL, "null config");
+  auto req = [](bool ok, const char* m) { if (!ok) fail(SSB_EINVAL, m); };
+  req(c->dtype == SSB_BF16 || c->dtype == SSB_F32, "dtype must be SSB_BF16 or SSB_F32");
+  req(c->n_layers >= 1, "n_layers must be >= 1");
+  req(c->head_dim == 32 || c->head_dim == 64, "head_dim must be 32 or 64");
+  req(c->n_heads >= 1 && c->n_kv_heads >= 1 && c->n_heads % c->n_kv_heads == 0,
+      "n_heads must be a multiple of n_kv_heads");
+  req(c->n_heads / c->n_kv_heads == 1 || c->n_heads / c->n_kv_heads == 4, "n_heads/n_kv_heads must be 1 or 4");
+  req(c->hidden % 128 == 0 && pow2(c->hidden / 128), "hidden must be 128 * 2^k");
+  req((c->n_heads * c->head_dim) % 128 == 0 && pow2(c->n_heads * c->head_dim / 128),
+      "n_heads*head_dim must be 128 * 2^k");
+  req(c->ffn % 128 == 0 && pow2(c->ffn / 128), "ffn must be 128 * 2^k");
+  req(c->vocab >= 2, "vocab must be >= 2");
+  req(c->mask_id >= 0 && c->mask_id < c->vocab, "mask_id out of range");
+  req(c->eos_id >= 0 && c->eos_id < c->vocab && c->eos_id != c->mask_id, "eos_id out of range or == mask_id");
+  req(c->block_B >= 0 && c->block_B <= SSB_MAX_BLOCK, "block_B must be in [0, 64]");
+  req(c->page_tokens == kPage, "page_tokens must be 16");
+  req(c->max_rows >= 1 && c->max_rows <= kMaxTasks * kTaskRows, "max_rows must be in [1, 3072]");
+  req(c->max_rows >= c->block_B + 1, "max_rows must hold one window (block_B + 1 rows)");
+  req(c->max_positions >= 2, "max_positions must be >= 2");
+  req(c->rms_eps >= 0.f && c->rope_theta > 0.f, "bad rms_eps or rope_theta");
+}
+
+template <typename T>
+void pack_all(ssb_model* m, const ssb_weights* w, hipStream_t st) {
+  const ssb_config& c = m->c;
+  const int H = c.hidden, F = c.ffn, qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  for (int l = 0; l < c.n_layers; ++l) {
+    hip_check(launch_pack<T>(const_cast<uint4*>(m->qkv[l].W), (qd + 2 * kvd) / 16, H, 1, w->wq[l], w->wk[l],
+                             w->wv[l], qd, kvd, st), "pack qkv");
+    hip_check(launch_pack<T>(const_cast<uint4*>(m->o[l].W), H / 16, qd, 0, w->wo[l], nullptr, nullptr, H, 0, st),
+              "pack o");
+    hip_check(launch_pack<T>(const_cast<uint4*>(m->gu[l].W), 2 * F / 16, H, 2, w->wg[l], w->wu[l], nullptr, 0, 0,
+                             st), "pack gate/up");
+    hip_check(launch_pack<T>(const_cast<uint4*>(m->d[l].W), H / 16, F, 0, w->wd[l], nullptr, nullptr, H, 0, st),
+              "pack down");
+  }
+  hip_check(launch_pack<T>(const_cast<uint4*>(m->lm.W), m->lm.n_groups * 4, H, 0, w->lm_head, nullptr, nullptr,
+                           c.vocab, 0, st), "pack lm_head");
+}
+
+void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb_model** out) {
+  check_config(cfg);
+  if (!w || !out) fail(SSB_EINVAL, "null weights or output pointer");
+  const ssb_config& c = *cfg;
+  auto* m = new ssb_model();
+  std::unique_ptr<ssb_model> hold(m);
+  m->c = c;
+  hip_check(hipGetDevice(&m->device), "hipGetDevice");
+  m->elem = c.dtype == SSB_BF16 ? 2 : 4;
+  const int H = c.hidden, F = c.ffn, V = c.vocab, L = c.n_layers;
+  const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  const size_t E = m->elem;
+
+  // ---- packed weights ----
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  const size_t o_embed = take((size_t)V * H * E);
+  const size_t o_fnorm = take((size_t)H * 4);
+  std::vector<size_t> o_an(L), o_mn(L), o_qkv(L), o_o(L), o_gu(L), o_d(L);
+  for (int l = 0; l < L; ++l) {
+    o_an[l] = take((size_t)H * 4);
+    o_mn[l] = take((size_t)H * 4);
+    o_qkv[l] = take((size_t)(qd + 2 * kvd) * H * E);
+    o_o[l] = take((size_t)H * qd * E);
+    o_gu[l] = take((size_t)2 * F * H * E);
+    o_d[l] = take((size_t)H * F * E);
+  }
+  const int lm_groups = (V + 63) / 64;
+  const size_t o_lm = take((size_t)lm_groups * 64 * H * E);
+  const size_t o_rope = take((size_t)c.max_positions * (c.head_dim / 2) * sizeof(float2));
+  if (hipMalloc(&m->wmem, off) != hipSuccess) fail(SSB_ENOMEM, "hipMalloc of packed weights failed");
+  char* wb = static_cast<char*>(m->wmem);
+  m->embed = wb + o_embed;
+  m->final_norm = reinterpret_cast<const float*>(wb + o_fnorm);
+  const int hd = c.head_dim;
+  for (int l = 0; l < L; ++l) {
+    m->attn_norm.push_back(reinterpret_cast<const float*>(wb + o_an[l]));
+    m->mlp_norm.push_back(reinterpret_cast<const float*>(wb + o_mn[l]));
+    m->qkv.push_back({reinterpret_cast<const uint4*>(wb + o_qkv[l]), H, c.n_heads + 2 * c.n_kv_heads,
+                      split_for(c.n_heads + 2 * c.n_kv_heads, H / kChunkK), hd / 16});
+    m->o.push_back({reinterpret_cast<const uint4*>(wb + o_o[l]), qd, H / 64, split_for(H / 64, qd / kChunkK), 4});
+    m->gu.push_back({reinterpret_cast<const uint4*>(wb + o_gu[l]), H, 2 * F / 64,
+                     split_for(2 * F / 64, H / kChunkK), 4});
+    m->d.push_back({reinterpret_cast<const uint4*>(wb + o_d[l]), F, H / 64, split_for(H / 64, F / kChunkK), 4});
+  }
+  m->lm = {reinterpret_cast<const uint4*>(wb + o_lm), H, lm_groups, split_for(lm_groups, H / kChunkK), 4};
+  m->rope = reinterpret_cast<float2*>(wb + o_rope);
+
+  hip_check(hipMemcpyAsync(wb + o_embed, w->embed, (size_t)V * H * E, hipMemcpyDeviceToDevice, st), "copy embed");
+  hip_check(hipMemcpyAsync(wb + o_fnorm, w->final_norm, (size_t)H * 4, hipMemcpyDeviceToDevice, st), "copy norm");
+  for (int l = 0; l < L; ++l) {
+    hip_check(hipMemcpyAsync(wb + o_an[l], w->attn_norm[l], (size_t)H * 4, hipMemcpyDeviceToDevice, st), "copy");
+    hip_check(hipMemcpyAsync(wb + o_mn[l], w->mlp_norm[l], (size_t)H * 4, hipMemcpyDeviceToDevice, st), "copy");
+  }
+  if (c.dtype == SSB_BF16) pack_all<bf16_t>(m, w, st);
+  else pack_all<float>(m, w, st);
+
+  // RoPE table: angle = pos * theta^(-2i/hd), computed in double
+  {
+    const int half = hd / 2;
+    std::vector<float2> tab((size_t)c.max_positions * half);
+    for (int p = 0; p < c.max_positions; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / hd);
+        tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
+    hip_check(hipMemcpyAsync(m->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice, st),
+              "copy rope");
+    hip_check(hipStreamSynchronize(st), "init sync");
+  }
+
+  // ---- workspace ----
+  const int MR = c.max_rows;
+  m->max_decode_rows = std::min(MR, SSB_MAX_BATCH * (std::max(c.block_B, 1) + 1));
+  m->max_chunks = (c.max_positions + kKeyChunk - 1) / kKeyChunk;
+  size_t gpart = 0;
+  auto gp = [&](const GemmShape& g) {
+    if (g.S > 1) gpart = std::max(gpart, (size_t)g.S * g.n_groups * 16 * g.nt);
+  };
+  gp(m->qkv[0]); gp(m->o[0]); gp(m->gu[0]); gp(m->d[0]); gp(m->lm);
+  off = 0;
+  const size_t w_h = take((size_t)MR * H * 4);
+  const size_t w_ssq = take((size_t)(H / 64) * MR * 4);
+  const size_t w_q = take((size_t)MR * qd * E);
+  const size_t w_attn = take((size_t)MR * qd * E);
+  const size_t w_act = take((size_t)MR * F * E);
+  const size_t w_meta = take((size_t)4 * MR * 4);
+  const size_t w_am = take((size_t)MR * 12);
+  const size_t w_amp = take((size_t)lm_groups * MR * 12);
+  const size_t w_gpart = take(gpart * MR * 4);
+  const int n_ctr = std::max({c.n_heads + 2 * c.n_kv_heads, H / 64, 2 * F / 64, lm_groups}) * (MR / 16 + 1);
+  const size_t w_ctr = take((size_t)n_ctr * 4);
+  const size_t w_apart = take((size_t)m->max_decode_rows * c.n_heads * m->max_chunks * (hd + 4) * 4);
+  const size_t w_acc = take((size_t)kMaxReq * kOutStride * 4);
+  const size_t w_tok = take((size_t)MR * 4);
+  if (hipMalloc(&m->ws, off) != hipSuccess) fail(SSB_ENOMEM, "hipMalloc of workspace failed");
+  char* wsb = static_cast<char*>(m->ws);
+  m->h = reinterpret_cast<float*>(wsb + w_h);
+  m->ssq = reinterpret_cast<float*>(wsb + w_ssq);
+  m->q = wsb + w_q;
+  m->attn = wsb + w_attn;
+  m->act = wsb + w_act;
+  m->row_tok = reinterpret_cast<int32_t*>(wsb + w_meta);
+  m->row_pos = m->row_tok + MR;
+  m->row_lim = m->row_pos + MR;
+  m->row_req = m->row_lim + MR;
+  m->am_tok = reinterpret_cast<int32_t*>(wsb + w_am);
+  m->am_top1 = reinterpret_cast<float*>(m->am_tok + MR);
+  m->am_top2 = m->am_top1 + MR;
+  m->amv1 = reinterpret_cast<float*>(wsb + w_amp);
+  m->amv2 = m->amv1 + (size_t)lm_groups * MR;
+  m->ami1 = reinterpret_cast<int32_t*>(m->amv2 + (size_t)lm_groups * MR);
+  m->gpart = reinterpret_cast<float*>(wsb + w_gpart);
+  m->counters = reinterpret_cast<int*>(wsb + w_ctr);
+  m->apart = reinterpret_cast<float*>(wsb + w_apart);
+  m->accept_dev = reinterpret_cast<int32_t*>(wsb + w_acc);
+  m->tok_dev = reinterpret_cast<int32_t*>(wsb + w_tok);
+  hip_check(hipMemsetAsync(m->counters, 0, (size_t)n_ctr * 4, st), "zero counters");
+  if (hipHostMalloc(reinterpret_cast<void**>(&m->pin_i32), (size_t)(MR + kMaxReq * kOutStride) * 4,
+                    hipHostMallocDefault) != hipSuccess)
+    fail(SSB_ENOMEM, "pinned host allocation failed");
+  if (hipHostMalloc(reinterpret_cast<void**>(&m->pin_f32), (size_t)2 * MR * 4, hipHostMallocDefault) !=
+      hipSuccess)
+    fail(SSB_ENOMEM, "pinned host allocation failed");
+  hip_check(hipStreamSynchronize(st), "init sync");
+  *out = hold.release();
+}
+
+// ---------------------------------------------------------------------------
+// Forward pass over a row set.
+// ---------------------------------------------------------------------------
+struct FwdSpec {
+  int mode;           // PrepMode
+  int M;              // rows
+  int pos0;           // PREFILL / TOKENS
+  const void* prefix; // PREFILL
+  ReqArgs ra;         // DRAFT / VERIFY (and page tables for all modes)
+  int max_pos;        // largest position of any row + 1
+  float* logits;      // nullable [M][vocab] (all rows) or [1][vocab] (last row only)
+  bool lm_last_only;  // LM head on the last row only (prefill)
+};
+
+template <typename T>
+void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
+  const ssb_config& c = m->c;
+  const int H = c.hidden, qd = c.n_heads * c.head_dim, MR = c.max_rows;
+  const int M = f.M;
+  PrepArgs pa{};
+  pa.mode = f.mode; pa.M = M; pa.hidden = H; pa.vocab = c.vocab; pa.mask_id = c.mask_id;
+  pa.pos0 = f.pos0; pa.prefix = f.prefix; pa.tokens = m->tok_dev; pa.am_prev = m->am_tok;
+  pa.embed = m->embed;
+  pa.row_tok = m->row_tok; pa.row_pos = m->row_pos; pa.row_lim = m->row_lim; pa.row_req = m->row_req;
+  pa.h = m->h; pa.ssq = m->ssq; pa.ssq_ld = MR; pa.req = f.ra;
+  hip_check(launch_prep<T>(pa, st), "prep");
+
+  GemmArgs g{};
+  g.M = M; g.part = m->gpart; g.counters = m->counters;
+  g.ssq = m->ssq; g.ssq_ld = MR; g.n_ssq = H / 64; g.eps = c.rms_eps; g.hidden = H;
+  g.h = m->h; g.h_out = m->h; g.ssq_out = m->ssq;
+  g.n_heads = c.n_heads; g.n_kv = c.n_kv_heads; g.head_dim = c.head_dim; g.n_pages = pool->n_pages;
+  g.kv_pool = pool->base; g.rope = m->rope; g.row_pos = m->row_pos; g.row_req = m->row_req;
+  for (int r = 0; r < kMaxReq; ++r) g.pt[r] = f.ra.pt[r];
+  g.vocab = c.vocab; g.mask_id = c.mask_id;
+
+  AttnArgs at{};
+  at.q = m->q; at.q_ld = qd; at.kv_pool = pool->base; at.n_pages = pool->n_pages;
+  at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads;
+  for (int r = 0; r < kMaxReq; ++r) at.pt[r] = f.ra.pt[r];
+  at.row_lim = m->row_lim; at.part = m->apart; at.max_chunks = m->max_chunks;
+  at.out = m->attn; at.out_ld = qd;
+  at.fold = M > m->max_decode_rows ? 1 : 0;
+  at.scale = 1.0f / std::sqrt((float)c.head_dim);
+  // row tasks: windows of each request (draft/verify) or one request's rows
+  at.tasks.n = 0;
+  auto add_tasks = [&](int req, int row0, int nrows) {
+    for (int r = 0; r < nrows; r += kTaskRows) {
+      if (at.tasks.n >= kMaxTasks) fail(SSB_EINVAL, "too many attention row tasks");
+      at.tasks.t[at.tasks.n++] = AttnTask{req, row0 + r, std::min(kTaskRows, nrows - r)};
+    }
+  };
+  if (f.mode == PREP_DRAFT || f.mode == PREP_VERIFY) {
+    for (int r = 0; r < f.ra.n; ++r) add_tasks(r, f.ra.row0[r], f.ra.B + 1);
+  } else {
+    add_tasks(0, 0, M);
+  }
+  const int chunk_slots = (f.max_pos - 1) / kKeyChunk + 1;
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    g.layer = l;
+    // QKV + RoPE + KV write
+    {
+      GemmArgs a = g;
+      const GemmShape& s = m->qkv[l];
+      a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
+      a.gain = m->attn_norm[l]; a.y = m->q; a.ldy = qd;
+      hip_check(launch_gemm<T>(a, EPI_QKV, s.nt, st), "qkv gemm");
+    }
+    at.layer = l;
+    hip_check(launch_attn<T>(at, chunk_slots, c.head_dim, st), "attention");
+    if (!at.fold)
+      hip_check(launch_attn_combine<T>(m->apart, m->max_chunks, c.n_heads, c.head_dim, m->row_lim, M, m->attn,
+                                       qd, st), "attention combine");
+    {
+      GemmArgs a = g;
+      const GemmShape& s = m->o[l];
+      a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
+      a.x = m->attn; a.ldx = qd;
+      hip_check(launch_gemm<T>(a, EPI_RESID, 4, st), "o gemm");
+    }
+    {
+      GemmArgs a = g;
+      const GemmShape& s = m->gu[l];
+      a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
+      a.gain = m->mlp_norm[l]; a.y = m->act; a.ldy = c.ffn;
+      hip_check(launch_gemm<T>(a, EPI_SWIGLU, 4, st), "gate/up gemm");
+    }
+    {
+      GemmArgs a = g;
+      const GemmShape& s = m->d[l];
+      a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
+      a.x = m->act; a.ldx = c.ffn;
+      hip_check(launch_gemm<T>(a, EPI_RESID, 4, st), "down gemm");
+    }
+  }
+  // LM head + argmax
+  {
+    GemmArgs a = g;
+    const GemmShape& s = m->lm;
+    a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
+    a.gain = m->final_norm; a.logits = f.logits;
+    a.am_v1 = m->amv1; a.am_i1 = m->ami1; a.am_v2 = m->amv2; a.am_ld = MR;
+    int rows = M;
+    int32_t* tok = m->am_tok;
+    float* t1 = m->am_top1;
+    float* t2 = m->am_top2;
+    if (f.lm_last_only) {
+      a.h = m->h + (size_t)(M - 1) * H;
+      a.ssq = m->ssq + (M - 1);
+      a.M = 1;
+      rows = 1;
+    }
+    hip_check(launch_gemm<T>(a, EPI_LOGITS, 4, st), "lm head gemm");
+    hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, s.n_groups, MR, rows, tok, t1, t2, st), "argmax");
+  }
+}
+
+void run_forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
+  if (m->c.dtype == SSB_BF16) forward<bf16_t>(m, pool, f, st);
+  else forward<float>(m, pool, f, st);
+}
+
+// ---------------------------------------------------------------------------
+// KV pages
+// ---------------------------------------------------------------------------
+void kv_ensure(ssb_kv* kv, int n_tokens, hipStream_t st) {
+  if (n_tokens > kv->max_tokens) fail(SSB_ENOKV, "sequence would exceed the kv's max_tokens");
+  const int need = (n_tokens + kPage - 1) / kPage;
+  const int first_new = (int)kv->pages.size();
+  if (need <= first_new) return;
+  ssb_pool* p = kv->pool;
+  if ((int)p->free_pages.size() < need - first_new) fail(SSB_ENOKV, "KV page pool exhausted");
+  for (int i = first_new; i < need; ++i) {
+    const int pg = p->free_pages.back();
+    p->free_pages.pop_back();
+    kv->pages.push_back(pg);
+    kv->pt_host[i] = pg;
+  }
+  hip_check(hipMemcpyAsync(kv->pt_dev + first_new, kv->pt_host + first_new, (size_t)(need - first_new) * 4,
+                           hipMemcpyHostToDevice, st), "page table upload");
+}
+
+// Return pages wholly at positions >= keep_tokens.
+void kv_trim(ssb_kv* kv, int keep_tokens) {
+  const int keep = (keep_tokens + kPage - 1) / kPage;
+  while ((int)kv->pages.size() > keep) {
+    kv->pool->free_pages.push_back(kv->pages.back());
+    kv->pages.pop_back();
+  }
+}
+
+hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+void check_model_kv(ssb_model* m, ssb_kv* kv) {
+  if (!m) fail(SSB_EINVAL, "null model");
+  if (!kv) fail(SSB_EINVAL, "null kv");
+  if (kv->pool->m != m) fail(SSB_EINVAL, "kv belongs to another model");
+  hip_check(hipSetDevice(m->device), "hipSetDevice");
+}
+
+ReqArgs single_req(ssb_kv* kv, int B, int max_commit) {
+  ReqArgs ra{};
+  ra.n = 1;
+  ra.B = B;
+  ra.p[0] = kv->seq_len;
+  ra.x0[0] = kv->x0;
+  ra.row0[0] = 0;
+  ra.max_commit[0] = max_commit;
+  ra.pt[0] = kv->pt_dev;
+  return ra;
+}
+
+void prefill(ssb_model* m, ssb_kv* kv, const void* prefix, int P, int32_t* first, hipStream_t st) {
+  check_model_kv(m, kv);
+  if (!prefix) fail(SSB_EINVAL, "null prefix");
+  if (P < 1) fail(SSB_EINVAL, "P must be >= 1");
+  if (kv->seq_len != 0 || kv->x0 >= 0) fail(SSB_ESTATE, "prefill needs an empty kv");
+  if (P + 1 > m->c.max_positions) fail(SSB_EINVAL, "P exceeds max_positions");
+  kv_ensure(kv, P, st);
+  for (int p0 = 0; p0 < P; p0 += m->c.max_rows) {
+    FwdSpec f{};
+    f.mode = PREP_PREFILL;
+    f.M = std::min(m->c.max_rows, P - p0);
+    f.pos0 = p0;
+    f.prefix = prefix;
+    f.ra = single_req(kv, 0, 1);
+    f.max_pos = p0 + f.M;
+    f.lm_last_only = true;
+    run_forward(m, kv->pool, f, st);
+  }
+  hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, 4, hipMemcpyDeviceToHost, st), "copy token");
+  hip_check(hipStreamSynchronize(st), "prefill sync");
+  const int32_t y1 = m->pin_i32[0];
+  if (y1 < 0 || y1 >= m->c.vocab) fail(SSB_EHIP, "prefill produced no valid token (NaN logits?)");
+  kv->seq_len = P;
+  kv->x0 = y1;
+  if (first) *first = y1;
+}
+
+struct RoundOut {
+  int A, n, next_x0, eos;
+  int32_t tok[SSB_MAX_BLOCK + 2];
+};
+
+// Runs draft + verify + accept for R requests (row windows concatenated).
+void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_commit, const int32_t* planted,
+                const int32_t* const* cont, const int* cont_len, const int* cont_c, const int* astar,
+                float* dlog, float* vlog, RoundOut* out, hipStream_t st) {
+  const ssb_config& c = m->c;
+  if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, 16]");
+  if (B < 0 || B > c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
+  if (R * (B + 1) > c.max_rows) fail(SSB_EINVAL, "R*(B+1) exceeds max_rows");
+  if ((dlog || vlog) && R != 1) fail(SSB_EINVAL, "logits output needs R == 1");
+  ssb_pool* pool = kvs[0]->pool;
+  for (int r = 0; r < R; ++r) {
+    check_model_kv(m, kvs[r]);
+    if (kvs[r]->pool != pool) fail(SSB_EINVAL, "batched kvs must share one pool");
+    if (kvs[r]->x0 < 0) fail(SSB_ESTATE, "round needs a prefilled kv (no boundary token)");
+    if (max_commit[r] < 1) fail(SSB_EINVAL, "max_commit must be >= 1");
+    if (kvs[r]->seq_len + B + 2 > c.max_positions) fail(SSB_ENOKV, "window exceeds max_positions");
+    for (int q = 0; q < r; ++q)
+      if (kvs[q] == kvs[r]) fail(SSB_EINVAL, "the same kv appears twice in a batch");
+  }
+  for (int r = 0; r < R; ++r) kv_ensure(kvs[r], kvs[r]->seq_len + B + 2, st);
+  ReqArgs ra{};
+  ra.n = R;
+  ra.B = B;
+  int maxpos = 0;
+  for (int r = 0; r < R; ++r) {
+    ra.p[r] = kvs[r]->seq_len;
+    ra.x0[r] = kvs[r]->x0;
+    ra.row0[r] = r * (B + 1);
+    ra.max_commit[r] = max_commit[r];
+    ra.pt[r] = kvs[r]->pt_dev;
+    ra.planted[r] = planted ? planted + (size_t)r * B : nullptr;
+    ra.cont[r] = cont ? cont[r] : nullptr;
+    ra.cont_len[r] = cont_len ? cont_len[r] : 0;
+    ra.cont_c[r] = cont_c ? cont_c[r] : 0;
+    ra.astar[r] = astar ? astar[r] : 0;
+    maxpos = std::max(maxpos, ra.p[r] + B + 2);
+  }
+  FwdSpec f{};
+  f.M = R * (B + 1);
+  f.ra = ra;
+  f.max_pos = maxpos;
+  f.mode = PREP_DRAFT;
+  f.logits = dlog;
+  run_forward(m, pool, f, st);
+  f.mode = PREP_VERIFY;
+  f.logits = vlog;
+  run_forward(m, pool, f, st);
+  hip_check(launch_accept(m->row_tok, m->am_tok, ra, c.eos_id, m->accept_dev, kOutStride, st), "accept");
+  hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)R * kOutStride * 4, hipMemcpyDeviceToHost, st),
+            "copy accept");
+  hip_check(hipStreamSynchronize(st), "round sync");
+  for (int r = 0; r < R; ++r) {
+    const int32_t* o = m->pin_i32 + (size_t)r * kOutStride;
+    RoundOut& ro = out[r];
+    ro.A = o[0];
+    ro.n = o[1];
+    ro.next_x0 = o[2];
+    ro.eos = o[3];
+    if (ro.A < 0 || ro.A > B || ro.n < 1 || ro.n > B + 2 || ro.next_x0 < 0 || ro.next_x0 >= c.vocab)
+      fail(SSB_EHIP, "round produced an invalid accept record (NaN logits?)");
+    for (int k = 0; k < ro.n; ++k) ro.tok[k] = o[4 + k];
+    ssb_kv* kv = kvs[r];
+    kv->seq_len = ra.p[r] + ro.A + 2;
+    kv->x0 = ro.next_x0;
+    kv_trim(kv, kv->seq_len + B + 2);
+  }
+}
+
+void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_t st) {
+  check_model_kv(m, kv);
+  if (kv->x0 < 0) fail(SSB_ESTATE, "AR step needs a prefilled kv (no boundary token)");
+  if (kv->seq_len + 1 > m->c.max_positions) fail(SSB_ENOKV, "position exceeds max_positions");
+  kv_ensure(kv, kv->seq_len + 1, st);
+  // an AR step is a draft window with no masks: [x0] at p, keys <= p
+  FwdSpec f{};
+  f.mode = PREP_DRAFT;
+  f.M = 1;
+  f.ra = single_req(kv, 0, 1);
+  f.max_pos = kv->seq_len + 1;
+  f.logits = logits;
+  run_forward(m, kv->pool, f, st);
+  hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, 4, hipMemcpyDeviceToHost, st), "copy token");
+  hip_check(hipStreamSynchronize(st), "ar sync");
+  const int32_t y = m->pin_i32[0];
+  if (y < 0 || y >= m->c.vocab) fail(SSB_EHIP, "AR step produced no valid token (NaN logits?)");
+  kv->seq_len += 1;
+  kv->x0 = y;
+  if (token) *token = y;
+}
+
+double now_us() {
+  return std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* ssb_last_error(void) { return g_err.c_str(); }
+
+int ssb_check_config(const ssb_config* cfg) {
+  return guard([&] { check_config(cfg); });
+}
+
+int ssb_init_model(const ssb_config* cfg, const ssb_weights* w, void* stream, ssb_model** out) {
+  return guard([&] { init_model(cfg, w, S(stream), out); });
+}
+
+void ssb_free_model(ssb_model* m) {
+  if (!m) return;
+  (void)hipSetDevice(m->device);
+  (void)hipDeviceSynchronize();
+  (void)hipFree(m->wmem);
+  (void)hipFree(m->ws);
+  (void)hipHostFree(m->pin_i32);
+  (void)hipHostFree(m->pin_f32);
+  delete m;
+}
+
+int ssb_pool_bytes(const ssb_model* m, int n_pages, size_t* bytes) {
+  return guard([&] {
+    if (!m || !bytes) fail(SSB_EINVAL, "null argument");
+    if (n_pages < 1) fail(SSB_EINVAL, "n_pages must be >= 1");
+    const ssb_config& c = m->c;
+    *bytes = (size_t)c.n_layers * n_pages * 2 * c.n_kv_heads * kPage * c.head_dim * m->elem;
+  });
+}
+
+int ssb_pool_init(ssb_model* m, void* dev_buf, size_t bytes, int n_pages, ssb_pool** out) {
+  return guard([&] {
+    if (!m || !dev_buf || !out) fail(SSB_EINVAL, "null argument");
+    size_t need = 0;
+    if (ssb_pool_bytes(m, n_pages, &need) != SSB_OK) fail(SSB_EINVAL, g_err);
+    if (bytes < need) fail(SSB_EINVAL, "pool buffer smaller than ssb_pool_bytes");
+    if (reinterpret_cast<uintptr_t>(dev_buf) % 256) fail(SSB_EINVAL, "pool buffer must be 256-byte aligned");
+    auto* p = new ssb_pool();
+    p->m = m;
+    p->base = static_cast<char*>(dev_buf);
+    p->n_pages = n_pages;
+    p->free_pages.reserve(n_pages);
+    for (int i = n_pages - 1; i >= 0; --i) p->free_pages.push_back(i);
+    *out = p;
+  });
+}
+
+void ssb_pool_free(ssb_pool* p) { delete p; }
+
+int ssb_pool_free_pages(const ssb_pool* p, int* n_free) {
+  return guard([&] {
+    if (!p || !n_free) fail(SSB_EINVAL, "null argument");
+    *n_free = (int)p->free_pages.size();
+  });
+}
+
+int ssb_kv_create(ssb_pool* p, int max_tokens, ssb_kv** out) {
+  return guard([&] {
+    if (!p || !out) fail(SSB_EINVAL, "null argument");
+    if (max_tokens < 2) fail(SSB_EINVAL, "max_tokens must be >= 2");
+    if (max_tokens > p->m->c.max_positions) fail(SSB_EINVAL, "max_tokens exceeds max_positions");
+    hip_check(hipSetDevice(p->m->device), "hipSetDevice");
+    auto* kv = new ssb_kv();
+    std::unique_ptr<ssb_kv> hold(kv);
+    kv->pool = p;
+    kv->max_tokens = max_tokens;
+    kv->max_pages = (max_tokens + kPage - 1) / kPage;
+    kv->seq_len = 0;
+    kv->x0 = -1;
+    if (hipMalloc(reinterpret_cast<void**>(&kv->pt_dev), (size_t)kv->max_pages * 4) != hipSuccess)
+      fail(SSB_ENOMEM, "page table allocation failed");
+    if (hipHostMalloc(reinterpret_cast<void**>(&kv->pt_host), (size_t)kv->max_pages * 4, hipHostMallocDefault) !=
+        hipSuccess) {
+      (void)hipFree(kv->pt_dev);
+      fail(SSB_ENOMEM, "pinned page table allocation failed");
+    }
+    *out = hold.release();
+  });
+}
+
+void ssb_kv_free(ssb_kv* kv) {
+  if (!kv) return;
+  (void)hipSetDevice(kv->pool->m->device);
+  (void)hipDeviceSynchronize();
+  kv_trim(kv, 0);
+  (void)hipFree(kv->pt_dev);
+  (void)hipHostFree(kv->pt_host);
+  delete kv;
+}
+
+int ssb_kv_reset(ssb_kv* kv) {
+  return guard([&] {
+    if (!kv) fail(SSB_EINVAL, "null kv");
+    kv_trim(kv, 0);
+    kv->seq_len = 0;
+    kv->x0 = -1;
+  });
+}
+
+int ssb_kv_rewind(ssb_kv* kv, int n, int32_t x0) {
+  return guard([&] {
+    if (!kv) fail(SSB_EINVAL, "null kv");
+    if (kv->x0 < 0) fail(SSB_ESTATE, "rewind needs a prefilled kv");
+    if (n < 1 || n > kv->seq_len) fail(SSB_EINVAL, "n must be in [1, current length]");
+    if (x0 < 0 || x0 >= kv->pool->m->c.vocab || x0 == kv->pool->m->c.mask_id) fail(SSB_EINVAL, "bad boundary token");
+    kv->seq_len = n;
+    kv->x0 = x0;
+    kv_trim(kv, n + kv->pool->m->c.block_B + 2);
+  });
+}
+
+int ssb_kv_state(const ssb_kv* kv, int* seq_len, int32_t* x0, int* pages_held) {
+  return guard([&] {
+    if (!kv) fail(SSB_EINVAL, "null kv");
+    if (seq_len) *seq_len = kv->seq_len;
+    if (x0) *x0 = kv->x0;
+    if (pages_held) *pages_held = (int)kv->pages.size();
+  });
+}
+
+int ssb_prefill(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int32_t* first_token, void* stream) {
+  return guard([&] { prefill(m, kv, prefix_dev, P, first_token, S(stream)); });
+}
+
+int ssb_round(ssb_model* m, ssb_kv* kv, int B, int max_commit, const int32_t* planted_dev, int32_t* committed,
+              int32_t* n_committed, int32_t* accept_len, float* draft_logits_dev, float* verify_logits_dev,
+              void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    RoundOut ro{};
+    ssb_kv* kvs[1] = {kv};
+    int mc[1] = {max_commit};
+    round_impl(m, kvs, 1, B, mc, planted_dev, nullptr, nullptr, nullptr, nullptr, draft_logits_dev,
+               verify_logits_dev, &ro, S(stream));
+    if (committed) std::memcpy(committed, ro.tok, (size_t)ro.n * 4);
+    if (n_committed) *n_committed = ro.n;
+    if (accept_len) *accept_len = ro.A;
+  });
+}
+
+int ssb_ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits_dev, void* stream) {
+  return guard([&] { ar_step(m, kv, token, logits_dev, S(stream)); });
+}
+
+int ssb_decode(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int B, int max_len, const int32_t* cont_dev,
+               int cont_len, const int32_t* astar, int n_astar, int32_t* out, int32_t* n_out, ssb_stats* stats,
+               void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    if (max_len < 0) fail(SSB_EINVAL, "max_len must be >= 0");
+    if (max_len > 0 && !out) fail(SSB_EINVAL, "null output buffer");
+    if (B < 0 || B > m->c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
+    if (cont_dev && cont_len < 0) fail(SSB_EINVAL, "negative cont_len");
+    ssb_stats st{};
+    int n = 0;
+    if (max_len > 0) {
+      const double t0 = now_us();
+      int32_t y1 = 0;
+      prefill(m, kv, prefix_dev, P, &y1, S(stream));
+      const double t1 = now_us();
+      st.prefill_us = t1 - t0;
+      out[n++] = y1;
+      bool done = y1 == m->c.eos_id || n >= max_len;
+      int k = 0;
+      while (!done) {
+        RoundOut ro{};
+        ssb_kv* kvs[1] = {kv};
+        int mc[1] = {max_len - n};
+        const bool plant = cont_dev && astar && k < n_astar;
+        const int32_t* conts[1] = {cont_dev};
+        int cl[1] = {cont_len}, cc[1] = {n}, as[1] = {plant ? astar[k] : 0};
+        round_impl(m, kvs, 1, B, mc, nullptr, plant ? conts : nullptr, plant ? cl : nullptr, plant ? cc : nullptr,
+                   plant ? as : nullptr, nullptr, nullptr, &ro, S(stream));
+        for (int i = 0; i < ro.n; ++i) out[n++] = ro.tok[i];
+        st.rounds += 1;
+        st.forwards += 2;
+        st.accepted += ro.A;
+        done = ro.eos || n >= max_len;
+        ++k;
+      }
+      st.decode_us = now_us() - t1;
+    }
+    st.tokens = n;
+    if (n_out) *n_out = n;
+    if (stats) *stats = st;
+  });
+}
+
+int ssb_decode_ar(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int max_len, int32_t* out, int32_t* n_out,
+                  ssb_stats* stats, void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    if (max_len < 0) fail(SSB_EINVAL, "max_len must be >= 0");
+    if (max_len > 0 && !out) fail(SSB_EINVAL, "null output buffer");
+    ssb_stats st{};
+    int n = 0;
+    if (max_len > 0) {
+      const double t0 = now_us();
+      int32_t y = 0;
+      prefill(m, kv, prefix_dev, P, &y, S(stream));
+      const double t1 = now_us();
+      st.prefill_us = t1 - t0;
+      out[n++] = y;
+      while (y != m->c.eos_id && n < max_len) {
+        ar_step(m, kv, &y, nullptr, S(stream));
+        out[n++] = y;
+        st.rounds += 1;
+        st.forwards += 1;
+      }
+      st.decode_us = now_us() - t1;
+    }
+    st.tokens = n;
+    if (n_out) *n_out = n;
+    if (stats) *stats = st;
+  });
+}
+
+int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_t* max_commit,
+                    const int32_t* planted_dev, int32_t* committed, int32_t* n_committed, int32_t* accept_len,
+                    void* stream) {
+  return guard([&] {
+    if (!m || !kvs || !max_commit) fail(SSB_EINVAL, "null argument");
+    if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, 16]");
+    for (int r = 0; r < R; ++r)
+      if (!kvs[r]) fail(SSB_EINVAL, "null kv in batch");
+    std::vector<RoundOut> ro(R);
+    std::vector<int> mc(max_commit, max_commit + R);
+    round_impl(m, kvs, R, B, mc.data(), planted_dev, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+               ro.data(), S(stream));
+    for (int r = 0; r < R; ++r) {
+      if (committed) std::memcpy(committed + (size_t)r * (B + 2), ro[r].tok, (size_t)ro[r].n * 4);
+      if (n_committed) n_committed[r] = ro[r].n;
+      if (accept_len) accept_len[r] = ro[r].A;
+    }
+  });
+}
+
+int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, int p, float* logits_dev,
+                       int32_t* argmax, float* top1, float* top2, void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    if (!tokens || !argmax) fail(SSB_EINVAL, "null tokens or argmax");
+    if (M < 1 || M > m->c.max_rows) fail(SSB_EINVAL, "M must be in [1, max_rows]");
+    if (p < 0 || p > kv->seq_len) fail(SSB_EINVAL, "p must be within the committed length");
+    if (p + M > m->c.max_positions) fail(SSB_ENOKV, "positions exceed max_positions");
+    for (int i = 0; i < M; ++i)
+      if (tokens[i] < 0 || tokens[i] >= m->c.vocab) fail(SSB_EINVAL, "token id out of range");
+    hipStream_t st = S(stream);
+    kv_ensure(kv, p + M, st);
+    std::memcpy(m->pin_i32, tokens, (size_t)M * 4);
+    hip_check(hipMemcpyAsync(m->tok_dev, m->pin_i32, (size_t)M * 4, hipMemcpyHostToDevice, st), "upload tokens");
+    FwdSpec f{};
+    f.mode = PREP_TOKENS;
+    f.M = M;
+    f.pos0 = p;
+    f.ra = single_req(kv, 0, 1);
+    f.max_pos = p + M;
+    f.logits = logits_dev;
+    run_forward(m, kv->pool, f, st);
+    hip_check(hipStreamSynchronize(st), "sync before reuse of staging");
+    hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, (size_t)M * 4, hipMemcpyDeviceToHost, st), "copy argmax");
+    hip_check(hipMemcpyAsync(m->pin_f32, m->am_top1, (size_t)M * 4, hipMemcpyDeviceToHost, st), "copy top1");
+    hip_check(hipMemcpyAsync(m->pin_f32 + m->c.max_rows, m->am_top2, (size_t)M * 4, hipMemcpyDeviceToHost, st),
+              "copy top2");
+    hip_check(hipStreamSynchronize(st), "forward sync");
+    std::memcpy(argmax, m->pin_i32, (size_t)M * 4);
+    if (top1) std::memcpy(top1, m->pin_f32, (size_t)M * 4);
+    if (top2) std::memcpy(top2, m->pin_f32 + m->c.max_rows, (size_t)M * 4);
+    // positions beyond the committed length hold no committed state
+    kv_trim(kv, std::max(kv->seq_len + m->c.block_B + 2, 0));
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,220 @@
+"""Python binding of the HIP engine: marshals arguments into the C ABI.
+
+PyTorch only provides device memory (weights, KV page pool, prefixes,
+logits buffers) and the current stream; every step of the decoding path
+runs in the library's HIP kernels.  The calls mirror include/ssb.h.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+byref = ctypes.byref
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _i32(n):
+    return (ctypes.c_int32 * max(n, 1))()
+
+
+def torch_dtype(cfg):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+class Model:
+    """A decoder on the GPU: packed weights plus the engine's fixed workspace."""
+
+    def __init__(self, cfg, weights, block_B, max_rows=2048, max_positions=8192, device="cuda:0"):
+        self.lib = L.load()
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.block_B = block_B
+        self.max_rows = max_rows
+        self.max_positions = max_positions
+        dt = torch_dtype(cfg)
+        with torch.cuda.device(self.device):
+            dev = lambda a, d=dt: torch.from_numpy(np.ascontiguousarray(a)).to(self.device).to(d)
+            keep = []
+
+            def put(name, d=dt):
+                t = dev(weights[name], d)
+                keep.append(t)
+                return t.data_ptr()
+
+            def arr(leaf, d=dt):
+                return (ctypes.c_void_p * cfg.n_layers)(*[put(f"layers.{l}.{leaf}", d)
+                                                          for l in range(cfg.n_layers)])
+
+            w = L.SsbWeights()
+            w.embed = put("embed")
+            w.lm_head = put("lm_head")
+            w.final_norm = put("final_norm", torch.float32)
+            arrays = {k: arr(k, torch.float32 if k.endswith("norm") else dt)
+                      for k in ("attn_norm", "mlp_norm", "wq", "wk", "wv", "wo", "wg", "wu", "wd")}
+            for k, v in arrays.items():
+                setattr(w, k, ctypes.cast(v, ctypes.POINTER(ctypes.c_void_p)))
+            self.config = self.make_config(cfg, block_B, max_rows, max_positions)
+            h = ctypes.c_void_p()
+            L.check(self.lib.ssb_init_model(byref(self.config), byref(w), _stream(), byref(h)))
+            torch.cuda.current_stream().synchronize()
+            del keep
+        self.h = h
+
+    @staticmethod
+    def make_config(cfg, block_B, max_rows, max_positions):
+        c = L.SsbConfig()
+        for k in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
+                  "mask_id", "eos_id"):
+            setattr(c, k, getattr(cfg, k))
+        c.block_B = block_B
+        c.page_tokens = 16
+        c.max_rows = max_rows
+        c.max_positions = max_positions
+        c.rms_eps = cfg.rms_eps
+        c.rope_theta = cfg.rope_theta
+        c.dtype = L.SSB_BF16 if cfg.dtype == "bf16" else L.SSB_F32
+        return c
+
+    def prefix_tensor(self, prefix):
+        """Upload prefix embeddings [P][hidden] in the model dtype."""
+        return torch.from_numpy(np.ascontiguousarray(prefix, dtype=np.float32)).to(self.device).to(
+            torch_dtype(self.cfg))
+
+    def close(self):
+        if self.h:
+            self.lib.ssb_free_model(self.h)
+            self.h = None
+
+
+class Pool:
+    """KV page pool in a torch-owned device buffer."""
+
+    def __init__(self, model, n_pages):
+        self.model = model
+        self.lib = model.lib
+        nb = ctypes.c_size_t()
+        L.check(self.lib.ssb_pool_bytes(model.h, n_pages, byref(nb)))
+        self.buf = torch.empty(nb.value, dtype=torch.uint8, device=model.device)
+        self.n_pages = n_pages
+        h = ctypes.c_void_p()
+        L.check(self.lib.ssb_pool_init(model.h, _ptr(self.buf), nb.value, n_pages, byref(h)))
+        self.h = h
+
+    def free_pages(self):
+        n = ctypes.c_int()
+        L.check(self.lib.ssb_pool_free_pages(self.h, byref(n)))
+        return n.value
+
+    def close(self):
+        if self.h:
+            self.lib.ssb_pool_free(self.h)
+            self.h = None
+
+
+class KV:
+    """One sequence's KV cache and decode state."""
+
+    def __init__(self, pool, max_tokens):
+        self.pool = pool
+        self.model = pool.model
+        self.lib = pool.lib
+        h = ctypes.c_void_p()
+        L.check(self.lib.ssb_kv_create(pool.h, max_tokens, byref(h)))
+        self.h = h
+
+    def close(self):
+        if self.h:
+            self.lib.ssb_kv_free(self.h)
+            self.h = None
+
+    def reset(self):
+        L.check(self.lib.ssb_kv_reset(self.h))
+
+    def rewind(self, n, x0):
+        L.check(self.lib.ssb_kv_rewind(self.h, n, x0))
+
+    def state(self):
+        n, x0, pages = ctypes.c_int(), ctypes.c_int32(), ctypes.c_int()
+        L.check(self.lib.ssb_kv_state(self.h, byref(n), byref(x0), byref(pages)))
+        return n.value, x0.value, pages.value
+
+    def prefill(self, prefix_dev):
+        y = ctypes.c_int32()
+        L.check(self.lib.ssb_prefill(self.model.h, self.h, _ptr(prefix_dev), prefix_dev.shape[0], byref(y),
+                                     _stream()))
+        return y.value
+
+    def round(self, B, max_commit=None, planted_dev=None, want_logits=False):
+        """One draft/verify/accept round; returns (committed, A, draft_logits, verify_logits)."""
+        max_commit = B + 2 if max_commit is None else max_commit
+        out = _i32(B + 2)
+        n, A = ctypes.c_int32(), ctypes.c_int32()
+        dl = vl = None
+        if want_logits:
+            V = self.model.cfg.vocab
+            dl = torch.empty((B + 1, V), dtype=torch.float32, device=self.model.device)
+            vl = torch.empty((B + 1, V), dtype=torch.float32, device=self.model.device)
+        L.check(self.lib.ssb_round(self.model.h, self.h, B, max_commit, _ptr(planted_dev), out, byref(n),
+                                   byref(A), _ptr(dl), _ptr(vl), _stream()))
+        return list(out[: n.value]), A.value, dl, vl
+
+    def ar_step(self, want_logits=False):
+        y = ctypes.c_int32()
+        lg = None
+        if want_logits:
+            lg = torch.empty((self.model.cfg.vocab,), dtype=torch.float32, device=self.model.device)
+        L.check(self.lib.ssb_ar_step(self.model.h, self.h, byref(y), _ptr(lg), _stream()))
+        return y.value, lg
+
+    def forward_tokens(self, tokens, p, want_logits=False):
+        M = len(tokens)
+        toks = (ctypes.c_int32 * M)(*[int(t) for t in tokens])
+        am = _i32(M)
+        t1 = (ctypes.c_float * M)()
+        t2 = (ctypes.c_float * M)()
+        lg = None
+        if want_logits:
+            lg = torch.empty((M, self.model.cfg.vocab), dtype=torch.float32, device=self.model.device)
+        L.check(self.lib.ssb_forward_tokens(self.model.h, self.h, toks, M, p, _ptr(lg), am, t1, t2, _stream()))
+        return list(am[:M]), np.array(t1[:M]), np.array(t2[:M]), lg
+
+    def decode(self, prefix_dev, B, max_len, cont_dev=None, astar=None):
+        out = _i32(max_len)
+        n = ctypes.c_int32()
+        st = L.SsbStats()
+        na = 0 if astar is None else len(astar)
+        astar_c = (ctypes.c_int32 * max(na, 1))(*([int(a) for a in astar] if astar is not None else [0]))
+        L.check(self.lib.ssb_decode(self.model.h, self.h, _ptr(prefix_dev), prefix_dev.shape[0], B, max_len,
+                                    _ptr(cont_dev), 0 if cont_dev is None else cont_dev.shape[0],
+                                    astar_c if na else None, na, out, byref(n), byref(st), _stream()))
+        return list(out[: n.value]), st
+
+    def decode_ar(self, prefix_dev, max_len):
+        out = _i32(max_len)
+        n = ctypes.c_int32()
+        st = L.SsbStats()
+        L.check(self.lib.ssb_decode_ar(self.model.h, self.h, _ptr(prefix_dev), prefix_dev.shape[0], max_len, out,
+                                       byref(n), byref(st), _stream()))
+        return list(out[: n.value]), st
+
+
+def round_batch(model, kvs, B, max_commit, planted_dev=None):
+    """One batched round over R requests; returns [(committed, A)] per request."""
+    R = len(kvs)
+    hs = (ctypes.c_void_p * R)(*[kv.h.value for kv in kvs])
+    mc = (ctypes.c_int32 * R)(*[int(x) for x in max_commit])
+    out = _i32(R * (B + 2))
+    n = _i32(R)
+    A = _i32(R)
+    L.check(model.lib.ssb_round_batch(model.h, hs, R, B, mc, _ptr(planted_dev), out, n, A, _stream()))
+    return [(list(out[r * (B + 2): r * (B + 2) + n[r]]), A[r]) for r in range(R)]

@@ -14,12 +14,18 @@ import numpy as np
 
 
 def bf16_round(a):
-    """Round float32 values to the nearest bfloat16 (ties to even), as float32."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = (u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)
-    return u.astype(np.uint32).view(np.float32)
+    """Round float32 values to the nearest bfloat16 (ties to even), as float32.
+
+    Works on the bit pattern: add 0x7FFF plus the lowest kept bit, then clear
+    the low 16 bits (no overflow for finite inputs).
+    """
+    a = np.array(a, dtype=np.float32, copy=True, order="C")
+    u = a.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return a
 
 
 def weight_names(cfg):

@@ -1,0 +1,215 @@
+"""GPU parity of the tiny fp32 decoder (2 layers, hidden 128, vocab 512, B = 8)
+against the CPU oracle, through the C ABI.
+
+Bars: logits within max-abs 2e-2 of the float64 oracle (fp32 arithmetic
+lands far inside); accept lengths and committed tokens exact given the same
+drafts; free-running greedy output identical to the oracle on >= 99% of
+the 200 seeded prefixes, any divergence at an oracle top-2 margin < 1e-2;
+GPU self-spec identical to GPU AR on every seed.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from ssb_inputs import generate_weights, prefix_embeddings, workload
+from oracle import (Decoder, ar_decode, build_plant, prefill, spec_round, teacher_forced_argmax)
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_TOL = 2e-2
+NEAR_TIE = 1e-2
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    from self_speculative_block_amd.engine import Model, Pool
+    wl = workload(1)
+    cfg = wl.model
+    w = generate_weights(cfg)
+    model = Model(cfg, w, block_B=wl.block, max_rows=256, max_positions=256)
+    pool = Pool(model, n_pages=64)
+    yield wl, cfg, w, model, pool, Decoder(cfg, w)
+    pool.close()
+    model.close()
+
+
+def _kv(pool, n=200):
+    from self_speculative_block_amd.engine import KV
+    return KV(pool, n)
+
+
+def test_teacher_forced_logits_match_oracle(tiny):
+    wl, cfg, w, model, pool, orc = tiny
+    for s in (0, 1, 2):
+        pre = prefix_embeddings(wl.wid, s, wl.prefix_len, cfg.hidden)
+        toks = ar_decode(orc, pre, 40)
+        kv = _kv(pool)
+        y1 = kv.prefill(model.prefix_tensor(pre))
+        am, t1, t2, lg = kv.forward_tokens(toks[:-1], wl.prefix_len, want_logits=True)
+        kv.close()
+        P = wl.prefix_len
+        h = np.concatenate([pre.astype(np.float64), orc.embed_tokens(toks[:-1])], axis=0)
+        pos = np.arange(P + len(toks) - 1)
+        ref = orc.forward(orc.new_cache(len(pos)), h, pos, pos[None, :] <= pos[:, None])
+        ref = ref[P:]
+        got = lg.cpu().numpy()
+        err = np.abs(got - ref).max()
+        assert err < LOGIT_TOL, err
+        assert err < 1e-4, f"fp32 path drifted: {err}"
+        np.testing.assert_array_equal(t1, np.delete(got, cfg.mask_id, axis=1).max(axis=1))
+        assert y1 == toks[0]
+
+
+def test_round_logits_and_accept_match_oracle(tiny):
+    wl, cfg, w, model, pool, orc = tiny
+    B = wl.block
+    for s in range(4):
+        pre = prefix_embeddings(wl.wid, s, wl.prefix_len, cfg.hidden)
+        kv = _kv(pool)
+        kv.prefill(model.prefix_tensor(pre))
+        st, _, _ = prefill(orc, pre, wl.prefix_len + 40)
+        for k in range(3):
+            committed, A, dl, vl = kv.round(B, want_logits=True)
+            r = spec_round(orc, st, B, keep_logits=True)
+            assert np.abs(dl.cpu().numpy() - r.draft_logits).max() < LOGIT_TOL
+            assert np.abs(vl.cpu().numpy() - r.verify_logits).max() < LOGIT_TOL
+            assert committed == r.committed and A == r.A
+            n, x0, _ = kv.state()
+            assert (n, x0) == (st.n, st.x0)
+        kv.close()
+
+
+def test_free_running_identity_and_gpu_spec_equals_gpu_ar(tiny):
+    wl, cfg, w, model, pool, orc = tiny
+    same = 0
+    for s in range(wl.n_regions):
+        pre = prefix_embeddings(wl.wid, s, wl.prefix_len, cfg.hidden)
+        pre_dev = model.prefix_tensor(pre)
+        kv = _kv(pool)
+        spec, st = kv.decode(pre_dev, wl.block, wl.max_len)
+        kv.reset()
+        ar, _ = kv.decode_ar(pre_dev, wl.max_len)
+        kv.close()
+        assert spec == ar, f"seed {s}: GPU self-spec differs from GPU AR"
+        ref = ar_decode(orc, pre, wl.max_len)
+        if spec == ref:
+            same += 1
+        else:
+            k = next(i for i, (a, b) in enumerate(zip(spec + [-1], ref + [-2])) if a != b)
+            _, margins = teacher_forced_argmax(orc, pre, ref[: k + 1])
+            assert margins[k] < NEAR_TIE, f"seed {s}: divergence at {k} with oracle margin {margins[k]}"
+    assert same >= 0.99 * wl.n_regions, same
+
+
+def test_planted_accept_lengths_realized_exactly(tiny):
+    wl, cfg, w, model, pool, orc = tiny
+    B = wl.block
+    for s in range(3):
+        pre = prefix_embeddings(wl.wid, s, wl.prefix_len, cfg.hidden)
+        pre_dev = model.prefix_tensor(pre)
+        kv = _kv(pool)
+        cont, _ = kv.decode_ar(pre_dev, 150)
+        kv.reset()
+        kv.prefill(pre_dev)
+        out = [cont[0]]
+        for k in range(B + 1):
+            astar = (k + s) % (B + 1)
+            plant = build_plant(cont, len(out), astar, B, cfg.vocab, cfg.mask_id)
+            pl = torch.tensor(plant, dtype=torch.int32, device=model.device)
+            committed, A, _, _ = kv.round(B, planted_dev=pl)
+            assert A == astar
+            assert committed == cont[len(out): len(out) + A + 2]
+            out += committed
+        kv.close()
+
+
+def test_decode_with_planted_continuation_matches_ar(tiny):
+    wl, cfg, w, model, pool, orc = tiny
+    B = wl.block
+    pre = prefix_embeddings(wl.wid, 9, wl.prefix_len, cfg.hidden)
+    pre_dev = model.prefix_tensor(pre)
+    kv = _kv(pool)
+    cont, _ = kv.decode_ar(pre_dev, 64)
+    kv.reset()
+    cont_dev = torch.tensor(cont, dtype=torch.int32, device=model.device)
+    astar = [B, 0, 3, B, 7, 1, 5, B, 2, 6]
+    out, st = kv.decode(pre_dev, B, 64, cont_dev=cont_dev, astar=astar)
+    kv.close()
+    assert out == cont
+    assert st.forwards == 2 * st.rounds
+
+
+def test_eos_and_max_len(tiny):
+    from self_speculative_block_amd.engine import KV, Model, Pool
+    wl, cfg, w, model, pool, orc = tiny
+    pre = prefix_embeddings(wl.wid, 11, wl.prefix_len, cfg.hidden)
+    pre_dev = model.prefix_tensor(pre)
+    kv = _kv(pool)
+    full, _ = kv.decode_ar(pre_dev, 40)
+    kv.reset()
+    for max_len in (0, 1, 2, 3, 9, 10, 11, 17):
+        spec, _ = kv.decode(pre_dev, wl.block, max_len)
+        kv.reset()
+        assert spec == full[:max_len]
+    kv.close()
+    eos = full[9]
+    cfg2 = dataclasses.replace(cfg, eos_id=eos)
+    m2 = Model(cfg2, w, block_B=wl.block, max_rows=64, max_positions=256)
+    p2 = Pool(m2, n_pages=16)
+    kv2 = KV(p2, 200)
+    for B in (0, 1, 4, 8):
+        spec, _ = kv2.decode(m2.prefix_tensor(pre), B, 40)
+        kv2.reset()
+        assert spec == full[: full.index(eos) + 1]
+    kv2.close()
+    p2.close()
+    m2.close()
+
+
+def test_error_paths(tiny):
+    from self_speculative_block_amd import SsbError, SSB_ESTATE, SSB_EINVAL, SSB_ENOKV
+    from self_speculative_block_amd.engine import KV
+    wl, cfg, w, model, pool, orc = tiny
+    kv = _kv(pool)
+    with pytest.raises(SsbError) as e:
+        kv.round(wl.block)
+    assert e.value.code == SSB_ESTATE
+    pre_dev = model.prefix_tensor(prefix_embeddings(wl.wid, 0, wl.prefix_len, cfg.hidden))
+    kv.prefill(pre_dev)
+    with pytest.raises(SsbError) as e:
+        kv.prefill(pre_dev)
+    assert e.value.code == SSB_ESTATE
+    with pytest.raises(SsbError) as e:
+        kv.round(wl.block + 1)
+    assert e.value.code == SSB_EINVAL
+    with pytest.raises(SsbError) as e:
+        kv.round(wl.block, max_commit=0)
+    assert e.value.code == SSB_EINVAL
+    n0 = kv.state()
+    assert n0[0] == wl.prefix_len
+    kv.close()
+    small = KV(pool, wl.prefix_len + 4)
+    small.prefill(pre_dev)
+    with pytest.raises(SsbError) as e:
+        small.round(wl.block)
+    assert e.value.code == SSB_ENOKV
+    assert small.state()[0] == wl.prefix_len          # state unchanged on error
+    small.close()
+    from self_speculative_block_amd.engine import Pool
+    tiny_pool = Pool(model, n_pages=6)                 # 96 positions
+    kv = KV(tiny_pool, 200)
+    kv.prefill(pre_dev)
+    with pytest.raises(SsbError) as e:
+        for _ in range(40):
+            kv.round(wl.block)
+    assert e.value.code == SSB_ENOKV
+    n_before = kv.state()[0]
+    with pytest.raises(SsbError):
+        kv.round(wl.block)
+    assert kv.state()[0] == n_before                 # state unchanged on error
+    kv.close()
+    assert tiny_pool.free_pages() == 6
+    tiny_pool.close()
