@@ -110,7 +110,7 @@ def test_planted_accept_lengths_realized_exactly(tiny):
     for s in range(3):
         pre = prefix_embeddings(wl.wid, s, wl.prefix_len, cfg.hidden)
         pre_dev = model.prefix_tensor(pre)
-        kv = _kv(pool)
+        kv = _kv(pool, 256)
         cont, _ = kv.decode_ar(pre_dev, 150)
         kv.reset()
         kv.prefill(pre_dev)
