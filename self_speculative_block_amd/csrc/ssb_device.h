@@ -3,8 +3,8 @@
 // Numerics contract (holds for every kernel here): the value computed for one
 // row never depends on how many rows share the launch, on the row's slot in
 // the window, or on how work is split across workgroups.  Reductions run in a
-// fixed order over fixed absolute structures (128-wide K chunks in GEMMs,
-// 64-key position chunks in attention, vocabulary groups in the argmax); no
+// fixed order over fixed structures (per-wave K slices in GEMMs, 64-key
+// position chunks in attention, vocabulary tiles in the argmax); no
 // floating-point atomics are used.  Consequently the verify rows of a round
 // reproduce an AR step at the same position bit for bit, which is what makes
 // greedy self-speculative output identical to greedy AR output on the GPU as
@@ -21,13 +21,12 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kWave = 64;
 constexpr int kThreads = 256;      // 4 waves per workgroup
-constexpr int kChunkK = 128;       // fixed K chunk of every GEMM reduction
 constexpr int kKeyChunk = 64;      // fixed key chunk of attention (absolute positions)
 constexpr int kPage = 16;          // tokens per KV page
-constexpr int kNormGroup = 64;     // columns per sum-of-squares partial of the residual
 constexpr int kMaxReq = 16;        // requests per batched launch
 constexpr int kMaxTasks = 64;      // attention row tasks per launch
 constexpr int kTaskRows = 48;      // rows per attention task (3 MFMA row tiles)
+constexpr int kMaxNormParts = 128; // per-16-column norm partials (hidden <= 2048)
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ bf16_t f2bf(float f) {
@@ -85,7 +84,7 @@ struct ReqArgs {
   int astar[kMaxReq];                 // planted accept length (continuation mode)
 };
 
-struct AttnTask { int req, row0, nrows; };
+struct AttnTask { int req, row0, nrows, max_lim; };
 struct AttnTasks { int n; AttnTask t[kMaxTasks]; };
 
 
@@ -99,25 +98,24 @@ struct PrepArgs {
   const int32_t* tokens;       // TOKENS: device [M]
   const int32_t* am_prev;      // VERIFY: argmax rows of the draft forward
   const void* embed;           // [vocab][hidden] of T
+  const float* gain;           // attn_norm gain of layer 0
   int32_t* row_tok; int32_t* row_pos; int32_t* row_lim; int32_t* row_req;
-  float* h; float* ssq; int ssq_ld;
+  float* h; void* xg; float* ssq; int ssq_ld;
   ReqArgs req;
 };
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
 struct GemmArgs {
-  const uint4* W; int K; int n_groups; int M; int S;
-  const float* h; const float* gain;           // RMSNorm input (QKV, SWIGLU, LOGITS)
-  const void* x; int ldx;                       // plain input (RESID)
-  float* part; int* counters;                   // split-K sums and tickets
-  const float* ssq; int ssq_ld; int n_ssq; float eps; int hidden;
-  float* h_out; float* ssq_out;                 // RESID
-  void* y; int ldy;                             // SWIGLU act / QKV q
-  int n_heads, n_kv, head_dim, layer, n_pages;  // QKV
+  const uint4* W; int K; int n_tiles; int M;
+  const void* x; int ldx;                       // input rows [M][ldx] of T
+  const float* ssq; int ssq_ld; int n_ssq; float eps; int hidden;   // 1/rms row scale (norm inputs)
+  float* h; const float* gain_next; void* xg_out; float* ssq_out;   // RESID: residual, next input
+  void* q; int q_ld; int n_heads, n_kv, head_dim, layer, n_pages;   // QKV
   void* kv_pool; const float2* rope;
   const int32_t* row_pos; const int32_t* row_req;
   const int32_t* pt[kMaxReq];
+  void* act; int act_ld;                        // SWIGLU
   float* logits; int vocab; int mask_id;        // LOGITS
   float* am_v1; int32_t* am_i1; float* am_v2; int am_ld;
 };
@@ -137,9 +135,9 @@ struct AttnArgs {
 // Launchers (defined in ssb_kernels.hip).
 template <typename T>
 hipError_t launch_pack(uint4* dst, int n_tiles, int K, int mode, const void* s0, const void* s1, const void* s2,
-                       int n0, int n1, hipStream_t st);
+                       int n0, int n1, int hd, hipStream_t st);
 template <typename T> hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
-template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, int nt, hipStream_t st);
+template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, int kpw, hipStream_t st);
 hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, int n_groups, int ld, int M,
                          int32_t* tok, float* top1, float* top2, hipStream_t st);
 template <typename T> hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipStream_t st);

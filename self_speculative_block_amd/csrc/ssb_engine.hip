@@ -83,7 +83,7 @@ struct ssb_kv {
 
 struct GemmShape {
   const uint4* W;
-  int K, n_groups, S, nt;
+  int K, n_tiles, kpw;   // reduction length, 16-column tiles, K steps per wave
 };
 
 struct ssb_model {
@@ -101,6 +101,7 @@ struct ssb_model {
   // workspace
   void* ws;
   float* h;
+  void* xg;
   float* ssq;
   void* q;
   void* attn;
@@ -110,8 +111,6 @@ struct ssb_model {
   float *am_top1, *am_top2;
   float *amv1, *amv2;
   int32_t* ami1;
-  float* gpart;
-  int* counters;
   float* apart;
   int max_chunks;
   int max_decode_rows;
@@ -126,11 +125,10 @@ namespace {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int split_for(int n_groups, int nchunks) {
-  int target = std::max(1, 256 / n_groups);
-  int s = 1;
-  while (s * 2 <= std::min(target, nchunks)) s *= 2;
-  return s;
+// K steps per wave: 8 waves per workgroup up to K = 8 * 8 steps, then 16
+int kpw_for(int K, int elem) {
+  const int ksteps = K / (elem == 2 ? 32 : 16);
+  return std::max(1, std::min(8, ksteps / 8));
 }
 
 void check_config(const ssb_config* c) {
@@ -146,6 +144,10 @@ void check_config(const ssb_config* c) {
   req((c->n_heads * c->head_dim) % 128 == 0 && pow2(c->n_heads * c->head_dim / 128),
       "n_heads*head_dim must be 128 * 2^k");
   req(c->ffn % 128 == 0 && pow2(c->ffn / 128), "ffn must be 128 * 2^k");
+  req(c->hidden <= 16 * kMaxNormParts, "hidden above 2048 is not supported");
+  req(c->ffn <= (c->dtype == SSB_BF16 ? 4096 : 2048) && c->hidden <= (c->dtype == SSB_BF16 ? 4096 : 2048) &&
+          c->n_heads * c->head_dim <= (c->dtype == SSB_BF16 ? 4096 : 2048),
+      "reduction lengths above 4096 (bf16) / 2048 (f32) are not supported");
   req(c->vocab >= 2, "vocab must be >= 2");
   req(c->mask_id >= 0 && c->mask_id < c->vocab, "mask_id out of range");
   req(c->eos_id >= 0 && c->eos_id < c->vocab && c->eos_id != c->mask_id, "eos_id out of range or == mask_id");
@@ -163,16 +165,16 @@ void pack_all(ssb_model* m, const ssb_weights* w, hipStream_t st) {
   const int H = c.hidden, F = c.ffn, qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
   for (int l = 0; l < c.n_layers; ++l) {
     hip_check(launch_pack<T>(const_cast<uint4*>(m->qkv[l].W), (qd + 2 * kvd) / 16, H, 1, w->wq[l], w->wk[l],
-                             w->wv[l], qd, kvd, st), "pack qkv");
-    hip_check(launch_pack<T>(const_cast<uint4*>(m->o[l].W), H / 16, qd, 0, w->wo[l], nullptr, nullptr, H, 0, st),
+                             w->wv[l], qd, kvd, c.head_dim, st), "pack qkv");
+    hip_check(launch_pack<T>(const_cast<uint4*>(m->o[l].W), H / 16, qd, 0, w->wo[l], nullptr, nullptr, H, 0, 0, st),
               "pack o");
-    hip_check(launch_pack<T>(const_cast<uint4*>(m->gu[l].W), 2 * F / 16, H, 2, w->wg[l], w->wu[l], nullptr, 0, 0,
+    hip_check(launch_pack<T>(const_cast<uint4*>(m->gu[l].W), 2 * F / 16, H, 2, w->wg[l], w->wu[l], nullptr, 0, 0, 0,
                              st), "pack gate/up");
-    hip_check(launch_pack<T>(const_cast<uint4*>(m->d[l].W), H / 16, F, 0, w->wd[l], nullptr, nullptr, H, 0, st),
+    hip_check(launch_pack<T>(const_cast<uint4*>(m->d[l].W), H / 16, F, 0, w->wd[l], nullptr, nullptr, H, 0, 0, st),
               "pack down");
   }
-  hip_check(launch_pack<T>(const_cast<uint4*>(m->lm.W), m->lm.n_groups * 4, H, 0, w->lm_head, nullptr, nullptr,
-                           c.vocab, 0, st), "pack lm_head");
+  hip_check(launch_pack<T>(const_cast<uint4*>(m->lm.W), m->lm.n_tiles, H, 0, w->lm_head, nullptr, nullptr,
+                           c.vocab, 0, 0, st), "pack lm_head");
 }
 
 void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb_model** out) {
@@ -202,8 +204,8 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
     o_gu[l] = take((size_t)2 * F * H * E);
     o_d[l] = take((size_t)H * F * E);
   }
-  const int lm_groups = (V + 63) / 64;
-  const size_t o_lm = take((size_t)lm_groups * 64 * H * E);
+  const int lm_tiles = (V + 15) / 16;
+  const size_t o_lm = take((size_t)lm_tiles * 16 * H * E);
   const size_t o_rope = take((size_t)c.max_positions * (c.head_dim / 2) * sizeof(float2));
   if (hipMalloc(&m->wmem, off) != hipSuccess) fail(SSB_ENOMEM, "hipMalloc of packed weights failed");
   char* wb = static_cast<char*>(m->wmem);
@@ -213,14 +215,12 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   for (int l = 0; l < L; ++l) {
     m->attn_norm.push_back(reinterpret_cast<const float*>(wb + o_an[l]));
     m->mlp_norm.push_back(reinterpret_cast<const float*>(wb + o_mn[l]));
-    m->qkv.push_back({reinterpret_cast<const uint4*>(wb + o_qkv[l]), H, c.n_heads + 2 * c.n_kv_heads,
-                      split_for(c.n_heads + 2 * c.n_kv_heads, H / kChunkK), hd / 16});
-    m->o.push_back({reinterpret_cast<const uint4*>(wb + o_o[l]), qd, H / 64, split_for(H / 64, qd / kChunkK), 4});
-    m->gu.push_back({reinterpret_cast<const uint4*>(wb + o_gu[l]), H, 2 * F / 64,
-                     split_for(2 * F / 64, H / kChunkK), 4});
-    m->d.push_back({reinterpret_cast<const uint4*>(wb + o_d[l]), F, H / 64, split_for(H / 64, F / kChunkK), 4});
+    m->qkv.push_back({reinterpret_cast<const uint4*>(wb + o_qkv[l]), H, (qd + 2 * kvd) / 16, kpw_for(H, m->elem)});
+    m->o.push_back({reinterpret_cast<const uint4*>(wb + o_o[l]), qd, H / 16, kpw_for(qd, m->elem)});
+    m->gu.push_back({reinterpret_cast<const uint4*>(wb + o_gu[l]), H, 2 * F / 16, kpw_for(H, m->elem)});
+    m->d.push_back({reinterpret_cast<const uint4*>(wb + o_d[l]), F, H / 16, kpw_for(F, m->elem)});
   }
-  m->lm = {reinterpret_cast<const uint4*>(wb + o_lm), H, lm_groups, split_for(lm_groups, H / kChunkK), 4};
+  m->lm = {reinterpret_cast<const uint4*>(wb + o_lm), H, lm_tiles, kpw_for(H, m->elem)};
   m->rope = reinterpret_cast<float2*>(wb + o_rope);
 
   hip_check(hipMemcpyAsync(wb + o_embed, w->embed, (size_t)V * H * E, hipMemcpyDeviceToDevice, st), "copy embed");
@@ -250,29 +250,23 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const int MR = c.max_rows;
   m->max_decode_rows = std::min(MR, SSB_MAX_BATCH * (std::max(c.block_B, 1) + 1));
   m->max_chunks = (c.max_positions + kKeyChunk - 1) / kKeyChunk;
-  size_t gpart = 0;
-  auto gp = [&](const GemmShape& g) {
-    if (g.S > 1) gpart = std::max(gpart, (size_t)g.S * g.n_groups * 16 * g.nt);
-  };
-  gp(m->qkv[0]); gp(m->o[0]); gp(m->gu[0]); gp(m->d[0]); gp(m->lm);
   off = 0;
   const size_t w_h = take((size_t)MR * H * 4);
-  const size_t w_ssq = take((size_t)(H / 64) * MR * 4);
+  const size_t w_xg = take((size_t)MR * H * E);
+  const size_t w_ssq = take((size_t)(H / 16) * MR * 4);
   const size_t w_q = take((size_t)MR * qd * E);
   const size_t w_attn = take((size_t)MR * qd * E);
   const size_t w_act = take((size_t)MR * F * E);
   const size_t w_meta = take((size_t)4 * MR * 4);
   const size_t w_am = take((size_t)MR * 12);
-  const size_t w_amp = take((size_t)lm_groups * MR * 12);
-  const size_t w_gpart = take(gpart * MR * 4);
-  const int n_ctr = std::max({c.n_heads + 2 * c.n_kv_heads, H / 64, 2 * F / 64, lm_groups}) * (MR / 16 + 1);
-  const size_t w_ctr = take((size_t)n_ctr * 4);
+  const size_t w_amp = take((size_t)lm_tiles * MR * 12);
   const size_t w_apart = take((size_t)m->max_decode_rows * c.n_heads * m->max_chunks * (hd + 4) * 4);
   const size_t w_acc = take((size_t)kMaxReq * kOutStride * 4);
   const size_t w_tok = take((size_t)MR * 4);
   if (hipMalloc(&m->ws, off) != hipSuccess) fail(SSB_ENOMEM, "hipMalloc of workspace failed");
   char* wsb = static_cast<char*>(m->ws);
   m->h = reinterpret_cast<float*>(wsb + w_h);
+  m->xg = wsb + w_xg;
   m->ssq = reinterpret_cast<float*>(wsb + w_ssq);
   m->q = wsb + w_q;
   m->attn = wsb + w_attn;
@@ -285,14 +279,11 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   m->am_top1 = reinterpret_cast<float*>(m->am_tok + MR);
   m->am_top2 = m->am_top1 + MR;
   m->amv1 = reinterpret_cast<float*>(wsb + w_amp);
-  m->amv2 = m->amv1 + (size_t)lm_groups * MR;
-  m->ami1 = reinterpret_cast<int32_t*>(m->amv2 + (size_t)lm_groups * MR);
-  m->gpart = reinterpret_cast<float*>(wsb + w_gpart);
-  m->counters = reinterpret_cast<int*>(wsb + w_ctr);
+  m->amv2 = m->amv1 + (size_t)lm_tiles * MR;
+  m->ami1 = reinterpret_cast<int32_t*>(m->amv2 + (size_t)lm_tiles * MR);
   m->apart = reinterpret_cast<float*>(wsb + w_apart);
   m->accept_dev = reinterpret_cast<int32_t*>(wsb + w_acc);
   m->tok_dev = reinterpret_cast<int32_t*>(wsb + w_tok);
-  hip_check(hipMemsetAsync(m->counters, 0, (size_t)n_ctr * 4, st), "zero counters");
   if (hipHostMalloc(reinterpret_cast<void**>(&m->pin_i32), (size_t)(MR + kMaxReq * kOutStride) * 4,
                     hipHostMallocDefault) != hipSuccess)
     fail(SSB_ENOMEM, "pinned host allocation failed");
@@ -325,19 +316,22 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   PrepArgs pa{};
   pa.mode = f.mode; pa.M = M; pa.hidden = H; pa.vocab = c.vocab; pa.mask_id = c.mask_id;
   pa.pos0 = f.pos0; pa.prefix = f.prefix; pa.tokens = m->tok_dev; pa.am_prev = m->am_tok;
-  pa.embed = m->embed;
+  pa.embed = m->embed; pa.gain = m->attn_norm[0];
   pa.row_tok = m->row_tok; pa.row_pos = m->row_pos; pa.row_lim = m->row_lim; pa.row_req = m->row_req;
-  pa.h = m->h; pa.ssq = m->ssq; pa.ssq_ld = MR; pa.req = f.ra;
+  pa.h = m->h; pa.xg = m->xg; pa.ssq = m->ssq; pa.ssq_ld = MR; pa.req = f.ra;
   hip_check(launch_prep<T>(pa, st), "prep");
 
   GemmArgs g{};
-  g.M = M; g.part = m->gpart; g.counters = m->counters;
-  g.ssq = m->ssq; g.ssq_ld = MR; g.n_ssq = H / 64; g.eps = c.rms_eps; g.hidden = H;
-  g.h = m->h; g.h_out = m->h; g.ssq_out = m->ssq;
+  g.M = M;
+  g.ssq = m->ssq; g.ssq_ld = MR; g.n_ssq = H / 16; g.eps = c.rms_eps; g.hidden = H;
+  g.h = m->h; g.xg_out = m->xg; g.ssq_out = m->ssq;
+  g.q = m->q; g.q_ld = qd;
   g.n_heads = c.n_heads; g.n_kv = c.n_kv_heads; g.head_dim = c.head_dim; g.n_pages = pool->n_pages;
   g.kv_pool = pool->base; g.rope = m->rope; g.row_pos = m->row_pos; g.row_req = m->row_req;
   for (int r = 0; r < kMaxReq; ++r) g.pt[r] = f.ra.pt[r];
+  g.act = m->act; g.act_ld = c.ffn;
   g.vocab = c.vocab; g.mask_id = c.mask_id;
+  auto set_w = [](GemmArgs& a, const GemmShape& s) { a.W = s.W; a.K = s.K; a.n_tiles = s.n_tiles; };
 
   AttnArgs at{};
   at.q = m->q; at.q_ld = qd; at.kv_pool = pool->base; at.n_pages = pool->n_pages;
@@ -349,75 +343,82 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   at.scale = 1.0f / std::sqrt((float)c.head_dim);
   // row tasks: windows of each request (draft/verify) or one request's rows
   at.tasks.n = 0;
-  auto add_tasks = [&](int req, int row0, int nrows) {
+  // lim_of(row j of a request window or of the row set): largest visible key
+  auto add_tasks = [&](int req, int row0, int nrows, auto lim_of) {
     for (int r = 0; r < nrows; r += kTaskRows) {
       if (at.tasks.n >= kMaxTasks) fail(SSB_EINVAL, "too many attention row tasks");
-      at.tasks.t[at.tasks.n++] = AttnTask{req, row0 + r, std::min(kTaskRows, nrows - r)};
+      const int n = std::min(kTaskRows, nrows - r);
+      int mx = -1;
+      for (int j = r; j < r + n; ++j) mx = std::max(mx, lim_of(j));
+      at.tasks.t[at.tasks.n++] = AttnTask{req, row0 + r, n, mx};
     }
   };
-  if (f.mode == PREP_DRAFT || f.mode == PREP_VERIFY) {
-    for (int r = 0; r < f.ra.n; ++r) add_tasks(r, f.ra.row0[r], f.ra.B + 1);
+  if (f.mode == PREP_DRAFT) {
+    for (int r = 0; r < f.ra.n; ++r) {
+      const int p = f.ra.p[r], B = f.ra.B;
+      add_tasks(r, f.ra.row0[r], B + 1, [&](int j) { return j == 0 ? p : p + B; });
+    }
+  } else if (f.mode == PREP_VERIFY) {
+    for (int r = 0; r < f.ra.n; ++r) {
+      const int p = f.ra.p[r];
+      add_tasks(r, f.ra.row0[r], f.ra.B + 1, [&](int j) { return p + 1 + j; });
+    }
   } else {
-    add_tasks(0, 0, M);
+    add_tasks(0, 0, M, [&](int j) { return f.pos0 + j; });
   }
   const int chunk_slots = (f.max_pos - 1) / kKeyChunk + 1;
 
   for (int l = 0; l < c.n_layers; ++l) {
     g.layer = l;
-    // QKV + RoPE + KV write
-    {
+    {  // RMSNorm -> QKV -> RoPE -> KV write (input xg = h * attn_norm[l])
       GemmArgs a = g;
-      const GemmShape& s = m->qkv[l];
-      a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
-      a.gain = m->attn_norm[l]; a.y = m->q; a.ldy = qd;
-      hip_check(launch_gemm<T>(a, EPI_QKV, s.nt, st), "qkv gemm");
+      set_w(a, m->qkv[l]);
+      a.x = m->xg; a.ldx = H;
+      hip_check(launch_gemm<T>(a, EPI_QKV, m->qkv[l].kpw, st), "qkv gemm");
     }
     at.layer = l;
     hip_check(launch_attn<T>(at, chunk_slots, c.head_dim, st), "attention");
     if (!at.fold)
       hip_check(launch_attn_combine<T>(m->apart, m->max_chunks, c.n_heads, c.head_dim, m->row_lim, M, m->attn,
                                        qd, st), "attention combine");
-    {
+    {  // O + residual; next input xg = h * mlp_norm[l]
       GemmArgs a = g;
-      const GemmShape& s = m->o[l];
-      a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
+      set_w(a, m->o[l]);
       a.x = m->attn; a.ldx = qd;
-      hip_check(launch_gemm<T>(a, EPI_RESID, 4, st), "o gemm");
+      a.gain_next = m->mlp_norm[l];
+      hip_check(launch_gemm<T>(a, EPI_RESID, m->o[l].kpw, st), "o gemm");
     }
-    {
+    {  // gate|up + SwiGLU
       GemmArgs a = g;
-      const GemmShape& s = m->gu[l];
-      a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
-      a.gain = m->mlp_norm[l]; a.y = m->act; a.ldy = c.ffn;
-      hip_check(launch_gemm<T>(a, EPI_SWIGLU, 4, st), "gate/up gemm");
+      set_w(a, m->gu[l]);
+      a.x = m->xg; a.ldx = H;
+      hip_check(launch_gemm<T>(a, EPI_SWIGLU, m->gu[l].kpw, st), "gate/up gemm");
     }
-    {
+    {  // down + residual; next input xg = h * (next attn_norm | final_norm)
       GemmArgs a = g;
-      const GemmShape& s = m->d[l];
-      a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
+      set_w(a, m->d[l]);
       a.x = m->act; a.ldx = c.ffn;
-      hip_check(launch_gemm<T>(a, EPI_RESID, 4, st), "down gemm");
+      a.gain_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
+      hip_check(launch_gemm<T>(a, EPI_RESID, m->d[l].kpw, st), "down gemm");
     }
   }
   // LM head + argmax
   {
     GemmArgs a = g;
-    const GemmShape& s = m->lm;
-    a.W = s.W; a.K = s.K; a.n_groups = s.n_groups; a.S = s.S;
-    a.gain = m->final_norm; a.logits = f.logits;
+    set_w(a, m->lm);
+    a.x = m->xg; a.ldx = H;
+    a.logits = f.logits;
     a.am_v1 = m->amv1; a.am_i1 = m->ami1; a.am_v2 = m->amv2; a.am_ld = MR;
     int rows = M;
-    int32_t* tok = m->am_tok;
-    float* t1 = m->am_top1;
-    float* t2 = m->am_top2;
     if (f.lm_last_only) {
-      a.h = m->h + (size_t)(M - 1) * H;
+      a.x = reinterpret_cast<const char*>(m->xg) + (size_t)(M - 1) * H * m->elem;
       a.ssq = m->ssq + (M - 1);
       a.M = 1;
       rows = 1;
     }
-    hip_check(launch_gemm<T>(a, EPI_LOGITS, 4, st), "lm head gemm");
-    hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, s.n_groups, MR, rows, tok, t1, t2, st), "argmax");
+    hip_check(launch_gemm<T>(a, EPI_LOGITS, m->lm.kpw, st), "lm head gemm");
+    hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, m->lm.n_tiles, MR, rows, m->am_tok, m->am_top1, m->am_top2,
+                            st), "argmax");
   }
 }
 

@@ -10,23 +10,30 @@
 //   accept : A = longest prefix with d_j == a_j, commit a0, d1..dA, a(A+1).
 // Every visibility rule on the path is "row r sees key j iff j <= lim[r]",
 // so one attention kernel serves prefill, AR steps, draft and verify.
+//
+// Batch-1 decode forwards are latency bound: every kernel here issues all of
+// its global loads up front (one dependent memory round trip), and no kernel
+// synchronizes with another workgroup; kernel boundaries are the only
+// cross-workgroup synchronization.
 #include "ssb_device.h"
 
 namespace ssb {
 
 // ---------------------------------------------------------------------------
-// Weight packing: W[N][K] row-major -> tiles [n_tile][k_step][lane][16 bytes],
-// lane l of (tile t, step s) holding row 16t + l%16, K values
-// s*kStepK + (kStepK/4)*(l/16) ... +kStepK/4.  One wave then reads 1 KiB of
+// Weight packing: W[N][K] -> tiles [n_tile][k_step][lane][16 bytes].  Lane l
+// of (tile t, step s) holds packed row 16t + l%16 and K values
+// s*kStepK + (kStepK/4)*(l/16) ... +kStepK/4, so one wave reads 1 KiB of
 // contiguous memory per step and feeds it straight to the matrix core.
-// Row sources: mode 0 = rows of src0 (rows >= n0 are zero padding);
-// mode 1 = concatenation src0 (n0 rows) | src1 (n1 rows) | src2 (rest);
-// mode 2 = SwiGLU interleave: packed group j of 64 rows holds rows
-// 32j..32j+31 of src0 (gate) then the same rows of src1 (up).
+// Packed-row -> source-row maps (tile row r = packed row % 16, j = tile):
+//   mode 0: identity; rows >= n0 are zero padding;
+//   mode 1 (q|k|v): head hh = j / (hd/16), jj = j % (hd/16); r < 8 holds head
+//           dim 8jj + r, r >= 8 holds dim hd/2 + 8jj + (r-8), so each rotary
+//           pair (i, i + hd/2) sits in rows (r, r+8) of one tile;
+//   mode 2 (gate|up): r < 8 holds gate row 8j + r, r >= 8 holds up row 8j + r-8.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void k_pack(uint4* dst, int n_tiles, int K, int mode, const T* src0, const T* src1,
-                       const T* src2, int n0, int n1) {
+                       const T* src2, int n0, int n1, int hd) {
   constexpr int KS = Ty<T>::kStepK;
   constexpr int PER = Ty<T>::kPerFrag;
   const int ksteps = K / KS;
@@ -37,20 +44,24 @@ __global__ void k_pack(uint4* dst, int n_tiles, int K, int mode, const T* src0, 
     const size_t ts = f / kWave;
     const int step = (int)(ts % ksteps);
     const int tile = (int)(ts / ksteps);
-    const int row = tile * 16 + lane % 16;
+    const int r = lane % 16;
     const int k = step * KS + PER * (lane / 16);
     const T* src = nullptr;
-    int srow = row;
+    int srow = 0;
     if (mode == 0) {
-      if (row < n0) src = src0;
+      srow = tile * 16 + r;
+      if (srow < n0) src = src0;
     } else if (mode == 1) {
-      if (row < n0) src = src0;
-      else if (row < n0 + n1) { src = src1; srow = row - n0; }
-      else { src = src2; srow = row - n0 - n1; }
+      const int tph = hd / 16;
+      const int hh = tile / tph, jj = tile % tph;
+      const int dim = r < 8 ? 8 * jj + r : hd / 2 + 8 * jj + (r - 8);
+      const int nq = n0 / hd, nk = n1 / hd;
+      if (hh < nq) { src = src0; srow = hh * hd + dim; }
+      else if (hh < nq + nk) { src = src1; srow = (hh - nq) * hd + dim; }
+      else { src = src2; srow = (hh - nq - nk) * hd + dim; }
     } else {
-      const int j = row / 64, i = row % 64;
-      src = i < 32 ? src0 : src1;
-      srow = 32 * j + (i % 32);
+      src = r < 8 ? src0 : src1;
+      srow = 8 * tile + (r % 8);
     }
     uint4 v = make_uint4(0, 0, 0, 0);
     if (src) v = *reinterpret_cast<const uint4*>(src + (size_t)srow * K + k);
@@ -60,12 +71,10 @@ __global__ void k_pack(uint4* dst, int n_tiles, int K, int mode, const T* src0, 
 
 // ---------------------------------------------------------------------------
 // Row preparation + embedding gather.  Writes the per-row metadata of a
-// forward (token, position, visibility limit, request) and the fp32 residual
-// h = E[token] (or a prefix-embedding row), plus per-64-column sums of
-// squares of h used by the next RMSNorm.
+// forward (token, position, visibility limit, request), the fp32 residual
+// h = E[token] (or a prefix-embedding row), the first GEMM's input
+// xg = h * attn_norm gain (in T) and per-16-column sums of squares of h.
 // ---------------------------------------------------------------------------
-
-
 __device__ __forceinline__ void window_row(const PrepArgs& a, int m, int& tok, int& pos, int& lim,
                                            int& req) {
   if (a.mode == PREP_PREFILL) {
@@ -116,199 +125,120 @@ __global__ __launch_bounds__(64) void k_prep_embed(PrepArgs a) {
   if (g == 0 && t == 0) {
     a.row_tok[m] = tok; a.row_pos[m] = pos; a.row_lim[m] = lim; a.row_req[m] = req;
   }
-  const int col = g * kNormGroup + t;
+  const int col = g * 64 + t;
   const T* src = tok >= 0 ? reinterpret_cast<const T*>(a.embed) + (size_t)tok * a.hidden
                           : reinterpret_cast<const T*>(a.prefix) + (size_t)pos * a.hidden;
   const float v = Ty<T>::to_f(src[col]);
   a.h[(size_t)m * a.hidden + col] = v;
+  reinterpret_cast<T*>(a.xg)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * a.gain[col]);
   float s = v * v;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
-  if (t == 0) a.ssq[(size_t)g * a.ssq_ld + m] = s;
+  for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+  if (t % 16 == 0) a.ssq[(size_t)(col / 16) * a.ssq_ld + m] = s;
 }
 
 // ---------------------------------------------------------------------------
-// Small-M / large-M GEMM with fused epilogues.
-//   out[m][n] = sum_k X[m][k] * W[n][k]
-// Grid: (n_groups, S, m_blocks).  A workgroup owns NT n-tiles (NG = 16*NT
-// output columns) of one m-block (16*MT rows) and K chunks
-// [split*cps, (split+1)*cps) of the fixed 128-wide chunks.  Each chunk is
-// reduced from zero and added to the running sum in chunk order; with S > 1
-// every split writes its sum and the last workgroup to arrive (atomic ticket)
-// adds the S split sums in split order.  The decomposition (S) is a fixed
-// property of each weight matrix for all decode forwards, so a row's value
-// never depends on M.
-// RMSNorm inputs are consumed as X = h * gain (rounded to T) and each output
-// row is scaled by 1/rms(h) in the epilogue; rms comes from the per-64-column
-// sum-of-squares partials of h, added in column order.
+// GEMM with fused epilogues:  out[m][n] = sum_k X[m][k] W[n][k].
+// Grid (n_tiles, m_blocks); a workgroup owns one 16-column tile for 16*MT
+// rows and the full K.  Wave w of W = ksteps/KPW waves reduces K steps
+// [w*KPW, (w+1)*KPW) with an MFMA chain in K order after loading all of its
+// weight and activation fragments at once; the W partial tiles are then
+// added in wave order through LDS.  The decomposition depends only on K, so
+// a row's value never depends on M.
+// RMSNorm inputs arrive as X = h * gain (in T) and each output row is scaled
+// by 1/rms(h), rms from the per-16-column sums of squares added in column
+// order (review section 3.1: both modes share these layers).
 // ---------------------------------------------------------------------------
-
-
-template <typename T, int MT, bool NORM>
-__device__ __forceinline__ void stage_x(unsigned char* xs, const GemmArgs& a, int m_base, int kc) {
-  constexpr int PER = Ty<T>::kPerFrag;
-  constexpr int FPR = kChunkK / PER;                         // fragments per row
-  constexpr int XSTRIDE = kChunkK * (int)sizeof(T) + 16;
-  for (int f = threadIdx.x; f < MT * 16 * FPR; f += kThreads) {
-    const int r = f / FPR, q = f % FPR;
-    const int m = m_base + r;
-    const int k = kc * kChunkK + q * PER;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (m < a.M) {
-      if constexpr (NORM) {
-        const float* hp = a.h + (size_t)m * a.hidden + k;
-        const float* gp = a.gain + k;
-        if constexpr (sizeof(T) == 2) {
-          float4 h0 = *reinterpret_cast<const float4*>(hp);
-          float4 h1 = *reinterpret_cast<const float4*>(hp + 4);
-          float4 g0 = *reinterpret_cast<const float4*>(gp);
-          float4 g1 = *reinterpret_cast<const float4*>(gp + 4);
-          v.x = (uint32_t)f2bf(h0.x * g0.x) | ((uint32_t)f2bf(h0.y * g0.y) << 16);
-          v.y = (uint32_t)f2bf(h0.z * g0.z) | ((uint32_t)f2bf(h0.w * g0.w) << 16);
-          v.z = (uint32_t)f2bf(h1.x * g1.x) | ((uint32_t)f2bf(h1.y * g1.y) << 16);
-          v.w = (uint32_t)f2bf(h1.z * g1.z) | ((uint32_t)f2bf(h1.w * g1.w) << 16);
-        } else {
-          float4 h0 = *reinterpret_cast<const float4*>(hp);
-          float4 g0 = *reinterpret_cast<const float4*>(gp);
-          v.x = __float_as_uint(h0.x * g0.x); v.y = __float_as_uint(h0.y * g0.y);
-          v.z = __float_as_uint(h0.z * g0.z); v.w = __float_as_uint(h0.w * g0.w);
-        }
-      } else {
-        v = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.x) + (size_t)m * a.ldx + k);
-      }
-    }
-    *reinterpret_cast<uint4*>(xs + r * XSTRIDE + q * 16) = v;
-  }
-}
-
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-template <typename T, int NT, int MT, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
-  constexpr int NG = NT * 16;
-  constexpr int MB = MT * 16;
+template <typename T, int MT, int EPI, int KPW>
+__global__ __launch_bounds__(1024) void k_gemm(GemmArgs a) {
   constexpr int KS = Ty<T>::kStepK;
   constexpr int PER = Ty<T>::kPerFrag;
-  constexpr int STEPS = kChunkK / KS;
-  constexpr int XSTRIDE = kChunkK * (int)sizeof(T) + 16;
+  constexpr int MB = MT * 16;
   constexpr bool NORM = (EPI != EPI_RESID);
-  constexpr int WPN = 4 / NT;          // waves sharing one n-tile (split over m-tiles)
-  __shared__ __align__(16) unsigned char xs[MB * XSTRIDE];
-  __shared__ float ctile[MB][NG + 4];
+  extern __shared__ __align__(16) unsigned char smem[];
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);          // [W][MT][64]
+  __shared__ float ctile[MB][17];
   __shared__ float s_inv[MB];
-  __shared__ int s_last;
+  __shared__ float s_ssq[kMaxNormParts * MB];
 
-  const int grp = blockIdx.x, split = blockIdx.y, mblk = blockIdx.z;
+  const int tile = blockIdx.x;
+  const int m_base = blockIdx.y * MB;
+  const int W = blockDim.x / kWave;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int nchunks = a.K / kChunkK;
-  const int cps = nchunks / a.S;
-  const int c0 = split * cps, c1 = c0 + cps;
   const int ksteps = a.K / KS;
-  const int m_base = mblk * MB;
-  const int nt = wave % NT;
-  const int mt0 = wave / NT;
-  const int tile = grp * NT + nt;
-  const uint4* wp = a.W + (size_t)tile * ksteps * kWave + lane;
-  const int Ntot = a.n_groups * NG;
+  const int k0 = wave * KPW;
 
+  // weights of this wave (the HBM-latency-critical loads) go out first, all at once
+  uint4 wf[KPW];
+  const uint4* wp = a.W + ((size_t)tile * ksteps + k0) * kWave + lane;
+#pragma unroll
+  for (int s = 0; s < KPW; ++s) wf[s] = wp[(size_t)s * kWave];
+  // row-norm statistics: every thread helps load the per-16-column partials
+  if constexpr (NORM) {
+    for (int e = threadIdx.x; e < a.n_ssq * MB; e += blockDim.x) {
+      const int gi = e / MB, r = e % MB;
+      const int m = m_base + r;
+      s_ssq[gi * MB + r] = m < a.M ? a.ssq[(size_t)gi * a.ssq_ld + m] : 0.f;
+    }
+  }
+  // activation fragments in phases of up to 4 K steps (bounded register use)
+  constexpr int PH = KPW < 4 ? KPW : 4;
+  const T* xb = reinterpret_cast<const T*>(a.x);
   f32x4_t acc[MT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 wnext[STEPS];
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s) wnext[s] = wp[(size_t)(c0 * STEPS + s) * kWave];
-
-  for (int c = c0; c < c1; ++c) {
-    uint4 wcur[STEPS];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) wcur[s] = wnext[s];
-    if (c + 1 < c1) {
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) wnext[s] = wp[(size_t)((c + 1) * STEPS + s) * kWave];
-    }
-    stage_x<T, MT, NORM>(xs, a, m_base, c);
-    __syncthreads();
-    f32x4_t accc[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) accc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (mt % WPN != mt0) continue;
-        const uint4 b = *reinterpret_cast<const uint4*>(
-            xs + (mt * 16 + lane % 16) * XSTRIDE + (s * KS + PER * (lane / 16)) * (int)sizeof(T));
-        mma_step(accc[mt], wcur[s], b, T());
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      if (mt % WPN == mt0) acc[mt] += accc[mt];
-    __syncthreads();
-  }
-
-  if (a.S > 1) {
-    // publish this split's sum, then the last arriving workgroup adds all splits in order
+  for (int p0 = 0; p0 < KPW; p0 += PH) {
+    uint4 xf[PH][MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      if (mt % WPN != mt0) continue;
-      const int m = m_base + mt * 16 + lane % 16;
-      if (m < a.M) {
-        float* dst = a.part + ((size_t)split * a.M + m) * Ntot + grp * NG + nt * 16 + 4 * (lane / 16);
-        *reinterpret_cast<f32x4_t*>(dst) = acc[mt];
-      }
-    }
-    __threadfence();
-    __syncthreads();
-    const int ctr = grp * gridDim.z + mblk;
-    if (threadIdx.x == 0) s_last = (atomicAdd(&a.counters[ctr], 1) == a.S - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+      const int row = m_base + mt * 16 + lane % 16;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt % WPN != mt0) continue;
-      acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int m = m_base + mt * 16 + lane % 16;
-      if (m < a.M) {
-        for (int s = 0; s < a.S; ++s) {
-          const float* src = a.part + ((size_t)s * a.M + m) * Ntot + grp * NG + nt * 16 + 4 * (lane / 16);
-          acc[mt] += *reinterpret_cast<const f32x4_t*>(src);
-        }
+      for (int s = 0; s < PH; ++s) {
+        xf[s][mt] = make_uint4(0, 0, 0, 0);
+        if (row < a.M)
+          xf[s][mt] = *reinterpret_cast<const uint4*>(xb + (size_t)row * a.ldx + (k0 + p0 + s) * KS +
+                                                      PER * (lane / 16));
       }
     }
-    if (threadIdx.x == 0) a.counters[ctr] = 0;
+#pragma unroll
+    for (int s = 0; s < PH; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) mma_step(acc[mt], wf[p0 + s], xf[s][mt], T());
   }
 
-  // full tile -> LDS
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (mt % WPN != mt0) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ctile[mt * 16 + lane % 16][nt * 16 + 4 * (lane / 16) + i] = acc[mt][i];
-  }
+  for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * kWave + lane] = acc[mt];
+  __syncthreads();
   if constexpr (NORM) {
-    for (int r = threadIdx.x; r < MB; r += kThreads) {
-      const int m = m_base + r;
+    for (int r = threadIdx.x; r < MB; r += blockDim.x) {
       float s = 0.f;
-      if (m < a.M)
-        for (int g = 0; g < a.n_ssq; ++g) s += a.ssq[(size_t)g * a.ssq_ld + m];
+      for (int gi = 0; gi < a.n_ssq; ++gi) s += s_ssq[gi * MB + r];
       s_inv[r] = 1.0f / sqrtf(s / (float)a.hidden + a.eps);
     }
+  }
+  for (int e = threadIdx.x; e < MT * kWave * 4; e += blockDim.x) {
+    const int mt = e / (kWave * 4), l = (e / 4) % kWave, i = e % 4;
+    float s = 0.f;
+    for (int w = 0; w < W; ++w) s += red[(w * MT + mt) * kWave + l][i];
+    ctile[mt * 16 + l % 16][4 * (l / 16) + i] = s;     // [row][tile column]
   }
   __syncthreads();
 
   if constexpr (EPI == EPI_QKV) {
-    const int hd = a.head_dim, half = hd / 2;
-    const int kind = grp < a.n_heads ? 0 : (grp < a.n_heads + a.n_kv ? 1 : 2);   // q, k, v
-    const int head = kind == 0 ? grp : (kind == 1 ? grp - a.n_heads : grp - a.n_heads - a.n_kv);
-    for (int e = threadIdx.x; e < MB * half; e += kThreads) {
-      const int r = e / half, i = e % half;
+    const int hd = a.head_dim, half = hd / 2, tph = hd / 16;
+    const int hh = tile / tph, jj = tile % tph;
+    const int kind = hh < a.n_heads ? 0 : (hh < a.n_heads + a.n_kv ? 1 : 2);   // q, k, v
+    const int head = kind == 0 ? hh : (kind == 1 ? hh - a.n_heads : hh - a.n_heads - a.n_kv);
+    for (int e = threadIdx.x; e < MB * 8; e += blockDim.x) {
+      const int r = e / 8, c = e % 8;
       const int m = m_base + r;
       if (m >= a.M) continue;
       const float inv = s_inv[r];
-      float x1 = ctile[r][i] * inv, x2 = ctile[r][i + half] * inv;
+      float x1 = ctile[r][c] * inv, x2 = ctile[r][c + 8] * inv;
+      const int i = 8 * jj + c;                 // rotary pair (i, i + hd/2)
       const int pos = a.row_pos[m];
       if (kind != 2) {
         const float2 cs = a.rope[(size_t)pos * half + i];
@@ -318,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
       }
       T* dst;
       if (kind == 0) {
-        dst = reinterpret_cast<T*>(a.y) + (size_t)m * a.ldy + head * hd;
+        dst = reinterpret_cast<T*>(a.q) + (size_t)m * a.q_ld + head * hd;
       } else {
         const int32_t* pt = a.pt[a.row_req[m]];
         const int page = pt[pos / kPage], slot = pos % kPage;
@@ -329,51 +259,52 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
       dst[i + half] = Ty<T>::from_f(x2);
     }
   } else if constexpr (EPI == EPI_RESID) {
-    for (int e = threadIdx.x; e < MB * NG; e += kThreads) {
-      const int r = e / NG, n = e % NG;
+    for (int e = threadIdx.x; e < MB * 16; e += blockDim.x) {
+      const int r = e / 16, n = e % 16;
       const int m = m_base + r;
       if (m >= a.M) continue;
-      float* hp = a.h_out + (size_t)m * a.hidden + grp * NG + n;
+      const int col = tile * 16 + n;
+      float* hp = a.h + (size_t)m * a.hidden + col;
       const float v = *hp + ctile[r][n];
       *hp = v;
+      reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * a.gain_next[col]);
       ctile[r][n] = v;
     }
     __syncthreads();
-    for (int r = threadIdx.x; r < MB; r += kThreads) {
+    for (int r = threadIdx.x; r < MB; r += blockDim.x) {
       const int m = m_base + r;
       if (m >= a.M) continue;
       float s = 0.f;
-      for (int n = 0; n < NG; ++n) s += ctile[r][n] * ctile[r][n];
-      a.ssq_out[(size_t)grp * a.ssq_ld + m] = s;
+      for (int n = 0; n < 16; ++n) s += ctile[r][n] * ctile[r][n];
+      a.ssq_out[(size_t)tile * a.ssq_ld + m] = s;
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    constexpr int HG = NG / 2;
-    for (int e = threadIdx.x; e < MB * HG; e += kThreads) {
-      const int r = e / HG, i = e % HG;
+    for (int e = threadIdx.x; e < MB * 8; e += blockDim.x) {
+      const int r = e / 8, c = e % 8;
       const int m = m_base + r;
       if (m >= a.M) continue;
-      const float g = ctile[r][i] * s_inv[r];
-      const float u = ctile[r][HG + i] * s_inv[r];
-      reinterpret_cast<T*>(a.y)[(size_t)m * a.ldy + grp * HG + i] = Ty<T>::from_f(silu_f(g) * u);
+      const float g = ctile[r][c] * s_inv[r];
+      const float u = ctile[r][c + 8] * s_inv[r];
+      reinterpret_cast<T*>(a.act)[(size_t)m * a.act_ld + tile * 8 + c] = Ty<T>::from_f(silu_f(g) * u);
     }
   } else {  // EPI_LOGITS
-    for (int e = threadIdx.x; e < MB * NG; e += kThreads) {
-      const int r = e / NG, n = e % NG;
+    for (int e = threadIdx.x; e < MB * 16; e += blockDim.x) {
+      const int r = e / 16, n = e % 16;
       const int m = m_base + r;
       const float z = ctile[r][n] * s_inv[r];
       ctile[r][n] = z;
-      const int col = grp * NG + n;
+      const int col = tile * 16 + n;
       if (a.logits && m < a.M && col < a.vocab) a.logits[(size_t)m * a.vocab + col] = z;
     }
     __syncthreads();
-    for (int r = threadIdx.x; r < MB; r += kThreads) {
+    for (int r = threadIdx.x; r < MB; r += blockDim.x) {
       const int m = m_base + r;
       if (m >= a.M) continue;
       float v1 = -INFINITY, v2 = -INFINITY;
       int i1 = 0x7fffffff;
       bool nan = false;
-      for (int n = 0; n < NG; ++n) {
-        const int col = grp * NG + n;
+      for (int n = 0; n < 16; ++n) {
+        const int col = tile * 16 + n;
         if (col >= a.vocab || col == a.mask_id) continue;
         const float z = ctile[r][n];
         if (z != z) { nan = true; continue; }
@@ -381,9 +312,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
         else if (z > v2) { v2 = z; }
       }
       if (nan) { v1 = NAN; v2 = NAN; i1 = -1; }
-      a.am_v1[(size_t)grp * a.am_ld + m] = v1;
-      a.am_i1[(size_t)grp * a.am_ld + m] = i1;
-      a.am_v2[(size_t)grp * a.am_ld + m] = v2;
+      a.am_v1[(size_t)tile * a.am_ld + m] = v1;
+      a.am_i1[(size_t)tile * a.am_ld + m] = i1;
+      a.am_v2[(size_t)tile * a.am_ld + m] = v2;
     }
   }
 }
@@ -411,9 +342,19 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
                                                     float* top2) {
   __shared__ Top2 sh[kThreads];
   const int m = blockIdx.x;
+  constexpr int BATCH = 16;
   Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
-  for (int g = threadIdx.x; g < n_groups; g += kThreads)
-    t = merge_top2(t, Top2{v1[(size_t)g * ld + m], i1[(size_t)g * ld + m], v2[(size_t)g * ld + m]});
+  for (int g0 = threadIdx.x; g0 < n_groups; g0 += BATCH * kThreads) {
+    Top2 rec[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int g = g0 + b * kThreads;
+      rec[b] = Top2{-INFINITY, 0x7fffffff, -INFINITY};
+      if (g < n_groups) rec[b] = Top2{v1[(size_t)g * ld + m], i1[(size_t)g * ld + m], v2[(size_t)g * ld + m]};
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) t = merge_top2(t, rec[b]);
+  }
   sh[threadIdx.x] = t;
   __syncthreads();
   for (int s = kThreads / 2; s > 0; s >>= 1) {
@@ -438,9 +379,9 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
 // k_attn_combine adds them in chunk order; prefill (fold = 1) loops over the
 // chunks in the same order and writes the normalized output directly.
 // S^T = K Q^T puts keys on the matrix-core row side so the probabilities land
-// in the lanes that feed P^T to the V^T P^T product without shuffles.
+// in the lanes that feed P^T to the V^T P^T product without shuffles; V is
+// stored transposed in LDS so a V^T fragment is one or two vector reads.
 // ---------------------------------------------------------------------------
-
 // Online-softmax merge of a running (m, l, o) with a chunk record (mc, lc, oc):
 // m' = max(m, mc), l' = l e^(m-m') + lc e^(mc-m'), o' likewise.
 __device__ __forceinline__ void fold_coef(float m, float mc, float& mn, float& al, float& be) {
@@ -460,30 +401,27 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   constexpr int QKS = HD / KS;             // steps of S^T over the head dimension
   constexpr int KT = kKeyChunk / 16;       // key tiles per chunk
   constexpr int PVS = kKeyChunk / KS;      // steps of P V over keys
-  constexpr int KSTR = HD * (int)sizeof(T) + 16;
+  constexpr int KSTR = HD * (int)sizeof(T) + 16;              // K rows [key][d]
+  constexpr int VSTR = kKeyChunk * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);   // V^T rows [d][key]
   constexpr int MT = kTaskRows / 16;
   constexpr int REC = HD + 4;
+  constexpr int MAXU = 3;                  // units per wave: ceil(4 heads * 3 tiles / 4 waves)
+  constexpr int FPK = HD / PER;            // 16-byte fragments per key row
+  constexpr int KVF = 2 * kKeyChunk * FPK / kThreads;   // fragments per thread
   __shared__ __align__(16) unsigned char ks[kKeyChunk * KSTR];
-  __shared__ __align__(16) unsigned char vs[kKeyChunk * KSTR];
+  __shared__ __align__(16) unsigned char vts[HD * VSTR];
   __shared__ int s_lim[kTaskRows];
-  __shared__ int s_maxlim;
 
   const AttnTask task = a.tasks.t[blockIdx.z];
   const int g = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n_rep = a.n_heads / a.n_kv;
   const int32_t* pt = a.pt[task.req];
+  const int n_units = n_rep * MT;
 
   if (threadIdx.x < kTaskRows)
     s_lim[threadIdx.x] = threadIdx.x < task.nrows ? a.row_lim[task.row0 + threadIdx.x] : -1;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int mx = -1;
-    for (int r = 0; r < task.nrows; ++r) mx = max(mx, s_lim[r]);
-    s_maxlim = mx;
-  }
-  __syncthreads();
-  const int maxlim = s_maxlim;
+  const int maxlim = task.max_lim;          // largest visibility limit of the task's rows
   int cbeg, cend;
   if (a.fold) { cbeg = 0; cend = maxlim / kKeyChunk + 1; }
   else {
@@ -491,9 +429,23 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
     if (cbeg * kKeyChunk > maxlim) return;
   }
 
-  // units: (head within group, row tile) handled by this wave
-  const int n_units = n_rep * MT;
-  constexpr int MAXU = 3;                  // ceil(4 heads * 3 tiles / 4 waves)
+  // query fragments of this wave's units (B operand of S^T): issued first
+  uint4 qf[MAXU][QKS];
+#pragma unroll
+  for (int ui = 0; ui < MAXU; ++ui) {
+    const int u = wave + 4 * ui;
+    const int hl = u / MT, mt = u % MT;
+    const int row_local = mt * 16 + lane % 16;
+#pragma unroll
+    for (int st = 0; st < QKS; ++st) {
+      qf[ui][st] = make_uint4(0, 0, 0, 0);
+      if (u < n_units && row_local < task.nrows)
+        qf[ui][st] = *reinterpret_cast<const uint4*>(
+            reinterpret_cast<const T*>(a.q) + (size_t)(task.row0 + row_local) * a.q_ld + (g * n_rep + hl) * HD +
+            st * KS + PER * (lane / 16));
+    }
+  }
+
   float run_m[MAXU], run_l[MAXU];
   f32x4_t run_o[MAXU][DT];
 #pragma unroll
@@ -504,21 +456,35 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   }
 
   for (int c = cbeg; c < cend; ++c) {
-    // stage K and V of keys [c*64, c*64+64) that any row of the task may see
-    constexpr int FPK = HD / PER;          // 16-byte fragments per key row
-    for (int f = threadIdx.x; f < 2 * kKeyChunk * FPK; f += kThreads) {
+    // K and V of keys [c*64, c*64+64) that any row of the task may see
+    uint4 kvv[KVF];
+#pragma unroll
+    for (int q = 0; q < KVF; ++q) {
+      const int f = threadIdx.x + q * kThreads;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
-      const int kk = rem / FPK, q = rem % FPK;
-      const int key = c * kKeyChunk + kk;
-      uint4 v = make_uint4(0, 0, 0, 0);
+      const int key = c * kKeyChunk + rem / FPK;
+      kvv[q] = make_uint4(0, 0, 0, 0);
       if (key <= maxlim) {
         const int page = pt[key / kPage], slot = key % kPage;
         const size_t base = (((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.n_kv + g;
-        v = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kv_pool) +
-                                            (base * kPage + slot) * HD + q * PER);
+        kvv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kv_pool) +
+                                                 (base * kPage + slot) * HD + (rem % FPK) * PER);
       }
-      *reinterpret_cast<uint4*>((kv ? vs : ks) + kk * KSTR + q * 16) = v;
+    }
+#pragma unroll
+    for (int q = 0; q < KVF; ++q) {
+      const int f = threadIdx.x + q * kThreads;
+      const int kv = f / (kKeyChunk * FPK);
+      const int rem = f % (kKeyChunk * FPK);
+      const int kk = rem / FPK, d0 = (rem % FPK) * PER;
+      if (kv == 0) {
+        *reinterpret_cast<uint4*>(ks + kk * KSTR + d0 * (int)sizeof(T)) = kvv[q];
+      } else {
+        const T* vals = reinterpret_cast<const T*>(&kvv[q]);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) *reinterpret_cast<T*>(vts + (d0 + i) * VSTR + kk * (int)sizeof(T)) = vals[i];
+      }
     }
     __syncthreads();
 
@@ -530,16 +496,6 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
       if (mt * 16 >= task.nrows) continue;
       const int head = g * n_rep + hl;
       const int row_local = mt * 16 + lane % 16;
-      // Q^T fragments (B operand): row_local's query, head dims of this lane
-      uint4 qf[QKS];
-#pragma unroll
-      for (int st = 0; st < QKS; ++st) {
-        qf[st] = make_uint4(0, 0, 0, 0);
-        if (row_local < task.nrows)
-          qf[st] = *reinterpret_cast<const uint4*>(
-              reinterpret_cast<const T*>(a.q) + (size_t)(task.row0 + row_local) * a.q_ld + head * HD +
-              st * KS + PER * (lane / 16));
-      }
       // S^T tiles: element i of tile kt = score of key kt*16 + 4*(lane/16) + i for row_local
       f32x4_t s[KT];
 #pragma unroll
@@ -549,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
         for (int st = 0; st < QKS; ++st) {
           const uint4 kf = *reinterpret_cast<const uint4*>(
               ks + (kt * 16 + lane % 16) * KSTR + (st * KS + PER * (lane / 16)) * (int)sizeof(T));
-          mma_step(s[kt], kf, qf[st], T());
+          mma_step(s[kt], kf, qf[ui][st], T());
         }
       }
       const int lim = s_lim[row_local];
@@ -581,37 +537,25 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const unsigned char* vrow = vts + (dt * 16 + lane % 16) * VSTR;
 #pragma unroll
         for (int st = 0; st < PVS; ++st) {
           uint4 pf, vf;
           if constexpr (sizeof(T) == 2) {
-            // keys 32st + 4(l/16) + {0..3} from tile 2st, then +16 from tile 2st+1
+            // keys 32st + 4(l/16) + {0..3} from tile 2st, then the same +16 from tile 2st+1
             const f32x4_t p0 = s[2 * st], p1 = s[2 * st + 1];
             pf.x = (uint32_t)f2bf(p0[0]) | ((uint32_t)f2bf(p0[1]) << 16);
             pf.y = (uint32_t)f2bf(p0[2]) | ((uint32_t)f2bf(p0[3]) << 16);
             pf.z = (uint32_t)f2bf(p1[0]) | ((uint32_t)f2bf(p1[1]) << 16);
             pf.w = (uint32_t)f2bf(p1[2]) | ((uint32_t)f2bf(p1[3]) << 16);
-            const int d = dt * 16 + lane % 16;
-            uint16_t vv[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int key = 32 * st + (j < 4 ? 4 * (lane / 16) + j : 16 + 4 * (lane / 16) + j - 4);
-              vv[j] = *reinterpret_cast<const uint16_t*>(vs + key * KSTR + d * 2);
-            }
-            vf.x = vv[0] | ((uint32_t)vv[1] << 16); vf.y = vv[2] | ((uint32_t)vv[3] << 16);
-            vf.z = vv[4] | ((uint32_t)vv[5] << 16); vf.w = vv[6] | ((uint32_t)vv[7] << 16);
+            const uint2 va = *reinterpret_cast<const uint2*>(vrow + (32 * st + 4 * (lane / 16)) * 2);
+            const uint2 vb = *reinterpret_cast<const uint2*>(vrow + (32 * st + 16 + 4 * (lane / 16)) * 2);
+            vf = make_uint4(va.x, va.y, vb.x, vb.y);
           } else {
             const f32x4_t p0 = s[st];
             pf = make_uint4(__float_as_uint(p0[0]), __float_as_uint(p0[1]), __float_as_uint(p0[2]),
                             __float_as_uint(p0[3]));
-            const int d = dt * 16 + lane % 16;
-            uint32_t vv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int key = 16 * st + 4 * (lane / 16) + j;
-              vv[j] = *reinterpret_cast<const uint32_t*>(vs + key * KSTR + d * 4);
-            }
-            vf = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+            vf = *reinterpret_cast<const uint4*>(vrow + (16 * st + 4 * (lane / 16)) * 4);
           }
           mma_step(o[dt], vf, pf, T());
         }
@@ -657,12 +601,14 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
 }
 
 // Combine the per-chunk records of each (row, head) in chunk order.
-// One wave per (row, head); lane d holds output dimension d.
+// One wave per (row, head); lane d holds output dimension d.  Records are
+// loaded 32 chunks at a time before folding.
 template <typename T, int HD>
 __global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, int max_chunks, int n_heads,
                                                           const int32_t* row_lim, int M, void* out,
                                                           int out_ld) {
   constexpr int REC = HD + 4;
+  constexpr int BATCH = 32;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int idx = blockIdx.x * 4 + wave;
   if (idx >= M * n_heads) return;
@@ -670,14 +616,28 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, in
   const int nch = row_lim[row] / kKeyChunk + 1;
   const float* rec = part + ((size_t)row * n_heads + head) * max_chunks * REC;
   float m = -INFINITY, l = 0.f, o = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float mc = rec[c * REC + HD], lc = rec[c * REC + HD + 1];
-    const float oc = lane < HD ? rec[c * REC + lane] : 0.f;
-    float mn, al, be;
-    fold_coef(m, mc, mn, al, be);
-    l = fold_val(l, al, lc, be);
-    o = fold_val(o, al, oc, be);
-    m = mn;
+  for (int c0 = 0; c0 < nch; c0 += BATCH) {
+    float mc[BATCH], lc[BATCH], oc[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int c = c0 + b;
+      mc[b] = -INFINITY; lc[b] = 0.f; oc[b] = 0.f;
+      if (c < nch) {
+        const float2 ml = *reinterpret_cast<const float2*>(rec + c * REC + HD);
+        mc[b] = ml.x; lc[b] = ml.y;
+        if (lane < HD) oc[b] = rec[c * REC + lane];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      if (c0 + b < nch) {
+        float mn, al, be;
+        fold_coef(m, mc[b], mn, al, be);
+        l = fold_val(l, al, lc[b], be);
+        o = fold_val(o, al, oc[b], be);
+        m = mn;
+      }
+    }
   }
   if (lane < HD) reinterpret_cast<T*>(out)[(size_t)row * out_ld + head * HD + lane] = Ty<T>::from_f(o / l);
 }
@@ -721,47 +681,59 @@ __global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int
 // ---------------------------------------------------------------------------
 template <typename T>
 hipError_t launch_pack(uint4* dst, int n_tiles, int K, int mode, const void* s0, const void* s1,
-                       const void* s2, int n0, int n1, hipStream_t st) {
+                       const void* s2, int n0, int n1, int hd, hipStream_t st) {
   hipLaunchKernelGGL(k_pack<T>, dim3(1024), dim3(256), 0, st, dst, n_tiles, K, mode,
-                     (const T*)s0, (const T*)s1, (const T*)s2, n0, n1);
+                     (const T*)s0, (const T*)s1, (const T*)s2, n0, n1, hd);
   return hipGetLastError();
 }
 template hipError_t launch_pack<bf16_t>(uint4*, int, int, int, const void*, const void*, const void*, int,
-                                        int, hipStream_t);
+                                        int, int, hipStream_t);
 template hipError_t launch_pack<float>(uint4*, int, int, int, const void*, const void*, const void*, int,
-                                       int, hipStream_t);
+                                       int, int, hipStream_t);
 
 template <typename T>
 hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_prep_embed<T>, dim3(a.M, a.hidden / kNormGroup), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(k_prep_embed<T>, dim3(a.M, a.hidden / 64), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 template hipError_t launch_prep<bf16_t>(const PrepArgs&, hipStream_t);
 template hipError_t launch_prep<float>(const PrepArgs&, hipStream_t);
 
-template <typename T, int NT, int EPI>
-static hipError_t launch_gemm_nt(const GemmArgs& a, int m_blocks, int MT, hipStream_t st) {
-  dim3 grid(a.n_groups, a.S, m_blocks);
+template <typename T, int EPI, int KPW>
+static hipError_t launch_gemm_kpw(const GemmArgs& a, int MT, hipStream_t st) {
+  const int ksteps = a.K / Ty<T>::kStepK;
+  const int W = ksteps / KPW;
+  const int m_blocks = (a.M + 16 * MT - 1) / (16 * MT);
+  const dim3 grid(a.n_tiles, m_blocks), block(W * kWave);
+  const size_t shm = (size_t)W * MT * kWave * sizeof(f32x4_t);
   switch (MT) {
-    case 1: hipLaunchKernelGGL((k_gemm<T, NT, 1, EPI>), grid, dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm<T, NT, 2, EPI>), grid, dim3(kThreads), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm<T, NT, 3, EPI>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm<T, NT, 4, EPI>), grid, dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_gemm<T, 1, EPI, KPW>), grid, block, shm, st, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm<T, 2, EPI, KPW>), grid, block, shm, st, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm<T, 3, EPI, KPW>), grid, block, shm, st, a); break;
+    default: hipLaunchKernelGGL((k_gemm<T, 4, EPI, KPW>), grid, block, shm, st, a); break;
   }
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_gemm(const GemmArgs& a, int epi, int nt, hipStream_t st) {
-  const int MT = a.M <= 16 ? 1 : a.M <= 32 ? 2 : a.M <= 48 ? 3 : 4;
-  const int m_blocks = (a.M + 16 * MT - 1) / (16 * MT);
-  if (epi == EPI_QKV) {
-    return nt == 2 ? launch_gemm_nt<T, 2, EPI_QKV>(a, m_blocks, MT, st)
-                   : launch_gemm_nt<T, 4, EPI_QKV>(a, m_blocks, MT, st);
+template <typename T, int EPI>
+static hipError_t launch_gemm_epi(const GemmArgs& a, int kpw, int MT, hipStream_t st) {
+  switch (kpw) {
+    case 1: return launch_gemm_kpw<T, EPI, 1>(a, MT, st);
+    case 2: return launch_gemm_kpw<T, EPI, 2>(a, MT, st);
+    case 4: return launch_gemm_kpw<T, EPI, 4>(a, MT, st);
+    default: return launch_gemm_kpw<T, EPI, 8>(a, MT, st);
   }
-  if (epi == EPI_RESID) return launch_gemm_nt<T, 4, EPI_RESID>(a, m_blocks, MT, st);
-  if (epi == EPI_SWIGLU) return launch_gemm_nt<T, 4, EPI_SWIGLU>(a, m_blocks, MT, st);
-  return launch_gemm_nt<T, 4, EPI_LOGITS>(a, m_blocks, MT, st);
+}
+
+template <typename T>
+hipError_t launch_gemm(const GemmArgs& a, int epi, int kpw, hipStream_t st) {
+  const int MT = a.M <= 16 ? 1 : a.M <= 32 ? 2 : a.M <= 48 ? 3 : 4;
+  switch (epi) {
+    case EPI_QKV: return launch_gemm_epi<T, EPI_QKV>(a, kpw, MT, st);
+    case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, kpw, MT, st);
+    case EPI_SWIGLU: return launch_gemm_epi<T, EPI_SWIGLU>(a, kpw, MT, st);
+    default: return launch_gemm_epi<T, EPI_LOGITS>(a, kpw, MT, st);
+  }
 }
 template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, int, hipStream_t);
 template hipError_t launch_gemm<float>(const GemmArgs&, int, int, hipStream_t);
