@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Round microbenchmark: committed tokens/s of greedy self-speculative rounds.
+
+Workload (the round microbenchmark): the 24-layer bf16 decoder (hidden 1024,
+16 query heads over 4 KV heads of 64, SwiGLU 4096, vocab 60000) with a KV
+cache prefilled from 1280 synthetic prefix embeddings, block size B = 32,
+batch 1.  One step = one full round on the GPU: draft forward over
+[x0, [M] x 32], verify forward over [a0, d1..d32], greedy argmax, accept,
+commit and rollback (GravityOCR review, section 3.2 and Appendix B.2).
+Every rep restarts from the same state (n = 1280, x0 = y1).  Drafts are
+planted from the GPU's own AR continuation with the first mismatch at
+min(Geometric(1/20), B), so accept lengths cover 0..32 with mean ~15.3.
+
+Prints one JSON line.  Extra diagnostics go to stderr.
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def alg_bytes_round(cfg, n, B):
+    """Algorithmic bytes of one round: weights streamed twice, KV read by both
+    forwards, KV written for B+1 rows by each forward (bf16)."""
+    layer_w = cfg.layer_params() * 2
+    w = cfg.n_layers * layer_w + cfg.hidden * 4 + cfg.vocab * cfg.hidden * 2
+    kvp = cfg.kv_bytes_per_position(2)
+    return 2 * w + kvp * ((n + B + 1) + (n + B + 2)) + 2 * kvp * (B + 1)
+
+
+def alg_bytes_kernel(kind, cfg, M, n_keys):
+    """Algorithmic bytes one launch must move (weights + inputs + outputs)."""
+    H, F, V, qd, kvd = cfg.hidden, cfg.ffn, cfg.vocab, cfg.q_dim, cfg.kv_dim
+    e = 2
+    if kind == "qkv":
+        return (qd + 2 * kvd) * H * e + M * H * e + M * (qd + 2 * kvd) * e
+    if kind == "o":
+        return H * qd * e + M * qd * e + M * H * (4 + 4 + e)
+    if kind == "gate_up":
+        return 2 * F * H * e + M * H * e + M * F * e
+    if kind == "down":
+        return H * F * e + M * F * e + M * H * (4 + 4 + e)
+    if kind == "lm_head":
+        return V * H * e + M * H * e + M * 12
+    if kind == "attention":
+        return n_keys * 2 * kvd * e + M * qd * e
+    if kind == "combine":
+        return M * qd * e
+    return M * 12
+
+
+def cpu_baseline(cfg, weights, prefix, planted_rows, B, target_s=15.0):
+    """The oracle (float64 numpy) timed on the host on a bounded sample of rounds."""
+    import numpy as np
+    from oracle import Decoder, prefill, spec_round
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    model = Decoder(cfg, weights)
+    P = prefix.shape[0]
+    st, y1, _ = prefill(model, prefix, P + B + 4)
+    committed = 0
+    t_total = 0.0
+    rounds = 0
+    for planted in planted_rows:
+        st.n, st.x0 = P, y1
+        t0 = time.perf_counter()
+        r = spec_round(model, st, B, planted=[int(x) for x in planted])
+        t_total += time.perf_counter() - t0
+        committed += len(r.committed)
+        rounds += 1
+        if t_total >= target_s and rounds >= 3:
+            break
+    return {"value": committed / t_total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rounds} rounds of the round microbenchmark (float64 numpy oracle, n=1280, B=32, "
+                      f"same planted drafts), {t_total:.1f} s of CPU time; prefill excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the round engine is a single-GPU path "
+              "(requests would shard across GPUs with no exchange step); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from ssb_inputs import generate_weights, plant_accept_lengths, prefix_embeddings, workload
+    from self_speculative_block_amd.engine import KV, Model, Pool
+
+    wl = workload(2)
+    cfg = wl.model
+    B = wl.block
+    P = wl.prefix_len
+    torch.cuda.set_device(0)
+    weights = generate_weights(cfg)
+    model = Model(cfg, weights, block_B=B, max_rows=2048, max_positions=P + 256)
+    pool = Pool(model, n_pages=(P + 256) // 16 + 8)
+    kv = KV(pool, P + 200)
+    prefix = prefix_embeddings(wl.wid, 0, P, cfg.hidden)
+    pre_dev = model.prefix_tensor(prefix)
+    y1 = kv.prefill(pre_dev)
+    # GPU AR continuation y1..y_{B+3}: the drafts are planted from it
+    cont = [y1]
+    for _ in range(B + 3):
+        cont.append(kv.ar_step()[0])
+    kv.rewind(P, y1)
+    n_reps = args.warmup + max(args.steps, args.profile_steps)
+    astar = plant_accept_lengths(wl.wid, 0, n_reps, B, wl.plant_p)
+    planted = np.full((n_reps, B), -1, dtype=np.int32)
+    for r, a in enumerate(astar):
+        # output so far is [y1] (c = 1); a0 = y2, so d_j = y_{2+j} = cont[j + 1] for j <= A*,
+        # and d_{A*+1} differs from y_{A*+3}
+        for j in range(1, B + 1):
+            if j <= a:
+                planted[r, j - 1] = cont[j + 1]
+            elif j == a + 1:
+                planted[r, j - 1] = (cont[j + 1] + 1) % (cfg.vocab - 1)
+                break
+    planted_dev = torch.from_numpy(planted).to("cuda")
+
+    def run(rep):
+        kv.rewind(P, y1)
+        c, A, _, _ = kv.round(B, planted_dev=planted_dev[rep])
+        return len(c), A
+
+    for r in range(args.warmup):
+        run(r)
+    torch.cuda.synchronize()
+    committed = 0
+    accepts = []
+    per_round = []
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ts = time.perf_counter()
+        n, A = run(args.warmup + k)
+        per_round.append(time.perf_counter() - ts)
+        committed += n
+        accepts.append(A)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for k in range(args.steps):
+        assert accepts[k] == min(int(astar[args.warmup + k]), B), "planted accept length not realized"
+    value = committed / elapsed
+    ms_step = elapsed * 1e3 / args.steps
+    t_med = statistics.median(per_round)
+    bytes_round = alg_bytes_round(cfg, P, B)
+
+    # per-kernel timing with HIP events (every launch of one kind per pass)
+    kinds = ["qkv", "attention", "combine", "o", "gate_up", "down", "lm_head", "argmax"]
+    breakdown = {}
+    for kind in kinds:
+        model.profile_kernel(kind)
+        model.profile_read(reset=True)
+        for k in range(args.profile_steps):
+            run(args.warmup + k)
+        us, launches = model.profile_read(reset=True)
+        breakdown[kind] = {"avg_us": us / max(launches, 1), "us_per_round": us / args.profile_steps,
+                           "launches_per_round": launches / args.profile_steps}
+    model.profile_kernel(None)
+    dom = max(breakdown, key=lambda k: breakdown[k]["us_per_round"])
+    M = B + 1
+    n_keys = P + B + 1
+    ab = alg_bytes_kernel(dom, cfg, M, n_keys)
+    achieved = ab / (breakdown[dom]["avg_us"] * 1e-6) / 1e9
+    print(json.dumps({"kernel_breakdown_us": breakdown, "dominant": dom}), file=sys.stderr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, weights, prefix, planted[args.warmup:], B)
+
+    line = {
+        "metric": "committed tokens/s (B=32, batch 1) + round time as % of HBM roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": cfg.n_layers, "hidden": cfg.hidden, "heads": cfg.n_heads,
+                   "kv_heads": cfg.n_kv_heads, "ffn": cfg.ffn, "vocab": cfg.vocab, "block_B": B,
+                   "cached_positions": P, "batch": 1, "mean_accept": float(np.mean(accepts)),
+                   "committed_per_round": committed / args.steps},
+        "round_us_median": t_med * 1e6,
+        "round_roofline_frac": bytes_round / t_med / (PEAK_HBM_GBS * 1e9),
+        "round_alg_bytes": bytes_round,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "alg_bytes_per_launch": ab,
+                     "avg_launch_us": breakdown[dom]["avg_us"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -209,6 +209,23 @@ int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_
 int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, int p, float* logits_dev,
                        int32_t* argmax, float* top1, float* top2, void* stream);
 
+/* Kernel timing hook for measurement. While a kind is selected, every
+ * launch of that kernel kind is bracketed by HIP events recorded on the
+ * stream it is launched on. Rounds and AR steps then run without graph
+ * replay. ssb_profile_read returns the summed event time and the launch
+ * count since the last reset; reset != 0 clears them.
+ * kind: one of SSB_K_*, or -1 to stop timing. */
+#define SSB_K_QKV 0
+#define SSB_K_ATTN 1
+#define SSB_K_COMBINE 2
+#define SSB_K_O 3
+#define SSB_K_GATEUP 4
+#define SSB_K_DOWN 5
+#define SSB_K_LMHEAD 6
+#define SSB_K_ARGMAX 7
+int ssb_profile_kernel(ssb_model* m, int kind);
+int ssb_profile_read(ssb_model* m, double* total_us, long long* launches, int reset);
+
 #ifdef __cplusplus
 }
 #endif

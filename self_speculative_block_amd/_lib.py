@@ -9,6 +9,7 @@ SSB_OK, SSB_EINVAL, SSB_ENOKV, SSB_EHIP, SSB_ESTATE, SSB_ENOMEM = 0, -1, -2, -3,
 SSB_F32, SSB_BF16 = 0, 1
 SSB_MAX_BATCH = 16
 SSB_MAX_BLOCK = 64
+KERNEL_KINDS = {"qkv": 0, "attention": 1, "combine": 2, "o": 3, "gate_up": 4, "down": 5, "lm_head": 6, "argmax": 7}
 
 c_int, c_float, c_double, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
 c_void_p = ctypes.c_void_p
@@ -63,6 +64,8 @@ SIGNATURES = {
                               ctypes.POINTER(SsbStats), c_void_p]),
     "ssb_round_batch": (c_int, [c_void_p, ctypes.POINTER(c_void_p), c_int, c_int, P_i32, c_void_p, P_i32,
                                 P_i32, P_i32, c_void_p]),
+    "ssb_profile_kernel": (c_int, [c_void_p, c_int]),
+    "ssb_profile_read": (c_int, [c_void_p, ctypes.POINTER(c_double), ctypes.POINTER(ctypes.c_longlong), c_int]),
     "ssb_forward_tokens": (c_int, [c_void_p, c_void_p, P_i32, c_int, c_int, c_void_p, P_i32, P_f32, P_f32,
                                    c_void_p]),
 }

@@ -84,7 +84,10 @@ struct ReqArgs {
   int astar[kMaxReq];                 // planted accept length (continuation mode)
 };
 
-struct AttnTask { int req, row0, nrows, max_lim; };
+// Row task of the attention kernel.  lim_mode 0: max_lim given; 1: draft
+// window (max limit p + B); 2: verify window (max limit p + B + 1), with p
+// read from the device request state.
+struct AttnTask { int req, row0, nrows, max_lim, lim_mode; };
 struct AttnTasks { int n; AttnTask t[kMaxTasks]; };
 
 
@@ -101,7 +104,7 @@ struct PrepArgs {
   const float* gain;           // attn_norm gain of layer 0
   int32_t* row_tok; int32_t* row_pos; int32_t* row_lim; int32_t* row_req;
   float* h; void* xg; float* ssq; int ssq_ld;
-  ReqArgs req;
+  const ReqArgs* req;          // device request state
 };
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
@@ -114,7 +117,7 @@ struct GemmArgs {
   void* q; int q_ld; int n_heads, n_kv, head_dim, layer, n_pages;   // QKV
   void* kv_pool; const float2* rope;
   const int32_t* row_pos; const int32_t* row_req;
-  const int32_t* pt[kMaxReq];
+  const ReqArgs* req;                           // device request state (page tables)
   void* act; int act_ld;                        // SWIGLU
   float* logits; int vocab; int mask_id;        // LOGITS
   float* am_v1; int32_t* am_i1; float* am_v2; int am_ld;
@@ -123,7 +126,7 @@ struct GemmArgs {
 struct AttnArgs {
   const void* q; int q_ld;                 // [rows][n_heads*hd]
   const void* kv_pool; int layer; int n_pages; int n_heads; int n_kv;
-  const int32_t* pt[kMaxReq];
+  const ReqArgs* req;                      // device request state (page tables, p)
   const int32_t* row_lim;
   float* part; int max_chunks;             // records [row][head][chunk][hd+4]
   void* out; int out_ld;                   // fold: [rows][n_heads*hd]
@@ -144,7 +147,7 @@ template <typename T> hipError_t launch_attn(const AttnArgs& a, int n_chunk_slot
 template <typename T>
 hipError_t launch_attn_combine(const float* part, int max_chunks, int n_heads, int head_dim, const int32_t* row_lim,
                                int M, void* out, int out_ld, hipStream_t st);
-hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs& ra, int eos_id, int32_t* out,
-                         int out_stride, hipStream_t st);
+hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
+                         int32_t* out, int out_stride, hipStream_t st);
 
 }  // namespace ssb

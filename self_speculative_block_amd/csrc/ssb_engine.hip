@@ -14,7 +14,10 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <map>
 #include <memory>
+#include <tuple>
 #include <new>
 #include <string>
 #include <vector>
@@ -116,6 +119,16 @@ struct ssb_model {
   int max_decode_rows;
   int32_t* accept_dev;
   int32_t* tok_dev;
+  ReqArgs* req_dev;   // device request state read by every kernel of a forward
+  ReqArgs* req_pin;   // pinned staging of the request state
+  hipStream_t cap;    // private stream used only to capture graphs
+  std::map<std::tuple<int, void*, int, int>, hipGraphExec_t> graphs;   // (kind, pool, R, B)
+  // kernel timing hook
+  int prof_kind = -1;
+  std::vector<hipEvent_t> prof_ev;    // pairs (start, end)
+  int prof_used = 0;                  // pairs recorded since the last collect
+  double prof_us = 0;
+  long long prof_launches = 0;
   // pinned host staging
   int32_t* pin_i32;   // [max_rows + kMaxReq*kOutStride]
   float* pin_f32;     // [2*max_rows]
@@ -124,6 +137,28 @@ struct ssb_model {
 namespace {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Kernel timing hook: an event pair around each launch of the selected kind.
+void prof_begin(ssb_model* m, int kind, hipStream_t st) {
+  if (m->prof_kind != kind) return;
+  if (m->prof_used * 2 + 2 > (int)m->prof_ev.size()) fail(SSB_EINVAL, "kernel timing: too many launches per call");
+  hip_check(hipEventRecord(m->prof_ev[2 * m->prof_used], st), "profile event");
+}
+void prof_end(ssb_model* m, int kind, hipStream_t st) {
+  if (m->prof_kind != kind) return;
+  hip_check(hipEventRecord(m->prof_ev[2 * m->prof_used + 1], st), "profile event");
+  ++m->prof_used;
+}
+// Called after the stream has been synchronized.
+void prof_collect(ssb_model* m) {
+  for (int i = 0; i < m->prof_used; ++i) {
+    float ms = 0.f;
+    hip_check(hipEventElapsedTime(&ms, m->prof_ev[2 * i], m->prof_ev[2 * i + 1]), "profile elapsed");
+    m->prof_us += ms * 1000.0;
+  }
+  m->prof_launches += m->prof_used;
+  m->prof_used = 0;
+}
 
 // K steps per wave: 8 waves per workgroup up to K = 8 * 8 steps, then 16
 int kpw_for(int K, int elem) {
@@ -263,6 +298,7 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const size_t w_apart = take((size_t)m->max_decode_rows * c.n_heads * m->max_chunks * (hd + 4) * 4);
   const size_t w_acc = take((size_t)kMaxReq * kOutStride * 4);
   const size_t w_tok = take((size_t)MR * 4);
+  const size_t w_req = take(sizeof(ReqArgs));
   if (hipMalloc(&m->ws, off) != hipSuccess) fail(SSB_ENOMEM, "hipMalloc of workspace failed");
   char* wsb = static_cast<char*>(m->ws);
   m->h = reinterpret_cast<float*>(wsb + w_h);
@@ -284,6 +320,10 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   m->apart = reinterpret_cast<float*>(wsb + w_apart);
   m->accept_dev = reinterpret_cast<int32_t*>(wsb + w_acc);
   m->tok_dev = reinterpret_cast<int32_t*>(wsb + w_tok);
+  m->req_dev = reinterpret_cast<ReqArgs*>(wsb + w_req);
+  if (hipHostMalloc(reinterpret_cast<void**>(&m->req_pin), sizeof(ReqArgs), hipHostMallocDefault) != hipSuccess)
+    fail(SSB_ENOMEM, "pinned host allocation failed");
+  hip_check(hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking), "capture stream");
   if (hipHostMalloc(reinterpret_cast<void**>(&m->pin_i32), (size_t)(MR + kMaxReq * kOutStride) * 4,
                     hipHostMallocDefault) != hipSuccess)
     fail(SSB_ENOMEM, "pinned host allocation failed");
@@ -302,8 +342,9 @@ struct FwdSpec {
   int M;              // rows
   int pos0;           // PREFILL / TOKENS
   const void* prefix; // PREFILL
-  ReqArgs ra;         // DRAFT / VERIFY (and page tables for all modes)
+  ReqArgs ra;         // host copy of the request state (already uploaded to the device)
   int max_pos;        // largest position of any row + 1
+  bool graph;         // launches are being captured: no round-dependent launch shapes
   float* logits;      // nullable [M][vocab] (all rows) or [1][vocab] (last row only)
   bool lm_last_only;  // LM head on the last row only (prefill)
 };
@@ -318,7 +359,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   pa.pos0 = f.pos0; pa.prefix = f.prefix; pa.tokens = m->tok_dev; pa.am_prev = m->am_tok;
   pa.embed = m->embed; pa.gain = m->attn_norm[0];
   pa.row_tok = m->row_tok; pa.row_pos = m->row_pos; pa.row_lim = m->row_lim; pa.row_req = m->row_req;
-  pa.h = m->h; pa.xg = m->xg; pa.ssq = m->ssq; pa.ssq_ld = MR; pa.req = f.ra;
+  pa.h = m->h; pa.xg = m->xg; pa.ssq = m->ssq; pa.ssq_ld = MR; pa.req = m->req_dev;
   hip_check(launch_prep<T>(pa, st), "prep");
 
   GemmArgs g{};
@@ -328,7 +369,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   g.q = m->q; g.q_ld = qd;
   g.n_heads = c.n_heads; g.n_kv = c.n_kv_heads; g.head_dim = c.head_dim; g.n_pages = pool->n_pages;
   g.kv_pool = pool->base; g.rope = m->rope; g.row_pos = m->row_pos; g.row_req = m->row_req;
-  for (int r = 0; r < kMaxReq; ++r) g.pt[r] = f.ra.pt[r];
+  g.req = m->req_dev;
   g.act = m->act; g.act_ld = c.ffn;
   g.vocab = c.vocab; g.mask_id = c.mask_id;
   auto set_w = [](GemmArgs& a, const GemmShape& s) { a.W = s.W; a.K = s.K; a.n_tiles = s.n_tiles; };
@@ -336,37 +377,28 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   AttnArgs at{};
   at.q = m->q; at.q_ld = qd; at.kv_pool = pool->base; at.n_pages = pool->n_pages;
   at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads;
-  for (int r = 0; r < kMaxReq; ++r) at.pt[r] = f.ra.pt[r];
+  at.req = m->req_dev;
   at.row_lim = m->row_lim; at.part = m->apart; at.max_chunks = m->max_chunks;
   at.out = m->attn; at.out_ld = qd;
   at.fold = M > m->max_decode_rows ? 1 : 0;
   at.scale = 1.0f / std::sqrt((float)c.head_dim);
   // row tasks: windows of each request (draft/verify) or one request's rows
   at.tasks.n = 0;
-  // lim_of(row j of a request window or of the row set): largest visible key
-  auto add_tasks = [&](int req, int row0, int nrows, auto lim_of) {
+  // row tasks; window tasks read their largest visibility limit (p + B, or
+  // p + B + 1 for verify) from the device request state
+  auto add_tasks = [&](int req, int row0, int nrows, int lim_mode, int last_pos) {
     for (int r = 0; r < nrows; r += kTaskRows) {
       if (at.tasks.n >= kMaxTasks) fail(SSB_EINVAL, "too many attention row tasks");
       const int n = std::min(kTaskRows, nrows - r);
-      int mx = -1;
-      for (int j = r; j < r + n; ++j) mx = std::max(mx, lim_of(j));
-      at.tasks.t[at.tasks.n++] = AttnTask{req, row0 + r, n, mx};
+      at.tasks.t[at.tasks.n++] = AttnTask{req, row0 + r, n, last_pos < 0 ? -1 : last_pos - (nrows - r - n), lim_mode};
     }
   };
-  if (f.mode == PREP_DRAFT) {
-    for (int r = 0; r < f.ra.n; ++r) {
-      const int p = f.ra.p[r], B = f.ra.B;
-      add_tasks(r, f.ra.row0[r], B + 1, [&](int j) { return j == 0 ? p : p + B; });
-    }
-  } else if (f.mode == PREP_VERIFY) {
-    for (int r = 0; r < f.ra.n; ++r) {
-      const int p = f.ra.p[r];
-      add_tasks(r, f.ra.row0[r], f.ra.B + 1, [&](int j) { return p + 1 + j; });
-    }
+  if (f.mode == PREP_DRAFT || f.mode == PREP_VERIFY) {
+    for (int r = 0; r < f.ra.n; ++r) add_tasks(r, f.ra.row0[r], f.ra.B + 1, f.mode == PREP_DRAFT ? 1 : 2, -1);
   } else {
-    add_tasks(0, 0, M, [&](int j) { return f.pos0 + j; });
+    add_tasks(0, 0, M, 0, f.pos0 + M - 1);
   }
-  const int chunk_slots = (f.max_pos - 1) / kKeyChunk + 1;
+  const int chunk_slots = f.graph ? m->max_chunks : (f.max_pos - 1) / kKeyChunk + 1;
 
   for (int l = 0; l < c.n_layers; ++l) {
     g.layer = l;
@@ -374,32 +406,45 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       GemmArgs a = g;
       set_w(a, m->qkv[l]);
       a.x = m->xg; a.ldx = H;
+      prof_begin(m, SSB_K_QKV, st);
       hip_check(launch_gemm<T>(a, EPI_QKV, m->qkv[l].kpw, st), "qkv gemm");
+      prof_end(m, SSB_K_QKV, st);
     }
     at.layer = l;
+    prof_begin(m, SSB_K_ATTN, st);
     hip_check(launch_attn<T>(at, chunk_slots, c.head_dim, st), "attention");
-    if (!at.fold)
+    prof_end(m, SSB_K_ATTN, st);
+    if (!at.fold) {
+      prof_begin(m, SSB_K_COMBINE, st);
       hip_check(launch_attn_combine<T>(m->apart, m->max_chunks, c.n_heads, c.head_dim, m->row_lim, M, m->attn,
                                        qd, st), "attention combine");
+      prof_end(m, SSB_K_COMBINE, st);
+    }
     {  // O + residual; next input xg = h * mlp_norm[l]
       GemmArgs a = g;
       set_w(a, m->o[l]);
       a.x = m->attn; a.ldx = qd;
       a.gain_next = m->mlp_norm[l];
+      prof_begin(m, SSB_K_O, st);
       hip_check(launch_gemm<T>(a, EPI_RESID, m->o[l].kpw, st), "o gemm");
+      prof_end(m, SSB_K_O, st);
     }
     {  // gate|up + SwiGLU
       GemmArgs a = g;
       set_w(a, m->gu[l]);
       a.x = m->xg; a.ldx = H;
+      prof_begin(m, SSB_K_GATEUP, st);
       hip_check(launch_gemm<T>(a, EPI_SWIGLU, m->gu[l].kpw, st), "gate/up gemm");
+      prof_end(m, SSB_K_GATEUP, st);
     }
     {  // down + residual; next input xg = h * (next attn_norm | final_norm)
       GemmArgs a = g;
       set_w(a, m->d[l]);
       a.x = m->act; a.ldx = c.ffn;
       a.gain_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
+      prof_begin(m, SSB_K_DOWN, st);
       hip_check(launch_gemm<T>(a, EPI_RESID, m->d[l].kpw, st), "down gemm");
+      prof_end(m, SSB_K_DOWN, st);
     }
   }
   // LM head + argmax
@@ -416,9 +461,13 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       a.M = 1;
       rows = 1;
     }
+    prof_begin(m, SSB_K_LMHEAD, st);
     hip_check(launch_gemm<T>(a, EPI_LOGITS, m->lm.kpw, st), "lm head gemm");
+    prof_end(m, SSB_K_LMHEAD, st);
+    prof_begin(m, SSB_K_ARGMAX, st);
     hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, m->lm.n_tiles, MR, rows, m->am_tok, m->am_top1, m->am_top2,
                             st), "argmax");
+    prof_end(m, SSB_K_ARGMAX, st);
   }
 }
 
@@ -458,11 +507,48 @@ void kv_trim(ssb_kv* kv, int keep_tokens) {
 
 hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
+
 void check_model_kv(ssb_model* m, ssb_kv* kv) {
   if (!m) fail(SSB_EINVAL, "null model");
   if (!kv) fail(SSB_EINVAL, "null kv");
   if (kv->pool->m != m) fail(SSB_EINVAL, "kv belongs to another model");
   hip_check(hipSetDevice(m->device), "hipSetDevice");
+}
+
+// Copies the request state to the device (stream-ordered before the launches
+// that read it).  The pinned staging buffer is reused: every ABI call
+// synchronizes its stream before returning.
+void upload_req(ssb_model* m, const ReqArgs& ra, hipStream_t st) {
+  *m->req_pin = ra;
+  hip_check(hipMemcpyAsync(m->req_dev, m->req_pin, sizeof(ReqArgs), hipMemcpyHostToDevice, st),
+            "upload request state");
+}
+
+// Graph of a fixed launch sequence, captured once per (kind, pool, R, B) on a
+// private stream and replayed on the caller's stream.  Launch shapes inside
+// never depend on the round; round state is read from the device.
+hipGraphExec_t get_graph(ssb_model* m, int kind, ssb_pool* pool, int R, int B,
+                         const std::function<void(hipStream_t)>& body) {
+  const auto key = std::make_tuple(kind, static_cast<void*>(pool), R, B);
+  auto it = m->graphs.find(key);
+  if (it != m->graphs.end()) return it->second;
+  hip_check(hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal), "begin capture");
+  try {
+    body(m->cap);
+  } catch (...) {
+    hipGraph_t tmp = nullptr;
+    (void)hipStreamEndCapture(m->cap, &tmp);
+    if (tmp) (void)hipGraphDestroy(tmp);
+    throw;
+  }
+  hipGraph_t g = nullptr;
+  hip_check(hipStreamEndCapture(m->cap, &g), "end capture");
+  hipGraphExec_t ex = nullptr;
+  const hipError_t e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  hip_check(e, "graph instantiate");
+  m->graphs[key] = ex;
+  return ex;
 }
 
 ReqArgs single_req(ssb_kv* kv, int B, int max_commit) {
@@ -484,19 +570,22 @@ void prefill(ssb_model* m, ssb_kv* kv, const void* prefix, int P, int32_t* first
   if (kv->seq_len != 0 || kv->x0 >= 0) fail(SSB_ESTATE, "prefill needs an empty kv");
   if (P + 1 > m->c.max_positions) fail(SSB_EINVAL, "P exceeds max_positions");
   kv_ensure(kv, P, st);
+  const ReqArgs ra = single_req(kv, 0, 1);
+  upload_req(m, ra, st);
   for (int p0 = 0; p0 < P; p0 += m->c.max_rows) {
     FwdSpec f{};
     f.mode = PREP_PREFILL;
     f.M = std::min(m->c.max_rows, P - p0);
     f.pos0 = p0;
     f.prefix = prefix;
-    f.ra = single_req(kv, 0, 1);
+    f.ra = ra;
     f.max_pos = p0 + f.M;
     f.lm_last_only = true;
     run_forward(m, kv->pool, f, st);
   }
   hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, 4, hipMemcpyDeviceToHost, st), "copy token");
   hip_check(hipStreamSynchronize(st), "prefill sync");
+  prof_collect(m);
   const int32_t y1 = m->pin_i32[0];
   if (y1 < 0 || y1 >= m->c.vocab) fail(SSB_EHIP, "prefill produced no valid token (NaN logits?)");
   kv->seq_len = P;
@@ -529,6 +618,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
       if (kvs[q] == kvs[r]) fail(SSB_EINVAL, "the same kv appears twice in a batch");
   }
   for (int r = 0; r < R; ++r) kv_ensure(kvs[r], kvs[r]->seq_len + B + 2, st);
+  if (cont && R != 1) fail(SSB_EINVAL, "planting from a continuation needs R == 1");
   ReqArgs ra{};
   ra.n = R;
   ra.B = B;
@@ -546,20 +636,32 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
     ra.astar[r] = astar ? astar[r] : 0;
     maxpos = std::max(maxpos, ra.p[r] + B + 2);
   }
-  FwdSpec f{};
-  f.M = R * (B + 1);
-  f.ra = ra;
-  f.max_pos = maxpos;
-  f.mode = PREP_DRAFT;
-  f.logits = dlog;
-  run_forward(m, pool, f, st);
-  f.mode = PREP_VERIFY;
-  f.logits = vlog;
-  run_forward(m, pool, f, st);
-  hip_check(launch_accept(m->row_tok, m->am_tok, ra, c.eos_id, m->accept_dev, kOutStride, st), "accept");
-  hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)R * kOutStride * 4, hipMemcpyDeviceToHost, st),
-            "copy accept");
+  upload_req(m, ra, st);
+  auto body = [&](hipStream_t s, bool graph) {
+    FwdSpec f{};
+    f.M = R * (B + 1);
+    f.ra = ra;
+    f.max_pos = maxpos;
+    f.graph = graph;
+    f.mode = PREP_DRAFT;
+    f.logits = dlog;
+    run_forward(m, pool, f, s);
+    f.mode = PREP_VERIFY;
+    f.logits = vlog;
+    run_forward(m, pool, f, s);
+    hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, R, c.eos_id, m->accept_dev, kOutStride, s),
+              "accept");
+    hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)R * kOutStride * 4, hipMemcpyDeviceToHost, s),
+              "copy accept");
+  };
+  if (dlog || vlog || m->prof_kind >= 0) {
+    body(st, false);
+  } else {
+    hipGraphExec_t ex = get_graph(m, 0, pool, R, B, [&](hipStream_t s) { body(s, true); });
+    hip_check(hipGraphLaunch(ex, st), "round graph launch");
+  }
   hip_check(hipStreamSynchronize(st), "round sync");
+  prof_collect(m);
   for (int r = 0; r < R; ++r) {
     const int32_t* o = m->pin_i32 + (size_t)r * kOutStride;
     RoundOut& ro = out[r];
@@ -583,15 +685,27 @@ void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_
   if (kv->seq_len + 1 > m->c.max_positions) fail(SSB_ENOKV, "position exceeds max_positions");
   kv_ensure(kv, kv->seq_len + 1, st);
   // an AR step is a draft window with no masks: [x0] at p, keys <= p
-  FwdSpec f{};
-  f.mode = PREP_DRAFT;
-  f.M = 1;
-  f.ra = single_req(kv, 0, 1);
-  f.max_pos = kv->seq_len + 1;
-  f.logits = logits;
-  run_forward(m, kv->pool, f, st);
-  hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, 4, hipMemcpyDeviceToHost, st), "copy token");
+  const ReqArgs ra = single_req(kv, 0, 1);
+  upload_req(m, ra, st);
+  auto body = [&](hipStream_t s, bool graph) {
+    FwdSpec f{};
+    f.mode = PREP_DRAFT;
+    f.M = 1;
+    f.ra = ra;
+    f.max_pos = kv->seq_len + 1;
+    f.graph = graph;
+    f.logits = logits;
+    run_forward(m, kv->pool, f, s);
+    hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, 4, hipMemcpyDeviceToHost, s), "copy token");
+  };
+  if (logits || m->prof_kind >= 0) {
+    body(st, false);
+  } else {
+    hipGraphExec_t ex = get_graph(m, 1, kv->pool, 1, 0, [&](hipStream_t s) { body(s, true); });
+    hip_check(hipGraphLaunch(ex, st), "AR graph launch");
+  }
   hip_check(hipStreamSynchronize(st), "ar sync");
+  prof_collect(m);
   const int32_t y = m->pin_i32[0];
   if (y < 0 || y >= m->c.vocab) fail(SSB_EHIP, "AR step produced no valid token (NaN logits?)");
   kv->seq_len += 1;
@@ -626,6 +740,10 @@ void ssb_free_model(ssb_model* m) {
   (void)hipDeviceSynchronize();
   (void)hipFree(m->wmem);
   (void)hipFree(m->ws);
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (hipEvent_t e : m->prof_ev) (void)hipEventDestroy(e);
+  (void)hipStreamDestroy(m->cap);
+  (void)hipHostFree(m->req_pin);
   (void)hipHostFree(m->pin_i32);
   (void)hipHostFree(m->pin_f32);
   delete m;
@@ -866,6 +984,7 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
     f.M = M;
     f.pos0 = p;
     f.ra = single_req(kv, 0, 1);
+    upload_req(m, f.ra, st);
     f.max_pos = p + M;
     f.logits = logits_dev;
     run_forward(m, kv->pool, f, st);
@@ -875,11 +994,37 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
     hip_check(hipMemcpyAsync(m->pin_f32 + m->c.max_rows, m->am_top2, (size_t)M * 4, hipMemcpyDeviceToHost, st),
               "copy top2");
     hip_check(hipStreamSynchronize(st), "forward sync");
+    prof_collect(m);
     std::memcpy(argmax, m->pin_i32, (size_t)M * 4);
     if (top1) std::memcpy(top1, m->pin_f32, (size_t)M * 4);
     if (top2) std::memcpy(top2, m->pin_f32 + m->c.max_rows, (size_t)M * 4);
     // positions beyond the committed length hold no committed state
     kv_trim(kv, std::max(kv->seq_len + m->c.block_B + 2, 0));
+  });
+}
+
+int ssb_profile_kernel(ssb_model* m, int kind) {
+  return guard([&] {
+    if (!m) fail(SSB_EINVAL, "null model");
+    if (kind < -1 || kind > SSB_K_ARGMAX) fail(SSB_EINVAL, "unknown kernel kind");
+    hip_check(hipSetDevice(m->device), "hipSetDevice");
+    if (kind >= 0 && m->prof_ev.empty()) {
+      // two forwards of a round launch each kind at most n_layers + 1 times, plus prefill chunks
+      const int pairs = 8 * (m->c.n_layers + 2);
+      m->prof_ev.resize(2 * pairs);
+      for (auto& e : m->prof_ev) hip_check(hipEventCreate(&e), "event create");
+    }
+    m->prof_kind = kind;
+    m->prof_used = 0;
+  });
+}
+
+int ssb_profile_read(ssb_model* m, double* total_us, long long* launches, int reset) {
+  return guard([&] {
+    if (!m) fail(SSB_EINVAL, "null model");
+    if (total_us) *total_us = m->prof_us;
+    if (launches) *launches = m->prof_launches;
+    if (reset) { m->prof_us = 0; m->prof_launches = 0; }
   });
 }
 

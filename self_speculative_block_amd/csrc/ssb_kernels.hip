@@ -82,15 +82,16 @@ __device__ __forceinline__ void window_row(const PrepArgs& a, int m, int& tok, i
   } else if (a.mode == PREP_TOKENS) {
     tok = a.tokens[m]; pos = a.pos0 + m; lim = pos; req = 0;
   } else {
-    const int W = a.req.B + 1;
+    const ReqArgs& ra = *a.req;
+    const int W = ra.B + 1;
     const int r = m / W, j = m % W;
     req = r;
-    const int p = a.req.p[r];
+    const int p = ra.p[r];
     if (a.mode == PREP_DRAFT) {
       // draft window: boundary x0 at p (causal), masks at p+1..p+B (see the window)
-      tok = j == 0 ? a.req.x0[r] : a.mask_id;
+      tok = j == 0 ? ra.x0[r] : a.mask_id;
       pos = p + j;
-      lim = j == 0 ? p : p + a.req.B;
+      lim = j == 0 ? p : p + ra.B;
     } else {
       // verify window [a0, d1..dB] at p+1..p+B+1, causal; row j of the draft
       // predicted a0 (j = 0) or d_j
@@ -99,14 +100,14 @@ __device__ __forceinline__ void window_row(const PrepArgs& a, int m, int& tok, i
       tok = a.am_prev[m];
       if (j >= 1) {
         int pl = -1;
-        if (a.req.planted[r]) {
-          pl = a.req.planted[r][j - 1];
-        } else if (a.req.cont[r]) {
-          const int idx = a.req.cont_c[r] + j;          // 0-based index of y_{c+1+j}
-          const int as = a.req.astar[r];
-          if (idx < a.req.cont_len[r]) {
-            if (j <= as) pl = a.req.cont[r][idx];
-            else if (j == as + 1) pl = (a.req.cont[r][idx] + 1) % (a.vocab - 1);
+        if (ra.planted[r]) {
+          pl = ra.planted[r][j - 1];
+        } else if (ra.cont[r]) {
+          const int idx = ra.cont_c[r] + j;             // 0-based index of y_{c+1+j}
+          const int as = ra.astar[r];
+          if (idx < ra.cont_len[r]) {
+            if (j <= as) pl = ra.cont[r][idx];
+            else if (j == as + 1) pl = (ra.cont[r][idx] + 1) % (a.vocab - 1);
           }
         }
         if (pl >= 0 && pl < a.vocab) tok = pl;
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(1024) void k_gemm(GemmArgs a) {
       if (kind == 0) {
         dst = reinterpret_cast<T*>(a.q) + (size_t)m * a.q_ld + head * hd;
       } else {
-        const int32_t* pt = a.pt[a.row_req[m]];
+        const int32_t* pt = a.req->pt[a.row_req[m]];
         const int page = pt[pos / kPage], slot = pos % kPage;
         const size_t base = (((size_t)a.layer * a.n_pages + page) * 2 + (kind - 1)) * a.n_kv + head;
         dst = reinterpret_cast<T*>(a.kv_pool) + (base * kPage + slot) * hd;
@@ -416,12 +417,13 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   const int g = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n_rep = a.n_heads / a.n_kv;
-  const int32_t* pt = a.pt[task.req];
+  const int32_t* pt = a.req->pt[task.req];
   const int n_units = n_rep * MT;
 
   if (threadIdx.x < kTaskRows)
     s_lim[threadIdx.x] = threadIdx.x < task.nrows ? a.row_lim[task.row0 + threadIdx.x] : -1;
-  const int maxlim = task.max_lim;          // largest visibility limit of the task's rows
+  // largest visibility limit of the task's rows
+  const int maxlim = task.lim_mode == 0 ? task.max_lim : a.req->p[task.req] + a.req->B + (task.lim_mode == 2 ? 1 : 0);
   int cbeg, cend;
   if (a.fold) { cbeg = 0; cend = maxlim / kKeyChunk + 1; }
   else {
@@ -650,8 +652,9 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, in
 // first EOS and at the output budget; a_{A+1} becomes the next boundary.
 // Output per request: [A, n_committed, next_x0, eos_seen, committed...].
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int32_t* am, ReqArgs ra,
+__global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* rap,
                                                int eos_id, int32_t* out, int out_stride) {
+  const ReqArgs& ra = *rap;
   const int r = blockIdx.x, j = threadIdx.x;
   const int B = ra.B, row0 = ra.row0[r];
   const bool mismatch = j < B && row_tok[row0 + 1 + j] != am[row0 + j];
@@ -771,9 +774,9 @@ template hipError_t launch_attn_combine<bf16_t>(const float*, int, int, int, con
 template hipError_t launch_attn_combine<float>(const float*, int, int, int, const int32_t*, int, void*, int,
                                                hipStream_t);
 
-hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs& ra, int eos_id,
+hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
                          int32_t* out, int out_stride, hipStream_t st) {
-  hipLaunchKernelGGL(k_accept, dim3(ra.n), dim3(64), 0, st, row_tok, am, ra, eos_id, out, out_stride);
+  hipLaunchKernelGGL(k_accept, dim3(n_req), dim3(64), 0, st, row_tok, am, ra, eos_id, out, out_stride);
   return hipGetLastError();
 }
 

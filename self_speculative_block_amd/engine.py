@@ -90,6 +90,15 @@ class Model:
         return torch.from_numpy(np.ascontiguousarray(prefix, dtype=np.float32)).to(self.device).to(
             torch_dtype(self.cfg))
 
+    def profile_kernel(self, kind):
+        """Start timing every launch of one kernel kind (name in KERNEL_KINDS), or stop (None)."""
+        L.check(self.lib.ssb_profile_kernel(self.h, -1 if kind is None else L.KERNEL_KINDS[kind]))
+
+    def profile_read(self, reset=True):
+        us, n = ctypes.c_double(), ctypes.c_longlong()
+        L.check(self.lib.ssb_profile_read(self.h, byref(us), byref(n), 1 if reset else 0))
+        return us.value, n.value
+
     def close(self):
         if self.h:
             self.lib.ssb_free_model(self.h)
