@@ -77,6 +77,7 @@ struct ReqArgs {
   int row0[kMaxReq];                  // first row of this request's window
   int max_commit[kMaxReq];            // remaining output budget
   const int32_t* pt[kMaxReq];         // device page table of the request
+  int npg[kMaxReq];                   // valid entries of pt
   const int32_t* planted[kMaxReq];    // nullable device [B]: -1 keeps the draft's own token
   const int32_t* cont[kMaxReq];       // nullable device AR continuation for planting
   int cont_len[kMaxReq];
@@ -103,30 +104,59 @@ struct PrepArgs {
   const void* embed;           // [vocab][hidden] of T
   const float* gain;           // attn_norm gain of layer 0
   int32_t* row_tok; int32_t* row_pos; int32_t* row_lim; int32_t* row_req;
-  float* h; void* xg; float* ssq; int ssq_ld;
+  int32_t* row_slot;           // physical KV slot (page * 16 + offset) of each row
+  float2* row_cs;              // rotary (cos, sin) of each row [M][hd/2]
+  const float2* rope; int half;   // rotary table [max_positions][hd/2]
+  int32_t* fwd_pt; int pt_ld;     // page ids of this forward's requests [req][pt_ld] (0 past npg)
+  float* h; void* xg; float* ssq; int ssq_ld;   // ssq: per-16-column sums of squares [M][ssq_ld]
   const ReqArgs* req;          // device request state
 };
 
-enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };
 
 struct GemmArgs {
   const uint4* W; int K; int n_tiles; int M;
+  int NT, KSL, S;                               // tiles per workgroup, K slices per tile, K ranges (grid y)
+  float* part; int part_ld;                     // PARTIAL: [S][M][part_ld] fp32 sums
   const void* x; int ldx;                       // input rows [M][ldx] of T
-  const float* ssq; int ssq_ld; int n_ssq; float eps; int hidden;   // 1/rms row scale (norm inputs)
+  const float* ssq; int ssq_ld; int n_ssq; float eps; int hidden;   // 1/rms row scale: ssq [M][ssq_ld]
   float* h; const float* gain_next; void* xg_out; float* ssq_out;   // RESID: residual, next input
   void* q; int q_ld; int n_heads, n_kv, head_dim, layer, n_pages;   // QKV
-  void* kv_pool; const float2* rope;
-  const int32_t* row_pos; const int32_t* row_req;
-  const ReqArgs* req;                           // device request state (page tables)
+  void* kv_pool;
+  const int32_t* row_slot; const float2* row_cs;   // QKV: physical KV slot, rotary (cos, sin) [M][hd/2]
   void* act; int act_ld;                        // SWIGLU
   float* logits; int vocab; int mask_id;        // LOGITS
-  float* am_v1; int32_t* am_i1; float* am_v2; int am_ld;
+  float* am_v1; int32_t* am_i1; float* am_v2; int am_ld;   // LOGITS: records [M][am_ld]
 };
+
+// Dynamic LDS layout of k_gemm (byte offsets), shared by the kernel and its launcher:
+// activation slab [MB][K range + 16 B pad], K-slice partial tiles [W][MT][64] f32x4,
+// result tiles [NT][MB][17] f32, epilogue inputs.
+struct GemmLds { int red, ctile, ssq, pre, total; };
+__host__ __device__ inline GemmLds gemm_lds(int MT, int kr_bytes, int NT, int KSL, int n_ssq, int epi) {
+  const int MB = 16 * MT;
+  GemmLds L;
+  L.red = MB * (kr_bytes + 16);
+  L.ctile = L.red + NT * KSL * MT * 64 * 16;
+  L.ssq = L.ctile + NT * MB * 17 * 4;
+  const bool norm = epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_LOGITS;
+  (void)norm; (void)n_ssq;
+  L.pre = (L.ssq + 15) / 16 * 16;
+  int pre = 0;
+  if (epi == EPI_QKV) pre = MB * 8 * 8 + MB * 4;           // (cos, sin) of 8 pairs per row, KV slot per row
+  if (epi == EPI_RESID) pre = NT * MB * 16 * 4 + NT * 16 * 4;   // h tile, next gain
+  L.total = L.pre + pre;
+  return L;
+}
+constexpr int kGemmMaxLds = 160 * 1024 - 1024;   // dynamic LDS budget (static arrays take < 1 KiB)
+constexpr int kGemmThreads = 512;                 // 8 waves per GEMM workgroup
+constexpr int kAttnThreads = 1024;                // 16 waves per attention workgroup: one (head, row tile) each
 
 struct AttnArgs {
   const void* q; int q_ld;                 // [rows][n_heads*hd]
   const void* kv_pool; int layer; int n_pages; int n_heads; int n_kv;
-  const ReqArgs* req;                      // device request state (page tables, p)
+  const ReqArgs* req;                      // device request state (p, B)
+  const int32_t* fwd_pt; int pt_ld;        // page ids [req][pt_ld], gathered by the prep kernel
   const int32_t* row_lim;
   float* part; int max_chunks;             // records [row][head][chunk][hd+4]
   void* out; int out_ld;                   // fold: [rows][n_heads*hd]
@@ -140,13 +170,15 @@ template <typename T>
 hipError_t launch_pack(uint4* dst, int n_tiles, int K, int mode, const void* s0, const void* s1, const void* s2,
                        int n0, int n1, int hd, hipStream_t st);
 template <typename T> hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
-template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, int kpw, hipStream_t st);
+template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
+template <typename T> hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st);
+int gemm_max_mt(int elem, int K, int S, int NT, int KSL, int n_ssq, int epi);
 hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, int n_groups, int ld, int M,
                          int32_t* tok, float* top1, float* top2, hipStream_t st);
 template <typename T> hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipStream_t st);
 template <typename T>
-hipError_t launch_attn_combine(const float* part, int max_chunks, int n_heads, int head_dim, const int32_t* row_lim,
-                               int M, void* out, int out_ld, hipStream_t st);
+hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, int n_heads, int head_dim,
+                               const int32_t* row_lim, int M, void* out, int out_ld, hipStream_t st);
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
                          int32_t* out, int out_stride, hipStream_t st);
 

@@ -86,7 +86,8 @@ struct ssb_kv {
 
 struct GemmShape {
   const uint4* W;
-  int K, n_tiles, kpw;   // reduction length, 16-column tiles, K steps per wave
+  int K, n_tiles;        // reduction length, 16-column tiles
+  int NT, KSL, S;        // tiles per workgroup, K slices per tile, K ranges
 };
 
 struct ssb_model {
@@ -109,7 +110,11 @@ struct ssb_model {
   void* q;
   void* attn;
   void* act;
-  int32_t *row_tok, *row_pos, *row_lim, *row_req;
+  int32_t *row_tok, *row_pos, *row_lim, *row_req, *row_slot;
+  float2* row_cs;
+  float* part;        // K-split partial sums [S][max_rows][hidden]
+  int32_t* fwd_pt;    // page ids of the current forward's requests [kMaxReq][pt_ld]
+  int pt_ld;
   int32_t* am_tok;
   float *am_top1, *am_top2;
   float *amv1, *amv2;
@@ -160,10 +165,31 @@ void prof_collect(ssb_model* m) {
   m->prof_used = 0;
 }
 
-// K steps per wave: 8 waves per workgroup up to K = 8 * 8 steps, then 16
-int kpw_for(int K, int elem) {
-  const int ksteps = K / (elem == 2 ? 32 : 16);
-  return std::max(1, std::min(8, ksteps / 8));
+// Workgroup shape of a GEMM: NT 16-column tiles per workgroup, KSL K slices
+// per tile (8 waves in all), and S K ranges over the grid's y axis for a GEMM
+// with too few tiles to cover the CUs (its epilogue then runs in
+// k_resid_reduce).  Each wave chains 4..16 K steps (bf16) or 1..4 (f32).
+// The shape depends on the GEMM's dimensions only, never on the row count.
+GemmShape plan_gemm(int K, int n_tiles, int elem, int epi) {
+  const int KS = elem == 2 ? 32 : 16, ksteps = K / KS;
+  const int kmin = elem == 2 ? 4 : 1, kmax = elem == 2 ? 16 : 4;
+  GemmShape g{};
+  g.K = K;
+  g.NT = epi == EPI_SWIGLU ? 2 : epi == EPI_LOGITS ? 4 : 1;
+  g.KSL = epi == EPI_SWIGLU ? 4 : epi == EPI_LOGITS ? 2 : 8;
+  g.S = 1;
+  g.n_tiles = (n_tiles + g.NT - 1) / g.NT * g.NT;
+  if (epi == EPI_PARTIAL)
+    while (g.n_tiles / g.NT * g.S < 256 && g.S < 8 && ksteps / (2 * g.S * g.KSL) >= kmin) g.S *= 2;
+  while (g.KSL > 1 && ksteps / (g.S * g.KSL) < kmin) g.KSL /= 2;
+  while (ksteps / (g.S * g.KSL) > kmax) {
+    if (g.NT * g.KSL < 8) g.KSL *= 2;
+    else if (g.NT > 1 && n_tiles % (g.NT / 2) == 0) { g.NT /= 2; g.KSL *= 2; g.n_tiles = (n_tiles + g.NT - 1) / g.NT * g.NT; }
+    else fail(SSB_EINVAL, "reduction length too large for the GEMM kernel");
+  }
+  const int kpw = ksteps / (g.S * g.KSL);
+  if (kpw < kmin || g.S * g.KSL * kpw != ksteps) fail(SSB_EINVAL, "reduction length too small for the GEMM kernel");
+  return g;
 }
 
 void check_config(const ssb_config* c) {
@@ -239,7 +265,20 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
     o_gu[l] = take((size_t)2 * F * H * E);
     o_d[l] = take((size_t)H * F * E);
   }
-  const int lm_tiles = (V + 15) / 16;
+  const GemmShape p_qkv = plan_gemm(H, (qd + 2 * kvd) / 16, (int)E, EPI_QKV);
+  const GemmShape p_o = plan_gemm(qd, H / 16, (int)E, EPI_RESID);
+  const GemmShape p_gu = plan_gemm(H, 2 * F / 16, (int)E, EPI_SWIGLU);
+  const GemmShape p_d = plan_gemm(F, H / 16, (int)E, EPI_PARTIAL);
+  const GemmShape p_lm = plan_gemm(H, (V + 15) / 16, (int)E, EPI_LOGITS);
+  {
+    auto fits = [&](const GemmShape& g, int epi) {
+      if (gemm_max_mt((int)E, g.K, g.S, g.NT, g.KSL, H / 16, epi) < 1)
+        fail(SSB_EINVAL, "GEMM slab does not fit in LDS for this configuration");
+    };
+    fits(p_qkv, EPI_QKV); fits(p_o, EPI_RESID); fits(p_gu, EPI_SWIGLU);
+    fits(p_d, p_d.S > 1 ? EPI_PARTIAL : EPI_RESID); fits(p_lm, EPI_LOGITS);
+  }
+  const int lm_tiles = p_lm.n_tiles;
   const size_t o_lm = take((size_t)lm_tiles * 16 * H * E);
   const size_t o_rope = take((size_t)c.max_positions * (c.head_dim / 2) * sizeof(float2));
   if (hipMalloc(&m->wmem, off) != hipSuccess) fail(SSB_ENOMEM, "hipMalloc of packed weights failed");
@@ -250,12 +289,13 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   for (int l = 0; l < L; ++l) {
     m->attn_norm.push_back(reinterpret_cast<const float*>(wb + o_an[l]));
     m->mlp_norm.push_back(reinterpret_cast<const float*>(wb + o_mn[l]));
-    m->qkv.push_back({reinterpret_cast<const uint4*>(wb + o_qkv[l]), H, (qd + 2 * kvd) / 16, kpw_for(H, m->elem)});
-    m->o.push_back({reinterpret_cast<const uint4*>(wb + o_o[l]), qd, H / 16, kpw_for(qd, m->elem)});
-    m->gu.push_back({reinterpret_cast<const uint4*>(wb + o_gu[l]), H, 2 * F / 16, kpw_for(H, m->elem)});
-    m->d.push_back({reinterpret_cast<const uint4*>(wb + o_d[l]), F, H / 16, kpw_for(F, m->elem)});
+    m->qkv.push_back(p_qkv); m->qkv.back().W = reinterpret_cast<const uint4*>(wb + o_qkv[l]);
+    m->o.push_back(p_o); m->o.back().W = reinterpret_cast<const uint4*>(wb + o_o[l]);
+    m->gu.push_back(p_gu); m->gu.back().W = reinterpret_cast<const uint4*>(wb + o_gu[l]);
+    m->d.push_back(p_d); m->d.back().W = reinterpret_cast<const uint4*>(wb + o_d[l]);
   }
-  m->lm = {reinterpret_cast<const uint4*>(wb + o_lm), H, lm_tiles, kpw_for(H, m->elem)};
+  m->lm = p_lm;
+  m->lm.W = reinterpret_cast<const uint4*>(wb + o_lm);
   m->rope = reinterpret_cast<float2*>(wb + o_rope);
 
   hip_check(hipMemcpyAsync(wb + o_embed, w->embed, (size_t)V * H * E, hipMemcpyDeviceToDevice, st), "copy embed");
@@ -292,9 +332,13 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const size_t w_q = take((size_t)MR * qd * E);
   const size_t w_attn = take((size_t)MR * qd * E);
   const size_t w_act = take((size_t)MR * F * E);
-  const size_t w_meta = take((size_t)4 * MR * 4);
+  const size_t w_meta = take((size_t)5 * MR * 4);
+  const size_t w_cs = take((size_t)MR * (hd / 2) * sizeof(float2));
+  m->pt_ld = m->max_chunks * (kKeyChunk / kPage);
+  const size_t w_fpt = take((size_t)kMaxReq * m->pt_ld * 4);
+  const size_t w_part = take((size_t)p_d.S * MR * H * 4);
   const size_t w_am = take((size_t)MR * 12);
-  const size_t w_amp = take((size_t)lm_tiles * MR * 12);
+  const size_t w_amp = take((size_t)(lm_tiles / p_lm.NT) * MR * 12);
   const size_t w_apart = take((size_t)m->max_decode_rows * c.n_heads * m->max_chunks * (hd + 4) * 4);
   const size_t w_acc = take((size_t)kMaxReq * kOutStride * 4);
   const size_t w_tok = take((size_t)MR * 4);
@@ -311,12 +355,16 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   m->row_pos = m->row_tok + MR;
   m->row_lim = m->row_pos + MR;
   m->row_req = m->row_lim + MR;
+  m->row_slot = m->row_req + MR;
+  m->row_cs = reinterpret_cast<float2*>(wsb + w_cs);
+  m->part = reinterpret_cast<float*>(wsb + w_part);
+  m->fwd_pt = reinterpret_cast<int32_t*>(wsb + w_fpt);
   m->am_tok = reinterpret_cast<int32_t*>(wsb + w_am);
   m->am_top1 = reinterpret_cast<float*>(m->am_tok + MR);
   m->am_top2 = m->am_top1 + MR;
   m->amv1 = reinterpret_cast<float*>(wsb + w_amp);
-  m->amv2 = m->amv1 + (size_t)lm_tiles * MR;
-  m->ami1 = reinterpret_cast<int32_t*>(m->amv2 + (size_t)lm_tiles * MR);
+  m->amv2 = m->amv1 + (size_t)(lm_tiles / p_lm.NT) * MR;
+  m->ami1 = reinterpret_cast<int32_t*>(m->amv2 + (size_t)(lm_tiles / p_lm.NT) * MR);
   m->apart = reinterpret_cast<float*>(wsb + w_apart);
   m->accept_dev = reinterpret_cast<int32_t*>(wsb + w_acc);
   m->tok_dev = reinterpret_cast<int32_t*>(wsb + w_tok);
@@ -359,25 +407,30 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   pa.pos0 = f.pos0; pa.prefix = f.prefix; pa.tokens = m->tok_dev; pa.am_prev = m->am_tok;
   pa.embed = m->embed; pa.gain = m->attn_norm[0];
   pa.row_tok = m->row_tok; pa.row_pos = m->row_pos; pa.row_lim = m->row_lim; pa.row_req = m->row_req;
-  pa.h = m->h; pa.xg = m->xg; pa.ssq = m->ssq; pa.ssq_ld = MR; pa.req = m->req_dev;
+  pa.row_slot = m->row_slot; pa.row_cs = m->row_cs; pa.rope = m->rope; pa.half = c.head_dim / 2;
+  pa.fwd_pt = m->fwd_pt; pa.pt_ld = m->pt_ld;
+  pa.h = m->h; pa.xg = m->xg; pa.ssq = m->ssq; pa.ssq_ld = H / 16; pa.req = m->req_dev;
   hip_check(launch_prep<T>(pa, st), "prep");
 
   GemmArgs g{};
   g.M = M;
-  g.ssq = m->ssq; g.ssq_ld = MR; g.n_ssq = H / 16; g.eps = c.rms_eps; g.hidden = H;
+  g.ssq = m->ssq; g.ssq_ld = H / 16; g.n_ssq = H / 16; g.eps = c.rms_eps; g.hidden = H;
   g.h = m->h; g.xg_out = m->xg; g.ssq_out = m->ssq;
   g.q = m->q; g.q_ld = qd;
   g.n_heads = c.n_heads; g.n_kv = c.n_kv_heads; g.head_dim = c.head_dim; g.n_pages = pool->n_pages;
-  g.kv_pool = pool->base; g.rope = m->rope; g.row_pos = m->row_pos; g.row_req = m->row_req;
-  g.req = m->req_dev;
+  g.kv_pool = pool->base; g.row_slot = m->row_slot; g.row_cs = m->row_cs;
+  g.part = m->part; g.part_ld = H;
   g.act = m->act; g.act_ld = c.ffn;
   g.vocab = c.vocab; g.mask_id = c.mask_id;
-  auto set_w = [](GemmArgs& a, const GemmShape& s) { a.W = s.W; a.K = s.K; a.n_tiles = s.n_tiles; };
+  auto set_w = [](GemmArgs& a, const GemmShape& s) {
+    a.W = s.W; a.K = s.K; a.n_tiles = s.n_tiles; a.NT = s.NT; a.KSL = s.KSL; a.S = s.S;
+  };
 
   AttnArgs at{};
   at.q = m->q; at.q_ld = qd; at.kv_pool = pool->base; at.n_pages = pool->n_pages;
   at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads;
   at.req = m->req_dev;
+  at.fwd_pt = m->fwd_pt; at.pt_ld = m->pt_ld;
   at.row_lim = m->row_lim; at.part = m->apart; at.max_chunks = m->max_chunks;
   at.out = m->attn; at.out_ld = qd;
   at.fold = M > m->max_decode_rows ? 1 : 0;
@@ -407,7 +460,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       set_w(a, m->qkv[l]);
       a.x = m->xg; a.ldx = H;
       prof_begin(m, SSB_K_QKV, st);
-      hip_check(launch_gemm<T>(a, EPI_QKV, m->qkv[l].kpw, st), "qkv gemm");
+      hip_check(launch_gemm<T>(a, EPI_QKV, st), "qkv gemm");
       prof_end(m, SSB_K_QKV, st);
     }
     at.layer = l;
@@ -416,8 +469,8 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     prof_end(m, SSB_K_ATTN, st);
     if (!at.fold) {
       prof_begin(m, SSB_K_COMBINE, st);
-      hip_check(launch_attn_combine<T>(m->apart, m->max_chunks, c.n_heads, c.head_dim, m->row_lim, M, m->attn,
-                                       qd, st), "attention combine");
+      hip_check(launch_attn_combine<T>(m->apart, m->max_chunks, chunk_slots, c.n_heads, c.head_dim, m->row_lim, M,
+                                       m->attn, qd, st), "attention combine");
       prof_end(m, SSB_K_COMBINE, st);
     }
     {  // O + residual; next input xg = h * mlp_norm[l]
@@ -426,7 +479,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       a.x = m->attn; a.ldx = qd;
       a.gain_next = m->mlp_norm[l];
       prof_begin(m, SSB_K_O, st);
-      hip_check(launch_gemm<T>(a, EPI_RESID, m->o[l].kpw, st), "o gemm");
+      hip_check(launch_gemm<T>(a, EPI_RESID, st), "o gemm");
       prof_end(m, SSB_K_O, st);
     }
     {  // gate|up + SwiGLU
@@ -434,7 +487,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       set_w(a, m->gu[l]);
       a.x = m->xg; a.ldx = H;
       prof_begin(m, SSB_K_GATEUP, st);
-      hip_check(launch_gemm<T>(a, EPI_SWIGLU, m->gu[l].kpw, st), "gate/up gemm");
+      hip_check(launch_gemm<T>(a, EPI_SWIGLU, st), "gate/up gemm");
       prof_end(m, SSB_K_GATEUP, st);
     }
     {  // down + residual; next input xg = h * (next attn_norm | final_norm)
@@ -443,7 +496,12 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       a.x = m->act; a.ldx = c.ffn;
       a.gain_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
       prof_begin(m, SSB_K_DOWN, st);
-      hip_check(launch_gemm<T>(a, EPI_RESID, m->d[l].kpw, st), "down gemm");
+      if (a.S > 1) {
+        hip_check(launch_gemm<T>(a, EPI_PARTIAL, st), "down gemm");
+        hip_check(launch_resid_reduce<T>(a, st), "down reduce");
+      } else {
+        hip_check(launch_gemm<T>(a, EPI_RESID, st), "down gemm");
+      }
       prof_end(m, SSB_K_DOWN, st);
     }
   }
@@ -453,20 +511,21 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     set_w(a, m->lm);
     a.x = m->xg; a.ldx = H;
     a.logits = f.logits;
-    a.am_v1 = m->amv1; a.am_i1 = m->ami1; a.am_v2 = m->amv2; a.am_ld = MR;
+    const int n_groups = m->lm.n_tiles / m->lm.NT;
+    a.am_v1 = m->amv1; a.am_i1 = m->ami1; a.am_v2 = m->amv2; a.am_ld = n_groups;
     int rows = M;
     if (f.lm_last_only) {
       a.x = reinterpret_cast<const char*>(m->xg) + (size_t)(M - 1) * H * m->elem;
-      a.ssq = m->ssq + (M - 1);
+      a.ssq = m->ssq + (size_t)(M - 1) * (H / 16);
       a.M = 1;
       rows = 1;
     }
     prof_begin(m, SSB_K_LMHEAD, st);
-    hip_check(launch_gemm<T>(a, EPI_LOGITS, m->lm.kpw, st), "lm head gemm");
+    hip_check(launch_gemm<T>(a, EPI_LOGITS, st), "lm head gemm");
     prof_end(m, SSB_K_LMHEAD, st);
     prof_begin(m, SSB_K_ARGMAX, st);
-    hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, m->lm.n_tiles, MR, rows, m->am_tok, m->am_top1, m->am_top2,
-                            st), "argmax");
+    hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, n_groups, n_groups, rows, m->am_tok, m->am_top1,
+                            m->am_top2, st), "argmax");
     prof_end(m, SSB_K_ARGMAX, st);
   }
 }
@@ -560,6 +619,7 @@ ReqArgs single_req(ssb_kv* kv, int B, int max_commit) {
   ra.row0[0] = 0;
   ra.max_commit[0] = max_commit;
   ra.pt[0] = kv->pt_dev;
+  ra.npg[0] = (int)kv->pages.size();
   return ra;
 }
 
@@ -629,6 +689,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
     ra.row0[r] = r * (B + 1);
     ra.max_commit[r] = max_commit[r];
     ra.pt[r] = kvs[r]->pt_dev;
+    ra.npg[r] = (int)kvs[r]->pages.size();
     ra.planted[r] = planted ? planted + (size_t)r * B : nullptr;
     ra.cont[r] = cont ? cont[r] : nullptr;
     ra.cont_len[r] = cont_len ? cont_len[r] : 0;

@@ -125,6 +125,15 @@ __global__ __launch_bounds__(64) void k_prep_embed(PrepArgs a) {
   window_row(a, m, tok, pos, lim, req);
   if (g == 0 && t == 0) {
     a.row_tok[m] = tok; a.row_pos[m] = pos; a.row_lim[m] = lim; a.row_req[m] = req;
+    a.row_slot[m] = a.req->pt[req][pos / kPage] * kPage + pos % kPage;
+  }
+  if (g == 0 && t < a.half) a.row_cs[(size_t)m * a.half + t] = a.rope[(size_t)pos * a.half + t];
+  // page ids of each request of the forward, gathered once for every layer's attention
+  const int n_req = (a.mode == PREP_DRAFT || a.mode == PREP_VERIFY) ? a.req->n : 1;
+  if (g == 1 && m < n_req) {
+    const int32_t* pt = a.req->pt[m];
+    const int npg = a.req->npg[m];
+    for (int i = t; i < a.pt_ld; i += 64) a.fwd_pt[(size_t)m * a.pt_ld + i] = i < npg ? pt[i] : 0;
   }
   const int col = g * 64 + t;
   const T* src = tok >= 0 ? reinterpret_cast<const T*>(a.embed) + (size_t)tok * a.hidden
@@ -135,198 +144,9 @@ __global__ __launch_bounds__(64) void k_prep_embed(PrepArgs a) {
   float s = v * v;
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
-  if (t % 16 == 0) a.ssq[(size_t)(col / 16) * a.ssq_ld + m] = s;
+  if (t % 16 == 0) a.ssq[(size_t)m * a.ssq_ld + col / 16] = s;
 }
 
-// ---------------------------------------------------------------------------
-// GEMM with fused epilogues:  out[m][n] = sum_k X[m][k] W[n][k].
-// Grid (n_tiles, m_blocks); a workgroup owns one 16-column tile for 16*MT
-// rows and the full K.  Wave w of W = ksteps/KPW waves reduces K steps
-// [w*KPW, (w+1)*KPW) with an MFMA chain in K order after loading all of its
-// weight and activation fragments at once; the W partial tiles are then
-// added in wave order through LDS.  The decomposition depends only on K, so
-// a row's value never depends on M.
-// RMSNorm inputs arrive as X = h * gain (in T) and each output row is scaled
-// by 1/rms(h), rms from the per-16-column sums of squares added in column
-// order (review section 3.1: both modes share these layers).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
-
-template <typename T, int MT, int EPI, int KPW>
-__global__ __launch_bounds__(1024) void k_gemm(GemmArgs a) {
-  constexpr int KS = Ty<T>::kStepK;
-  constexpr int PER = Ty<T>::kPerFrag;
-  constexpr int MB = MT * 16;
-  constexpr bool NORM = (EPI != EPI_RESID);
-  extern __shared__ __align__(16) unsigned char smem[];
-  f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);          // [W][MT][64]
-  __shared__ float ctile[MB][17];
-  __shared__ float s_inv[MB];
-  __shared__ float s_ssq[kMaxNormParts * MB];
-
-  const int tile = blockIdx.x;
-  const int m_base = blockIdx.y * MB;
-  const int W = blockDim.x / kWave;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int ksteps = a.K / KS;
-  const int k0 = wave * KPW;
-
-  // weights of this wave (the HBM-latency-critical loads) go out first, all at once
-  uint4 wf[KPW];
-  const uint4* wp = a.W + ((size_t)tile * ksteps + k0) * kWave + lane;
-#pragma unroll
-  for (int s = 0; s < KPW; ++s) wf[s] = wp[(size_t)s * kWave];
-  // row-norm statistics: every thread helps load the per-16-column partials
-  if constexpr (NORM) {
-    for (int e = threadIdx.x; e < a.n_ssq * MB; e += blockDim.x) {
-      const int gi = e / MB, r = e % MB;
-      const int m = m_base + r;
-      s_ssq[gi * MB + r] = m < a.M ? a.ssq[(size_t)gi * a.ssq_ld + m] : 0.f;
-    }
-  }
-  // activation fragments in phases of up to 4 K steps (bounded register use)
-  constexpr int PH = KPW < 4 ? KPW : 4;
-  const T* xb = reinterpret_cast<const T*>(a.x);
-  f32x4_t acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int p0 = 0; p0 < KPW; p0 += PH) {
-    uint4 xf[PH][MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int row = m_base + mt * 16 + lane % 16;
-#pragma unroll
-      for (int s = 0; s < PH; ++s) {
-        xf[s][mt] = make_uint4(0, 0, 0, 0);
-        if (row < a.M)
-          xf[s][mt] = *reinterpret_cast<const uint4*>(xb + (size_t)row * a.ldx + (k0 + p0 + s) * KS +
-                                                      PER * (lane / 16));
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < PH; ++s)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) mma_step(acc[mt], wf[p0 + s], xf[s][mt], T());
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * kWave + lane] = acc[mt];
-  __syncthreads();
-  if constexpr (NORM) {
-    for (int r = threadIdx.x; r < MB; r += blockDim.x) {
-      float s = 0.f;
-      for (int gi = 0; gi < a.n_ssq; ++gi) s += s_ssq[gi * MB + r];
-      s_inv[r] = 1.0f / sqrtf(s / (float)a.hidden + a.eps);
-    }
-  }
-  for (int e = threadIdx.x; e < MT * kWave * 4; e += blockDim.x) {
-    const int mt = e / (kWave * 4), l = (e / 4) % kWave, i = e % 4;
-    float s = 0.f;
-    for (int w = 0; w < W; ++w) s += red[(w * MT + mt) * kWave + l][i];
-    ctile[mt * 16 + l % 16][4 * (l / 16) + i] = s;     // [row][tile column]
-  }
-  __syncthreads();
-
-  if constexpr (EPI == EPI_QKV) {
-    const int hd = a.head_dim, half = hd / 2, tph = hd / 16;
-    const int hh = tile / tph, jj = tile % tph;
-    const int kind = hh < a.n_heads ? 0 : (hh < a.n_heads + a.n_kv ? 1 : 2);   // q, k, v
-    const int head = kind == 0 ? hh : (kind == 1 ? hh - a.n_heads : hh - a.n_heads - a.n_kv);
-    for (int e = threadIdx.x; e < MB * 8; e += blockDim.x) {
-      const int r = e / 8, c = e % 8;
-      const int m = m_base + r;
-      if (m >= a.M) continue;
-      const float inv = s_inv[r];
-      float x1 = ctile[r][c] * inv, x2 = ctile[r][c + 8] * inv;
-      const int i = 8 * jj + c;                 // rotary pair (i, i + hd/2)
-      const int pos = a.row_pos[m];
-      if (kind != 2) {
-        const float2 cs = a.rope[(size_t)pos * half + i];
-        const float o1 = x1 * cs.x - x2 * cs.y;
-        const float o2 = x2 * cs.x + x1 * cs.y;
-        x1 = o1; x2 = o2;
-      }
-      T* dst;
-      if (kind == 0) {
-        dst = reinterpret_cast<T*>(a.q) + (size_t)m * a.q_ld + head * hd;
-      } else {
-        const int32_t* pt = a.req->pt[a.row_req[m]];
-        const int page = pt[pos / kPage], slot = pos % kPage;
-        const size_t base = (((size_t)a.layer * a.n_pages + page) * 2 + (kind - 1)) * a.n_kv + head;
-        dst = reinterpret_cast<T*>(a.kv_pool) + (base * kPage + slot) * hd;
-      }
-      dst[i] = Ty<T>::from_f(x1);
-      dst[i + half] = Ty<T>::from_f(x2);
-    }
-  } else if constexpr (EPI == EPI_RESID) {
-    for (int e = threadIdx.x; e < MB * 16; e += blockDim.x) {
-      const int r = e / 16, n = e % 16;
-      const int m = m_base + r;
-      if (m >= a.M) continue;
-      const int col = tile * 16 + n;
-      float* hp = a.h + (size_t)m * a.hidden + col;
-      const float v = *hp + ctile[r][n];
-      *hp = v;
-      reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * a.gain_next[col]);
-      ctile[r][n] = v;
-    }
-    __syncthreads();
-    for (int r = threadIdx.x; r < MB; r += blockDim.x) {
-      const int m = m_base + r;
-      if (m >= a.M) continue;
-      float s = 0.f;
-      for (int n = 0; n < 16; ++n) s += ctile[r][n] * ctile[r][n];
-      a.ssq_out[(size_t)tile * a.ssq_ld + m] = s;
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    for (int e = threadIdx.x; e < MB * 8; e += blockDim.x) {
-      const int r = e / 8, c = e % 8;
-      const int m = m_base + r;
-      if (m >= a.M) continue;
-      const float g = ctile[r][c] * s_inv[r];
-      const float u = ctile[r][c + 8] * s_inv[r];
-      reinterpret_cast<T*>(a.act)[(size_t)m * a.act_ld + tile * 8 + c] = Ty<T>::from_f(silu_f(g) * u);
-    }
-  } else {  // EPI_LOGITS
-    for (int e = threadIdx.x; e < MB * 16; e += blockDim.x) {
-      const int r = e / 16, n = e % 16;
-      const int m = m_base + r;
-      const float z = ctile[r][n] * s_inv[r];
-      ctile[r][n] = z;
-      const int col = tile * 16 + n;
-      if (a.logits && m < a.M && col < a.vocab) a.logits[(size_t)m * a.vocab + col] = z;
-    }
-    __syncthreads();
-    for (int r = threadIdx.x; r < MB; r += blockDim.x) {
-      const int m = m_base + r;
-      if (m >= a.M) continue;
-      float v1 = -INFINITY, v2 = -INFINITY;
-      int i1 = 0x7fffffff;
-      bool nan = false;
-      for (int n = 0; n < 16; ++n) {
-        const int col = tile * 16 + n;
-        if (col >= a.vocab || col == a.mask_id) continue;
-        const float z = ctile[r][n];
-        if (z != z) { nan = true; continue; }
-        if (z > v1) { v2 = v1; v1 = z; i1 = col; }
-        else if (z > v2) { v2 = z; }
-      }
-      if (nan) { v1 = NAN; v2 = NAN; i1 = -1; }
-      a.am_v1[(size_t)tile * a.am_ld + m] = v1;
-      a.am_i1[(size_t)tile * a.am_ld + m] = i1;
-      a.am_v2[(size_t)tile * a.am_ld + m] = v2;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Greedy argmax over the vocabulary without [M], lowest id on ties, with the
-// runner-up value (GravityOCR review, section 2 "Speculative Decoding":
-// greedy top-1 verification).  Merging (top1 value, top1 id, top2 value)
-// records is associative and commutative, so any reduction tree gives the
-// same bits.  A NaN anywhere makes the row's record NaN.
-// ---------------------------------------------------------------------------
 struct Top2 { float v1; int i1; float v2; };
 
 __device__ __forceinline__ Top2 merge_top2(Top2 a, Top2 b) {
@@ -338,6 +158,346 @@ __device__ __forceinline__ Top2 merge_top2(Top2 a, Top2 b) {
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// GEMM with fused epilogues:  out[m][n] = sum_k X[m][k] W[n][k].
+// Grid (n_tiles / NT, S, m_blocks).  A workgroup owns NT 16-column tiles for
+// 16*MT rows and one of S equal K ranges; it has NT*KSL waves.  Wave
+// w = t*KSL + j reduces K steps [j*KPW, (j+1)*KPW) of the range for tile t
+// with an MFMA chain in K order.  The workgroup issues every global load it
+// needs before its first MFMA: the weight fragments of each wave, the
+// activation slab (rows x K range, staged once in LDS and shared by all
+// waves), the norm partials and the inputs of its epilogue.  The KSL partial
+// tiles of a tile are added in a fixed pairwise tree through LDS.
+// The decomposition depends only on K and the GEMM, never on M or MT, so a
+// row's value never depends on how many rows share the launch.
+// Workgroups stream disjoint weight slices spread over every CU (one CU
+// alone pulls only ~20-25 GB/s from HBM on this chip).
+// RMSNorm inputs arrive as X = h * gain (in T) and each output row is scaled
+// by 1/rms(h), rms from the per-16-column sums of squares added in column
+// order (review section 3.1: both modes share these layers).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+template <typename T, int MT, int EPI, int KPW>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
+  constexpr int KS = Ty<T>::kStepK;
+  constexpr int PER = Ty<T>::kPerFrag;
+  constexpr int MB = MT * 16;
+  constexpr int NTH = kGemmThreads;
+  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
+  constexpr int SB = 12;                            // slab fragments per thread in the first batch
+  constexpr int PMAX = kMaxNormParts / 8;           // norm partials per lane (8 lanes per row)
+  const int NT = a.NT, KSL = a.KSL;
+  const int KR = KSL * KPW * KS;                    // K range of one workgroup
+  const int XSTR = KR * (int)sizeof(T) + 16;        // LDS row stride of the slab
+  const GemmLds L = gemm_lds(MT, KR * (int)sizeof(T), NT, KSL, a.n_ssq, EPI);
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* slab = smem;
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + L.red);
+  float* ctile = reinterpret_cast<float*>(smem + L.ctile);
+  __shared__ float s_inv[MB];
+
+  const int tg = blockIdx.x, split = blockIdx.y;
+  const int m_base = blockIdx.z * MB;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const bool cwave = wave < NT * KSL;               // waves past NT*KSL only help with loads
+  const int ksl = wave % KSL;
+  const int tile = tg * NT + (cwave ? wave / KSL : 0);
+  const int ksteps = a.K / KS;
+  const int kstep0 = split * (KSL * KPW) + ksl * KPW;
+  const int m_last = a.M - 1;
+
+  // ---- every global load of the prologue is issued before the first wait ----
+  // 1. this wave's weight fragments (HBM)
+  uint4 wf[KPW];
+  {
+    const uint4* wp = a.W + ((size_t)tile * ksteps + kstep0) * kWave + lane;
+#pragma unroll
+    for (int s = 0; s < KPW; ++s) wf[s] = wp[(size_t)s * kWave];
+  }
+  // 2. activation slab (rows x K range); rows past M read row M-1 and are zeroed below
+  const int FPR = KR / PER;                         // 16-byte fragments per slab row
+  const int total = MB * FPR;
+  const T* xb = reinterpret_cast<const T*>(a.x) + split * KR;
+  uint4 xs[SB];
+#pragma unroll
+  for (int b = 0; b < SB; ++b) {
+    const int e = min((int)threadIdx.x + b * NTH, total - 1);
+    const int m = min(m_base + e / FPR, m_last);
+    xs[b] = *reinterpret_cast<const uint4*>(xb + (size_t)m * a.ldx + (e % FPR) * PER);
+  }
+  // 3. norm partials of row r = tid/8: lane j = tid%8 takes [j*P, (j+1)*P)
+  float sv[PMAX];
+  const int nr = threadIdx.x / 8, nj = threadIdx.x % 8;
+  if constexpr (NORM) {
+    const int P = a.n_ssq / 8;
+    const float* sp = a.ssq + (size_t)min(m_base + min(nr, MB - 1), m_last) * a.ssq_ld + nj * P;
+    // branch-free: a uniform branch here makes the compiler wait for every earlier load
+#pragma unroll
+    for (int i = 0; i < PMAX; ++i) {
+      const float v = sp[min(i, P - 1)];
+      sv[i] = i < P ? v : 0.f;
+    }
+  }
+  // 4. epilogue inputs that do not depend on the product
+  float2 pcs = make_float2(0.f, 0.f);
+  int pslot = 0;
+  float ph[2] = {0.f, 0.f}, pg = 0.f;
+  if constexpr (EPI == EPI_QKV) {   // NT == 1: rotary pairs 8jj..8jj+7 of this tile's head
+    const int half = a.head_dim / 2, jj = tg % (a.head_dim / 16);
+    const int m = min(m_base + min((int)threadIdx.x / 8, MB - 1), m_last);
+    pcs = a.row_cs[(size_t)m * half + 8 * jj + threadIdx.x % 8];
+    pslot = a.row_slot[min(m_base + min((int)threadIdx.x, MB - 1), m_last)];
+  }
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int e = min((int)threadIdx.x + b * NTH, NT * MB * 16 - 1);
+      const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
+      ph[b] = a.h[(size_t)min(m_base + r, m_last) * a.hidden + (tg * NT + t) * 16 + n];
+    }
+    pg = a.gain_next[tg * NT * 16 + min((int)threadIdx.x, NT * 16 - 1)];
+  }
+
+  // ---- stores to LDS ----
+#pragma unroll
+  for (int b = 0; b < SB; ++b) {
+    const int e = threadIdx.x + b * NTH;
+    if (e < total) {
+      const int r = e / FPR;
+      *reinterpret_cast<uint4*>(slab + r * XSTR + (e % FPR) * 16) =
+          m_base + r <= m_last ? xs[b] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  for (int e = threadIdx.x + SB * NTH; e < total; e += NTH) {   // K ranges above SB*NTH fragments
+    const int r = e / FPR;
+    *reinterpret_cast<uint4*>(slab + r * XSTR + (e % FPR) * 16) =
+        m_base + r <= m_last ? *reinterpret_cast<const uint4*>(xb + (size_t)(m_base + r) * a.ldx + (e % FPR) * PER)
+                             : make_uint4(0, 0, 0, 0);
+  }
+  if constexpr (NORM) {
+    // sum of squares of the row: each lane adds its partials in column order, then a fixed
+    // butterfly over the 8 lanes
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < PMAX; ++i) sum += sv[i];
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    sum += __shfl_xor(sum, 4);
+    if (nj == 0 && nr < MB) s_inv[nr] = 1.0f / sqrtf(sum / (float)a.hidden + a.eps);
+  }
+  if constexpr (EPI == EPI_QKV) {
+    float2* s_cs = reinterpret_cast<float2*>(smem + L.pre);
+    int* s_slot = reinterpret_cast<int*>(smem + L.pre + MB * 8 * 8);
+    if (threadIdx.x < MB * 8) s_cs[threadIdx.x] = pcs;
+    if (threadIdx.x < MB) s_slot[threadIdx.x] = pslot;
+  }
+  if constexpr (EPI == EPI_RESID) {
+    float* s_h = reinterpret_cast<float*>(smem + L.pre);
+    float* s_g = s_h + NT * MB * 16;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      if (threadIdx.x + b * NTH < NT * MB * 16) s_h[threadIdx.x + b * NTH] = ph[b];
+    if (threadIdx.x < NT * 16) s_g[threadIdx.x] = pg;
+  }
+  __syncthreads();
+
+  // 5. MFMA chain over this wave's K steps
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (cwave) {
+#pragma unroll
+    for (int s = 0; s < KPW; ++s) {
+      const int kb = ((ksl * KPW + s) * KS + PER * (lane / 16)) * (int)sizeof(T);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint4 b = *reinterpret_cast<const uint4*>(slab + (mt * 16 + lane % 16) * XSTR + kb);
+        mma_step(acc[mt], wf[s], b, T());
+      }
+    }
+  }
+  // 6. K-slice partial tiles: fixed pairwise tree (stride 1, 2, 4, ...)
+  if (cwave) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * kWave + lane] = acc[mt];
+  }
+  __syncthreads();
+  for (int st = 1; st < KSL; st *= 2) {
+    if (cwave && ksl % (2 * st) == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4_t& mine = red[(wave * MT + mt) * kWave + lane];
+        mine = mine + red[((wave + st) * MT + mt) * kWave + lane];
+      }
+    }
+    __syncthreads();
+  }
+  // tile t's sum sits in wave t*KSL's slot: element i of lane l = [4(l/16) + i][l % 16] of the
+  // transposed product, i.e. row 16mt + l%16, column 4(l/16) + i
+  for (int e = threadIdx.x; e < NT * MT * kWave; e += NTH) {
+    const int t = e / (MT * kWave), mt = (e / kWave) % MT, l = e % kWave;
+    const f32x4_t v = red[((t * KSL) * MT + mt) * kWave + l];
+    float* dst = ctile + (t * MB + mt * 16 + l % 16) * 17 + 4 * (l / 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = v[i];
+  }
+  __syncthreads();
+
+  // 7. epilogue
+  if constexpr (EPI == EPI_QKV) {
+    const float2* s_cs = reinterpret_cast<const float2*>(smem + L.pre);
+    const int* s_slot = reinterpret_cast<const int*>(smem + L.pre + MB * 8 * 8);
+    const int hd = a.head_dim, half = hd / 2, tph = hd / 16;
+    const int hh = tg / tph, jj = tg % tph;
+    const int kind = hh < a.n_heads ? 0 : (hh < a.n_heads + a.n_kv ? 1 : 2);   // q, k, v
+    const int head = kind == 0 ? hh : (kind == 1 ? hh - a.n_heads : hh - a.n_heads - a.n_kv);
+    for (int e = threadIdx.x; e < MB * 8; e += NTH) {
+      const int r = e / 8, c = e % 8;
+      const int m = m_base + r;
+      if (m >= a.M) continue;
+      const float inv = s_inv[r];
+      const float* ct = ctile + r * 17;
+      float x1 = ct[c] * inv, x2 = ct[c + 8] * inv;
+      const int i = 8 * jj + c;                 // rotary pair (i, i + hd/2)
+      if (kind != 2) {
+        const float2 cs = s_cs[e];
+        const float o1 = x1 * cs.x - x2 * cs.y;
+        const float o2 = x2 * cs.x + x1 * cs.y;
+        x1 = o1; x2 = o2;
+      }
+      T* dst;
+      if (kind == 0) {
+        dst = reinterpret_cast<T*>(a.q) + (size_t)m * a.q_ld + head * hd;
+      } else {
+        const int sl = s_slot[r];
+        const size_t base = (((size_t)a.layer * a.n_pages + sl / kPage) * 2 + (kind - 1)) * a.n_kv + head;
+        dst = reinterpret_cast<T*>(a.kv_pool) + (base * kPage + sl % kPage) * hd;
+      }
+      dst[i] = Ty<T>::from_f(x1);
+      dst[i + half] = Ty<T>::from_f(x2);
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    const float* s_h = reinterpret_cast<const float*>(smem + L.pre);
+    const float* s_g = s_h + NT * MB * 16;
+    for (int e = threadIdx.x; e < NT * MB * 16; e += NTH) {
+      const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
+      const int m = m_base + r;
+      float* ct = ctile + (t * MB + r) * 17;
+      const float v = s_h[e] + ct[n];
+      ct[n] = v;
+      if (m >= a.M) continue;
+      const int col = (tg * NT + t) * 16 + n;
+      a.h[(size_t)m * a.hidden + col] = v;
+      reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * s_g[t * 16 + n]);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < NT * MB; e += NTH) {
+      const int t = e / MB, r = e % MB;
+      const int m = m_base + r;
+      if (m >= a.M) continue;
+      const float* ct = ctile + (t * MB + r) * 17;
+      float sum = 0.f;
+      for (int n = 0; n < 16; ++n) sum += ct[n] * ct[n];
+      a.ssq_out[(size_t)m * a.ssq_ld + tg * NT + t] = sum;
+    }
+  } else if constexpr (EPI == EPI_PARTIAL) {
+    for (int e = threadIdx.x; e < NT * MB * 16; e += NTH) {
+      const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
+      const int m = m_base + r;
+      if (m >= a.M) continue;
+      const int col = (tg * NT + t) * 16 + n;
+      a.part[((size_t)split * a.M + m) * a.part_ld + col] = ctile[(t * MB + r) * 17 + n];
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    for (int e = threadIdx.x; e < NT * MB * 8; e += NTH) {
+      const int t = e / (MB * 8), r = (e / 8) % MB, c = e % 8;
+      const int m = m_base + r;
+      if (m >= a.M) continue;
+      const float* ct = ctile + (t * MB + r) * 17;
+      const float g = ct[c] * s_inv[r];
+      const float u = ct[c + 8] * s_inv[r];
+      reinterpret_cast<T*>(a.act)[(size_t)m * a.act_ld + (tg * NT + t) * 8 + c] = Ty<T>::from_f(silu_f(g) * u);
+    }
+  } else {  // EPI_LOGITS
+    for (int e = threadIdx.x; e < NT * MB * 16; e += NTH) {
+      const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
+      const int m = m_base + r;
+      float* ct = ctile + (t * MB + r) * 17;
+      const float z = ct[n] * s_inv[r];
+      ct[n] = z;
+      const int col = (tg * NT + t) * 16 + n;
+      if (a.logits && m < a.M && col < a.vocab) a.logits[(size_t)m * a.vocab + col] = z;
+    }
+    __syncthreads();
+    // one (top1, id, top2) record per row over the workgroup's NT*16 columns:
+    // 8 lanes per row scan 2*NT columns each, then merge across the 8 lanes
+    const int groups = NTH / 8, cpl = 2 * NT;
+    const int n_it = (MB + groups - 1) / groups;
+    for (int it = 0; it < n_it; ++it) {
+      const int r = it * groups + threadIdx.x / 8, sub = threadIdx.x % 8;
+      Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
+      bool nan = false;
+      if (r < MB) {
+        for (int k = 0; k < cpl; ++k) {
+          const int cc = sub * cpl + k;               // column within the workgroup's span
+          const int col = tg * NT * 16 + cc;
+          if (col >= a.vocab || col == a.mask_id) continue;
+          const float z = ctile[((cc / 16) * MB + r) * 17 + cc % 16];
+          if (z != z) { nan = true; continue; }
+          if (z > best.v1) { best.v2 = best.v1; best.v1 = z; best.i1 = col; }
+          else if (z > best.v2) { best.v2 = z; }
+        }
+      }
+      if (nan) best = Top2{NAN, -1, NAN};
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const Top2 other{__shfl_xor(best.v1, o), __shfl_xor(best.i1, o), __shfl_xor(best.v2, o)};
+        best = merge_top2(best, other);
+      }
+      const int m = m_base + r;
+      if (sub == 0 && r < MB && m < a.M) {
+        const size_t o = (size_t)m * a.am_ld + tg;
+        a.am_v1[o] = best.v1;
+        a.am_i1[o] = best.i1;
+        a.am_v2[o] = best.v2;
+      }
+    }
+  }
+}
+
+// Residual update after a K-split GEMM: h += sum of the S partial sums (in
+// split order), then the next GEMM's input xg = h * gain_next and the
+// per-16-column sums of squares of h.  Grid (M, hidden / 64), 64 threads.
+template <typename T>
+__global__ __launch_bounds__(64) void k_resid_reduce(GemmArgs a) {
+  constexpr int SMAX = 8;
+  const int m = blockIdx.x, col = blockIdx.y * 64 + threadIdx.x;
+  float p[SMAX];
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) p[s] = s < a.S ? a.part[((size_t)s * a.M + m) * a.part_ld + col] : 0.f;
+  const float h0 = a.h[(size_t)m * a.hidden + col];
+  const float g = a.gain_next[col];
+  float v = p[0];
+#pragma unroll
+  for (int s = 1; s < SMAX; ++s)
+    if (s < a.S) v += p[s];
+  v = h0 + v;
+  a.h[(size_t)m * a.hidden + col] = v;
+  reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * g);
+  float sq = v * v;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
+  if (threadIdx.x % 16 == 0) a.ssq_out[(size_t)m * a.ssq_ld + col / 16] = sq;
+}
+
+// ---------------------------------------------------------------------------
+// Greedy argmax over the vocabulary without [M], lowest id on ties, with the
+// runner-up value (GravityOCR review, section 2 "Speculative Decoding":
+// greedy top-1 verification).  Merging (top1 value, top1 id, top2 value)
+// records is associative and commutative, so any reduction tree gives the
+// same bits.  A NaN anywhere makes the row's record NaN.
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int32_t* i1, const float* v2,
                                                     int n_groups, int ld, int32_t* tok, float* top1,
                                                     float* top2) {
@@ -351,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
     for (int b = 0; b < BATCH; ++b) {
       const int g = g0 + b * kThreads;
       rec[b] = Top2{-INFINITY, 0x7fffffff, -INFINITY};
-      if (g < n_groups) rec[b] = Top2{v1[(size_t)g * ld + m], i1[(size_t)g * ld + m], v2[(size_t)g * ld + m]};
+      if (g < n_groups) rec[b] = Top2{v1[(size_t)m * ld + g], i1[(size_t)m * ld + g], v2[(size_t)m * ld + g]};
     }
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) t = merge_top2(t, rec[b]);
@@ -395,7 +555,8 @@ __device__ __forceinline__ float fold_val(float v, float al, float vc, float be)
 }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
+  constexpr int NTH = kAttnThreads;
   constexpr int KS = Ty<T>::kStepK;
   constexpr int PER = Ty<T>::kPerFrag;
   constexpr int DT = HD / 16;
@@ -406,9 +567,9 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   constexpr int VSTR = kKeyChunk * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);   // V^T rows [d][key]
   constexpr int MT = kTaskRows / 16;
   constexpr int REC = HD + 4;
-  constexpr int MAXU = 3;                  // units per wave: ceil(4 heads * 3 tiles / 4 waves)
   constexpr int FPK = HD / PER;            // 16-byte fragments per key row
-  constexpr int KVF = 2 * kKeyChunk * FPK / kThreads;   // fragments per thread
+  constexpr int NKF = 2 * kKeyChunk * FPK; // K and V fragments of one chunk
+  constexpr int KVF = (NKF + NTH - 1) / NTH;
   __shared__ __align__(16) unsigned char ks[kKeyChunk * KSTR];
   __shared__ __align__(16) unsigned char vts[HD * VSTR];
   __shared__ int s_lim[kTaskRows];
@@ -417,66 +578,69 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   const int g = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n_rep = a.n_heads / a.n_kv;
-  const int32_t* pt = a.req->pt[task.req];
-  const int n_units = n_rep * MT;
+  // one (query head, 16-row tile) unit per wave
+  const int hl = wave / MT, mt = wave % MT;
+  const bool active = wave < n_rep * MT && mt * 16 < task.nrows;
+  const int row_local = mt * 16 + lane % 16;
+  const int head = g * n_rep + hl;
+  const int32_t* pt = a.fwd_pt + (size_t)task.req * a.pt_ld;
 
-  if (threadIdx.x < kTaskRows)
-    s_lim[threadIdx.x] = threadIdx.x < task.nrows ? a.row_lim[task.row0 + threadIdx.x] : -1;
+  // ---- first memory round trip: limits, query fragments, page ids ----
+  const int lim_v = threadIdx.x < task.nrows ? a.row_lim[task.row0 + threadIdx.x] : -1;
+  uint4 qf[QKS];
+#pragma unroll
+  for (int st = 0; st < QKS; ++st) {
+    qf[st] = make_uint4(0, 0, 0, 0);
+    if (active && row_local < task.nrows)
+      qf[st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.q) +
+                                               (size_t)(task.row0 + row_local) * a.q_ld + head * HD + st * KS +
+                                               PER * (lane / 16));
+  }
+  const int cbeg = a.fold ? 0 : blockIdx.x;
+  int pg[KVF];
+#pragma unroll
+  for (int q = 0; q < KVF; ++q) {
+    const int f = min((int)threadIdx.x + q * NTH, NKF - 1);
+    pg[q] = pt[(cbeg * kKeyChunk + (f % (kKeyChunk * FPK)) / FPK) / kPage];
+  }
   // largest visibility limit of the task's rows
   const int maxlim = task.lim_mode == 0 ? task.max_lim : a.req->p[task.req] + a.req->B + (task.lim_mode == 2 ? 1 : 0);
-  int cbeg, cend;
-  if (a.fold) { cbeg = 0; cend = maxlim / kKeyChunk + 1; }
-  else {
-    cbeg = blockIdx.x; cend = cbeg + 1;
-    if (cbeg * kKeyChunk > maxlim) return;
-  }
+  const int cend = a.fold ? maxlim / kKeyChunk + 1 : cbeg + 1;
+  if (cbeg * kKeyChunk > maxlim) return;     // no visible key in this chunk slot
+  if (threadIdx.x < kTaskRows) s_lim[threadIdx.x] = lim_v;
 
-  // query fragments of this wave's units (B operand of S^T): issued first
-  uint4 qf[MAXU][QKS];
+  float run_m = -INFINITY, run_l = 0.f;
+  f32x4_t run_o[DT];
 #pragma unroll
-  for (int ui = 0; ui < MAXU; ++ui) {
-    const int u = wave + 4 * ui;
-    const int hl = u / MT, mt = u % MT;
-    const int row_local = mt * 16 + lane % 16;
-#pragma unroll
-    for (int st = 0; st < QKS; ++st) {
-      qf[ui][st] = make_uint4(0, 0, 0, 0);
-      if (u < n_units && row_local < task.nrows)
-        qf[ui][st] = *reinterpret_cast<const uint4*>(
-            reinterpret_cast<const T*>(a.q) + (size_t)(task.row0 + row_local) * a.q_ld + (g * n_rep + hl) * HD +
-            st * KS + PER * (lane / 16));
-    }
-  }
-
-  float run_m[MAXU], run_l[MAXU];
-  f32x4_t run_o[MAXU][DT];
-#pragma unroll
-  for (int u = 0; u < MAXU; ++u) {
-    run_m[u] = -INFINITY; run_l[u] = 0.f;
-#pragma unroll
-    for (int d = 0; d < DT; ++d) run_o[u][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int d = 0; d < DT; ++d) run_o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int c = cbeg; c < cend; ++c) {
-    // K and V of keys [c*64, c*64+64) that any row of the task may see
+    if (c != cbeg) {
+#pragma unroll
+      for (int q = 0; q < KVF; ++q) {
+        const int f = min((int)threadIdx.x + q * NTH, NKF - 1);
+        pg[q] = pt[(c * kKeyChunk + (f % (kKeyChunk * FPK)) / FPK) / kPage];
+      }
+    }
+    // ---- second round trip: K and V of keys [c*64, c*64+64) that a row of the task may see ----
     uint4 kvv[KVF];
 #pragma unroll
     for (int q = 0; q < KVF; ++q) {
-      const int f = threadIdx.x + q * kThreads;
+      const int f = threadIdx.x + q * NTH;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
       const int key = c * kKeyChunk + rem / FPK;
       kvv[q] = make_uint4(0, 0, 0, 0);
-      if (key <= maxlim) {
-        const int page = pt[key / kPage], slot = key % kPage;
-        const size_t base = (((size_t)a.layer * a.n_pages + page) * 2 + kv) * a.n_kv + g;
+      if (f < NKF && key <= maxlim) {
+        const size_t base = (((size_t)a.layer * a.n_pages + pg[q]) * 2 + kv) * a.n_kv + g;
         kvv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kv_pool) +
-                                                 (base * kPage + slot) * HD + (rem % FPK) * PER);
+                                                 (base * kPage + key % kPage) * HD + (rem % FPK) * PER);
       }
     }
 #pragma unroll
     for (int q = 0; q < KVF; ++q) {
-      const int f = threadIdx.x + q * kThreads;
+      const int f = threadIdx.x + q * NTH;
+      if (f >= NKF) continue;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
       const int kk = rem / FPK, d0 = (rem % FPK) * PER;
@@ -490,14 +654,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
     }
     __syncthreads();
 
-#pragma unroll
-    for (int ui = 0; ui < MAXU; ++ui) {
-      const int u = wave + 4 * ui;
-      if (u >= n_units) break;
-      const int hl = u / MT, mt = u % MT;
-      if (mt * 16 >= task.nrows) continue;
-      const int head = g * n_rep + hl;
-      const int row_local = mt * 16 + lane % 16;
+    if (active) {
       // S^T tiles: element i of tile kt = score of key kt*16 + 4*(lane/16) + i for row_local
       f32x4_t s[KT];
 #pragma unroll
@@ -507,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
         for (int st = 0; st < QKS; ++st) {
           const uint4 kf = *reinterpret_cast<const uint4*>(
               ks + (kt * 16 + lane % 16) * KSTR + (st * KS + PER * (lane / 16)) * (int)sizeof(T));
-          mma_step(s[kt], kf, qf[ui][st], T());
+          mma_step(s[kt], kf, qf[st], T());
         }
       }
       const int lim = s_lim[row_local];
@@ -565,13 +722,13 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
       // o[dt][i] = o_c[d = dt*16 + 4*(lane/16) + i] of row_local
       if (a.fold) {
         float mn, al, be;
-        fold_coef(run_m[ui], mx, mn, al, be);
-        run_l[ui] = fold_val(run_l[ui], al, lsum, be);
+        fold_coef(run_m, mx, mn, al, be);
+        run_l = fold_val(run_l, al, lsum, be);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) run_o[ui][dt][i] = fold_val(run_o[ui][dt][i], al, o[dt][i], be);
-        run_m[ui] = mn;
+          for (int i = 0; i < 4; ++i) run_o[dt][i] = fold_val(run_o[dt][i], al, o[dt][i], be);
+        run_m = mn;
       } else if (row_local < task.nrows) {
         float* rec = a.part + (((size_t)(task.row0 + row_local) * a.n_heads + head) * a.max_chunks + c) * REC;
 #pragma unroll
@@ -583,31 +740,24 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
     __syncthreads();
   }
 
-  if (a.fold) {
+  if (a.fold && active && row_local < task.nrows) {
+    T* dst = reinterpret_cast<T*>(a.out) + (size_t)(task.row0 + row_local) * a.out_ld + head * HD;
 #pragma unroll
-    for (int ui = 0; ui < MAXU; ++ui) {
-      const int u = wave + 4 * ui;
-      if (u >= n_units) break;
-      const int hl = u / MT, mt = u % MT;
-      const int row_local = mt * 16 + lane % 16;
-      if (row_local >= task.nrows) continue;
-      const int head = g * n_rep + hl;
-      T* dst = reinterpret_cast<T*>(a.out) + (size_t)(task.row0 + row_local) * a.out_ld + head * HD;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[dt * 16 + 4 * (lane / 16) + i] = Ty<T>::from_f(run_o[ui][dt][i] / run_l[ui]);
-    }
+      for (int i = 0; i < 4; ++i) dst[dt * 16 + 4 * (lane / 16) + i] = Ty<T>::from_f(run_o[dt][i] / run_l);
   }
 }
 
-// Combine the per-chunk records of each (row, head) in chunk order.
-// One wave per (row, head); lane d holds output dimension d.  Records are
-// loaded 32 chunks at a time before folding.
+// Combine the per-chunk records of each (row, head).  One wave per (row,
+// head); lane d holds output dimension d.  The row's limit and up to 32
+// records are loaded in one round trip; records of chunks past the limit
+// were never written and are replaced by empty ones.  Within a batch of 32
+// chunks: m* = max m_c, then l = sum l_c e^(m_c - m*) and
+// o = sum o_c e^(m_c - m*) in chunk order; batches fold online.
 template <typename T, int HD>
-__global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, int max_chunks, int n_heads,
-                                                          const int32_t* row_lim, int M, void* out,
+__global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, int max_chunks, int n_slots,
+                                                          int n_heads, const int32_t* row_lim, int M, void* out,
                                                           int out_ld) {
   constexpr int REC = HD + 4;
   constexpr int BATCH = 32;
@@ -615,30 +765,41 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, in
   const int idx = blockIdx.x * 4 + wave;
   if (idx >= M * n_heads) return;
   const int row = idx / n_heads, head = idx % n_heads;
-  const int nch = row_lim[row] / kKeyChunk + 1;
+  const int lim = row_lim[row];
   const float* rec = part + ((size_t)row * n_heads + head) * max_chunks * REC;
   float m = -INFINITY, l = 0.f, o = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += BATCH) {
+  for (int c0 = 0; c0 < n_slots; c0 += BATCH) {
     float mc[BATCH], lc[BATCH], oc[BATCH];
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
-      const int c = c0 + b;
-      mc[b] = -INFINITY; lc[b] = 0.f; oc[b] = 0.f;
-      if (c < nch) {
-        const float2 ml = *reinterpret_cast<const float2*>(rec + c * REC + HD);
-        mc[b] = ml.x; lc[b] = ml.y;
-        if (lane < HD) oc[b] = rec[c * REC + lane];
-      }
+      const int c = min(c0 + b, n_slots - 1);
+      const float2 ml = *reinterpret_cast<const float2*>(rec + c * REC + HD);
+      mc[b] = ml.x; lc[b] = ml.y;
+      oc[b] = rec[c * REC + min(lane, HD - 1)];
     }
+    const int nvis = lim / kKeyChunk + 1;          // chunks that hold a visible key of this row
+    float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
-      if (c0 + b < nch) {
-        float mn, al, be;
-        fold_coef(m, mc[b], mn, al, be);
-        l = fold_val(l, al, lc[b], be);
-        o = fold_val(o, al, oc[b], be);
-        m = mn;
-      }
+      if (c0 + b >= nvis || c0 + b >= n_slots) { mc[b] = -INFINITY; lc[b] = 0.f; oc[b] = 0.f; }
+      mx = fmaxf(mx, mc[b]);
+    }
+    if (mx == -INFINITY) continue;
+    float lb = 0.f, ob = 0.f;
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const float w = expf(mc[b] - mx);
+      lb = __fadd_rn(lb, __fmul_rn(lc[b], w));
+      ob = __fadd_rn(ob, __fmul_rn(oc[b], w));
+    }
+    if (m == -INFINITY) {
+      m = mx; l = lb; o = ob;
+    } else {
+      float mn, al, be;
+      fold_coef(m, mx, mn, al, be);
+      l = fold_val(l, al, lb, be);
+      o = fold_val(o, al, ob, be);
+      m = mn;
     }
   }
   if (lane < HD) reinterpret_cast<T*>(out)[(size_t)row * out_ld + head * HD + lane] = Ty<T>::from_f(o / l);
@@ -702,44 +863,78 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
 template hipError_t launch_prep<bf16_t>(const PrepArgs&, hipStream_t);
 template hipError_t launch_prep<float>(const PrepArgs&, hipStream_t);
 
-template <typename T, int EPI, int KPW>
-static hipError_t launch_gemm_kpw(const GemmArgs& a, int MT, hipStream_t st) {
-  const int ksteps = a.K / Ty<T>::kStepK;
-  const int W = ksteps / KPW;
+template <typename T, int EPI, int MT, int KPW>
+static hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
+  const int KR = a.KSL * KPW * Ty<T>::kStepK;
+  const GemmLds L = gemm_lds(MT, KR * (int)sizeof(T), a.NT, a.KSL, a.n_ssq, EPI);
   const int m_blocks = (a.M + 16 * MT - 1) / (16 * MT);
-  const dim3 grid(a.n_tiles, m_blocks), block(W * kWave);
-  const size_t shm = (size_t)W * MT * kWave * sizeof(f32x4_t);
-  switch (MT) {
-    case 1: hipLaunchKernelGGL((k_gemm<T, 1, EPI, KPW>), grid, block, shm, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm<T, 2, EPI, KPW>), grid, block, shm, st, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm<T, 3, EPI, KPW>), grid, block, shm, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm<T, 4, EPI, KPW>), grid, block, shm, st, a); break;
-  }
+  const dim3 grid(a.n_tiles / a.NT, a.S, m_blocks), block(kGemmThreads);
+  hipLaunchKernelGGL((k_gemm<T, MT, EPI, KPW>), grid, block, L.total, st, a);
   return hipGetLastError();
 }
 
-template <typename T, int EPI>
-static hipError_t launch_gemm_epi(const GemmArgs& a, int kpw, int MT, hipStream_t st) {
-  switch (kpw) {
-    case 1: return launch_gemm_kpw<T, EPI, 1>(a, MT, st);
-    case 2: return launch_gemm_kpw<T, EPI, 2>(a, MT, st);
-    case 4: return launch_gemm_kpw<T, EPI, 4>(a, MT, st);
-    default: return launch_gemm_kpw<T, EPI, 8>(a, MT, st);
+template <typename T, int EPI, int MT>
+static hipError_t launch_gemm_mt(const GemmArgs& a, hipStream_t st) {
+  const int kpw = a.K / a.S / Ty<T>::kStepK / a.KSL;      // K steps per wave
+  if constexpr (sizeof(T) == 2) {
+    switch (kpw) {
+      case 4: return launch_gemm_cfg<T, EPI, MT, 4>(a, st);
+      case 8: return launch_gemm_cfg<T, EPI, MT, 8>(a, st);
+      case 16: return launch_gemm_cfg<T, EPI, MT, 16>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (kpw) {
+      case 1: return launch_gemm_cfg<T, EPI, MT, 1>(a, st);
+      case 2: return launch_gemm_cfg<T, EPI, MT, 2>(a, st);
+      case 4: return launch_gemm_cfg<T, EPI, MT, 4>(a, st);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
+// Largest row-tile count MT <= 3 whose LDS fits (0: none fits).
+int gemm_max_mt(int elem, int K, int S, int NT, int KSL, int n_ssq, int epi) {
+  for (int mt = 3; mt >= 1; --mt)
+    if (gemm_lds(mt, K / S * elem, NT, KSL, n_ssq, epi).total <= kGemmMaxLds) return mt;
+  return 0;
+}
+
+template <typename T, int EPI>
+static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t st) {
+  const int fit = gemm_max_mt((int)sizeof(T), a.K, a.S, a.NT, a.KSL, a.n_ssq, EPI);
+  if (fit == 0 || a.NT * a.KSL > kGemmThreads / kWave || a.n_tiles % a.NT != 0 || a.n_ssq > kMaxNormParts ||
+      a.n_ssq % 8 != 0)
+    return hipErrorInvalidValue;
+  const int want = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 3;
+  const int MT = want < fit ? want : fit;
+  if (EPI == EPI_RESID && a.NT * MT * 16 * 16 > 2 * kGemmThreads) return hipErrorInvalidValue;
+  if (MT == 1) return launch_gemm_mt<T, EPI, 1>(a, st);
+  if (MT == 2) return launch_gemm_mt<T, EPI, 2>(a, st);
+  return launch_gemm_mt<T, EPI, 3>(a, st);
+}
+
 template <typename T>
-hipError_t launch_gemm(const GemmArgs& a, int epi, int kpw, hipStream_t st) {
-  const int MT = a.M <= 16 ? 1 : a.M <= 32 ? 2 : a.M <= 48 ? 3 : 4;
+hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   switch (epi) {
-    case EPI_QKV: return launch_gemm_epi<T, EPI_QKV>(a, kpw, MT, st);
-    case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, kpw, MT, st);
-    case EPI_SWIGLU: return launch_gemm_epi<T, EPI_SWIGLU>(a, kpw, MT, st);
-    default: return launch_gemm_epi<T, EPI_LOGITS>(a, kpw, MT, st);
+    case EPI_QKV: return a.NT == 1 ? launch_gemm_epi<T, EPI_QKV>(a, st) : hipErrorInvalidValue;
+    case EPI_RESID: return launch_gemm_epi<T, EPI_RESID>(a, st);
+    case EPI_PARTIAL: return launch_gemm_epi<T, EPI_PARTIAL>(a, st);
+    case EPI_SWIGLU: return launch_gemm_epi<T, EPI_SWIGLU>(a, st);
+    default: return launch_gemm_epi<T, EPI_LOGITS>(a, st);
   }
 }
-template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, int, hipStream_t);
-template hipError_t launch_gemm<float>(const GemmArgs&, int, int, hipStream_t);
+template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
+template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
+
+template <typename T>
+hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st) {
+  if (a.S < 1 || a.S > 8 || a.hidden % 64 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_resid_reduce<T>, dim3(a.M, a.hidden / 64), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+template hipError_t launch_resid_reduce<bf16_t>(const GemmArgs&, hipStream_t);
+template hipError_t launch_resid_reduce<float>(const GemmArgs&, hipStream_t);
 
 hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, int n_groups, int ld, int M,
                          int32_t* tok, float* top1, float* top2, hipStream_t st) {
@@ -749,29 +944,32 @@ hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, in
 
 template <typename T>
 hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipStream_t st) {
+  if (a.n_heads / a.n_kv * (kTaskRows / 16) > kAttnThreads / kWave) return hipErrorInvalidValue;
+  if (!a.fold && n_chunk_slots > a.max_chunks) return hipErrorInvalidValue;
   dim3 grid(a.fold ? 1 : n_chunk_slots, a.n_kv, a.tasks.n);
-  if (head_dim == 64) hipLaunchKernelGGL((k_attn<T, 64>), grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((k_attn<T, 32>), grid, dim3(kThreads), 0, st, a);
+  if (head_dim == 64) hipLaunchKernelGGL((k_attn<T, 64>), grid, dim3(kAttnThreads), 0, st, a);
+  else hipLaunchKernelGGL((k_attn<T, 32>), grid, dim3(kAttnThreads), 0, st, a);
   return hipGetLastError();
 }
 template hipError_t launch_attn<bf16_t>(const AttnArgs&, int, int, hipStream_t);
 template hipError_t launch_attn<float>(const AttnArgs&, int, int, hipStream_t);
 
 template <typename T>
-hipError_t launch_attn_combine(const float* part, int max_chunks, int n_heads, int head_dim,
+hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, int n_heads, int head_dim,
                                const int32_t* row_lim, int M, void* out, int out_ld, hipStream_t st) {
+  if (n_slots < 1 || n_slots > max_chunks) return hipErrorInvalidValue;
   const int blocks = (M * n_heads + 3) / 4;
   if (head_dim == 64)
-    hipLaunchKernelGGL((k_attn_combine<T, 64>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks,
+    hipLaunchKernelGGL((k_attn_combine<T, 64>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks, n_slots,
                        n_heads, row_lim, M, out, out_ld);
   else
-    hipLaunchKernelGGL((k_attn_combine<T, 32>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks,
+    hipLaunchKernelGGL((k_attn_combine<T, 32>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks, n_slots,
                        n_heads, row_lim, M, out, out_ld);
   return hipGetLastError();
 }
-template hipError_t launch_attn_combine<bf16_t>(const float*, int, int, int, const int32_t*, int, void*, int,
+template hipError_t launch_attn_combine<bf16_t>(const float*, int, int, int, int, const int32_t*, int, void*, int,
                                                 hipStream_t);
-template hipError_t launch_attn_combine<float>(const float*, int, int, int, const int32_t*, int, void*, int,
+template hipError_t launch_attn_combine<float>(const float*, int, int, int, int, const int32_t*, int, void*, int,
                                                hipStream_t);
 
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
