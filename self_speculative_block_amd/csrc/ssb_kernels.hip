@@ -178,6 +178,62 @@ __device__ __forceinline__ Top2 merge_top2(Top2 a, Top2 b) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
+// Sum over aligned groups of g lanes (g a power of two, 1..64), result in every lane of the
+// group.  Steps: swap within pairs, within quads (DPP quad permutes), mirror within 8 and 16
+// lanes (DPP row half-mirror and mirror), then xor 16 and 32 through ds_bpermute.  The
+// pattern is fixed, so the rounding of the sum is too.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int moved;
+  const int iv = __float_as_int(v);
+  switch (ctrl_sel) {
+    case 0: moved = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false); break;    // quad_perm [1,0,3,2]
+    case 1: moved = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false); break;    // quad_perm [2,3,0,1]
+    case 2: moved = __builtin_amdgcn_update_dpp(0, iv, 0x141, 0xF, 0xF, false); break;   // row_half_mirror
+    default: moved = __builtin_amdgcn_update_dpp(0, iv, 0x140, 0xF, 0xF, false); break;  // row_mirror
+  }
+  return v + __int_as_float(moved);
+}
+__device__ __forceinline__ float lane_group_sum(float v, int g) {
+  if (g >= 2) v = dpp_add(v, 0);
+  if (g >= 4) v = dpp_add(v, 1);
+  if (g >= 8) v = dpp_add(v, 2);
+  if (g >= 16) v = dpp_add(v, 3);
+  if (g >= 32) v += __shfl_xor(v, 16);
+  if (g >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Residual epilogue of a [MB x 16*NT] output tile held in LDS (row stride 17): h += tile,
+// next input xg = h * gain_next, per-16-column sums of squares of h.  s_pre holds the
+// prefetched h tile [NT][MB][16] and the next gain [NT*16].
+template <typename T, int MB>
+__device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, const float* s_pre, int tg, int NT,
+                                               int m_base) {
+  const float* s_h = s_pre;
+  const float* s_g = s_pre + NT * MB * 16;
+  for (int e = threadIdx.x; e < NT * MB * 16; e += kGemmThreads) {
+    const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
+    const int m = m_base + r;
+    float* ct = ctile + (t * MB + r) * 17;
+    const float v = s_h[e] + ct[n];
+    ct[n] = v;
+    if (m >= a.M) continue;
+    const int col = (tg * NT + t) * 16 + n;
+    a.h[(size_t)m * a.hidden + col] = v;
+    reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * s_g[t * 16 + n]);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < NT * MB; e += kGemmThreads) {
+    const int t = e / MB, r = e % MB;
+    const int m = m_base + r;
+    if (m >= a.M) continue;
+    const float* ct = ctile + (t * MB + r) * 17;
+    float sum = 0.f;
+    for (int n = 0; n < 16; ++n) sum += ct[n] * ct[n];
+    a.ssq_out[(size_t)m * a.ssq_ld + tg * NT + t] = sum;
+  }
+}
+
 template <typename T, int MT, int EPI, int KPW>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   constexpr int KS = Ty<T>::kStepK;
@@ -186,7 +242,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   constexpr int NTH = kGemmThreads;
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
   constexpr int SB = 12;                            // slab fragments per thread in the first batch
-  constexpr int PMAX = kMaxNormParts / 8;           // norm partials per lane (8 lanes per row)
   const int NT = a.NT, KSL = a.KSL;
   const int KR = KSL * KPW * KS;                    // K range of one workgroup
   const int XSTR = KR * (int)sizeof(T) + 16;        // LDS row stride of the slab
@@ -215,28 +270,33 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < KPW; ++s) wf[s] = wp[(size_t)s * kWave];
   }
-  // 2. activation slab (rows x K range); rows past M read row M-1 and are zeroed below
-  const int FPR = KR / PER;                         // 16-byte fragments per slab row
+  // 2. activation slab (rows x K range) through a buffer resource bounded at row M: rows past M
+  //    read as zero without a memory request
+  const int FPR = KR / PER;                         // 16-byte fragments per slab row (a power of two)
+  const int fsh = 31 - __builtin_clz(FPR);          // e / FPR == e >> fsh (no integer division)
   const int total = MB * FPR;
   const T* xb = reinterpret_cast<const T*>(a.x) + split * KR;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0, a.M * a.ldx * (int)sizeof(T), kBufWord3);
   uint4 xs[SB];
 #pragma unroll
   for (int b = 0; b < SB; ++b) {
     const int e = min((int)threadIdx.x + b * NTH, total - 1);
-    const int m = min(m_base + e / FPR, m_last);
-    xs[b] = *reinterpret_cast<const uint4*>(xb + (size_t)m * a.ldx + (e % FPR) * PER);
+    const int off = ((m_base + (e >> fsh)) * a.ldx + split * KR + (e & (FPR - 1)) * PER) * (int)sizeof(T);
+    xs[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
   }
-  // 3. norm partials of row r = tid/8: lane j = tid%8 takes [j*P, (j+1)*P)
-  float sv[PMAX];
-  const int nr = threadIdx.x / 8, nj = threadIdx.x % 8;
+  // 3. norm partials: G = n_ssq/4 lanes per row, one float4 each, up to 3 passes of rows
+  constexpr int NPASS = 3;
+  float4 sv[NPASS];
+  const int G = a.n_ssq / 4, gsh = 31 - __builtin_clz(G), RP = NTH >> gsh;   // G is a power of two
   if constexpr (NORM) {
-    const int P = a.n_ssq / 8;
-    const float* sp = a.ssq + (size_t)min(m_base + min(nr, MB - 1), m_last) * a.ssq_ld + nj * P;
-    // branch-free: a uniform branch here makes the compiler wait for every earlier load
+    const __amdgpu_buffer_rsrc_t sr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.ssq), (short)0, a.M * a.ssq_ld * 4, kBufWord3);
 #pragma unroll
-    for (int i = 0; i < PMAX; ++i) {
-      const float v = sp[min(i, P - 1)];
-      sv[i] = i < P ? v : 0.f;
+    for (int k = 0; k < NPASS; ++k) {
+      const int row = min(k * RP + ((int)threadIdx.x >> gsh), MB - 1);
+      const int off = ((m_base + row) * a.ssq_ld + ((int)threadIdx.x & (G - 1)) * 4) * 4;
+      sv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
     }
   }
   // 4. epilogue inputs that do not depend on the product
@@ -263,28 +323,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
 #pragma unroll
   for (int b = 0; b < SB; ++b) {
     const int e = threadIdx.x + b * NTH;
-    if (e < total) {
-      const int r = e / FPR;
-      *reinterpret_cast<uint4*>(slab + r * XSTR + (e % FPR) * 16) =
-          m_base + r <= m_last ? xs[b] : make_uint4(0, 0, 0, 0);
-    }
+    if (e < total) *reinterpret_cast<uint4*>(slab + (e >> fsh) * XSTR + (e & (FPR - 1)) * 16) = xs[b];
   }
   for (int e = threadIdx.x + SB * NTH; e < total; e += NTH) {   // K ranges above SB*NTH fragments
-    const int r = e / FPR;
-    *reinterpret_cast<uint4*>(slab + r * XSTR + (e % FPR) * 16) =
-        m_base + r <= m_last ? *reinterpret_cast<const uint4*>(xb + (size_t)(m_base + r) * a.ldx + (e % FPR) * PER)
+    const int r = e >> fsh, q = e & (FPR - 1);
+    *reinterpret_cast<uint4*>(slab + r * XSTR + q * 16) =
+        m_base + r <= m_last ? *reinterpret_cast<const uint4*>(xb + (size_t)(m_base + r) * a.ldx + q * PER)
                              : make_uint4(0, 0, 0, 0);
-  }
-  if constexpr (NORM) {
-    // sum of squares of the row: each lane adds its partials in column order, then a fixed
-    // butterfly over the 8 lanes
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < PMAX; ++i) sum += sv[i];
-    sum += __shfl_xor(sum, 1);
-    sum += __shfl_xor(sum, 2);
-    sum += __shfl_xor(sum, 4);
-    if (nj == 0 && nr < MB) s_inv[nr] = 1.0f / sqrtf(sum / (float)a.hidden + a.eps);
   }
   if constexpr (EPI == EPI_QKV) {
     float2* s_cs = reinterpret_cast<float2*>(smem + L.pre);
@@ -317,27 +362,27 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       }
     }
   }
-  // 6. K-slice partial tiles: fixed pairwise tree (stride 1, 2, 4, ...)
+  if constexpr (NORM) {
+    // 1/rms of each row (needed only by the epilogue, so it runs behind the MFMA chain): each
+    // lane adds its 4 partials in column order, then a fixed butterfly over the row's G lanes
+#pragma unroll
+    for (int k = 0; k < NPASS; ++k) {
+      const float sum = lane_group_sum(((sv[k].x + sv[k].y) + sv[k].z) + sv[k].w, G);
+      const int row = k * RP + ((int)threadIdx.x >> gsh);
+      if (((int)threadIdx.x & (G - 1)) == 0 && row < MB) s_inv[row] = 1.0f / sqrtf(sum / (float)a.hidden + a.eps);
+    }
+  }
+  // 6. K-slice partial tiles added in slice order: element i of lane l of a tile is
+  //    [4(l/16) + i][l % 16] of the transposed product, i.e. row 16mt + l%16, column 4(l/16) + i
   if (cwave) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * kWave + lane] = acc[mt];
   }
   __syncthreads();
-  for (int st = 1; st < KSL; st *= 2) {
-    if (cwave && ksl % (2 * st) == 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4_t& mine = red[(wave * MT + mt) * kWave + lane];
-        mine = mine + red[((wave + st) * MT + mt) * kWave + lane];
-      }
-    }
-    __syncthreads();
-  }
-  // tile t's sum sits in wave t*KSL's slot: element i of lane l = [4(l/16) + i][l % 16] of the
-  // transposed product, i.e. row 16mt + l%16, column 4(l/16) + i
   for (int e = threadIdx.x; e < NT * MT * kWave; e += NTH) {
     const int t = e / (MT * kWave), mt = (e / kWave) % MT, l = e % kWave;
-    const f32x4_t v = red[((t * KSL) * MT + mt) * kWave + l];
+    f32x4_t v = red[((t * KSL) * MT + mt) * kWave + l];
+    for (int j = 1; j < KSL; ++j) v = v + red[((t * KSL + j) * MT + mt) * kWave + l];
     float* dst = ctile + (t * MB + mt * 16 + l % 16) * 17 + 4 * (l / 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = v[i];
@@ -378,29 +423,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       dst[i + half] = Ty<T>::from_f(x2);
     }
   } else if constexpr (EPI == EPI_RESID) {
-    const float* s_h = reinterpret_cast<const float*>(smem + L.pre);
-    const float* s_g = s_h + NT * MB * 16;
-    for (int e = threadIdx.x; e < NT * MB * 16; e += NTH) {
-      const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
-      const int m = m_base + r;
-      float* ct = ctile + (t * MB + r) * 17;
-      const float v = s_h[e] + ct[n];
-      ct[n] = v;
-      if (m >= a.M) continue;
-      const int col = (tg * NT + t) * 16 + n;
-      a.h[(size_t)m * a.hidden + col] = v;
-      reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * s_g[t * 16 + n]);
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < NT * MB; e += NTH) {
-      const int t = e / MB, r = e % MB;
-      const int m = m_base + r;
-      if (m >= a.M) continue;
-      const float* ct = ctile + (t * MB + r) * 17;
-      float sum = 0.f;
-      for (int n = 0; n < 16; ++n) sum += ct[n] * ct[n];
-      a.ssq_out[(size_t)m * a.ssq_ld + tg * NT + t] = sum;
-    }
+    resid_epilogue<T, MB>(a, ctile, reinterpret_cast<const float*>(smem + L.pre), tg, NT, m_base);
   } else if constexpr (EPI == EPI_PARTIAL) {
     for (int e = threadIdx.x; e < NT * MB * 16; e += NTH) {
       const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
@@ -909,6 +932,7 @@ static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t st) {
   const int want = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 3;
   const int MT = want < fit ? want : fit;
   if (EPI == EPI_RESID && a.NT * MT * 16 * 16 > 2 * kGemmThreads) return hipErrorInvalidValue;
+  if (EPI == EPI_PARTIAL && (a.S < 2 || a.S > 8)) return hipErrorInvalidValue;
   if (MT == 1) return launch_gemm_mt<T, EPI, 1>(a, st);
   if (MT == 2) return launch_gemm_mt<T, EPI, 2>(a, st);
   return launch_gemm_mt<T, EPI, 3>(a, st);
@@ -926,6 +950,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
 }
 template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
 template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
+
 
 template <typename T>
 hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st) {
