@@ -153,7 +153,7 @@ constexpr int kGemmThreads = 512;                 // 8 waves per GEMM workgroup
 // Word 3 of a raw buffer resource (32-bit data format): loads past num_records return zero
 // without a memory request.
 constexpr int kBufWord3 = 0x00020000;
-constexpr int kAttnThreads = 1024;                // 16 waves per attention workgroup: one (head, row tile) each
+constexpr int kAttnThreads = 256;                 // 4 waves per attention workgroup: one query head each
 
 struct AttnArgs {
   const void* q; int q_ld;                 // [rows][n_heads*hd]

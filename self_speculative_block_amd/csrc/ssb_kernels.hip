@@ -566,12 +566,19 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
 // in the lanes that feed P^T to the V^T P^T product without shuffles; V is
 // stored transposed in LDS so a V^T fragment is one or two vector reads.
 // ---------------------------------------------------------------------------
-// Online-softmax merge of a running (m, l, o) with a chunk record (mc, lc, oc):
-// m' = max(m, mc), l' = l e^(m-m') + lc e^(mc-m'), o' likewise.
+// Online-softmax merge of a running (m, l, o) with a chunk record (mc, lc, oc), maxima in
+// log2 units: m' = max(m, mc), l' = l 2^(m-m') + lc 2^(mc-m'), o' likewise.
 __device__ __forceinline__ void fold_coef(float m, float mc, float& mn, float& al, float& be) {
   mn = fmaxf(m, mc);
-  al = expf(m - mn);
-  be = expf(mc - mn);
+  al = __builtin_amdgcn_exp2f(m - mn);     // m = -inf (empty running state) gives 0
+  be = __builtin_amdgcn_exp2f(mc - mn);
+}
+// Two fp32 values rounded to bf16 (nearest even) and packed, low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  const f32x2v f = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 __device__ __forceinline__ float fold_val(float v, float al, float vc, float be) {
   return __fadd_rn(__fmul_rn(v, al), __fmul_rn(vc, be));
@@ -588,28 +595,31 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   constexpr int PVS = kKeyChunk / KS;      // steps of P V over keys
   constexpr int KSTR = HD * (int)sizeof(T) + 16;              // K rows [key][d]
   constexpr int VSTR = kKeyChunk * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);   // V^T rows [d][key]
-  constexpr int MT = kTaskRows / 16;
+  constexpr int TILES = kTaskRows / 16;    // 16-row tiles per task
   constexpr int REC = HD + 4;
   constexpr int FPK = HD / PER;            // 16-byte fragments per key row
   constexpr int NKF = 2 * kKeyChunk * FPK; // K and V fragments of one chunk
   constexpr int KVF = (NKF + NTH - 1) / NTH;
   __shared__ __align__(16) unsigned char ks[kKeyChunk * KSTR];
   __shared__ __align__(16) unsigned char vts[HD * VSTR];
-  __shared__ int s_lim[kTaskRows];
+  __shared__ int s_lim[16];
 
-  const AttnTask task = a.tasks.t[blockIdx.z];
+  const AttnTask task = a.tasks.t[blockIdx.z / TILES];
+  const int mt = blockIdx.z % TILES;       // this workgroup's 16-row tile of the task
+  if (mt * 16 >= task.nrows) return;
   const int g = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n_rep = a.n_heads / a.n_kv;
-  // one (query head, 16-row tile) unit per wave
-  const int hl = wave / MT, mt = wave % MT;
-  const bool active = wave < n_rep * MT && mt * 16 < task.nrows;
+  const bool active = wave < n_rep;        // wave = query head within the KV group
   const int row_local = mt * 16 + lane % 16;
-  const int head = g * n_rep + hl;
+  const int head = g * n_rep + wave;
   const int32_t* pt = a.fwd_pt + (size_t)task.req * a.pt_ld;
+  // scores are kept in log2 units: s * scale * log2(e), so the softmax uses exp2
+  const float qscale = a.scale * 1.4426950408889634f;
 
   // ---- first memory round trip: limits, query fragments, page ids ----
-  const int lim_v = threadIdx.x < task.nrows ? a.row_lim[task.row0 + threadIdx.x] : -1;
+  const int lim_v = threadIdx.x < 16 && mt * 16 + (int)threadIdx.x < task.nrows
+                        ? a.row_lim[task.row0 + mt * 16 + threadIdx.x] : -1;
   uint4 qf[QKS];
 #pragma unroll
   for (int st = 0; st < QKS; ++st) {
@@ -630,7 +640,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   const int maxlim = task.lim_mode == 0 ? task.max_lim : a.req->p[task.req] + a.req->B + (task.lim_mode == 2 ? 1 : 0);
   const int cend = a.fold ? maxlim / kKeyChunk + 1 : cbeg + 1;
   if (cbeg * kKeyChunk > maxlim) return;     // no visible key in this chunk slot
-  if (threadIdx.x < kTaskRows) s_lim[threadIdx.x] = lim_v;
+  if (threadIdx.x < 16) s_lim[threadIdx.x] = lim_v;
 
   float run_m = -INFINITY, run_l = 0.f;
   f32x4_t run_o[DT];
@@ -690,25 +700,27 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
           mma_step(s[kt], kf, qf[st], T());
         }
       }
-      const int lim = s_lim[row_local];
+      const int lim = s_lim[lane % 16];
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = c * kKeyChunk + kt * 16 + 4 * (lane / 16) + i;
-          const float z = key <= lim ? s[kt][i] * a.scale : -INFINITY;
+          const float z = key <= lim ? s[kt][i] * qscale : -INFINITY;
           s[kt][i] = z;
           mx = fmaxf(mx, z);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // a row with no visible key in this chunk has mx = -inf and contributes nothing
+      const float mref = mx == -INFINITY ? 0.f : mx;
       float lsum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = (s[kt][i] == -INFINITY) ? 0.f : expf(s[kt][i] - mx);
+          const float p = __builtin_amdgcn_exp2f(s[kt][i] - mref);   // exp2(-inf) = 0
           s[kt][i] = p;
           lsum += p;
         }
@@ -717,41 +729,48 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
       // o^T = V^T P^T ; lane supplies keys pi(lane, j) for P^T and V^T alike
       f32x4_t o[DT];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const unsigned char* vrow = vts + (dt * 16 + lane % 16) * VSTR;
+      for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < PVS; ++st) {
-          uint4 pf, vf;
+      for (int st = 0; st < PVS; ++st) {
+        uint4 pf;
+        if constexpr (sizeof(T) == 2) {
+          // keys 32st + 4(l/16) + {0..3} from tile 2st, then the same +16 from tile 2st+1
+          const f32x4_t p0 = s[2 * st], p1 = s[2 * st + 1];
+          pf.x = pack_bf16x2(p0[0], p0[1]);
+          pf.y = pack_bf16x2(p0[2], p0[3]);
+          pf.z = pack_bf16x2(p1[0], p1[1]);
+          pf.w = pack_bf16x2(p1[2], p1[3]);
+        } else {
+          const f32x4_t p0 = s[st];
+          pf = make_uint4(__float_as_uint(p0[0]), __float_as_uint(p0[1]), __float_as_uint(p0[2]),
+                          __float_as_uint(p0[3]));
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const unsigned char* vrow = vts + (dt * 16 + lane % 16) * VSTR;
+          uint4 vf;
           if constexpr (sizeof(T) == 2) {
-            // keys 32st + 4(l/16) + {0..3} from tile 2st, then the same +16 from tile 2st+1
-            const f32x4_t p0 = s[2 * st], p1 = s[2 * st + 1];
-            pf.x = (uint32_t)f2bf(p0[0]) | ((uint32_t)f2bf(p0[1]) << 16);
-            pf.y = (uint32_t)f2bf(p0[2]) | ((uint32_t)f2bf(p0[3]) << 16);
-            pf.z = (uint32_t)f2bf(p1[0]) | ((uint32_t)f2bf(p1[1]) << 16);
-            pf.w = (uint32_t)f2bf(p1[2]) | ((uint32_t)f2bf(p1[3]) << 16);
             const uint2 va = *reinterpret_cast<const uint2*>(vrow + (32 * st + 4 * (lane / 16)) * 2);
             const uint2 vb = *reinterpret_cast<const uint2*>(vrow + (32 * st + 16 + 4 * (lane / 16)) * 2);
             vf = make_uint4(va.x, va.y, vb.x, vb.y);
           } else {
-            const f32x4_t p0 = s[st];
-            pf = make_uint4(__float_as_uint(p0[0]), __float_as_uint(p0[1]), __float_as_uint(p0[2]),
-                            __float_as_uint(p0[3]));
             vf = *reinterpret_cast<const uint4*>(vrow + (16 * st + 4 * (lane / 16)) * 4);
           }
           mma_step(o[dt], vf, pf, T());
         }
       }
-      // o[dt][i] = o_c[d = dt*16 + 4*(lane/16) + i] of row_local
+      // o[dt][i] = o_c[d = dt*16 + 4*(lane/16) + i] of row_local; the record's max is mref
       if (a.fold) {
-        float mn, al, be;
-        fold_coef(run_m, mx, mn, al, be);
-        run_l = fold_val(run_l, al, lsum, be);
+        if (mx != -INFINITY) {
+          float mn, al, be;
+          fold_coef(run_m, mref, mn, al, be);
+          run_l = fold_val(run_l, al, lsum, be);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+          for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) run_o[dt][i] = fold_val(run_o[dt][i], al, o[dt][i], be);
-        run_m = mn;
+            for (int i = 0; i < 4; ++i) run_o[dt][i] = fold_val(run_o[dt][i], al, o[dt][i], be);
+          run_m = mn;
+        }
       } else if (row_local < task.nrows) {
         float* rec = a.part + (((size_t)(task.row0 + row_local) * a.n_heads + head) * a.max_chunks + c) * REC;
 #pragma unroll
@@ -776,8 +795,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 // head); lane d holds output dimension d.  The row's limit and up to 32
 // records are loaded in one round trip; records of chunks past the limit
 // were never written and are replaced by empty ones.  Within a batch of 32
-// chunks: m* = max m_c, then l = sum l_c e^(m_c - m*) and
-// o = sum o_c e^(m_c - m*) in chunk order; batches fold online.
+// chunks: m* = max m_c, then l = sum l_c 2^(m_c - m*) and
+// o = sum o_c 2^(m_c - m*) in chunk order (maxima in log2 units); batches fold online.
 template <typename T, int HD>
 __global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, int max_chunks, int n_slots,
                                                           int n_heads, const int32_t* row_lim, int M, void* out,
@@ -811,7 +830,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, in
     float lb = 0.f, ob = 0.f;
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
-      const float w = expf(mc[b] - mx);
+      const float w = __builtin_amdgcn_exp2f(mc[b] - mx);
       lb = __fadd_rn(lb, __fmul_rn(lc[b], w));
       ob = __fadd_rn(ob, __fmul_rn(oc[b], w));
     }
@@ -969,9 +988,9 @@ hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, in
 
 template <typename T>
 hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipStream_t st) {
-  if (a.n_heads / a.n_kv * (kTaskRows / 16) > kAttnThreads / kWave) return hipErrorInvalidValue;
+  if (a.n_heads / a.n_kv > kAttnThreads / kWave) return hipErrorInvalidValue;
   if (!a.fold && n_chunk_slots > a.max_chunks) return hipErrorInvalidValue;
-  dim3 grid(a.fold ? 1 : n_chunk_slots, a.n_kv, a.tasks.n);
+  dim3 grid(a.fold ? 1 : n_chunk_slots, a.n_kv, a.tasks.n * (kTaskRows / 16));
   if (head_dim == 64) hipLaunchKernelGGL((k_attn<T, 64>), grid, dim3(kAttnThreads), 0, st, a);
   else hipLaunchKernelGGL((k_attn<T, 32>), grid, dim3(kAttnThreads), 0, st, a);
   return hipGetLastError();
