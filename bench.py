@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+COPY_CALIB_BYTES = 64 << 20
 
 
 def alg_bytes_round(cfg, n, B):
@@ -46,8 +47,10 @@ def alg_bytes_kernel(kind, cfg, M, n_keys):
         return H * qd * e + M * qd * e + M * H * (4 + 4 + e)
     if kind == "gate_up":
         return 2 * F * H * e + M * H * e + M * F * e
-    if kind == "down":
-        return H * F * e + M * F * e + M * H * (4 + 4 + e)
+    if kind == "down":      # K-split into fp32 partial sums: weights + input + S partial outputs
+        return H * F * e + M * F * e + 4 * M * H * 4
+    if kind == "reduce":    # S partials + residual in, residual + next input + norm partials out
+        return 4 * M * H * 4 + M * H * 4 + M * H * (4 + e) + M * (H // 16) * 4
     if kind == "lm_head":
         return V * H * e + M * H * e + M * 12
     if kind == "attention":
@@ -55,6 +58,43 @@ def alg_bytes_kernel(kind, cfg, M, n_keys):
     if kind == "combine":
         return M * qd * e
     return M * 12
+
+
+def traffic_from_profiles(kind):
+    """HBM bytes per launch of `kind` from a committed rocprofv3 counter summary
+    (profiles/*_traffic.txt), or None when there is none or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    src = os.path.join(ROOT, "self_speculative_block_amd", "csrc", "ssb_kernels.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    pdir = os.path.join(ROOT, "profiles")
+    for fn in sorted(os.listdir(pdir)) if os.path.isdir(pdir) else []:
+        if not fn.endswith("_traffic.txt"):
+            continue
+        kv = {}
+        with open(os.path.join(pdir, fn)) as f:
+            for line in f:
+                if ":" in line and not line.startswith(" "):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_kind") == kind and kv.get("source_sha256") == sha:
+            return int(kv["traffic_bytes_per_launch"])
+    return None
+
+
+def event_pair_overhead_us(torch, n=200):
+    """Median time between two HIP events recorded back to back on the current stream."""
+    st = torch.cuda.current_stream()
+    vals = []
+    for _ in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        e1.record(st)
+        e1.synchronize()
+        vals.append(e0.elapsed_time(e1) * 1e3)
+    return statistics.median(vals)
 
 
 def cpu_baseline(cfg, weights, prefix, planted_rows, B, target_s=15.0):
@@ -164,8 +204,12 @@ def main():
     t_med = statistics.median(per_round)
     bytes_round = alg_bytes_round(cfg, P, B)
 
-    # per-kernel timing with HIP events (every launch of one kind per pass)
-    kinds = ["qkv", "attention", "combine", "o", "gate_up", "down", "lm_head", "argmax"]
+    # per-kernel timing with HIP events: the engine launches every kernel of one kind with
+    # hipExtLaunchKernel and a start/stop event pair attached to the dispatch (the dispatch's
+    # own begin/end timestamps, the basis rocprofv3 reports); an empty event pair recorded on
+    # the stream is given for reference only
+    ev_over = event_pair_overhead_us(torch)
+    kinds = ["qkv", "attention", "combine", "o", "gate_up", "down", "reduce", "lm_head", "argmax"]
     breakdown = {}
     for kind in kinds:
         model.profile_kernel(kind)
@@ -173,7 +217,8 @@ def main():
         for k in range(args.profile_steps):
             run(args.warmup + k)
         us, launches = model.profile_read(reset=True)
-        breakdown[kind] = {"avg_us": us / max(launches, 1), "us_per_round": us / args.profile_steps,
+        n = max(launches, 1)
+        breakdown[kind] = {"avg_us": us / n, "us_per_round": us / args.profile_steps,
                            "launches_per_round": launches / args.profile_steps}
     model.profile_kernel(None)
     dom = max(breakdown, key=lambda k: breakdown[k]["us_per_round"])
@@ -182,6 +227,14 @@ def main():
     ab = alg_bytes_kernel(dom, cfg, M, n_keys)
     achieved = ab / (breakdown[dom]["avg_us"] * 1e-6) / 1e9
     print(json.dumps({"kernel_breakdown_us": breakdown, "dominant": dom}), file=sys.stderr)
+
+    # calibration copy for the HBM byte counters: one device-to-device copy of a known size
+    # (outside the timed region); its FETCH_SIZE / WRITE_SIZE scale the counters of the GEMM
+    calib_src = torch.ones(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -208,8 +261,8 @@ def main():
         "round_roofline_frac": bytes_round / t_med / (PEAK_HBM_GBS * 1e9),
         "round_alg_bytes": bytes_round,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "alg_bytes_per_launch": ab,
-                     "avg_launch_us": breakdown[dom]["avg_us"]},
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles(dom), "alg_bytes_per_launch": ab,
+                     "avg_launch_us": breakdown[dom]["avg_us"], "empty_event_pair_us": ev_over},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

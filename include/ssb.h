@@ -210,11 +210,14 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
                        int32_t* argmax, float* top1, float* top2, void* stream);
 
 /* Kernel timing hook for measurement. While a kind is selected, every
- * launch of that kernel kind is bracketed by HIP events recorded on the
+ * launch of that kernel kind is issued with hipExtLaunchKernel and a start /
+ * stop event pair that the runtime attaches to the dispatch itself, on the
  * stream it is launched on. Rounds and AR steps then run without graph
  * replay. ssb_profile_read returns the summed event time and the launch
  * count since the last reset; reset != 0 clears them.
- * kind: one of SSB_K_*, or -1 to stop timing. */
+ * kind: one of SSB_K_*, or -1 to stop timing. SSB_K_DOWN is the down
+ * projection GEMM; SSB_K_REDUCE its K-split reduce (absent when the down
+ * projection is not split). */
 #define SSB_K_QKV 0
 #define SSB_K_ATTN 1
 #define SSB_K_COMBINE 2
@@ -223,6 +226,7 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
 #define SSB_K_DOWN 5
 #define SSB_K_LMHEAD 6
 #define SSB_K_ARGMAX 7
+#define SSB_K_REDUCE 8
 int ssb_profile_kernel(ssb_model* m, int kind);
 int ssb_profile_read(ssb_model* m, double* total_us, long long* launches, int reset);
 

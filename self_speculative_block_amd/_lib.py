@@ -9,7 +9,8 @@ SSB_OK, SSB_EINVAL, SSB_ENOKV, SSB_EHIP, SSB_ESTATE, SSB_ENOMEM = 0, -1, -2, -3,
 SSB_F32, SSB_BF16 = 0, 1
 SSB_MAX_BATCH = 16
 SSB_MAX_BLOCK = 64
-KERNEL_KINDS = {"qkv": 0, "attention": 1, "combine": 2, "o": 3, "gate_up": 4, "down": 5, "lm_head": 6, "argmax": 7}
+KERNEL_KINDS = {"qkv": 0, "attention": 1, "combine": 2, "o": 3, "gate_up": 4, "down": 5, "lm_head": 6, "argmax": 7,
+                "reduce": 8}
 
 c_int, c_float, c_double, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
 c_void_p = ctypes.c_void_p

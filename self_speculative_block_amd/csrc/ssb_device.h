@@ -168,6 +168,10 @@ struct AttnArgs {
   AttnTasks tasks;
 };
 
+// Timing hook of the launchers: while g_prof_ev[0] is set, launches use hipExtLaunchKernel with
+// this start/stop pair (single-threaded use, set and cleared by the engine around one launch).
+extern hipEvent_t g_prof_ev[2];
+
 // Launchers (defined in ssb_kernels.hip).
 template <typename T>
 hipError_t launch_pack(uint4* dst, int n_tiles, int K, int mode, const void* s0, const void* s1, const void* s2,

@@ -49,6 +49,7 @@ int guard(F&& f) {
     f();
     return SSB_OK;
   } catch (const Error& e) {
+    ssb::g_prof_ev[0] = ssb::g_prof_ev[1] = nullptr;   // a launch that failed inside the timing hook
     g_err = e.msg;
     return e.code;
   } catch (const std::bad_alloc&) {
@@ -144,14 +145,15 @@ namespace {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Kernel timing hook: an event pair around each launch of the selected kind.
-void prof_begin(ssb_model* m, int kind, hipStream_t st) {
+void prof_begin(ssb_model* m, int kind, hipStream_t) {
   if (m->prof_kind != kind) return;
   if (m->prof_used * 2 + 2 > (int)m->prof_ev.size()) fail(SSB_EINVAL, "kernel timing: too many launches per call");
-  hip_check(hipEventRecord(m->prof_ev[2 * m->prof_used], st), "profile event");
+  g_prof_ev[0] = m->prof_ev[2 * m->prof_used];
+  g_prof_ev[1] = m->prof_ev[2 * m->prof_used + 1];
 }
-void prof_end(ssb_model* m, int kind, hipStream_t st) {
+void prof_end(ssb_model* m, int kind, hipStream_t) {
   if (m->prof_kind != kind) return;
-  hip_check(hipEventRecord(m->prof_ev[2 * m->prof_used + 1], st), "profile event");
+  g_prof_ev[0] = g_prof_ev[1] = nullptr;
   ++m->prof_used;
 }
 // Called after the stream has been synchronized.
@@ -496,13 +498,13 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       a.x = m->act; a.ldx = c.ffn;
       a.gain_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
       prof_begin(m, SSB_K_DOWN, st);
-      if (a.S > 1) {
-        hip_check(launch_gemm<T>(a, EPI_PARTIAL, st), "down gemm");
-        hip_check(launch_resid_reduce<T>(a, st), "down reduce");
-      } else {
-        hip_check(launch_gemm<T>(a, EPI_RESID, st), "down gemm");
-      }
+      hip_check(launch_gemm<T>(a, a.S > 1 ? EPI_PARTIAL : EPI_RESID, st), "down gemm");
       prof_end(m, SSB_K_DOWN, st);
+      if (a.S > 1) {
+        prof_begin(m, SSB_K_REDUCE, st);
+        hip_check(launch_resid_reduce<T>(a, st), "down reduce");
+        prof_end(m, SSB_K_REDUCE, st);
+      }
     }
   }
   // LM head + argmax
@@ -1067,7 +1069,7 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
 int ssb_profile_kernel(ssb_model* m, int kind) {
   return guard([&] {
     if (!m) fail(SSB_EINVAL, "null model");
-    if (kind < -1 || kind > SSB_K_ARGMAX) fail(SSB_EINVAL, "unknown kernel kind");
+    if (kind < -1 || kind > SSB_K_REDUCE) fail(SSB_EINVAL, "unknown kernel kind");
     hip_check(hipSetDevice(m->device), "hipSetDevice");
     if (kind >= 0 && m->prof_ev.empty()) {
       // two forwards of a round launch each kind at most n_layers + 1 times, plus prefill chunks

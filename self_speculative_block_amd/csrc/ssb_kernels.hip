@@ -17,7 +17,18 @@
 // cross-workgroup synchronization.
 #include "ssb_device.h"
 
+#include <hip/hip_ext.h>
+
 namespace ssb {
+
+// Timing hook: while set, the next launch carries this start/stop event pair on its dispatch.
+hipEvent_t g_prof_ev[2] = {nullptr, nullptr};
+
+#define SSB_LAUNCH(K, G, B, SHM, ST, ...)                                                            \
+  do {                                                                                               \
+    if (g_prof_ev[0]) hipExtLaunchKernelGGL(K, G, B, SHM, ST, g_prof_ev[0], g_prof_ev[1], 0, __VA_ARGS__); \
+    else hipLaunchKernelGGL(K, G, B, SHM, ST, __VA_ARGS__);                                          \
+  } while (0)
 
 // ---------------------------------------------------------------------------
 // Weight packing: W[N][K] -> tiles [n_tile][k_step][lane][16 bytes].  Lane l
@@ -899,7 +910,7 @@ template hipError_t launch_pack<float>(uint4*, int, int, int, const void*, const
 
 template <typename T>
 hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_prep_embed<T>, dim3(a.M, a.hidden / 64), dim3(64), 0, st, a);
+  SSB_LAUNCH(k_prep_embed<T>, dim3(a.M, a.hidden / 64), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 template hipError_t launch_prep<bf16_t>(const PrepArgs&, hipStream_t);
@@ -911,7 +922,7 @@ static hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
   const GemmLds L = gemm_lds(MT, KR * (int)sizeof(T), a.NT, a.KSL, a.n_ssq, EPI);
   const int m_blocks = (a.M + 16 * MT - 1) / (16 * MT);
   const dim3 grid(a.n_tiles / a.NT, a.S, m_blocks), block(kGemmThreads);
-  hipLaunchKernelGGL((k_gemm<T, MT, EPI, KPW>), grid, block, L.total, st, a);
+  SSB_LAUNCH((k_gemm<T, MT, EPI, KPW>), grid, block, L.total, st, a);
   return hipGetLastError();
 }
 
@@ -974,7 +985,7 @@ template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
 template <typename T>
 hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st) {
   if (a.S < 1 || a.S > 8 || a.hidden % 64 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_resid_reduce<T>, dim3(a.M, a.hidden / 64), dim3(64), 0, st, a);
+  SSB_LAUNCH(k_resid_reduce<T>, dim3(a.M, a.hidden / 64), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 template hipError_t launch_resid_reduce<bf16_t>(const GemmArgs&, hipStream_t);
@@ -982,7 +993,7 @@ template hipError_t launch_resid_reduce<float>(const GemmArgs&, hipStream_t);
 
 hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, int n_groups, int ld, int M,
                          int32_t* tok, float* top1, float* top2, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, n_groups, ld, tok, top1, top2);
+  SSB_LAUNCH(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, n_groups, ld, tok, top1, top2);
   return hipGetLastError();
 }
 
@@ -991,8 +1002,8 @@ hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipSt
   if (a.n_heads / a.n_kv > kAttnThreads / kWave) return hipErrorInvalidValue;
   if (!a.fold && n_chunk_slots > a.max_chunks) return hipErrorInvalidValue;
   dim3 grid(a.fold ? 1 : n_chunk_slots, a.n_kv, a.tasks.n * (kTaskRows / 16));
-  if (head_dim == 64) hipLaunchKernelGGL((k_attn<T, 64>), grid, dim3(kAttnThreads), 0, st, a);
-  else hipLaunchKernelGGL((k_attn<T, 32>), grid, dim3(kAttnThreads), 0, st, a);
+  if (head_dim == 64) SSB_LAUNCH((k_attn<T, 64>), grid, dim3(kAttnThreads), 0, st, a);
+  else SSB_LAUNCH((k_attn<T, 32>), grid, dim3(kAttnThreads), 0, st, a);
   return hipGetLastError();
 }
 template hipError_t launch_attn<bf16_t>(const AttnArgs&, int, int, hipStream_t);
@@ -1004,10 +1015,10 @@ hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, i
   if (n_slots < 1 || n_slots > max_chunks) return hipErrorInvalidValue;
   const int blocks = (M * n_heads + 3) / 4;
   if (head_dim == 64)
-    hipLaunchKernelGGL((k_attn_combine<T, 64>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks, n_slots,
+    SSB_LAUNCH((k_attn_combine<T, 64>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks, n_slots,
                        n_heads, row_lim, M, out, out_ld);
   else
-    hipLaunchKernelGGL((k_attn_combine<T, 32>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks, n_slots,
+    SSB_LAUNCH((k_attn_combine<T, 32>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks, n_slots,
                        n_heads, row_lim, M, out, out_ld);
   return hipGetLastError();
 }
@@ -1018,7 +1029,7 @@ template hipError_t launch_attn_combine<float>(const float*, int, int, int, int,
 
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
                          int32_t* out, int out_stride, hipStream_t st) {
-  hipLaunchKernelGGL(k_accept, dim3(n_req), dim3(64), 0, st, row_tok, am, ra, eos_id, out, out_stride);
+  SSB_LAUNCH(k_accept, dim3(n_req), dim3(64), 0, st, row_tok, am, ra, eos_id, out, out_stride);
   return hipGetLastError();
 }
 
