@@ -126,6 +126,149 @@ def cpu_baseline(cfg, weights, prefix, planted_rows, B, target_s=15.0):
                       f"same planted drafts), {t_total:.1f} s of CPU time; prefill excluded"}
 
 
+def plant_rows(cont, c, astar, B, vocab):
+    """Draft for a round that starts after output token y_c (1-based), from the GPU's own AR
+    output cont = [y1, y2, ...]: d_j = y_{c+1+j} for j <= A*, then a token different from
+    y_{c+A*+2}; -1 (keep the draft's own token) elsewhere and past the end of cont."""
+    row = [-1] * B
+    for j in range(1, B + 1):
+        idx = c + j
+        if idx >= len(cont):
+            break
+        if j <= astar:
+            row[j - 1] = int(cont[idx])
+        elif j == astar + 1:
+            row[j - 1] = int((cont[idx] + 1) % (vocab - 1))
+            break
+    return row
+
+
+def decode_workload(args, wid):
+    """Configs 3 and 4: per region, GPU AR decode (its output plants the drafts), then GPU
+    self-speculative decode of the same region; decode-only committed tokens/s of both."""
+    import numpy as np
+    import torch
+    from ssb_inputs import generate_weights, plant_accept_lengths, prefix_embeddings, workload
+    from ssb_inputs.schedule import target_lengths
+    from self_speculative_block_amd.engine import KV, Model, Pool
+
+    wl = workload(wid)
+    cfg, B, P = wl.model, wl.block, wl.prefix_len
+    lengths = target_lengths(wl)
+    n = min(args.regions or wl.n_regions, wl.n_regions)
+    cap = max(lengths[:n])
+    torch.cuda.set_device(0)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8)
+    pool = Pool(model, n_pages=(P + cap + 2 * B + 8) // 16 + 8)
+    kv = KV(pool, P + cap + 2 * B + 8)
+    tot = {"spec_tokens": 0, "spec_us": 0.0, "ar_tokens": 0, "ar_us": 0.0, "rounds": 0, "forwards": 0,
+           "accepted": 0}
+    hist = np.zeros(B + 1, dtype=np.int64)
+    for i in range(n):
+        pre_dev = model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden))
+        L = lengths[i]
+        kv.reset()
+        ar, st_ar = kv.decode_ar(pre_dev, L)
+        astar = plant_accept_lengths(wl.wid, i, L, B, wl.plant_p, wl.full_accept_p)
+        kv.reset()
+        spec, st = kv.decode(pre_dev, B, L, cont_dev=torch.tensor(ar, dtype=torch.int32, device="cuda"),
+                             astar=astar)
+        assert spec == ar, f"region {i}: self-speculative output differs from AR"
+        tot["spec_tokens"] += st.tokens - 1
+        tot["spec_us"] += st.decode_us
+        tot["ar_tokens"] += st_ar.tokens - 1
+        tot["ar_us"] += st_ar.decode_us
+        tot["rounds"] += st.rounds
+        tot["forwards"] += st.forwards
+        tot["accepted"] += st.accepted
+        for a in astar[: st.rounds]:
+            hist[min(int(a), B)] += 1
+    spec_tps = tot["spec_tokens"] / (tot["spec_us"] * 1e-6)
+    ar_tps = tot["ar_tokens"] / (tot["ar_us"] * 1e-6)
+    line = {
+        "metric": "decode-only committed tokens/s, self-speculative (B=32, batch 1), prefill excluded",
+        "value": spec_tps, "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "regions": n, "prefix": P, "block_B": B,
+                   "mean_target_len": float(np.mean(lengths[:n]))},
+        "ar_tokens_per_s": ar_tps, "speedup_vs_ar": spec_tps / ar_tps,
+        "tpf": tot["spec_tokens"] / max(tot["forwards"], 1),
+        "mean_accept": tot["accepted"] / max(tot["rounds"], 1), "rounds": tot["rounds"],
+        "planted_accept_histogram": hist.tolist(),
+        "outputs_identical_to_ar": True,
+    }
+    print(json.dumps(line))
+
+
+def batched_workload(args):
+    """Config 5: 16 concurrent requests (12 text, 3 table, 1 formula), one launch per stage per
+    round for all unfinished requests; aggregate committed tokens/s and page decode time."""
+    import numpy as np
+    import torch
+    from ssb_inputs import generate_weights, plant_accept_lengths, prefix_embeddings, workload
+    from ssb_inputs.schedule import target_lengths
+    from self_speculative_block_amd.engine import KV, Model, Pool, round_batch
+
+    wl = workload(5)
+    cfg, P = wl.model, wl.prefix_len
+    lengths = target_lengths(wl)
+    R = len(lengths)
+    torch.cuda.set_device(0)
+    Bmax = max((wl.block,) + tuple(wl.blocks_extra))
+    cap = max(lengths) + 2 * Bmax + 8
+    model = Model(cfg, generate_weights(cfg), block_B=Bmax, max_rows=2048, max_positions=P + cap)
+    pool = Pool(model, n_pages=R * ((P + cap) // 16 + 2))
+    kvs = [KV(pool, P + cap) for _ in range(R)]
+    pres = [model.prefix_tensor(prefix_embeddings(wl.wid, r, P, cfg.hidden)) for r in range(R)]
+    # AR reference per request (plants the drafts), and the AR page time when requests run one by one
+    ars, ar_us = [], 0.0
+    for r in range(R):
+        kvs[r].reset()
+        out, st = kvs[r].decode_ar(pres[r], lengths[r])
+        ars.append(out)
+        ar_us += st.decode_us
+    results = {}
+    for B in (wl.block,) + tuple(wl.blocks_extra):
+        astars = [plant_accept_lengths(wl.wid, r, lengths[r], B, wl.plant_p) for r in range(R)]
+        outs = []
+        for r in range(R):
+            kvs[r].reset()
+            outs.append([kvs[r].prefill(pres[r])])
+        rounds = [0] * R
+        n_launch = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while True:
+            act = [r for r in range(R) if len(outs[r]) < lengths[r] and outs[r][-1] != cfg.eos_id]
+            if not act:
+                break
+            rows = [plant_rows(ars[r], len(outs[r]), int(astars[r][rounds[r]]), B, cfg.vocab) for r in act]
+            planted = torch.tensor(rows, dtype=torch.int32, device="cuda")
+            res = round_batch(model, [kvs[r] for r in act], B, [lengths[r] - len(outs[r]) for r in act],
+                              planted_dev=planted)
+            for r, (c, _A) in zip(act, res):
+                outs[r] += c
+                rounds[r] += 1
+            n_launch += 1
+        t = time.perf_counter() - t0
+        for r in range(R):
+            assert outs[r] == ars[r], f"request {r}: batched self-speculative output differs from AR"
+        toks = sum(len(o) - 1 for o in outs)
+        results[B] = {"tokens_per_s": toks / t, "page_decode_ms": t * 1e3, "batched_rounds": n_launch,
+                      "tokens": toks}
+    ar_tps = sum(len(o) - 1 for o in ars) / (ar_us * 1e-6)
+    line = {
+        "metric": "aggregate decode-only committed tokens/s, batched self-speculative page (16 requests)",
+        "value": results[wl.block]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "requests": R, "prefix": P, "lengths": lengths},
+        "by_block": {str(k): v for k, v in results.items()},
+        "ar_one_by_one_tokens_per_s": ar_tps,
+        "outputs_identical_to_ar": True,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,12 +276,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--workload", choices=["round", "text", "table", "batched"], default="round",
+                    help="round: the round microbenchmark (the headline line); text / table: decode "
+                         "of text or table regions; batched: the 16-request page")
+    ap.add_argument("--regions", type=int, default=0, help="text / table: number of regions (0 = all)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the round engine is a single-GPU path "
               "(requests would shard across GPUs with no exchange step); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "text":
+        return decode_workload(args, 3)
+    if args.workload == "table":
+        return decode_workload(args, 4)
+    if args.workload == "batched":
+        return batched_workload(args)
 
     import numpy as np
     import torch
@@ -188,15 +341,31 @@ def main():
     committed = 0
     accepts = []
     per_round = []
+    events = []
+    st = torch.cuda.current_stream()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         ts = time.perf_counter()
+        e0.record(st)
         n, A = run(args.warmup + k)
+        e1.record(st)
         per_round.append(time.perf_counter() - ts)
+        events.append((e0, e1))
         committed += n
         accepts.append(A)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    dev_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in events)
+
+    # rounds without planting (the draft's own proposals), same state
+    unplanted = []
+    for k in range(min(args.steps, 50)):
+        kv.rewind(P, y1)
+        ts = time.perf_counter()
+        kv.round(B)
+        unplanted.append(time.perf_counter() - ts)
     for k in range(args.steps):
         assert accepts[k] == min(int(astar[args.warmup + k]), B), "planted accept length not realized"
     value = committed / elapsed
@@ -234,6 +403,14 @@ def main():
     calib_dst = torch.empty_like(calib_src)
     calib_dst.copy_(calib_src)
     torch.cuda.synchronize()
+    # attainable-bandwidth probe: the same copy, timed (read + write bytes / time)
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record()
+    for _ in range(10):
+        calib_dst.copy_(calib_src)
+    ce1.record()
+    ce1.synchronize()
+    copy_gbs = 10 * 2 * COPY_CALIB_BYTES / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
     del calib_src, calib_dst
 
     cpu = None
@@ -258,6 +435,10 @@ def main():
                    "cached_positions": P, "batch": 1, "mean_accept": float(np.mean(accepts)),
                    "committed_per_round": committed / args.steps},
         "round_us_median": t_med * 1e6,
+        "round_device_us": {"median": statistics.median(dev_us), "p10": dev_us[len(dev_us) // 10],
+                            "p90": dev_us[(len(dev_us) * 9) // 10]},
+        "round_us_unplanted_median": statistics.median(unplanted) * 1e6,
+        "copy_probe_GBs": copy_gbs,
         "round_roofline_frac": bytes_round / t_med / (PEAK_HBM_GBS * 1e9),
         "round_alg_bytes": bytes_round,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
