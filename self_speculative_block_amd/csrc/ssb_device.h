@@ -150,6 +150,7 @@ __host__ __device__ inline GemmLds gemm_lds(int MT, int kr_bytes, int NT, int KS
 }
 constexpr int kGemmMaxLds = 160 * 1024 - 1024;   // dynamic LDS budget (static arrays take < 1 KiB)
 constexpr int kGemmThreads = 512;                 // 8 waves per GEMM workgroup
+constexpr int kGemmPersistentWgs = 256;           // LM head: resident workgroups (one per CU)
 // Word 3 of a raw buffer resource (32-bit data format): loads past num_records return zero
 // without a memory request.
 constexpr int kBufWord3 = 0x00020000;

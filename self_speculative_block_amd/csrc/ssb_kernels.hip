@@ -263,7 +263,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   float* ctile = reinterpret_cast<float*>(smem + L.ctile);
   __shared__ float s_inv[MB];
 
-  const int tg = blockIdx.x, split = blockIdx.y;
+  constexpr bool LOOP = (EPI == EPI_LOGITS);         // LM head: persistent over tile groups
+  int tg = blockIdx.x;
+  const int split = blockIdx.y;
   const int m_base = blockIdx.z * MB;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const bool cwave = wave < NT * KSL;               // waves past NT*KSL only help with loads
@@ -358,6 +360,22 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   }
   __syncthreads();
 
+  // The LM head's workgroups stay resident: the slab and 1/rms are staged once, then each
+  // workgroup walks its tile groups (stride gridDim.x), loading the next group's weights while
+  // the current one is multiplied and reduced.  Every other GEMM runs the body once.
+  const int n_groups = a.n_tiles / NT;
+  bool first = true;
+  for (;;) {
+  const int tg_next = tg + (int)gridDim.x;
+  const bool more = LOOP && tg_next < n_groups;
+  uint4 wn[KPW];
+  if constexpr (LOOP) {
+    // branch-free: past the last group, the current group's lines are read again (L2 hits)
+    const int tg_load = more ? tg_next : tg;
+    const uint4* wp = a.W + ((size_t)(tg_load * NT + (cwave ? wave / KSL : 0)) * ksteps + kstep0) * kWave + lane;
+#pragma unroll
+    for (int s = 0; s < KPW; ++s) wn[s] = wp[(size_t)s * kWave];
+  }
   // 5. MFMA chain over this wave's K steps
   f32x4_t acc[MT];
 #pragma unroll
@@ -373,7 +391,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       }
     }
   }
-  if constexpr (NORM) {
+  if (NORM && first) {
     // 1/rms of each row (needed only by the epilogue, so it runs behind the MFMA chain): each
     // lane adds its 4 partials in column order, then a fixed butterfly over the row's G lanes
 #pragma unroll
@@ -497,6 +515,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
         a.am_v2[o] = best.v2;
       }
     }
+  }
+  if (!more) break;
+  tg = tg_next;
+#pragma unroll
+  for (int s = 0; s < KPW; ++s) wf[s] = wn[s];
+  first = false;
+  __syncthreads();   // red and ctile are reused by the next group
   }
 }
 
@@ -921,7 +946,12 @@ static hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
   const int KR = a.KSL * KPW * Ty<T>::kStepK;
   const GemmLds L = gemm_lds(MT, KR * (int)sizeof(T), a.NT, a.KSL, a.n_ssq, EPI);
   const int m_blocks = (a.M + 16 * MT - 1) / (16 * MT);
-  const dim3 grid(a.n_tiles / a.NT, a.S, m_blocks), block(kGemmThreads);
+  int gx = a.n_tiles / a.NT;
+  if (EPI == EPI_LOGITS) {           // persistent: about one workgroup per CU, equal group counts
+    const int per = (gx + kGemmPersistentWgs - 1) / kGemmPersistentWgs;
+    gx = (gx + per - 1) / per;
+  }
+  const dim3 grid(gx, a.S, m_blocks), block(kGemmThreads);
   SSB_LAUNCH((k_gemm<T, MT, EPI, KPW>), grid, block, L.total, st, a);
   return hipGetLastError();
 }
