@@ -24,6 +24,8 @@ from .decode import (
     build_plant, tpf, teacher_forced_argmax,
 )
 from .training_rules import complementary_masks, training_visibility
+from .direct import (confidence, select_positions, BlockResult, dd_fill, dd_cache_write, dd_release,
+                     DDStats, dd_tpf, dd_decode)
 
 __all__ = [
     "Decoder", "KVCache", "rms_norm", "rope", "silu", "attend", "argmax_excluding",
@@ -31,4 +33,6 @@ __all__ = [
     "spec_decode", "draft_visibility", "verify_visibility", "causal_visibility",
     "accept_length", "commit_tokens", "build_plant", "tpf", "teacher_forced_argmax",
     "complementary_masks", "training_visibility",
+    "confidence", "select_positions", "BlockResult", "dd_fill", "dd_cache_write", "dd_release",
+    "DDStats", "dd_tpf", "dd_decode",
 ]
