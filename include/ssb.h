@@ -96,16 +96,19 @@ typedef struct ssb_model ssb_model;
 typedef struct ssb_pool ssb_pool;
 typedef struct ssb_kv ssb_kv;
 
-/* Per-decode statistics (ssb_decode / ssb_decode_ar). Accept counts exclude
- * a0 and a(A+1) (GravityOCR review, section 4.1). Forwards count draft and
- * verify passes, not prefill. */
+/* Per-decode statistics (ssb_decode / ssb_decode_ar / ssb_decode_dd).
+ * Accept counts exclude a0 and a(A+1) (GravityOCR review, section 4.1).
+ * Forwards count draft and verify passes, not prefill. Direct diffusion
+ * counts only the forwards that commit tokens; its cache-write forwards are
+ * counted apart (GravityOCR review, Appendix C, forward accounting). */
 typedef struct ssb_stats {
-  int rounds;            /* rounds run (AR: steps) */
-  int forwards;          /* decode forwards: 2 per round, 1 per AR step */
+  int rounds;            /* rounds run (AR: steps; direct diffusion: blocks) */
+  int forwards;          /* decode forwards: 2 per round, 1 per AR step, denoising steps */
   int tokens;            /* output tokens, y1 from prefill included */
   int accepted;          /* sum of A over rounds */
   double decode_us;      /* wall time of the decode loop, prefill excluded */
   double prefill_us;     /* wall time of prefill */
+  int cache_forwards;    /* direct diffusion: cache-write forwards */
 } ssb_stats;
 
 const char* ssb_last_error(void);
@@ -199,6 +202,39 @@ int ssb_decode_ar(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int m
 int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_t* max_commit,
                     const int32_t* planted_dev, int32_t* committed, int32_t* n_committed,
                     int32_t* accept_len, void* stream);
+
+/* Direct block-diffusion decoding of one block (GravityOCR review, section 2
+ * "Block Diffusion" and Appendix B.1; Trillion Labs blog, "confidence
+ * threshold" entry). The block is the B positions p+1..p+B after the
+ * boundary x0 at p, all [M] at first. Each denoising step is one draft-mode
+ * forward over [x0, s_1..s_B] (s_j: committed token or [M]); position j
+ * takes the greedy token of window row j-1 (shift-by-one), its confidence
+ * is that token's softmax probability over the vocabulary without [M].
+ * Every undecided position with confidence >= tau is committed; if none,
+ * the single most confident one (lowest position on ties). At most B steps.
+ *   write_cache: 1 = run the cache-write forward (causal over s_1..s_{B-1}
+ *     at p+1..p+B-1; it verifies nothing) and advance the kv to length p+B
+ *     with boundary s_B; 0 = leave the kv's state at (p, x0).
+ *   tokens: host [B], the block. n_tokens: tokens that belong to the output
+ *     after the cut at the first EOS (inclusive) and at max_commit.
+ *   steps: denoising forwards run. step_of: host [B], nullable: the step
+ *     (0-based) that committed each position.
+ *   step_conf / step_tok: host [B][B], nullable: per step, the confidence and
+ *     greedy token of window rows 0..B-1 (rows of committed positions too).
+ *   step_logits_dev: nullable device fp32 [B][B+1][vocab]: each step's logits.
+ * Errors: SSB_ESTATE without a boundary token; SSB_EINVAL for B outside
+ * [1, block_B], tau NaN or max_commit < 1; SSB_ENOKV past max_positions;
+ * SSB_EHIP for NaN logits (the kv's state is then unchanged). */
+int ssb_dd_block(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, int write_cache, int32_t* tokens,
+                 int32_t* n_tokens, int32_t* steps, int32_t* step_of, float* step_conf, int32_t* step_tok,
+                 float* step_logits_dev, void* stream);
+
+/* Prefill, then direct block-diffusion blocks until EOS or max_len output
+ * tokens (y1 included). The block that ends the output (EOS inside, or the
+ * budget reached) runs no cache-write forward. stats: rounds = blocks,
+ * forwards = denoising forwards, cache_forwards = cache-write forwards. */
+int ssb_decode_dd(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int B, float tau, int max_len,
+                  int32_t* out, int32_t* n_out, ssb_stats* stats, void* stream);
 
 /* Teacher-forced causal forward over tokens (host [M], M <= max_rows) at
  * positions p..p+M-1 of the kv. Writes their KV but does not change the

@@ -36,7 +36,7 @@ class SsbWeights(ctypes.Structure):
 
 class SsbStats(ctypes.Structure):
     _fields_ = [("rounds", c_int), ("forwards", c_int), ("tokens", c_int), ("accepted", c_int),
-                ("decode_us", c_double), ("prefill_us", c_double)]
+                ("decode_us", c_double), ("prefill_us", c_double), ("cache_forwards", c_int)]
 
 
 # name -> (restype, argtypes)
@@ -65,6 +65,10 @@ SIGNATURES = {
                               ctypes.POINTER(SsbStats), c_void_p]),
     "ssb_round_batch": (c_int, [c_void_p, ctypes.POINTER(c_void_p), c_int, c_int, P_i32, c_void_p, P_i32,
                                 P_i32, P_i32, c_void_p]),
+    "ssb_dd_block": (c_int, [c_void_p, c_void_p, c_int, c_float, c_int, c_int, P_i32, P_i32, P_i32, P_i32,
+                             P_f32, P_i32, c_void_p, c_void_p]),
+    "ssb_decode_dd": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_float, c_int, P_i32, P_i32,
+                              ctypes.POINTER(SsbStats), c_void_p]),
     "ssb_profile_kernel": (c_int, [c_void_p, c_int]),
     "ssb_profile_read": (c_int, [c_void_p, ctypes.POINTER(c_double), ctypes.POINTER(ctypes.c_longlong), c_int]),
     "ssb_forward_tokens": (c_int, [c_void_p, c_void_p, P_i32, c_int, c_int, c_void_p, P_i32, P_f32, P_f32,

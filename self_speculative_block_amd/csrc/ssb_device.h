@@ -27,6 +27,7 @@ constexpr int kMaxReq = 16;        // requests per batched launch
 constexpr int kMaxTasks = 64;      // attention row tasks per launch
 constexpr int kTaskRows = 48;      // rows per attention task (3 MFMA row tiles)
 constexpr int kMaxNormParts = 128; // per-16-column norm partials (hidden <= 2048)
+constexpr float kLog2e = 1.4426950408889634f;   // exp(x) = exp2(x * log2(e))
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ bf16_t f2bf(float f) {
@@ -83,6 +84,10 @@ struct ReqArgs {
   int cont_len[kMaxReq];
   int cont_c[kMaxReq];                // output tokens committed before this round
   int astar[kMaxReq];                 // planted accept length (continuation mode)
+  // direct block diffusion: the request's block tokens (device [B], [M] while undecided).
+  // DRAFT rows 1..B embed win[j-1]; VERIFY rows j embed win[j] (the cache-write forward).
+  int32_t* win[kMaxReq];
+  float tau;                          // confidence threshold of the denoising step
 };
 
 // Row task of the attention kernel.  lim_mode 0: max_lim given; 1: draft
@@ -127,6 +132,7 @@ struct GemmArgs {
   void* act; int act_ld;                        // SWIGLU
   float* logits; int vocab; int mask_id;        // LOGITS
   float* am_v1; int32_t* am_i1; float* am_v2; int am_ld;   // LOGITS: records [M][am_ld]
+  float* am_s;                                  // LOGITS, nullable: sum of exp(z - group max) [M][am_ld]
 };
 
 // Dynamic LDS layout of k_gemm (byte offsets), shared by the kernel and its launcher:
@@ -181,13 +187,18 @@ template <typename T> hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
 template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
 template <typename T> hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st);
 int gemm_max_mt(int elem, int K, int S, int NT, int KSL, int n_ssq, int epi);
-hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, int n_groups, int ld, int M,
-                         int32_t* tok, float* top1, float* top2, hipStream_t st);
+// gs (nullable, then conf too): per-group softmax sums of the LM head; conf [M] gets the
+// greedy token's softmax probability.
+hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, int n_groups, int ld,
+                         int M, int32_t* tok, float* top1, float* top2, float* conf, hipStream_t st);
 template <typename T> hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipStream_t st);
 template <typename T>
 hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, int n_heads, int head_dim,
                                const int32_t* row_lim, int M, void* out, int out_ld, hipStream_t st);
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
                          int32_t* out, int out_stride, hipStream_t st);
+hipError_t launch_dd_init(const ReqArgs* ra, int n_req, int mask_id, int32_t* rec, int rec_stride, hipStream_t st);
+hipError_t launch_dd_select(const int32_t* am, const float* conf, const ReqArgs* ra, int n_req, int mask_id,
+                            int vocab, int32_t* rec, int rec_stride, hipStream_t st);
 
 }  // namespace ssb

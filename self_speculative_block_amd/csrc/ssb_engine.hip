@@ -64,6 +64,7 @@ int guard(F&& f) {
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 constexpr int kOutStride = 4 + SSB_MAX_BLOCK + 2;  // accept record per request
+constexpr int kDDRec = 4 + 4 * SSB_MAX_BLOCK;      // direct-diffusion step record per request
 
 }  // namespace
 
@@ -120,6 +121,10 @@ struct ssb_model {
   float *am_top1, *am_top2;
   float *amv1, *amv2;
   int32_t* ami1;
+  float* ams;         // per-group softmax sums of the LM head (direct-diffusion confidence)
+  float* am_conf;     // greedy token's softmax probability per row
+  int32_t* dd_win;    // block tokens of the direct-diffusion request [kMaxReq][SSB_MAX_BLOCK]
+  int32_t* dd_rec;    // step records [kMaxReq][kDDRec]
   float* apart;
   int max_chunks;
   int max_decode_rows;
@@ -341,6 +346,10 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const size_t w_part = take((size_t)p_d.S * MR * H * 4);
   const size_t w_am = take((size_t)MR * 12);
   const size_t w_amp = take((size_t)(lm_tiles / p_lm.NT) * MR * 12);
+  const size_t w_ams = take((size_t)(lm_tiles / p_lm.NT) * MR * 4);
+  const size_t w_conf = take((size_t)MR * 4);
+  const size_t w_ddw = take((size_t)kMaxReq * SSB_MAX_BLOCK * 4);
+  const size_t w_ddr = take((size_t)kMaxReq * kDDRec * 4);
   const size_t w_apart = take((size_t)m->max_decode_rows * c.n_heads * m->max_chunks * (hd + 4) * 4);
   const size_t w_acc = take((size_t)kMaxReq * kOutStride * 4);
   const size_t w_tok = take((size_t)MR * 4);
@@ -367,6 +376,10 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   m->amv1 = reinterpret_cast<float*>(wsb + w_amp);
   m->amv2 = m->amv1 + (size_t)(lm_tiles / p_lm.NT) * MR;
   m->ami1 = reinterpret_cast<int32_t*>(m->amv2 + (size_t)(lm_tiles / p_lm.NT) * MR);
+  m->ams = reinterpret_cast<float*>(wsb + w_ams);
+  m->am_conf = reinterpret_cast<float*>(wsb + w_conf);
+  m->dd_win = reinterpret_cast<int32_t*>(wsb + w_ddw);
+  m->dd_rec = reinterpret_cast<int32_t*>(wsb + w_ddr);
   m->apart = reinterpret_cast<float*>(wsb + w_apart);
   m->accept_dev = reinterpret_cast<int32_t*>(wsb + w_acc);
   m->tok_dev = reinterpret_cast<int32_t*>(wsb + w_tok);
@@ -397,6 +410,8 @@ struct FwdSpec {
   bool graph;         // launches are being captured: no round-dependent launch shapes
   float* logits;      // nullable [M][vocab] (all rows) or [1][vocab] (last row only)
   bool lm_last_only;  // LM head on the last row only (prefill)
+  bool no_head;       // no LM head (cache-write forward)
+  bool want_conf;     // softmax confidence of each row's greedy token
 };
 
 template <typename T>
@@ -508,13 +523,14 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     }
   }
   // LM head + argmax
-  {
+  if (!f.no_head) {
     GemmArgs a = g;
     set_w(a, m->lm);
     a.x = m->xg; a.ldx = H;
     a.logits = f.logits;
     const int n_groups = m->lm.n_tiles / m->lm.NT;
     a.am_v1 = m->amv1; a.am_i1 = m->ami1; a.am_v2 = m->amv2; a.am_ld = n_groups;
+    a.am_s = f.want_conf ? m->ams : nullptr;
     int rows = M;
     if (f.lm_last_only) {
       a.x = reinterpret_cast<const char*>(m->xg) + (size_t)(M - 1) * H * m->elem;
@@ -526,8 +542,8 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     hip_check(launch_gemm<T>(a, EPI_LOGITS, st), "lm head gemm");
     prof_end(m, SSB_K_LMHEAD, st);
     prof_begin(m, SSB_K_ARGMAX, st);
-    hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, n_groups, n_groups, rows, m->am_tok, m->am_top1,
-                            m->am_top2, st), "argmax");
+    hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, f.want_conf ? m->ams : nullptr, n_groups, n_groups, rows,
+                            m->am_tok, m->am_top1, m->am_top2, m->am_conf, st), "argmax");
     prof_end(m, SSB_K_ARGMAX, st);
   }
 }
@@ -774,6 +790,123 @@ void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_
   kv->seq_len += 1;
   kv->x0 = y;
   if (token) *token = y;
+}
+
+// ---------------------------------------------------------------------------
+// Direct block-diffusion decoding (GravityOCR review, section 2 "Block
+// Diffusion" and Appendix B.1; Trillion Labs blog, "confidence threshold").
+// ---------------------------------------------------------------------------
+struct DDOut {
+  int steps, n, eos, advanced;
+  int32_t tok[SSB_MAX_BLOCK];
+  int32_t step_of[SSB_MAX_BLOCK];
+};
+
+// One block of B positions after the boundary of one request: denoising steps
+// (draft-mode forward over [x0, s_1..s_B], then the commit rule on the device)
+// until every position is committed, then, by write_mode, the cache-write
+// forward: 1 always, 0 never, 2 unless the output ends in this block (EOS
+// inside or max_commit <= B).  The host reads one small record per step.
+void dd_block_impl(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, int write_mode, float* step_conf,
+                   int32_t* step_tok, float* step_logits, DDOut* out, hipStream_t st) {
+  const ssb_config& c = m->c;
+  check_model_kv(m, kv);
+  if (kv->x0 < 0) fail(SSB_ESTATE, "direct diffusion needs a prefilled kv (no boundary token)");
+  if (B < 1 || B > c.block_B) fail(SSB_EINVAL, "B must be in [1, block_B]");
+  if (B + 1 > c.max_rows) fail(SSB_EINVAL, "B + 1 exceeds max_rows");
+  if (tau != tau) fail(SSB_EINVAL, "tau must not be NaN");
+  if (max_commit < 1) fail(SSB_EINVAL, "max_commit must be >= 1");
+  if (write_mode < 0 || write_mode > 2) fail(SSB_EINVAL, "bad cache-write mode");
+  if (kv->seq_len + B + 1 > c.max_positions) fail(SSB_ENOKV, "window exceeds max_positions");
+  kv_ensure(kv, kv->seq_len + B + 1, st);
+  ssb_pool* pool = kv->pool;
+  ReqArgs ra = single_req(kv, B, max_commit);
+  ra.win[0] = m->dd_win;
+  ra.tau = tau;
+  upload_req(m, ra, st);
+  hip_check(launch_dd_init(m->req_dev, 1, c.mask_id, m->dd_rec, kDDRec, st), "direct diffusion init");
+  const int p = kv->seq_len;
+  auto step_body = [&](hipStream_t s, bool graph, float* logits) {
+    FwdSpec f{};
+    f.mode = PREP_DRAFT;
+    f.M = B + 1;
+    f.ra = ra;
+    f.max_pos = p + B + 1;
+    f.graph = graph;
+    f.logits = logits;
+    f.want_conf = true;
+    run_forward(m, pool, f, s);
+    hip_check(launch_dd_select(m->am_tok, m->am_conf, m->req_dev, 1, c.mask_id, c.vocab, m->dd_rec, kDDRec, s),
+              "direct diffusion select");
+    hip_check(hipMemcpyAsync(m->pin_i32, m->dd_rec, (size_t)kDDRec * 4, hipMemcpyDeviceToHost, s),
+              "copy step record");
+  };
+  const bool eager = step_logits || m->prof_kind >= 0;
+  int steps = 0;
+  const int32_t* o = m->pin_i32;
+  for (;;) {
+    if (eager) {
+      step_body(st, false, step_logits ? step_logits + (size_t)steps * (B + 1) * c.vocab : nullptr);
+    } else {
+      hipGraphExec_t ex = get_graph(m, 2, pool, 1, B, [&](hipStream_t s) { step_body(s, true, nullptr); });
+      hip_check(hipGraphLaunch(ex, st), "direct diffusion step graph launch");
+    }
+    hip_check(hipStreamSynchronize(st), "direct diffusion step sync");
+    prof_collect(m);
+    if (o[2]) fail(SSB_EHIP, "direct diffusion step produced an invalid token or confidence (NaN logits?)");
+    if (o[0] < 1 || o[3] != steps + 1 || o[1] < 0 || o[1] >= B)
+      fail(SSB_EHIP, "direct diffusion step record is inconsistent");
+    for (int j = 0; j < B; ++j) {
+      if (step_conf) std::memcpy(step_conf + (size_t)steps * B + j, o + 4 + 2 * B + j, 4);
+      if (step_tok) step_tok[(size_t)steps * B + j] = o[4 + 3 * B + j];
+    }
+    ++steps;
+    if (o[1] == 0) break;
+    if (steps >= B) fail(SSB_EHIP, "direct diffusion block not complete after B steps");
+  }
+  out->steps = steps;
+  out->eos = 0;
+  out->n = B;
+  for (int j = 0; j < B; ++j) {
+    out->tok[j] = o[4 + B + j];
+    out->step_of[j] = o[4 + j];
+    if (out->tok[j] < 0 || out->tok[j] >= c.vocab || out->tok[j] == c.mask_id)
+      fail(SSB_EHIP, "direct diffusion block holds an invalid token");
+  }
+  for (int j = 0; j < B; ++j)
+    if (out->tok[j] == c.eos_id) { out->n = j + 1; out->eos = 1; break; }
+  out->n = std::min(out->n, max_commit);
+  const bool write = write_mode == 1 || (write_mode == 2 && !out->eos && max_commit > B);
+  out->advanced = write ? 1 : 0;
+  if (write) {
+    if (B > 1) {
+      // causal forward over s_1..s_{B-1} at p+1..p+B-1: a verify-mode window of B-1 rows
+      ReqArgs rc = ra;
+      rc.B = B - 2;
+      upload_req(m, rc, st);    // the stream is idle: the staging buffer is free
+      auto cw_body = [&](hipStream_t s, bool graph) {
+        FwdSpec f{};
+        f.mode = PREP_VERIFY;
+        f.M = B - 1;
+        f.ra = rc;
+        f.max_pos = p + B;
+        f.graph = graph;
+        f.no_head = true;
+        run_forward(m, pool, f, s);
+      };
+      if (eager) {
+        cw_body(st, false);
+      } else {
+        hipGraphExec_t ex = get_graph(m, 3, pool, 1, B, [&](hipStream_t s) { cw_body(s, true); });
+        hip_check(hipGraphLaunch(ex, st), "cache-write graph launch");
+      }
+      hip_check(hipStreamSynchronize(st), "cache-write sync");
+      prof_collect(m);
+    }
+    kv->seq_len = p + B;
+    kv->x0 = out->tok[B - 1];
+  }
+  kv_trim(kv, kv->seq_len + B + 1);
 }
 
 double now_us() {
@@ -1025,6 +1158,56 @@ int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_
       if (n_committed) n_committed[r] = ro[r].n;
       if (accept_len) accept_len[r] = ro[r].A;
     }
+  });
+}
+
+int ssb_dd_block(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, int write_cache, int32_t* tokens,
+                 int32_t* n_tokens, int32_t* steps, int32_t* step_of, float* step_conf, int32_t* step_tok,
+                 float* step_logits_dev, void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    if (write_cache != 0 && write_cache != 1) fail(SSB_EINVAL, "write_cache must be 0 or 1");
+    DDOut o{};
+    dd_block_impl(m, kv, B, tau, max_commit, write_cache, step_conf, step_tok, step_logits_dev, &o, S(stream));
+    if (tokens) std::memcpy(tokens, o.tok, (size_t)B * 4);
+    if (step_of) std::memcpy(step_of, o.step_of, (size_t)B * 4);
+    if (n_tokens) *n_tokens = o.n;
+    if (steps) *steps = o.steps;
+  });
+}
+
+int ssb_decode_dd(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int B, float tau, int max_len,
+                  int32_t* out, int32_t* n_out, ssb_stats* stats, void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    if (max_len < 0) fail(SSB_EINVAL, "max_len must be >= 0");
+    if (max_len > 0 && !out) fail(SSB_EINVAL, "null output buffer");
+    if (B < 1 || B > m->c.block_B) fail(SSB_EINVAL, "B must be in [1, block_B]");
+    if (tau != tau) fail(SSB_EINVAL, "tau must not be NaN");
+    ssb_stats st{};
+    int n = 0;
+    if (max_len > 0) {
+      const double t0 = now_us();
+      int32_t y1 = 0;
+      prefill(m, kv, prefix_dev, P, &y1, S(stream));
+      const double t1 = now_us();
+      st.prefill_us = t1 - t0;
+      out[n++] = y1;
+      bool done = y1 == m->c.eos_id || n >= max_len;
+      while (!done) {
+        DDOut o{};
+        dd_block_impl(m, kv, B, tau, max_len - n, 2, nullptr, nullptr, nullptr, &o, S(stream));
+        for (int i = 0; i < o.n; ++i) out[n++] = o.tok[i];
+        st.rounds += 1;
+        st.forwards += o.steps;
+        st.cache_forwards += (o.advanced && B > 1) ? 1 : 0;
+        done = o.eos || n >= max_len;
+      }
+      st.decode_us = now_us() - t1;
+    }
+    st.tokens = n;
+    if (n_out) *n_out = n;
+    if (stats) *stats = st;
   });
 }
 

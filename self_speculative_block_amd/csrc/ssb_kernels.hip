@@ -100,16 +100,17 @@ __device__ __forceinline__ void window_row(const PrepArgs& a, int m, int& tok, i
     const int p = ra.p[r];
     if (a.mode == PREP_DRAFT) {
       // draft window: boundary x0 at p (causal), masks at p+1..p+B (see the window)
-      tok = j == 0 ? ra.x0[r] : a.mask_id;
+      tok = j == 0 ? ra.x0[r] : (ra.win[r] ? ra.win[r][j - 1] : a.mask_id);
       pos = p + j;
       lim = j == 0 ? p : p + ra.B;
+      if (tok < 0 || tok >= a.vocab) tok = a.mask_id;   // keep the gather in bounds
     } else {
       // verify window [a0, d1..dB] at p+1..p+B+1, causal; row j of the draft
       // predicted a0 (j = 0) or d_j
       pos = p + 1 + j;
       lim = pos;
-      tok = a.am_prev[m];
-      if (j >= 1) {
+      tok = ra.win[r] ? ra.win[r][j] : a.am_prev[m];
+      if (j >= 1 && !ra.win[r]) {
         int pl = -1;
         if (ra.planted[r]) {
           pl = ra.planted[r][j - 1];
@@ -514,6 +515,22 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
         a.am_i1[o] = best.i1;
         a.am_v2[o] = best.v2;
       }
+      if (a.am_s) {
+        // softmax denominator of the group relative to its own max (the confidence of the
+        // direct-diffusion step); the same 8 lanes, the same columns, a fixed lane order
+        float se = 0.f;
+        if (r < MB && best.i1 >= 0 && best.v1 > -INFINITY) {
+          for (int k = 0; k < cpl; ++k) {
+            const int cc = sub * cpl + k;
+            const int col = tg * NT * 16 + cc;
+            if (col >= a.vocab || col == a.mask_id) continue;
+            se += __builtin_amdgcn_exp2f((ctile[((cc / 16) * MB + r) * 17 + cc % 16] - best.v1) * kLog2e);
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) se += __shfl_xor(se, o);
+        if (sub == 0 && r < MB && m < a.M) a.am_s[(size_t)m * a.am_ld + tg] = best.i1 >= 0 ? se : NAN;
+      }
     }
   }
   if (!more) break;
@@ -558,9 +575,10 @@ __global__ __launch_bounds__(64) void k_resid_reduce(GemmArgs a) {
 // same bits.  A NaN anywhere makes the row's record NaN.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int32_t* i1, const float* v2,
-                                                    int n_groups, int ld, int32_t* tok, float* top1,
-                                                    float* top2) {
+                                                    const float* gs, int n_groups, int ld, int32_t* tok,
+                                                    float* top1, float* top2, float* conf) {
   __shared__ Top2 sh[kThreads];
+  __shared__ float ssum[kThreads];
   const int m = blockIdx.x;
   constexpr int BATCH = 16;
   Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
@@ -585,6 +603,23 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
     tok[m] = sh[0].i1;
     top1[m] = sh[0].v1;
     top2[m] = sh[0].v2;
+  }
+  if (gs) {
+    // confidence = softmax probability of the greedy token, [M] excluded:
+    // 1 / sum over groups of gs_g * exp(v1_g - max), groups in a fixed thread order and tree
+    const float mx = sh[0].v1;
+    float part = 0.f;
+    for (int g = threadIdx.x; g < n_groups; g += kThreads) {
+      const float gv = v1[(size_t)m * ld + g];
+      if (gv > -INFINITY) part += gs[(size_t)m * ld + g] * __builtin_amdgcn_exp2f((gv - mx) * kLog2e);
+    }
+    ssum[threadIdx.x] = part;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+      if (threadIdx.x < s) ssum[threadIdx.x] += ssum[threadIdx.x + s];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) conf[m] = sh[0].i1 >= 0 ? 1.0f / ssum[0] : NAN;
   }
 }
 
@@ -651,7 +686,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   const int head = g * n_rep + wave;
   const int32_t* pt = a.fwd_pt + (size_t)task.req * a.pt_ld;
   // scores are kept in log2 units: s * scale * log2(e), so the softmax uses exp2
-  const float qscale = a.scale * 1.4426950408889634f;
+  const float qscale = a.scale * kLog2e;
 
   // ---- first memory round trip: limits, query fragments, page ids ----
   const int lim_v = threadIdx.x < 16 && mt * 16 + (int)threadIdx.x < task.nrows
@@ -919,6 +954,73 @@ __global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int
 }
 
 // ---------------------------------------------------------------------------
+// Direct block-diffusion step (GravityOCR review, Appendix B.1; Trillion Labs
+// blog, the "confidence threshold" entry): one wave per request.  Lane j owns
+// block position j + 1, whose prediction is window row j.  Every undecided
+// position whose confidence reaches tau is committed; when none does, the
+// single most confident undecided one is (lowest position on ties).
+// Record per request (rec_stride ints): [committed this step, still undecided,
+// invalid, steps so far, step_of[B], tokens[B], confidence bits[B], greedy
+// token of every row[B]].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_dd_init(const ReqArgs* rap, int mask_id, int32_t* rec, int rec_stride) {
+  const ReqArgs& ra = *rap;
+  const int r = blockIdx.x, j = threadIdx.x, B = ra.B;
+  int32_t* o = rec + (size_t)r * rec_stride;
+  if (j < B) {
+    ra.win[r][j] = mask_id;
+    o[4 + j] = -1;
+    o[4 + B + j] = mask_id;
+  }
+  if (j < 4) o[j] = 0;
+}
+
+__global__ __launch_bounds__(64) void k_dd_select(const int32_t* am, const float* conf, const ReqArgs* rap,
+                                                  int mask_id, int vocab, int32_t* rec, int rec_stride) {
+  const ReqArgs& ra = *rap;
+  const int r = blockIdx.x, j = threadIdx.x;
+  const int B = ra.B, row0 = ra.row0[r];
+  int32_t* win = ra.win[r];
+  int32_t* o = rec + (size_t)r * rec_stride;
+  const int step = o[3];
+  const bool lane = j < B;
+  const int cur = lane ? win[j] : mask_id;
+  const bool und = lane && cur == mask_id;
+  const int tk = lane ? am[row0 + j] : 0;
+  const float c = lane ? conf[row0 + j] : 0.f;
+  const bool bad = und && (tk < 0 || tk >= vocab || tk == mask_id || !(c >= 0.f));
+  const bool hit = und && c >= ra.tau;
+  bool take = hit;
+  if (__ballot(hit) == 0) {
+    float bc = und ? c : -INFINITY;
+    int bj = und ? j : kWave;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float oc = __shfl_xor(bc, off);
+      const int oj = __shfl_xor(bj, off);
+      if (oc > bc || (oc == bc && oj < bj)) { bc = oc; bj = oj; }
+    }
+    take = und && j == bj;
+  }
+  const unsigned long long tb = __ballot(take);
+  const unsigned long long ub = __ballot(und && !take);
+  const unsigned long long bb = __ballot(bad);
+  if (take && !bb) win[j] = tk;
+  if (lane) {
+    if (take) o[4 + j] = step;
+    o[4 + B + j] = take ? tk : cur;
+    o[4 + 2 * B + j] = __float_as_int(c);
+    o[4 + 3 * B + j] = tk;
+  }
+  if (j == 0) {
+    o[0] = __popcll(tb);
+    o[1] = __popcll(ub);
+    o[2] = bb ? 1 : 0;
+    o[3] = step + 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers (C++ linkage, used by the engine).
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -1021,9 +1123,10 @@ hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st) {
 template hipError_t launch_resid_reduce<bf16_t>(const GemmArgs&, hipStream_t);
 template hipError_t launch_resid_reduce<float>(const GemmArgs&, hipStream_t);
 
-hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, int n_groups, int ld, int M,
-                         int32_t* tok, float* top1, float* top2, hipStream_t st) {
-  SSB_LAUNCH(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, n_groups, ld, tok, top1, top2);
+hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, int n_groups, int ld,
+                         int M, int32_t* tok, float* top1, float* top2, float* conf, hipStream_t st) {
+  if (gs && !conf) return hipErrorInvalidValue;
+  SSB_LAUNCH(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, gs, n_groups, ld, tok, top1, top2, conf);
   return hipGetLastError();
 }
 
@@ -1060,6 +1163,21 @@ template hipError_t launch_attn_combine<float>(const float*, int, int, int, int,
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
                          int32_t* out, int out_stride, hipStream_t st) {
   SSB_LAUNCH(k_accept, dim3(n_req), dim3(64), 0, st, row_tok, am, ra, eos_id, out, out_stride);
+  return hipGetLastError();
+}
+
+// The request state's B must be <= 64 (one lane per block position) and rec_stride >= 4 + 4 * B;
+// both are checked by the engine before the request state is uploaded.
+hipError_t launch_dd_init(const ReqArgs* ra, int n_req, int mask_id, int32_t* rec, int rec_stride, hipStream_t st) {
+  if (n_req < 1 || n_req > kMaxReq || rec_stride < 4 + 4 * kWave) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_dd_init, dim3(n_req), dim3(kWave), 0, st, ra, mask_id, rec, rec_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_dd_select(const int32_t* am, const float* conf, const ReqArgs* ra, int n_req, int mask_id,
+                            int vocab, int32_t* rec, int rec_stride, hipStream_t st) {
+  if (n_req < 1 || n_req > kMaxReq || rec_stride < 4 + 4 * kWave) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_dd_select, dim3(n_req), dim3(kWave), 0, st, am, conf, ra, mask_id, vocab, rec, rec_stride);
   return hipGetLastError();
 }
 

@@ -217,6 +217,45 @@ class KV:
         return list(out[: n.value]), st
 
 
+    def dd_block(self, B, tau, max_commit=None, write_cache=True, want_steps=False, want_logits=False):
+        """One direct block-diffusion block.
+
+        Returns (tokens, n_out, steps, extra): the B block tokens, how many of
+        them belong to the output (EOS / budget cut), the denoising forwards,
+        and, if asked, a dict with step_of, per-step confidences and greedy
+        tokens of rows 0..B-1, and per-step logits.
+        """
+        max_commit = B if max_commit is None else max_commit
+        toks, step_of = _i32(B), _i32(B)
+        n, steps = ctypes.c_int32(), ctypes.c_int32()
+        conf = (ctypes.c_float * (B * B))() if want_steps else None
+        stok = _i32(B * B) if want_steps else None
+        lg = None
+        if want_logits:
+            lg = torch.full((B, B + 1, self.model.cfg.vocab), float("nan"), dtype=torch.float32,
+                            device=self.model.device)
+        L.check(self.lib.ssb_dd_block(self.model.h, self.h, B, float(tau), max_commit, 1 if write_cache else 0,
+                                      toks, byref(n), byref(steps), step_of, conf, stok, _ptr(lg), _stream()))
+        extra = None
+        if want_steps or want_logits:
+            k = steps.value
+            extra = {"step_of": list(step_of[:B])}
+            if want_steps:
+                extra["conf"] = np.array(conf[: k * B], dtype=np.float32).reshape(k, B)
+                extra["tok"] = np.array(stok[: k * B], dtype=np.int64).reshape(k, B)
+            if want_logits:
+                extra["logits"] = lg[:k]
+        return list(toks[:B]), n.value, steps.value, extra
+
+    def decode_dd(self, prefix_dev, B, tau, max_len):
+        out = _i32(max(max_len, 1))
+        n = ctypes.c_int32()
+        st = L.SsbStats()
+        L.check(self.lib.ssb_decode_dd(self.model.h, self.h, _ptr(prefix_dev), prefix_dev.shape[0], B, float(tau),
+                                       max_len, out, byref(n), byref(st), _stream()))
+        return list(out[: n.value]), st
+
+
 def round_batch(model, kvs, B, max_commit, planted_dev=None):
     """One batched round over R requests; returns [(committed, A)] per request."""
     R = len(kvs)

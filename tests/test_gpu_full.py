@@ -26,8 +26,9 @@ import pytest
 import torch
 
 from ssb_inputs import generate_weights, prefix_embeddings, workload
-from oracle import Decoder, ar_step, build_plant, prefill, spec_round
+from oracle import Decoder, ar_step, build_plant, dd_fill, prefill, spec_round
 from oracle.model import argmax_excluding
+from dd_checks import check_block_against_own_outputs
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +178,55 @@ def test_batched_round_equals_single_rounds(full, Bb):
         assert c == conts[r][1: 1 + min(A + 2, budgets[r])]
     for kv in kvs:
         kv.close()
+
+
+def test_direct_diffusion_block(full):
+    """Direct block diffusion at full width, B = 32.  The random-init decoder's
+    confidences all sit near 1/vocab, so the threshold is the median of the
+    first step's confidences (about half the block qualifies at once).
+    Every stack: decisions and tokens replayed exactly from the GPU's own
+    confidences and logits; tau = 0 gives the GPU's one-shot draft.  One
+    layer: each step's logits and confidences against the oracle for as long
+    as both sides have committed the same tokens."""
+    cfg, P, kv, orc = full["cfg"], full["P"], full["kv"], full["orc"]
+    y1 = full["y1_orc"]
+    if full["y1"] != y1:
+        pytest.skip("the prefill token is an oracle near-tie")
+    kv.rewind(P, y1)
+    toks0, _, steps0, ex0 = kv.dd_block(B, 0.0, write_cache=False, want_steps=True)
+    assert steps0 == 1
+    _, _, dl, _ = kv.round(B, want_logits=True)
+    dl = dl.cpu().numpy()
+    assert toks0 == [argmax_excluding(dl[j], cfg.mask_id)[0] for j in range(B)]
+    tau = float(np.median(ex0["conf"][0]))
+    kv.rewind(P, y1)
+    toks, n, steps, ex = kv.dd_block(B, tau, want_steps=True, want_logits=True)
+    assert 1 <= steps <= B and n == B
+    check_block_against_own_outputs(ex, toks, tau, B, cfg.mask_id, conf_rtol=1e-4)
+    assert kv.state()[:2] == (P + B, toks[-1])
+    if cfg.n_layers == 1:
+        st = full["st"]
+        st.n, st.x0 = P, y1
+        r = dd_fill(orc, st, B, tau, keep_logits=True)
+        lg = ex["logits"].cpu().numpy()
+        for k in range(min(steps, r.steps)):
+            err = np.abs(lg[k] - r.step_logits[k]).max()
+            assert err < full["tol"], (k, err)
+            rel = np.abs(ex["conf"][k] - np.array(r.step_conf[k])) / np.array(r.step_conf[k])
+            assert rel.max() < 0.1, (k, rel.max())
+            same = all((ex["step_of"][j] == k) == (r.step_of[j] == k) for j in range(B)) and \
+                all(toks[j] == r.tokens[j] for j in range(B) if r.step_of[j] == k)
+            if not same:
+                break
+    kv.rewind(P, y1)
+
+
+def test_direct_diffusion_block_one_is_ar(full):
+    kv, pre_dev = full["kv"], full["pre_dev"]
+    kv.reset()
+    ar, _ = kv.decode_ar(pre_dev, 24)
+    kv.reset()
+    dd, st = kv.decode_dd(pre_dev, 1, 0.5, 24)
+    assert dd == ar and st.forwards == len(dd) - 1
+    kv.reset()
+    assert kv.prefill(pre_dev) == full["y1"]
