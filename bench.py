@@ -269,6 +269,85 @@ def batched_workload(args):
     print(json.dumps(line))
 
 
+def direct_workload(args):
+    """Direct block-diffusion decoding of the text regions (config 3 shapes: prefix 1088,
+    lengths of mean 73), B = 32, batch 1.  The random-init decoder's confidences all sit near
+    1/vocab, so each threshold is a quantile of the first denoising step's confidences on the
+    first region; the sweep over quantiles plays the pages' threshold sweep.  Reports decode-only
+    tokens/s, tokens per forward in the pages' accounting (committing forwards only) and with the
+    cache-write forwards, and the device time of one denoising step and one cache-write."""
+    import numpy as np
+    import torch
+    from ssb_inputs import generate_weights, prefix_embeddings, workload
+    from ssb_inputs.schedule import target_lengths
+    from self_speculative_block_amd.engine import KV, Model, Pool
+
+    wl = workload(3)
+    cfg, B, P = wl.model, wl.block, wl.prefix_len
+    lengths = target_lengths(wl)
+    n = min(args.regions or wl.n_regions, wl.n_regions)
+    cap = max(lengths[:n])
+    torch.cuda.set_device(0)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8)
+    pool = Pool(model, n_pages=(P + cap + 2 * B + 8) // 16 + 8)
+    kv = KV(pool, P + cap + 2 * B + 8)
+    pres = [model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden)) for i in range(n)]
+    kv.reset()
+    kv.prefill(pres[0])
+    _, _, _, ex = kv.dd_block(B, 0.0, write_cache=False, want_steps=True)
+    conf0 = np.sort(ex["conf"][0])
+    # device time of one denoising step and of one cache-write forward (graph replays)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    kv.reset()
+    y1 = kv.prefill(pres[0])
+    step_ms = []
+    for rep in range(20):
+        kv.rewind(P, y1)
+        torch.cuda.synchronize()
+        ev[0].record()
+        kv.dd_block(B, 0.0, write_cache=False)       # one step, no cache-write
+        ev[1].record()
+        torch.cuda.synchronize()
+        step_ms.append(ev[0].elapsed_time(ev[1]))
+    blk_ms = []
+    for rep in range(20):
+        kv.rewind(P, y1)
+        torch.cuda.synchronize()
+        ev[0].record()
+        kv.dd_block(B, 0.0, write_cache=True)        # one step + the cache-write forward
+        ev[1].record()
+        torch.cuda.synchronize()
+        blk_ms.append(ev[0].elapsed_time(ev[1]))
+    step_med, blk_med = float(np.median(step_ms[5:])), float(np.median(blk_ms[5:]))
+    sweep = {}
+    for q in (0.25, 0.5, 0.75, 0.9):
+        tau = float(conf0[min(int(q * len(conf0)), len(conf0) - 1)])
+        toks = steps = cws = blocks = 0
+        us = 0.0
+        for i in range(n):
+            kv.reset()
+            out, st = kv.decode_dd(pres[i], B, tau, lengths[i])
+            toks += st.tokens - 1
+            steps += st.forwards
+            cws += st.cache_forwards
+            blocks += st.rounds
+            us += st.decode_us
+        sweep[str(q)] = {"tau": tau, "tokens_per_s": toks / (us * 1e-6), "tpf": toks / max(steps, 1),
+                         "tokens_per_forward_with_cache_writes": toks / max(steps + cws, 1),
+                         "steps_per_block": steps / max(blocks, 1), "blocks": blocks, "tokens": toks}
+    line = {
+        "metric": "decode-only tokens/s, direct block-diffusion decoding (B=32, batch 1), prefill excluded",
+        "value": sweep["0.5"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + "_direct_diffusion", "regions": n, "prefix": P, "block_B": B,
+                   "tau_rule": "quantile of the first step's confidences", "quantile": 0.5},
+        "sweep": sweep,
+        "denoising_step_device_ms": step_med,
+        "cache_write_device_ms": blk_med - step_med,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,9 +355,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=20)
-    ap.add_argument("--workload", choices=["round", "text", "table", "batched"], default="round",
+    ap.add_argument("--workload", choices=["round", "text", "table", "batched", "direct"], default="round",
                     help="round: the round microbenchmark (the headline line); text / table: decode "
-                         "of text or table regions; batched: the 16-request page")
+                         "of text or table regions; batched: the 16-request page; direct: direct "
+                         "block-diffusion decoding of the text regions")
     ap.add_argument("--regions", type=int, default=0, help="text / table: number of regions (0 = all)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -292,6 +372,8 @@ def main():
         return decode_workload(args, 4)
     if args.workload == "batched":
         return batched_workload(args)
+    if args.workload == "direct":
+        return direct_workload(args)
 
     import numpy as np
     import torch
