@@ -203,6 +203,42 @@ int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_
                     const int32_t* planted_dev, int32_t* committed, int32_t* n_committed,
                     int32_t* accept_len, void* stream);
 
+/* Stochastic self-speculative round (GravityOCR review, section 2
+ * "Speculative Decoding"; Trillion Labs blog, the speculative rejection rule
+ * that preserves the sampling distribution; the rule itself is the standard
+ * one of Leviathan et al. and Chen et al., 2023). Every distribution is
+ * softmax(logits / temperature) over the vocabulary without [M]; a draw with
+ * a uniform u takes the smallest token id whose cumulative mass exceeds u
+ * times the total.
+ *   - draft as in ssb_round; a0 and d1..dB are drawn from draft rows 0..B;
+ *   - verify over [a0, d1..dB]; d_j is accepted while
+ *     u_acc[j] * q_j(d_j) < p_j(d_j) (q_j: draft row j, p_j: verify row j-1);
+ *     A = number accepted before the first rejection;
+ *   - the next token t is drawn from max(0, p_{A+1} - q_{A+1}) (from p_{A+1}
+ *     if that has no mass) when A < B, from p_{B+1} when A = B;
+ *   - commits a0, d1..dA, t (cut after EOS and at max_commit); t becomes the
+ *     boundary; rollback as in ssb_round.
+ * u_dev: device float [2B+2], values in [0, 1): u_a0, u_d[1..B], u_acc[1..B],
+ * u_t. temperature > 0. Other arguments as ssb_round (no planting). */
+int ssb_round_sample(ssb_model* m, ssb_kv* kv, int B, int max_commit, float temperature, const float* u_dev,
+                     int32_t* committed, int32_t* n_committed, int32_t* accept_len, float* draft_logits_dev,
+                     float* verify_logits_dev, void* stream);
+
+/* Prefill with y1 drawn from the last prefix row, then stochastic rounds
+ * until EOS or max_len tokens. u_dev: device float [n_u_rows][2B+2]; row 0's
+ * first value draws y1, row k drives round k (SSB_EINVAL if the rows run
+ * out). */
+int ssb_decode_sample(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int B, float temperature,
+                      int max_len, const float* u_dev, int n_u_rows, int32_t* out, int32_t* n_out, ssb_stats* stats,
+                      void* stream);
+
+/* AR sampling with the same kernels: y1 from the last prefix row with
+ * u_dev[0], token k (k >= 1) from an AR step with u_dev[k]. u_dev: device
+ * float [max_len]. The output follows the same distribution as
+ * ssb_decode_sample's, not the same tokens. */
+int ssb_decode_ar_sample(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, float temperature, int max_len,
+                         const float* u_dev, int32_t* out, int32_t* n_out, ssb_stats* stats, void* stream);
+
 /* Direct block-diffusion decoding of one block (GravityOCR review, section 2
  * "Block Diffusion" and Appendix B.1; Trillion Labs blog, "confidence
  * threshold" entry). The block is the B positions p+1..p+B after the

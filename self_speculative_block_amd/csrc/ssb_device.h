@@ -88,6 +88,9 @@ struct ReqArgs {
   // DRAFT rows 1..B embed win[j-1]; VERIFY rows j embed win[j] (the cache-write forward).
   int32_t* win[kMaxReq];
   float tau;                          // confidence threshold of the denoising step
+  // stochastic rounds: the request's uniforms [2B + 2] = u_a0, u_d[1..B], u_acc[1..B], u_t
+  // (prefill and AR sampling steps: u[0] draws the token)
+  const float* u[kMaxReq];
 };
 
 // Row task of the attention kernel.  lim_mode 0: max_lim given; 1: draft
@@ -132,7 +135,28 @@ struct GemmArgs {
   void* act; int act_ld;                        // SWIGLU
   float* logits; int vocab; int mask_id;        // LOGITS
   float* am_v1; int32_t* am_i1; float* am_v2; int am_ld;   // LOGITS: records [M][am_ld]
-  float* am_s;                                  // LOGITS, nullable: sum of exp(z - group max) [M][am_ld]
+  float* am_s;                                  // LOGITS, nullable: sum of exp((z - group max) / T) [M][am_ld]
+  float am_scale;                               // log2(e) / T for am_s
+};
+
+// Inverse-CDF sampling of window rows from their LM-head records and logits.
+struct SampleArgs {
+  const float* v1; const float* gs; int ld, n_groups, gcols;   // per-group max and exp-sum [M][ld]
+  const float* logits; int vocab, mask_id;                    // [M][vocab]
+  const float* rmax; const float* rz; float sc;               // row max, row exp-sum, log2(e) / T
+  const ReqArgs* req;
+  int32_t* tok;                                               // out: sampled token per row
+};
+
+// Acceptance test and residual / bonus draw of a stochastic round.
+struct AcceptSampleArgs {
+  const int32_t* row_tok;                                     // verify rows: a0, d_1..d_B
+  const float* lg_d; const float* dmax; const float* dz;      // draft logits and row stats
+  const float* lg_v; const float* vmax; const float* vz;      // verify logits and row stats
+  int vocab, mask_id, eos_id; float sc;
+  const ReqArgs* req;
+  int32_t* acc;                                               // [kMaxReq] accepted count A
+  int32_t* out; int out_stride;                               // commit records (as k_accept)
 };
 
 // Dynamic LDS layout of k_gemm (byte offsets), shared by the kernel and its launcher:
@@ -187,10 +211,12 @@ template <typename T> hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
 template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
 template <typename T> hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st);
 int gemm_max_mt(int elem, int K, int S, int NT, int KSL, int n_ssq, int epi);
-// gs (nullable, then conf too): per-group softmax sums of the LM head; conf [M] gets the
-// greedy token's softmax probability.
-hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, int n_groups, int ld,
-                         int M, int32_t* tok, float* top1, float* top2, float* conf, hipStream_t st);
+// gs (nullable, then zs too): per-group exp-sums of the LM head at scale sc = log2(e) / T;
+// zs [M] gets the row's sum of exp((z - top1) / T) over the vocabulary without [M].
+hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, float sc, int n_groups,
+                         int ld, int M, int32_t* tok, float* top1, float* top2, float* zs, hipStream_t st);
+hipError_t launch_sample_rows(const SampleArgs& a, int rows_per_req, int n_req, hipStream_t st);
+hipError_t launch_accept_sample(const AcceptSampleArgs& a, int n_req, hipStream_t st);
 template <typename T> hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipStream_t st);
 template <typename T>
 hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, int n_heads, int head_dim,
@@ -198,7 +224,7 @@ hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, i
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
                          int32_t* out, int out_stride, hipStream_t st);
 hipError_t launch_dd_init(const ReqArgs* ra, int n_req, int mask_id, int32_t* rec, int rec_stride, hipStream_t st);
-hipError_t launch_dd_select(const int32_t* am, const float* conf, const ReqArgs* ra, int n_req, int mask_id,
+hipError_t launch_dd_select(const int32_t* am, const float* zs, const ReqArgs* ra, int n_req, int mask_id,
                             int vocab, int32_t* rec, int rec_stride, hipStream_t st);
 
 }  // namespace ssb

@@ -121,8 +121,10 @@ struct ssb_model {
   float *am_top1, *am_top2;
   float *amv1, *amv2;
   int32_t* ami1;
-  float* ams;         // per-group softmax sums of the LM head (direct-diffusion confidence)
-  float* am_conf;     // greedy token's softmax probability per row
+  float* ams;         // per-group softmax sums of the LM head (confidence, sampling)
+  float* am_z;        // per row: sum of exp((z - max) / T) over the vocabulary without [M]
+  float *slog_d, *slog_v;   // stochastic rounds: draft / verify logits [max_decode_rows][vocab]
+  float *smax_d, *sz_d, *smax_v, *sz_v;   // their row max and exp-sum [max_rows]
   int32_t* dd_win;    // block tokens of the direct-diffusion request [kMaxReq][SSB_MAX_BLOCK]
   int32_t* dd_rec;    // step records [kMaxReq][kDDRec]
   float* apart;
@@ -133,7 +135,7 @@ struct ssb_model {
   ReqArgs* req_dev;   // device request state read by every kernel of a forward
   ReqArgs* req_pin;   // pinned staging of the request state
   hipStream_t cap;    // private stream used only to capture graphs
-  std::map<std::tuple<int, void*, int, int>, hipGraphExec_t> graphs;   // (kind, pool, R, B)
+  std::map<std::tuple<int, void*, int, int, uint32_t>, hipGraphExec_t> graphs;   // (kind, pool, R, B, T bits)
   // kernel timing hook
   int prof_kind = -1;
   std::vector<hipEvent_t> prof_ev;    // pairs (start, end)
@@ -348,6 +350,8 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const size_t w_amp = take((size_t)(lm_tiles / p_lm.NT) * MR * 12);
   const size_t w_ams = take((size_t)(lm_tiles / p_lm.NT) * MR * 4);
   const size_t w_conf = take((size_t)MR * 4);
+  const size_t w_slog = take((size_t)2 * m->max_decode_rows * V * 4);
+  const size_t w_sst = take((size_t)4 * MR * 4);
   const size_t w_ddw = take((size_t)kMaxReq * SSB_MAX_BLOCK * 4);
   const size_t w_ddr = take((size_t)kMaxReq * kDDRec * 4);
   const size_t w_apart = take((size_t)m->max_decode_rows * c.n_heads * m->max_chunks * (hd + 4) * 4);
@@ -377,7 +381,13 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   m->amv2 = m->amv1 + (size_t)(lm_tiles / p_lm.NT) * MR;
   m->ami1 = reinterpret_cast<int32_t*>(m->amv2 + (size_t)(lm_tiles / p_lm.NT) * MR);
   m->ams = reinterpret_cast<float*>(wsb + w_ams);
-  m->am_conf = reinterpret_cast<float*>(wsb + w_conf);
+  m->am_z = reinterpret_cast<float*>(wsb + w_conf);
+  m->slog_d = reinterpret_cast<float*>(wsb + w_slog);
+  m->slog_v = m->slog_d + (size_t)m->max_decode_rows * V;
+  m->smax_d = reinterpret_cast<float*>(wsb + w_sst);
+  m->sz_d = m->smax_d + MR;
+  m->smax_v = m->sz_d + MR;
+  m->sz_v = m->smax_v + MR;
   m->dd_win = reinterpret_cast<int32_t*>(wsb + w_ddw);
   m->dd_rec = reinterpret_cast<int32_t*>(wsb + w_ddr);
   m->apart = reinterpret_cast<float*>(wsb + w_apart);
@@ -411,7 +421,10 @@ struct FwdSpec {
   float* logits;      // nullable [M][vocab] (all rows) or [1][vocab] (last row only)
   bool lm_last_only;  // LM head on the last row only (prefill)
   bool no_head;       // no LM head (cache-write forward)
-  bool want_conf;     // softmax confidence of each row's greedy token
+  float stat_sc;      // > 0: row softmax sums at scale log2(e) / T (confidence: T = 1; sampling)
+  bool sample;        // draw each window row's token from its distribution (needs logits, stat_sc)
+  float* st_max;      // nullable: row max output (default: the greedy top-1 buffer)
+  float* st_z;        // nullable: row exp-sum output (default: am_z)
 };
 
 template <typename T>
@@ -530,7 +543,8 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     a.logits = f.logits;
     const int n_groups = m->lm.n_tiles / m->lm.NT;
     a.am_v1 = m->amv1; a.am_i1 = m->ami1; a.am_v2 = m->amv2; a.am_ld = n_groups;
-    a.am_s = f.want_conf ? m->ams : nullptr;
+    a.am_s = f.stat_sc > 0.f ? m->ams : nullptr;
+    a.am_scale = f.stat_sc;
     int rows = M;
     if (f.lm_last_only) {
       a.x = reinterpret_cast<const char*>(m->xg) + (size_t)(M - 1) * H * m->elem;
@@ -542,9 +556,20 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     hip_check(launch_gemm<T>(a, EPI_LOGITS, st), "lm head gemm");
     prof_end(m, SSB_K_LMHEAD, st);
     prof_begin(m, SSB_K_ARGMAX, st);
-    hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, f.want_conf ? m->ams : nullptr, n_groups, n_groups, rows,
-                            m->am_tok, m->am_top1, m->am_top2, m->am_conf, st), "argmax");
+    float* top1 = f.st_max ? f.st_max : m->am_top1;
+    float* zs = f.st_z ? f.st_z : m->am_z;
+    hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, f.stat_sc > 0.f ? m->ams : nullptr, f.stat_sc, n_groups,
+                            n_groups, rows, m->am_tok, top1, m->am_top2, zs, st), "argmax");
     prof_end(m, SSB_K_ARGMAX, st);
+    if (f.sample) {
+      if (!f.logits || !(f.stat_sc > 0.f)) fail(SSB_EINVAL, "sampling needs logits and row sums");
+      SampleArgs sa{};
+      sa.v1 = m->amv1; sa.gs = m->ams; sa.ld = n_groups; sa.n_groups = n_groups; sa.gcols = m->lm.NT * 16;
+      sa.logits = f.logits; sa.vocab = c.vocab; sa.mask_id = c.mask_id;
+      sa.rmax = top1; sa.rz = zs; sa.sc = f.stat_sc; sa.req = m->req_dev; sa.tok = m->am_tok;
+      const bool win = f.mode == PREP_DRAFT || f.mode == PREP_VERIFY;
+      hip_check(launch_sample_rows(sa, win ? f.ra.B + 1 : 1, win ? f.ra.n : 1, st), "sample rows");
+    }
   }
 }
 
@@ -605,8 +630,10 @@ void upload_req(ssb_model* m, const ReqArgs& ra, hipStream_t st) {
 // private stream and replayed on the caller's stream.  Launch shapes inside
 // never depend on the round; round state is read from the device.
 hipGraphExec_t get_graph(ssb_model* m, int kind, ssb_pool* pool, int R, int B,
-                         const std::function<void(hipStream_t)>& body) {
-  const auto key = std::make_tuple(kind, static_cast<void*>(pool), R, B);
+                         const std::function<void(hipStream_t)>& body, float temperature = 0.f) {
+  uint32_t tb = 0;
+  std::memcpy(&tb, &temperature, 4);
+  const auto key = std::make_tuple(kind, static_cast<void*>(pool), R, B, tb);
   auto it = m->graphs.find(key);
   if (it != m->graphs.end()) return it->second;
   hip_check(hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal), "begin capture");
@@ -641,14 +668,30 @@ ReqArgs single_req(ssb_kv* kv, int B, int max_commit) {
   return ra;
 }
 
-void prefill(ssb_model* m, ssb_kv* kv, const void* prefix, int P, int32_t* first, hipStream_t st) {
+// Sampling variant of a call: temperature and, per request, its device uniforms.
+struct SampleSpec {
+  float temperature;
+  const float* const* u;
+};
+
+void check_sample(const SampleSpec* smp, int R) {
+  if (!smp) return;
+  if (!(smp->temperature > 0.f) || !(smp->temperature < INFINITY)) fail(SSB_EINVAL, "temperature must be > 0");
+  for (int r = 0; r < R; ++r)
+    if (!smp->u[r]) fail(SSB_EINVAL, "null uniforms");
+}
+
+void prefill(ssb_model* m, ssb_kv* kv, const void* prefix, int P, int32_t* first, hipStream_t st,
+             const SampleSpec* smp = nullptr) {
   check_model_kv(m, kv);
   if (!prefix) fail(SSB_EINVAL, "null prefix");
   if (P < 1) fail(SSB_EINVAL, "P must be >= 1");
   if (kv->seq_len != 0 || kv->x0 >= 0) fail(SSB_ESTATE, "prefill needs an empty kv");
   if (P + 1 > m->c.max_positions) fail(SSB_EINVAL, "P exceeds max_positions");
+  check_sample(smp, 1);
   kv_ensure(kv, P, st);
-  const ReqArgs ra = single_req(kv, 0, 1);
+  ReqArgs ra = single_req(kv, 0, 1);
+  if (smp) ra.u[0] = smp->u[0];
   upload_req(m, ra, st);
   for (int p0 = 0; p0 < P; p0 += m->c.max_rows) {
     FwdSpec f{};
@@ -659,6 +702,11 @@ void prefill(ssb_model* m, ssb_kv* kv, const void* prefix, int P, int32_t* first
     f.ra = ra;
     f.max_pos = p0 + f.M;
     f.lm_last_only = true;
+    if (smp && p0 + f.M == P) {   // y1 drawn from the last row's distribution
+      f.logits = m->slog_d;
+      f.stat_sc = kLog2e / smp->temperature;
+      f.sample = true;
+    }
     run_forward(m, kv->pool, f, st);
   }
   hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, 4, hipMemcpyDeviceToHost, st), "copy token");
@@ -679,8 +727,10 @@ struct RoundOut {
 // Runs draft + verify + accept for R requests (row windows concatenated).
 void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_commit, const int32_t* planted,
                 const int32_t* const* cont, const int* cont_len, const int* cont_c, const int* astar,
-                float* dlog, float* vlog, RoundOut* out, hipStream_t st) {
+                float* dlog, float* vlog, RoundOut* out, hipStream_t st, const SampleSpec* smp = nullptr) {
   const ssb_config& c = m->c;
+  check_sample(smp, R);
+  if (smp && (planted || cont)) fail(SSB_EINVAL, "planted drafts apply to greedy rounds only");
   if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, 16]");
   if (B < 0 || B > c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
   if (R * (B + 1) > c.max_rows) fail(SSB_EINVAL, "R*(B+1) exceeds max_rows");
@@ -713,6 +763,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
     ra.cont_len[r] = cont_len ? cont_len[r] : 0;
     ra.cont_c[r] = cont_c ? cont_c[r] : 0;
     ra.astar[r] = astar ? astar[r] : 0;
+    ra.u[r] = smp ? smp->u[r] : nullptr;
     maxpos = std::max(maxpos, ra.p[r] + B + 2);
   }
   upload_req(m, ra, st);
@@ -724,19 +775,44 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
     f.graph = graph;
     f.mode = PREP_DRAFT;
     f.logits = dlog;
+    if (smp) {
+      // stochastic round: every draft row drawn from its distribution (a0, d_1..d_B)
+      f.logits = dlog ? dlog : m->slog_d;
+      f.stat_sc = kLog2e / smp->temperature;
+      f.sample = true;
+      f.st_max = m->smax_d;
+      f.st_z = m->sz_d;
+    }
     run_forward(m, pool, f, s);
     f.mode = PREP_VERIFY;
     f.logits = vlog;
+    if (smp) {
+      f.logits = vlog ? vlog : m->slog_v;
+      f.sample = false;
+      f.st_max = m->smax_v;
+      f.st_z = m->sz_v;
+    }
     run_forward(m, pool, f, s);
-    hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, R, c.eos_id, m->accept_dev, kOutStride, s),
-              "accept");
+    if (smp) {
+      AcceptSampleArgs aa{};
+      aa.row_tok = m->row_tok;
+      aa.lg_d = dlog ? dlog : m->slog_d; aa.dmax = m->smax_d; aa.dz = m->sz_d;
+      aa.lg_v = vlog ? vlog : m->slog_v; aa.vmax = m->smax_v; aa.vz = m->sz_v;
+      aa.vocab = c.vocab; aa.mask_id = c.mask_id; aa.eos_id = c.eos_id; aa.sc = kLog2e / smp->temperature;
+      aa.req = m->req_dev; aa.out = m->accept_dev; aa.out_stride = kOutStride;
+      hip_check(launch_accept_sample(aa, R, s), "stochastic accept");
+    } else {
+      hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, R, c.eos_id, m->accept_dev, kOutStride, s),
+                "accept");
+    }
     hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)R * kOutStride * 4, hipMemcpyDeviceToHost, s),
               "copy accept");
   };
   if (dlog || vlog || m->prof_kind >= 0) {
     body(st, false);
   } else {
-    hipGraphExec_t ex = get_graph(m, 0, pool, R, B, [&](hipStream_t s) { body(s, true); });
+    hipGraphExec_t ex = get_graph(m, smp ? 4 : 0, pool, R, B, [&](hipStream_t s) { body(s, true); },
+                                  smp ? smp->temperature : 0.f);
     hip_check(hipGraphLaunch(ex, st), "round graph launch");
   }
   hip_check(hipStreamSynchronize(st), "round sync");
@@ -758,13 +834,16 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
   }
 }
 
-void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_t st) {
+void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_t st,
+             const SampleSpec* smp = nullptr) {
   check_model_kv(m, kv);
+  check_sample(smp, 1);
   if (kv->x0 < 0) fail(SSB_ESTATE, "AR step needs a prefilled kv (no boundary token)");
   if (kv->seq_len + 1 > m->c.max_positions) fail(SSB_ENOKV, "position exceeds max_positions");
   kv_ensure(kv, kv->seq_len + 1, st);
   // an AR step is a draft window with no masks: [x0] at p, keys <= p
-  const ReqArgs ra = single_req(kv, 0, 1);
+  ReqArgs ra = single_req(kv, 0, 1);
+  if (smp) ra.u[0] = smp->u[0];
   upload_req(m, ra, st);
   auto body = [&](hipStream_t s, bool graph) {
     FwdSpec f{};
@@ -774,13 +853,19 @@ void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_
     f.max_pos = kv->seq_len + 1;
     f.graph = graph;
     f.logits = logits;
+    if (smp) {
+      f.logits = logits ? logits : m->slog_d;
+      f.stat_sc = kLog2e / smp->temperature;
+      f.sample = true;
+    }
     run_forward(m, kv->pool, f, s);
     hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, 4, hipMemcpyDeviceToHost, s), "copy token");
   };
   if (logits || m->prof_kind >= 0) {
     body(st, false);
   } else {
-    hipGraphExec_t ex = get_graph(m, 1, kv->pool, 1, 0, [&](hipStream_t s) { body(s, true); });
+    hipGraphExec_t ex = get_graph(m, smp ? 5 : 1, kv->pool, 1, 0, [&](hipStream_t s) { body(s, true); },
+                                  smp ? smp->temperature : 0.f);
     hip_check(hipGraphLaunch(ex, st), "AR graph launch");
   }
   hip_check(hipStreamSynchronize(st), "ar sync");
@@ -834,9 +919,9 @@ void dd_block_impl(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, i
     f.max_pos = p + B + 1;
     f.graph = graph;
     f.logits = logits;
-    f.want_conf = true;
+    f.stat_sc = kLog2e;
     run_forward(m, pool, f, s);
-    hip_check(launch_dd_select(m->am_tok, m->am_conf, m->req_dev, 1, c.mask_id, c.vocab, m->dd_rec, kDDRec, s),
+    hip_check(launch_dd_select(m->am_tok, m->am_z, m->req_dev, 1, c.mask_id, c.vocab, m->dd_rec, kDDRec, s),
               "direct diffusion select");
     hip_check(hipMemcpyAsync(m->pin_i32, m->dd_rec, (size_t)kDDRec * 4, hipMemcpyDeviceToHost, s),
               "copy step record");
@@ -1158,6 +1243,105 @@ int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_
       if (n_committed) n_committed[r] = ro[r].n;
       if (accept_len) accept_len[r] = ro[r].A;
     }
+  });
+}
+
+int ssb_round_sample(ssb_model* m, ssb_kv* kv, int B, int max_commit, float temperature, const float* u_dev,
+                     int32_t* committed, int32_t* n_committed, int32_t* accept_len, float* draft_logits_dev,
+                     float* verify_logits_dev, void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    RoundOut ro{};
+    ssb_kv* kvs[1] = {kv};
+    int mc[1] = {max_commit};
+    const float* us[1] = {u_dev};
+    const SampleSpec smp{temperature, us};
+    round_impl(m, kvs, 1, B, mc, nullptr, nullptr, nullptr, nullptr, nullptr, draft_logits_dev, verify_logits_dev,
+               &ro, S(stream), &smp);
+    if (committed) std::memcpy(committed, ro.tok, (size_t)ro.n * 4);
+    if (n_committed) *n_committed = ro.n;
+    if (accept_len) *accept_len = ro.A;
+  });
+}
+
+int ssb_decode_sample(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int B, float temperature,
+                      int max_len, const float* u_dev, int n_u_rows, int32_t* out, int32_t* n_out, ssb_stats* stats,
+                      void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    if (max_len < 0) fail(SSB_EINVAL, "max_len must be >= 0");
+    if (max_len > 0 && !out) fail(SSB_EINVAL, "null output buffer");
+    if (B < 0 || B > m->c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
+    if (!u_dev || n_u_rows < 1) fail(SSB_EINVAL, "null uniforms");
+    const int W = 2 * B + 2;
+    ssb_stats st{};
+    int n = 0;
+    if (max_len > 0) {
+      const double t0 = now_us();
+      int32_t y1 = 0;
+      const float* u0[1] = {u_dev};
+      const SampleSpec s0{temperature, u0};
+      prefill(m, kv, prefix_dev, P, &y1, S(stream), &s0);
+      const double t1 = now_us();
+      st.prefill_us = t1 - t0;
+      out[n++] = y1;
+      bool done = y1 == m->c.eos_id || n >= max_len;
+      int k = 1;
+      while (!done) {
+        if (k >= n_u_rows) fail(SSB_EINVAL, "more rounds than rows of uniforms");
+        RoundOut ro{};
+        ssb_kv* kvs[1] = {kv};
+        int mc[1] = {max_len - n};
+        const float* us[1] = {u_dev + (size_t)k * W};
+        const SampleSpec smp{temperature, us};
+        round_impl(m, kvs, 1, B, mc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, &ro, S(stream),
+                   &smp);
+        for (int i = 0; i < ro.n; ++i) out[n++] = ro.tok[i];
+        st.rounds += 1;
+        st.forwards += 2;
+        st.accepted += ro.A;
+        done = ro.eos || n >= max_len;
+        ++k;
+      }
+      st.decode_us = now_us() - t1;
+    }
+    st.tokens = n;
+    if (n_out) *n_out = n;
+    if (stats) *stats = st;
+  });
+}
+
+int ssb_decode_ar_sample(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, float temperature, int max_len,
+                         const float* u_dev, int32_t* out, int32_t* n_out, ssb_stats* stats, void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    if (max_len < 0) fail(SSB_EINVAL, "max_len must be >= 0");
+    if (max_len > 0 && !out) fail(SSB_EINVAL, "null output buffer");
+    if (!u_dev) fail(SSB_EINVAL, "null uniforms");
+    ssb_stats st{};
+    int n = 0;
+    if (max_len > 0) {
+      const double t0 = now_us();
+      int32_t y = 0;
+      const float* u0[1] = {u_dev};
+      const SampleSpec s0{temperature, u0};
+      prefill(m, kv, prefix_dev, P, &y, S(stream), &s0);
+      const double t1 = now_us();
+      st.prefill_us = t1 - t0;
+      out[n++] = y;
+      while (y != m->c.eos_id && n < max_len) {
+        const float* uk[1] = {u_dev + n};
+        const SampleSpec sk{temperature, uk};
+        ar_step(m, kv, &y, nullptr, S(stream), &sk);
+        out[n++] = y;
+        st.rounds += 1;
+        st.forwards += 1;
+      }
+      st.decode_us = now_us() - t1;
+    }
+    st.tokens = n;
+    if (n_out) *n_out = n;
+    if (stats) *stats = st;
   });
 }
 

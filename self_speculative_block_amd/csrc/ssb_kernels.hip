@@ -524,7 +524,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
             const int cc = sub * cpl + k;
             const int col = tg * NT * 16 + cc;
             if (col >= a.vocab || col == a.mask_id) continue;
-            se += __builtin_amdgcn_exp2f((ctile[((cc / 16) * MB + r) * 17 + cc % 16] - best.v1) * kLog2e);
+            se += __builtin_amdgcn_exp2f((ctile[((cc / 16) * MB + r) * 17 + cc % 16] - best.v1) * a.am_scale);
           }
         }
 #pragma unroll
@@ -575,8 +575,8 @@ __global__ __launch_bounds__(64) void k_resid_reduce(GemmArgs a) {
 // same bits.  A NaN anywhere makes the row's record NaN.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int32_t* i1, const float* v2,
-                                                    const float* gs, int n_groups, int ld, int32_t* tok,
-                                                    float* top1, float* top2, float* conf) {
+                                                    const float* gs, float sc, int n_groups, int ld, int32_t* tok,
+                                                    float* top1, float* top2, float* zs) {
   __shared__ Top2 sh[kThreads];
   __shared__ float ssum[kThreads];
   const int m = blockIdx.x;
@@ -605,13 +605,14 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
     top2[m] = sh[0].v2;
   }
   if (gs) {
-    // confidence = softmax probability of the greedy token, [M] excluded:
-    // 1 / sum over groups of gs_g * exp(v1_g - max), groups in a fixed thread order and tree
+    // the row's softmax denominator relative to its max, [M] excluded: the sum over groups of
+    // gs_g * exp((v1_g - max) / T), groups in a fixed thread order and tree.  At T = 1 its
+    // inverse is the greedy token's softmax probability.
     const float mx = sh[0].v1;
     float part = 0.f;
     for (int g = threadIdx.x; g < n_groups; g += kThreads) {
       const float gv = v1[(size_t)m * ld + g];
-      if (gv > -INFINITY) part += gs[(size_t)m * ld + g] * __builtin_amdgcn_exp2f((gv - mx) * kLog2e);
+      if (gv > -INFINITY) part += gs[(size_t)m * ld + g] * __builtin_amdgcn_exp2f((gv - mx) * sc);
     }
     ssum[threadIdx.x] = part;
     __syncthreads();
@@ -619,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
       if (threadIdx.x < s) ssum[threadIdx.x] += ssum[threadIdx.x + s];
       __syncthreads();
     }
-    if (threadIdx.x == 0) conf[m] = sh[0].i1 >= 0 ? 1.0f / ssum[0] : NAN;
+    if (threadIdx.x == 0) zs[m] = sh[0].i1 >= 0 ? ssum[0] : NAN;
   }
 }
 
@@ -975,7 +976,7 @@ __global__ __launch_bounds__(64) void k_dd_init(const ReqArgs* rap, int mask_id,
   if (j < 4) o[j] = 0;
 }
 
-__global__ __launch_bounds__(64) void k_dd_select(const int32_t* am, const float* conf, const ReqArgs* rap,
+__global__ __launch_bounds__(64) void k_dd_select(const int32_t* am, const float* zs, const ReqArgs* rap,
                                                   int mask_id, int vocab, int32_t* rec, int rec_stride) {
   const ReqArgs& ra = *rap;
   const int r = blockIdx.x, j = threadIdx.x;
@@ -987,7 +988,7 @@ __global__ __launch_bounds__(64) void k_dd_select(const int32_t* am, const float
   const int cur = lane ? win[j] : mask_id;
   const bool und = lane && cur == mask_id;
   const int tk = lane ? am[row0 + j] : 0;
-  const float c = lane ? conf[row0 + j] : 0.f;
+  const float c = lane ? 1.0f / zs[row0 + j] : 0.f;   // softmax probability of the greedy token
   const bool bad = und && (tk < 0 || tk >= vocab || tk == mask_id || !(c >= 0.f));
   const bool hit = und && c >= ra.tau;
   bool take = hit;
@@ -1017,6 +1018,189 @@ __global__ __launch_bounds__(64) void k_dd_select(const int32_t* am, const float
     o[1] = __popcll(ub);
     o[2] = bb ? 1 : 0;
     o[3] = step + 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stochastic rounds (GravityOCR review, section 2 "Speculative Decoding";
+// Trillion Labs blog, the speculative rejection rule preserving the sampling
+// distribution).  Draws are inverse-CDF over token ids in increasing order:
+// the smallest id whose cumulative mass exceeds u times the total.
+// ---------------------------------------------------------------------------
+
+// Inclusive scan of one value per thread over the workgroup, in a fixed
+// (Hillis-Steele) order; sh[t] holds thread t's inclusive sum on return.
+__device__ __forceinline__ float block_incl_scan(float v, float* sh) {
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const float o = t >= off ? sh[t - off] : 0.f;
+    __syncthreads();
+    sh[t] += o;
+    __syncthreads();
+  }
+  return sh[t];
+}
+
+// One row's draw from softmax(z / T) without [M].  The row's mass is split by
+// LM-head column group (group g holds gs_g * exp((v1_g - max) / T)): thread i
+// adds a contiguous run of groups in id order, a workgroup scan of the runs
+// finds the group where u * S falls (S: the row's total), and one wave scans
+// that group's columns in id order.  Where rounding leaves u * S past the last
+// cumulative value, the last group / column of positive mass is taken.
+// Grid (rows per request, requests); row j of request r draws with u[r][j].
+__global__ __launch_bounds__(kThreads) void k_sample_rows(SampleArgs a) {
+  __shared__ float sh[kThreads];
+  __shared__ int s_thr, s_last, s_grp;
+  __shared__ float s_base;
+  const ReqArgs& ra = *a.req;
+  const int r = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int m = ra.row0[r] + j;
+  const float mx = a.rmax[m];
+  const float target = ra.u[r][j] * a.rz[m];
+  const int G = (a.n_groups + kThreads - 1) / kThreads, g0 = t * G;
+  const float* v1 = a.v1 + (size_t)m * a.ld;
+  const float* gs = a.gs + (size_t)m * a.ld;
+  auto mass = [&](int g) -> float {
+    const float gv = v1[g];
+    return gv > -INFINITY ? gs[g] * __builtin_amdgcn_exp2f((gv - mx) * a.sc) : 0.f;
+  };
+  float loc = 0.f;
+  for (int k = 0; k < G; ++k)
+    if (g0 + k < a.n_groups) loc += mass(g0 + k);
+  if (t == 0) { s_thr = 0x7fffffff; s_last = -1; s_grp = -1; s_base = 0.f; }
+  const float incl = block_incl_scan(loc, sh);
+  const float excl = t ? sh[t - 1] : 0.f;
+  if (loc > 0.f && excl <= target && target < incl) atomicMin(&s_thr, t);
+  if (loc > 0.f) atomicMax(&s_last, t);
+  __syncthreads();
+  if (t == (s_thr != 0x7fffffff ? s_thr : s_last)) {
+    float cum = excl, base_last = excl;
+    int grp = -1, last = -1;
+    for (int k = 0; k < G && g0 + k < a.n_groups; ++k) {
+      const float c = mass(g0 + k);
+      if (c > 0.f) {
+        last = g0 + k;
+        base_last = cum;
+        if (cum + c > target) { grp = g0 + k; break; }
+      }
+      cum += c;
+    }
+    if (grp < 0) { grp = last; cum = base_last; }
+    s_grp = grp;
+    s_base = cum;
+  }
+  __syncthreads();
+  if (t < kWave) {
+    const int grp = s_grp;     // -1 only for a row without positive mass (NaN logits)
+    const int col = grp * a.gcols + t;
+    float e = 0.f;
+    if (grp >= 0 && t < a.gcols && col < a.vocab && col != a.mask_id)
+      e = __builtin_amdgcn_exp2f((a.logits[(size_t)m * a.vocab + col] - mx) * a.sc);
+    float cs = e;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float o = __shfl_up(cs, off);
+      if (t >= off) cs += o;
+    }
+    const unsigned long long hit = __ballot(e > 0.f && s_base + cs > target);
+    const unsigned long long pos = __ballot(e > 0.f);
+    const int pick = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : -1);
+    if (t == 0) a.tok[m] = (grp >= 0 && pick >= 0) ? grp * a.gcols + pick : -1;
+  }
+}
+
+// Acceptance test and the next token of a stochastic round, one workgroup per
+// request.  Wave 0: lane j tests d_{j+1} (verify input row j+1): accepted iff
+// u_acc * q(d) < p(d), p from verify row j, q from draft row j+1; A = number
+// accepted before the first rejection.  Then the whole workgroup draws the
+// next token t: from max(0, p - q) at verify row A / draft row A+1 when
+// A < B (from p alone if that residual has no mass), from verify row B when
+// A = B; thread i adds a contiguous run of token ids, a workgroup scan finds
+// where u_t times the total falls.  Commit record as k_accept.
+__global__ __launch_bounds__(kThreads) void k_accept_sample(AcceptSampleArgs a) {
+  __shared__ float sh[kThreads];
+  __shared__ int s_A, s_thr, s_last, s_pick;
+  const ReqArgs& ra = *a.req;
+  const int r = blockIdx.x, t = threadIdx.x;
+  const int B = ra.B, row0 = ra.row0[r];
+  const float* u = ra.u[r];
+  const size_t V = (size_t)a.vocab;
+  if (t < kWave) {
+    bool rej = false;
+    if (t < B) {
+      const int d = a.row_tok[row0 + 1 + t];
+      const int pr = row0 + t, qr = row0 + t + 1;
+      const float p = __builtin_amdgcn_exp2f((a.lg_v[pr * V + d] - a.vmax[pr]) * a.sc) / a.vz[pr];
+      const float q = __builtin_amdgcn_exp2f((a.lg_d[qr * V + d] - a.dmax[qr]) * a.sc) / a.dz[qr];
+      rej = !(u[B + 1 + t] * q < p);
+    }
+    const unsigned long long b = __ballot(rej);
+    if (t == 0) { s_A = b ? __builtin_ctzll(b) : B; s_pick = -1; }
+  }
+  __syncthreads();
+  const int A = s_A;
+  const int pr = row0 + A, qr = row0 + A + 1;
+  const float pm = a.vmax[pr], pinv = 1.0f / a.vz[pr];
+  const float qm = A < B ? a.dmax[qr] : 0.f, qinv = A < B ? 1.0f / a.dz[qr] : 0.f;
+  const int chunk = (a.vocab + kThreads - 1) / kThreads;
+  const int v0 = min(t * chunk, a.vocab), v1 = min(a.vocab, v0 + chunk);
+  auto w = [&](int v, bool useq) -> float {
+    if (v == a.mask_id) return 0.f;
+    const float p = __builtin_amdgcn_exp2f((a.lg_v[pr * V + v] - pm) * a.sc) * pinv;
+    if (!useq) return p;
+    const float q = __builtin_amdgcn_exp2f((a.lg_d[qr * V + v] - qm) * a.sc) * qinv;
+    return fmaxf(p - q, 0.f);
+  };
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const bool useq = A < B && attempt == 0;
+    float loc = 0.f;
+    for (int v = v0; v < v1; ++v) loc += w(v, useq);
+    if (t == 0) { s_thr = 0x7fffffff; s_last = -1; }
+    const float incl = block_incl_scan(loc, sh);
+    const float excl = t ? sh[t - 1] : 0.f;
+    const float tot = sh[kThreads - 1];
+    if (!(tot > 0.f)) {      // same value in every thread: a uniform branch
+      __syncthreads();
+      continue;
+    }
+    const float target = u[2 * B + 1] * tot;
+    if (loc > 0.f && excl <= target && target < incl) atomicMin(&s_thr, t);
+    if (loc > 0.f) atomicMax(&s_last, t);
+    __syncthreads();
+    if (t == (s_thr != 0x7fffffff ? s_thr : s_last)) {
+      float cum = excl;
+      int pick = -1, last = -1;
+      for (int v = v0; v < v1; ++v) {
+        const float x = w(v, useq);
+        if (x > 0.f) {
+          last = v;
+          if (cum + x > target) { pick = v; break; }
+        }
+        cum += x;
+      }
+      s_pick = pick >= 0 ? pick : last;
+    }
+    break;
+  }
+  __syncthreads();
+  if (t == 0) {
+    const int tk = s_pick;
+    int32_t* o = a.out + (size_t)r * a.out_stride;
+    const int ncand = A + 2;
+    int eos_at = ncand;
+    for (int k = 0; k < ncand; ++k) {
+      const int x = k <= A ? a.row_tok[row0 + k] : tk;
+      if (x == a.eos_id) { eos_at = k; break; }
+    }
+    int n = min(ncand, eos_at + 1);
+    n = min(n, ra.max_commit[r]);
+    for (int k = 0; k < n; ++k) o[4 + k] = k <= A ? a.row_tok[row0 + k] : tk;
+    o[0] = A;
+    o[1] = n;
+    o[2] = tk;
+    o[3] = (eos_at < ncand && eos_at < n) ? 1 : 0;
   }
 }
 
@@ -1123,10 +1307,24 @@ hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st) {
 template hipError_t launch_resid_reduce<bf16_t>(const GemmArgs&, hipStream_t);
 template hipError_t launch_resid_reduce<float>(const GemmArgs&, hipStream_t);
 
-hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, int n_groups, int ld,
-                         int M, int32_t* tok, float* top1, float* top2, float* conf, hipStream_t st) {
-  if (gs && !conf) return hipErrorInvalidValue;
-  SSB_LAUNCH(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, gs, n_groups, ld, tok, top1, top2, conf);
+hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, float sc, int n_groups,
+                         int ld, int M, int32_t* tok, float* top1, float* top2, float* zs, hipStream_t st) {
+  if (gs && !zs) return hipErrorInvalidValue;
+  SSB_LAUNCH(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, gs, sc, n_groups, ld, tok, top1, top2, zs);
+  return hipGetLastError();
+}
+
+// Rows j = 0..rows_per_req-1 of every request (row row0[r] + j of the launch), each drawn
+// with u[r][j]; gcols (columns per LM-head group) must be <= 64.
+hipError_t launch_sample_rows(const SampleArgs& a, int rows_per_req, int n_req, hipStream_t st) {
+  if (a.gcols < 1 || a.gcols > kWave || rows_per_req < 1 || n_req < 1 || n_req > kMaxReq) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sample_rows, dim3(rows_per_req, n_req), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_sample(const AcceptSampleArgs& a, int n_req, hipStream_t st) {
+  if (n_req < 1 || n_req > kMaxReq) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_accept_sample, dim3(n_req), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1174,10 +1372,10 @@ hipError_t launch_dd_init(const ReqArgs* ra, int n_req, int mask_id, int32_t* re
   return hipGetLastError();
 }
 
-hipError_t launch_dd_select(const int32_t* am, const float* conf, const ReqArgs* ra, int n_req, int mask_id,
+hipError_t launch_dd_select(const int32_t* am, const float* zs, const ReqArgs* ra, int n_req, int mask_id,
                             int vocab, int32_t* rec, int rec_stride, hipStream_t st) {
   if (n_req < 1 || n_req > kMaxReq || rec_stride < 4 + 4 * kWave) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_dd_select, dim3(n_req), dim3(kWave), 0, st, am, conf, ra, mask_id, vocab, rec, rec_stride);
+  hipLaunchKernelGGL(k_dd_select, dim3(n_req), dim3(kWave), 0, st, am, zs, ra, mask_id, vocab, rec, rec_stride);
   return hipGetLastError();
 }
 

@@ -217,6 +217,39 @@ class KV:
         return list(out[: n.value]), st
 
 
+    def round_sample(self, B, u_dev, temperature=1.0, max_commit=None, want_logits=False):
+        """One stochastic round driven by the device uniforms u_dev [2B+2];
+        returns (committed, A, draft_logits, verify_logits)."""
+        max_commit = B + 2 if max_commit is None else max_commit
+        out = _i32(B + 2)
+        n, A = ctypes.c_int32(), ctypes.c_int32()
+        dl = vl = None
+        if want_logits:
+            V = self.model.cfg.vocab
+            dl = torch.empty((B + 1, V), dtype=torch.float32, device=self.model.device)
+            vl = torch.empty((B + 1, V), dtype=torch.float32, device=self.model.device)
+        L.check(self.lib.ssb_round_sample(self.model.h, self.h, B, max_commit, float(temperature), _ptr(u_dev), out,
+                                          byref(n), byref(A), _ptr(dl), _ptr(vl), _stream()))
+        return list(out[: n.value]), A.value, dl, vl
+
+    def decode_sample(self, prefix_dev, B, max_len, u_dev, temperature=1.0):
+        out = _i32(max(max_len, 1))
+        n = ctypes.c_int32()
+        st = L.SsbStats()
+        L.check(self.lib.ssb_decode_sample(self.model.h, self.h, _ptr(prefix_dev), prefix_dev.shape[0], B,
+                                           float(temperature), max_len, _ptr(u_dev), u_dev.shape[0], out, byref(n),
+                                           byref(st), _stream()))
+        return list(out[: n.value]), st
+
+    def decode_ar_sample(self, prefix_dev, max_len, u_dev, temperature=1.0):
+        out = _i32(max(max_len, 1))
+        n = ctypes.c_int32()
+        st = L.SsbStats()
+        L.check(self.lib.ssb_decode_ar_sample(self.model.h, self.h, _ptr(prefix_dev), prefix_dev.shape[0],
+                                              float(temperature), max_len, _ptr(u_dev), out, byref(n), byref(st),
+                                              _stream()))
+        return list(out[: n.value]), st
+
     def dd_block(self, B, tau, max_commit=None, write_cache=True, want_steps=False, want_logits=False):
         """One direct block-diffusion block.
 

@@ -29,6 +29,7 @@ from ssb_inputs import generate_weights, prefix_embeddings, workload
 from oracle import Decoder, ar_step, build_plant, dd_fill, prefill, spec_round
 from oracle.model import argmax_excluding
 from dd_checks import check_block_against_own_outputs
+from sample_checks import replay_round
 
 pytestmark = pytest.mark.gpu
 
@@ -230,3 +231,35 @@ def test_direct_diffusion_block_one_is_ar(full):
     assert dd == ar and st.forwards == len(dd) - 1
     kv.reset()
     assert kv.prefill(pre_dev) == full["y1"]
+
+
+@pytest.mark.parametrize("T", [1.0, 0.05])
+def test_stochastic_round_full_width(full, T):
+    """Stochastic rounds at full width, B = 32: every draw and acceptance decision
+    replayed in float64 from the GPU's own logits; with one layer, logits against
+    the oracle given the same uniforms."""
+    from oracle.stochastic import spec_round_sample
+    cfg, P, kv, orc = full["cfg"], full["P"], full["kv"], full["orc"]
+    y1 = full["y1_orc"]
+    if full["y1"] != y1:
+        pytest.skip("the prefill token is an oracle near-tie")
+    for k in range(3):
+        u = np.random.default_rng([31, k, int(T * 100)]).random(2 * B + 2).astype(np.float32)
+        kv.rewind(P, y1)
+        committed, A, dl, vl = kv.round_sample(B, torch.tensor(u, device="cuda"), temperature=T,
+                                               want_logits=True)
+        dl, vl = dl.cpu().numpy(), vl.cpu().numpy()
+        assert 0 <= A <= B and len(committed) == A + 2
+        replay_round(dl, vl, u, B, T, cfg.mask_id, cfg.eos_id, committed, A)
+        assert kv.state()[:2] == (P + A + 2, committed[-1])
+        if cfg.n_layers == 1:
+            st = full["st"]
+            st.n, st.x0 = P, y1
+            r = spec_round_sample(orc, st, B, u.astype(np.float64), temperature=T, keep_logits=True)
+            assert np.abs(dl - r.draft_logits).max() < full["tol"]
+            # verify row j sees a0, d_1..d_j: comparable while both sides drew the same tokens
+            same = [committed[0]] + committed[1: A + 1] == [r.a0] + r.d[:A]
+            rows = A + 1 if same else (1 if committed[0] == r.a0 else 0)
+            if rows:
+                assert np.abs(vl[:rows] - r.verify_logits[:rows]).max() < full["tol"]
+    kv.rewind(P, y1)
