@@ -348,6 +348,62 @@ def direct_workload(args):
     print(json.dumps(line))
 
 
+def sample_workload(args):
+    """Stochastic self-speculative decoding of the text regions (config 3 shapes), B = 32,
+    batch 1, against AR sampling through the same kernels, at temperatures 1.0 and 0.7.
+    Uniforms are seeded per region.  The random-init decoder's draft and target
+    distributions are both close to uniform, so acceptance here says nothing about a trained
+    model; the line measures the cost of a stochastic round (logits written, sampled rows,
+    the acceptance test and residual draw) against a greedy one."""
+    import numpy as np
+    import torch
+    from ssb_inputs import generate_weights, prefix_embeddings, workload
+    from ssb_inputs.schedule import target_lengths
+    from self_speculative_block_amd.engine import KV, Model, Pool
+
+    wl = workload(3)
+    cfg, B, P = wl.model, wl.block, wl.prefix_len
+    lengths = target_lengths(wl)
+    n = min(args.regions or 64, wl.n_regions)
+    cap = max(lengths[:n])
+    torch.cuda.set_device(0)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8)
+    pool = Pool(model, n_pages=(P + cap + 2 * B + 8) // 16 + 8)
+    kv = KV(pool, P + cap + 2 * B + 8)
+    pres = [model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden)) for i in range(n)]
+    res = {}
+    for T in (1.0, 0.7):
+        tot = {"spec_tokens": 0, "spec_us": 0.0, "ar_tokens": 0, "ar_us": 0.0, "rounds": 0, "accepted": 0}
+        for i in range(n):
+            L = lengths[i]
+            U = torch.tensor(np.random.default_rng([7, i, int(T * 10)]).random((L + 1, 2 * B + 2)),
+                             dtype=torch.float32, device="cuda")
+            kv.reset()
+            out, st = kv.decode_sample(pres[i], B, L, U, temperature=T)
+            tot["spec_tokens"] += st.tokens - 1
+            tot["spec_us"] += st.decode_us
+            tot["rounds"] += st.rounds
+            tot["accepted"] += st.accepted
+            kv.reset()
+            ar, sta = kv.decode_ar_sample(pres[i], L, U[:, 0].contiguous(), temperature=T)
+            tot["ar_tokens"] += sta.tokens - 1
+            tot["ar_us"] += sta.decode_us
+        spec_tps = tot["spec_tokens"] / (tot["spec_us"] * 1e-6)
+        ar_tps = tot["ar_tokens"] / (tot["ar_us"] * 1e-6)
+        res[str(T)] = {"tokens_per_s": spec_tps, "ar_sampling_tokens_per_s": ar_tps, "speedup_vs_ar": spec_tps / ar_tps,
+                       "tpf": tot["spec_tokens"] / max(2 * tot["rounds"], 1),
+                       "mean_accept": tot["accepted"] / max(tot["rounds"], 1), "rounds": tot["rounds"],
+                       "round_ms_mean": tot["spec_us"] / max(tot["rounds"], 1) / 1e3}
+    line = {
+        "metric": "decode-only tokens/s, stochastic self-speculative decoding (B=32, batch 1), prefill excluded",
+        "value": res["1.0"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + "_sampling", "regions": n, "prefix": P, "block_B": B, "temperature": 1.0},
+        "by_temperature": res,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,10 +411,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=20)
-    ap.add_argument("--workload", choices=["round", "text", "table", "batched", "direct"], default="round",
+    ap.add_argument("--workload", choices=["round", "text", "table", "batched", "direct", "sample"], default="round",
                     help="round: the round microbenchmark (the headline line); text / table: decode "
                          "of text or table regions; batched: the 16-request page; direct: direct "
-                         "block-diffusion decoding of the text regions")
+                         "block-diffusion decoding of the text regions; sample: stochastic decoding "
+                         "of the text regions")
     ap.add_argument("--regions", type=int, default=0, help="text / table: number of regions (0 = all)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -374,6 +431,8 @@ def main():
         return batched_workload(args)
     if args.workload == "direct":
         return direct_workload(args)
+    if args.workload == "sample":
+        return sample_workload(args)
 
     import numpy as np
     import torch
