@@ -25,7 +25,8 @@ from .decode import (
 )
 from .training_rules import complementary_masks, training_visibility
 from .direct import (confidence, select_positions, BlockResult, dd_fill, dd_cache_write, dd_release,
-                     DDStats, dd_tpf, dd_decode)
+                     DDStats, dd_tpf, dd_decode, MultiStepRoundResult, spec_round_multistep,
+                     spec_decode_multistep)
 
 __all__ = [
     "Decoder", "KVCache", "rms_norm", "rope", "silu", "attend", "argmax_excluding",
@@ -34,5 +35,6 @@ __all__ = [
     "accept_length", "commit_tokens", "build_plant", "tpf", "teacher_forced_argmax",
     "complementary_masks", "training_visibility",
     "confidence", "select_positions", "BlockResult", "dd_fill", "dd_cache_write", "dd_release",
-    "DDStats", "dd_tpf", "dd_decode",
+    "DDStats", "dd_tpf", "dd_decode", "MultiStepRoundResult", "spec_round_multistep",
+    "spec_decode_multistep",
 ]

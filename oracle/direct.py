@@ -36,14 +36,23 @@ Readings where the pages are silent (each also listed in the design notes):
   leaves every committed token but the new boundary s_B in the cache, the
   same state invariant as the self-speculative round (Appendix B.2);
 * ``max_len`` caps the total output length, as for the other decoders.
+
+The multi-step draft schedule of the self-speculative round (blog, the
+draft-schedule passage; review, Appendix D) uses the same denoising steps
+as its drafter.  Readings: a schedule of S steps runs at most S draft
+forwards, the last one committing every slot still open (S = 1 is the
+one-shot draft); slot i holds the prediction of row i - 1 (a0 for i = 1);
+d_B, which has no slot, is row B's prediction in the last draft forward.
 """
 
 from dataclasses import dataclass, field
-from typing import List
+from typing import List, Optional
 
 import numpy as np
 
-from .decode import causal_visibility, draft_visibility, prefill
+from .decode import (accept_length, causal_visibility, commit_tokens, draft_visibility, prefill,
+                     verify_visibility)
+from .model import argmax_excluding
 
 
 def confidence(logits, mask_id):
@@ -138,6 +147,84 @@ def dd_release(state):
     """End of output: the window's draft-mode slots are dropped, the state
     stays at the block's start."""
     state.cache.release_from(state.n)
+
+
+@dataclass
+class MultiStepRoundResult:
+    committed: List[int]
+    A: int
+    draft: List[int]                    # a0, d_1..d_B as verified
+    draft_forwards: int
+    step_of: List[int]                  # step at which each window slot was committed
+    verify_logits: Optional[np.ndarray] = None
+
+
+def spec_round_multistep(model, state, B, steps, tau_d, budget=None, keep_logits=False):
+    """Self-speculative round with a multi-step draft schedule (Trillion Labs
+    blog, the draft-schedule passage; review, Appendix D "Draft Schedule").
+
+    The draft is refined by denoising steps before verification: window slot
+    i (position p + i, i = 1..B) holds a0 (i = 1) or d_{i-1}, predicted by
+    window row i - 1.  Each step commits slots by the draft-side threshold
+    tau_d with the most-confident fallback; the last of at most ``steps``
+    forwards commits every slot still open.  d_B (position p + B + 1, which
+    has no slot) is window row B's prediction in the last draft forward.
+    Verification, acceptance and rollback are those of the greedy round.
+    With ``steps`` = 1 this is the one-shot round.
+    """
+    cfg = model.cfg
+    if steps < 1:
+        raise ValueError("a draft schedule needs at least one forward")
+    p, x0, cache = state.n, state.x0, state.cache
+    s = [cfg.mask_id] * B
+    step_of = [-1] * B
+    k = 0
+    last = None
+    while True:
+        h = model.embed_tokens([x0] + s)
+        logits = model.forward(cache, h, p + np.arange(B + 1), draft_visibility(p, B))
+        last = logits
+        tc = [confidence(logits[j], cfg.mask_id) for j in range(B)]
+        und = [t == cfg.mask_id for t in s]
+        if k == steps - 1:
+            chosen = [j for j in range(B) if und[j]]
+        else:
+            chosen = select_positions(und, [c for _, c in tc], tau_d)
+        for j in chosen:
+            s[j] = tc[j][0]
+            step_of[j] = k
+        k += 1
+        if cfg.mask_id not in s:
+            break
+    # slots s_1..s_B hold a0, d_1..d_{B-1}; d_B is row B's prediction (B = 0: a0 is row 0's)
+    draft = list(s) + [argmax_excluding(last[B], cfg.mask_id)[0]]
+    a0, d = draft[0], draft[1:]
+    h = model.embed_tokens([a0] + d)
+    vl = model.forward(cache, h, p + 1 + np.arange(B + 1), verify_visibility(p, B))
+    a = [argmax_excluding(vl[j], cfg.mask_id)[0] for j in range(B + 1)]
+    A = accept_length(d, a[:B])
+    committed = commit_tokens(a0, a, A, cfg.eos_id, B + 2 if budget is None else budget)
+    state.n = p + A + 2
+    state.x0 = a[A]
+    cache.release_from(state.n)
+    return MultiStepRoundResult(committed=committed, A=A, draft=draft, draft_forwards=k, step_of=step_of,
+                                verify_logits=vl if keep_logits else None)
+
+
+def spec_decode_multistep(model, prefix_emb, B, steps, tau_d, max_len, max_positions=None, rounds_out=None):
+    """Greedy self-speculative decoding with a multi-step draft schedule."""
+    cfg = model.cfg
+    if max_len <= 0:
+        return []
+    P = prefix_emb.shape[0]
+    state, y1, _ = prefill(model, prefix_emb, max_positions or P + max_len + B + 3)
+    out = [y1]
+    while out[-1] != cfg.eos_id and len(out) < max_len:
+        r = spec_round_multistep(model, state, B, steps, tau_d, budget=max_len - len(out))
+        if rounds_out is not None:
+            rounds_out.append(r)
+        out += r.committed
+    return out
 
 
 @dataclass

@@ -15,6 +15,10 @@ and the mathematics fix.
 * After the cache-write forward the cache equals a causal prefill of the
   committed tokens (review, Appendix B.1/B.2: only causal state survives).
 * EOS truncation and the output budget.
+* Multi-step draft schedule: one step is the one-shot round exactly; any
+  schedule leaves the output and the cache AR-identical (the verifier
+  decides every committed token); the causal boundary row makes a0 the AR
+  token whatever the schedule.
 """
 
 import dataclasses
@@ -27,6 +31,7 @@ from scipy.special import softmax
 from ssb_inputs import generate_weights, prefix_embeddings, workload
 from oracle import (Decoder, DecodeState, ar_decode, causal_visibility, confidence, dd_cache_write,
                     dd_decode, dd_fill, dd_tpf, prefill, select_positions, spec_round)
+from oracle import ar_step as ar_step_o
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -191,3 +196,66 @@ def test_eos_budget_and_tpf(tiny):
     # tau = 0: one forward per block, B tokens per forward
     out0, st0 = dd_decode(m, pre, B, 0.0, 1 + 5 * B)
     assert st0.steps == st0.blocks == 5 and dd_tpf(st0) == B
+
+
+# ---- multi-step draft schedule (blog, draft-schedule passage; review, Appendix D) ----
+
+def test_multistep_one_step_is_the_one_shot_round(tiny):
+    from oracle import spec_round_multistep
+    wl, m = tiny
+    B = wl.block
+    for s in range(4):
+        pre = prefix_embeddings(wl.wid, s, wl.prefix_len, m.cfg.hidden)
+        st, _, _ = prefill(m, pre, wl.prefix_len + 4 * B + 8)
+        sp = _copy(st)
+        for k in range(3):
+            r = spec_round_multistep(m, st, B, 1, 0.5)
+            rr = spec_round(m, sp, B)
+            assert r.committed == rr.committed and r.A == rr.A and r.draft_forwards == 1
+            assert r.draft == [rr.a0] + rr.d
+            assert (st.n, st.x0) == (sp.n, sp.x0)
+
+
+def test_multistep_decoding_is_ar_decoding(tiny):
+    """The verifier makes the output AR-identical whatever the draft schedule."""
+    from oracle import spec_decode_multistep, spec_round_multistep
+    wl, m = tiny
+    B = wl.block
+    for s in range(3):
+        pre = prefix_embeddings(wl.wid, s, wl.prefix_len, m.cfg.hidden)
+        ar = ar_decode(m, pre, 40)
+        tau = _mid_tau(m, pre, B)
+        for steps, td in ((2, tau), (4, tau), (B, 2.0), (3, 0.0)):
+            rounds = []
+            out = spec_decode_multistep(m, pre, B, steps, td, 40, rounds_out=rounds)
+            assert out == ar, (s, steps, td)
+            for r in rounds:
+                assert 1 <= r.draft_forwards <= steps
+                assert max(r.step_of) == r.draft_forwards - 1 and min(r.step_of) >= 0
+                if td == 0.0:
+                    assert r.draft_forwards == 1
+            # the boundary row is causal: a0 is always the AR token
+            c = 1
+            for r in rounds:
+                if c < len(ar):
+                    assert r.draft[0] == ar[c]
+                c += len(r.committed)
+
+
+def test_multistep_cache_is_ar_cache(tiny):
+    from oracle import spec_round_multistep
+    wl, m = tiny
+    B = wl.block
+    pre = prefix_embeddings(wl.wid, 5, wl.prefix_len, m.cfg.hidden)
+    tau = _mid_tau(m, pre, B)
+    cap = wl.prefix_len + 80
+    ar_state, _, _ = prefill(m, pre, cap)
+    for _ in range(60):
+        ar_step_o(m, ar_state)
+    st, _, _ = prefill(m, pre, cap)
+    for k in range(4):
+        spec_round_multistep(m, st, B, 3, tau)
+        n = st.n
+        np.testing.assert_allclose(st.cache.K[:, :n], ar_state.cache.K[:, :n], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(st.cache.V[:, :n], ar_state.cache.V[:, :n], rtol=0, atol=1e-12)
+        assert np.isnan(st.cache.K[:, n:]).all()
