@@ -239,6 +239,27 @@ int ssb_decode_sample(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, i
 int ssb_decode_ar_sample(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, float temperature, int max_len,
                          const float* u_dev, int32_t* out, int32_t* n_out, ssb_stats* stats, void* stream);
 
+/* Greedy self-speculative round with a multi-step draft schedule (Trillion
+ * Labs blog, the draft-schedule passage; GravityOCR review, Appendix D
+ * "Draft Schedule"). The draft window [x0, s_1..s_B] is refined by up to
+ * `steps` draft-mode forwards: slot i (position p+i) holds the prediction of
+ * window row i-1 (a0 for i = 1, d_{i-1} otherwise); each step commits the
+ * open slots whose confidence is >= tau (the single most confident if none),
+ * the last allowed step commits every open slot. d_B is window row B's
+ * prediction in the last draft forward. Verify, accept and rollback are those
+ * of ssb_round on [a0, d1..dB]; steps = 1 is exactly ssb_round's one-shot
+ * draft, and the output is AR-identical for every schedule.
+ * draft_forwards (host, nullable): draft forwards run (<= steps).
+ * verify_logits_dev: nullable device fp32 [B+1][vocab]. B >= 1. */
+int ssb_round_multistep(ssb_model* m, ssb_kv* kv, int B, int steps, float tau, int max_commit, int32_t* committed,
+                        int32_t* n_committed, int32_t* accept_len, int32_t* draft_forwards, float* verify_logits_dev,
+                        void* stream);
+
+/* Prefill, then multi-step-draft rounds until EOS or max_len tokens.
+ * stats.forwards counts draft and verify forwards. */
+int ssb_decode_multistep(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int B, int steps, float tau,
+                         int max_len, int32_t* out, int32_t* n_out, ssb_stats* stats, void* stream);
+
 /* Direct block-diffusion decoding of one block (GravityOCR review, section 2
  * "Block Diffusion" and Appendix B.1; Trillion Labs blog, "confidence
  * threshold" entry). The block is the B positions p+1..p+B after the

@@ -71,6 +71,10 @@ SIGNATURES = {
                                   P_i32, P_i32, ctypes.POINTER(SsbStats), c_void_p]),
     "ssb_decode_ar_sample": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_float, c_int, c_void_p, P_i32, P_i32,
                                      ctypes.POINTER(SsbStats), c_void_p]),
+    "ssb_round_multistep": (c_int, [c_void_p, c_void_p, c_int, c_int, c_float, c_int, P_i32, P_i32, P_i32, P_i32,
+                                    c_void_p, c_void_p]),
+    "ssb_decode_multistep": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_float, c_int, P_i32,
+                                     P_i32, ctypes.POINTER(SsbStats), c_void_p]),
     "ssb_dd_block": (c_int, [c_void_p, c_void_p, c_int, c_float, c_int, c_int, P_i32, P_i32, P_i32, P_i32,
                              P_f32, P_i32, c_void_p, c_void_p]),
     "ssb_decode_dd": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_float, c_int, P_i32, P_i32,

@@ -86,8 +86,9 @@ struct ReqArgs {
   int astar[kMaxReq];                 // planted accept length (continuation mode)
   // direct block diffusion: the request's block tokens (device [B], [M] while undecided).
   // DRAFT rows 1..B embed win[j-1]; VERIFY rows j embed win[j] (the cache-write forward).
-  int32_t* win[kMaxReq];
+  int32_t* win[kMaxReq];              // [B + 1]: slot B gets window row B's latest prediction
   float tau;                          // confidence threshold of the denoising step
+  int dsteps;                         // > 0: draft schedule of at most dsteps steps, the last commits all
   // stochastic rounds: the request's uniforms [2B + 2] = u_a0, u_d[1..B], u_acc[1..B], u_t
   // (prefill and AR sampling steps: u[0] draws the token)
   const float* u[kMaxReq];

@@ -125,7 +125,7 @@ struct ssb_model {
   float* am_z;        // per row: sum of exp((z - max) / T) over the vocabulary without [M]
   float *slog_d, *slog_v;   // stochastic rounds: draft / verify logits [max_decode_rows][vocab]
   float *smax_d, *sz_d, *smax_v, *sz_v;   // their row max and exp-sum [max_rows]
-  int32_t* dd_win;    // block tokens of the direct-diffusion request [kMaxReq][SSB_MAX_BLOCK]
+  int32_t* dd_win;    // block tokens of the direct-diffusion request [kMaxReq][SSB_MAX_BLOCK + 1]
   int32_t* dd_rec;    // step records [kMaxReq][kDDRec]
   float* apart;
   int max_chunks;
@@ -352,7 +352,7 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const size_t w_conf = take((size_t)MR * 4);
   const size_t w_slog = take((size_t)2 * m->max_decode_rows * V * 4);
   const size_t w_sst = take((size_t)4 * MR * 4);
-  const size_t w_ddw = take((size_t)kMaxReq * SSB_MAX_BLOCK * 4);
+  const size_t w_ddw = take((size_t)kMaxReq * (SSB_MAX_BLOCK + 1) * 4);
   const size_t w_ddr = take((size_t)kMaxReq * kDDRec * 4);
   const size_t w_apart = take((size_t)m->max_decode_rows * c.n_heads * m->max_chunks * (hd + 4) * 4);
   const size_t w_acc = take((size_t)kMaxReq * kOutStride * 4);
@@ -994,6 +994,98 @@ void dd_block_impl(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, i
   kv_trim(kv, kv->seq_len + B + 1);
 }
 
+// Self-speculative round whose draft is refined by up to `steps` denoising
+// steps (Trillion Labs blog, the draft-schedule passage; GravityOCR review,
+// Appendix D): the direct-diffusion step kernels fill the window slots by the
+// draft-side threshold, the last step commits the rest, then the greedy verify
+// and accept of ssb_round run on [a0, d_1..d_B] read from the slots.
+void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau, int max_commit, float* vlog,
+                          RoundOut* out, int* draft_forwards, hipStream_t st) {
+  const ssb_config& c = m->c;
+  check_model_kv(m, kv);
+  if (kv->x0 < 0) fail(SSB_ESTATE, "round needs a prefilled kv (no boundary token)");
+  if (B < 1 || B > c.block_B) fail(SSB_EINVAL, "B must be in [1, block_B]");
+  if (B + 1 > c.max_rows) fail(SSB_EINVAL, "B + 1 exceeds max_rows");
+  if (steps < 1) fail(SSB_EINVAL, "steps must be >= 1");
+  if (tau != tau) fail(SSB_EINVAL, "tau must not be NaN");
+  if (max_commit < 1) fail(SSB_EINVAL, "max_commit must be >= 1");
+  if (kv->seq_len + B + 2 > c.max_positions) fail(SSB_ENOKV, "window exceeds max_positions");
+  kv_ensure(kv, kv->seq_len + B + 2, st);
+  ssb_pool* pool = kv->pool;
+  ReqArgs ra = single_req(kv, B, max_commit);
+  ra.win[0] = m->dd_win;
+  ra.tau = tau;
+  ra.dsteps = steps;
+  upload_req(m, ra, st);
+  hip_check(launch_dd_init(m->req_dev, 1, c.mask_id, m->dd_rec, kDDRec, st), "draft schedule init");
+  const int p = kv->seq_len;
+  const bool eager = vlog || m->prof_kind >= 0;
+  auto step_body = [&](hipStream_t s, bool graph) {
+    FwdSpec f{};
+    f.mode = PREP_DRAFT;
+    f.M = B + 1;
+    f.ra = ra;
+    f.max_pos = p + B + 1;
+    f.graph = graph;
+    f.stat_sc = kLog2e;
+    run_forward(m, pool, f, s);
+    hip_check(launch_dd_select(m->am_tok, m->am_z, m->req_dev, 1, c.mask_id, c.vocab, m->dd_rec, kDDRec, s),
+              "draft schedule select");
+    hip_check(hipMemcpyAsync(m->pin_i32, m->dd_rec, (size_t)kDDRec * 4, hipMemcpyDeviceToHost, s),
+              "copy step record");
+  };
+  int k = 0;
+  for (;;) {
+    if (eager) {
+      step_body(st, false);
+    } else {
+      hipGraphExec_t ex = get_graph(m, 2, pool, 1, B, [&](hipStream_t s) { step_body(s, true); });
+      hip_check(hipGraphLaunch(ex, st), "draft step graph launch");
+    }
+    hip_check(hipStreamSynchronize(st), "draft step sync");
+    prof_collect(m);
+    const int32_t* o = m->pin_i32;
+    if (o[2]) fail(SSB_EHIP, "draft step produced an invalid token or confidence (NaN logits?)");
+    if (o[0] < 1 || o[3] != k + 1 || o[1] < 0 || o[1] >= B) fail(SSB_EHIP, "draft step record is inconsistent");
+    ++k;
+    if (o[1] == 0) break;
+    if (k >= steps) fail(SSB_EHIP, "draft schedule incomplete after its last step");
+  }
+  *draft_forwards = k;
+  auto verify_body = [&](hipStream_t s, bool graph) {
+    FwdSpec f{};
+    f.mode = PREP_VERIFY;
+    f.M = B + 1;
+    f.ra = ra;
+    f.max_pos = p + B + 2;
+    f.graph = graph;
+    f.logits = vlog;
+    run_forward(m, pool, f, s);
+    hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, 1, c.eos_id, m->accept_dev, kOutStride, s), "accept");
+    hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)kOutStride * 4, hipMemcpyDeviceToHost, s),
+              "copy accept");
+  };
+  if (eager) {
+    verify_body(st, false);
+  } else {
+    hipGraphExec_t ex = get_graph(m, 6, pool, 1, B, [&](hipStream_t s) { verify_body(s, true); });
+    hip_check(hipGraphLaunch(ex, st), "verify graph launch");
+  }
+  hip_check(hipStreamSynchronize(st), "verify sync");
+  prof_collect(m);
+  const int32_t* o = m->pin_i32;
+  out->A = o[0];
+  out->n = o[1];
+  out->next_x0 = o[2];
+  out->eos = o[3];
+  if (out->A < 0 || out->A > B || out->n < 1 || out->n > B + 2 || out->next_x0 < 0 || out->next_x0 >= c.vocab)
+    fail(SSB_EHIP, "round produced an invalid accept record (NaN logits?)");
+  for (int i = 0; i < out->n; ++i) out->tok[i] = o[4 + i];
+  kv->seq_len = p + out->A + 2;
+  kv->x0 = out->next_x0;
+  kv_trim(kv, kv->seq_len + B + 2);
+}
+
 double now_us() {
   return std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now().time_since_epoch()).count();
 }
@@ -1336,6 +1428,56 @@ int ssb_decode_ar_sample(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P
         out[n++] = y;
         st.rounds += 1;
         st.forwards += 1;
+      }
+      st.decode_us = now_us() - t1;
+    }
+    st.tokens = n;
+    if (n_out) *n_out = n;
+    if (stats) *stats = st;
+  });
+}
+
+int ssb_round_multistep(ssb_model* m, ssb_kv* kv, int B, int steps, float tau, int max_commit, int32_t* committed,
+                        int32_t* n_committed, int32_t* accept_len, int32_t* draft_forwards, float* verify_logits_dev,
+                        void* stream) {
+  return guard([&] {
+    RoundOut ro{};
+    int k = 0;
+    round_multistep_impl(m, kv, B, steps, tau, max_commit, verify_logits_dev, &ro, &k, S(stream));
+    if (committed) std::memcpy(committed, ro.tok, (size_t)ro.n * 4);
+    if (n_committed) *n_committed = ro.n;
+    if (accept_len) *accept_len = ro.A;
+    if (draft_forwards) *draft_forwards = k;
+  });
+}
+
+int ssb_decode_multistep(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int B, int steps, float tau,
+                         int max_len, int32_t* out, int32_t* n_out, ssb_stats* stats, void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    if (max_len < 0) fail(SSB_EINVAL, "max_len must be >= 0");
+    if (max_len > 0 && !out) fail(SSB_EINVAL, "null output buffer");
+    if (B < 1 || B > m->c.block_B) fail(SSB_EINVAL, "B must be in [1, block_B]");
+    if (steps < 1) fail(SSB_EINVAL, "steps must be >= 1");
+    ssb_stats st{};
+    int n = 0;
+    if (max_len > 0) {
+      const double t0 = now_us();
+      int32_t y1 = 0;
+      prefill(m, kv, prefix_dev, P, &y1, S(stream));
+      const double t1 = now_us();
+      st.prefill_us = t1 - t0;
+      out[n++] = y1;
+      bool done = y1 == m->c.eos_id || n >= max_len;
+      while (!done) {
+        RoundOut ro{};
+        int k = 0;
+        round_multistep_impl(m, kv, B, steps, tau, max_len - n, nullptr, &ro, &k, S(stream));
+        for (int i = 0; i < ro.n; ++i) out[n++] = ro.tok[i];
+        st.rounds += 1;
+        st.forwards += k + 1;
+        st.accepted += ro.A;
+        done = ro.eos || n >= max_len;
       }
       st.decode_us = now_us() - t1;
     }

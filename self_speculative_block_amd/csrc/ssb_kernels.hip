@@ -959,7 +959,10 @@ __global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int
 // blog, the "confidence threshold" entry): one wave per request.  Lane j owns
 // block position j + 1, whose prediction is window row j.  Every undecided
 // position whose confidence reaches tau is committed; when none does, the
-// single most confident undecided one is (lowest position on ties).
+// single most confident undecided one is (lowest position on ties).  Under a
+// draft schedule (dsteps > 0; blog, the draft-schedule passage) the last
+// allowed step commits every open position; slot B always receives row B's
+// prediction (the schedule's d_B).
 // Record per request (rec_stride ints): [committed this step, still undecided,
 // invalid, steps so far, step_of[B], tokens[B], confidence bits[B], greedy
 // token of every row[B]].
@@ -990,7 +993,8 @@ __global__ __launch_bounds__(64) void k_dd_select(const int32_t* am, const float
   const int tk = lane ? am[row0 + j] : 0;
   const float c = lane ? 1.0f / zs[row0 + j] : 0.f;   // softmax probability of the greedy token
   const bool bad = und && (tk < 0 || tk >= vocab || tk == mask_id || !(c >= 0.f));
-  const bool hit = und && c >= ra.tau;
+  const bool final_step = ra.dsteps > 0 && step + 1 >= ra.dsteps;
+  const bool hit = und && (final_step || c >= ra.tau);
   bool take = hit;
   if (__ballot(hit) == 0) {
     float bc = und ? c : -INFINITY;
@@ -1005,8 +1009,11 @@ __global__ __launch_bounds__(64) void k_dd_select(const int32_t* am, const float
   }
   const unsigned long long tb = __ballot(take);
   const unsigned long long ub = __ballot(und && !take);
-  const unsigned long long bb = __ballot(bad);
+  const int tB = am[row0 + B];
+  const bool badB = ra.dsteps > 0 && (tB < 0 || tB >= vocab || tB == mask_id);
+  const unsigned long long bb = __ballot(bad || (j == 0 && badB));
   if (take && !bb) win[j] = tk;
+  if (j == 0 && !bb) win[B] = tB;
   if (lane) {
     if (take) o[4 + j] = step;
     o[4 + B + j] = take ? tk : cur;

@@ -250,6 +250,27 @@ class KV:
                                               _stream()))
         return list(out[: n.value]), st
 
+    def round_multistep(self, B, steps, tau, max_commit=None, want_logits=False):
+        """Greedy round with a draft schedule of at most `steps` forwards;
+        returns (committed, A, draft_forwards, verify_logits)."""
+        max_commit = B + 2 if max_commit is None else max_commit
+        out = _i32(B + 2)
+        n, A, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        vl = None
+        if want_logits:
+            vl = torch.empty((B + 1, self.model.cfg.vocab), dtype=torch.float32, device=self.model.device)
+        L.check(self.lib.ssb_round_multistep(self.model.h, self.h, B, steps, float(tau), max_commit, out, byref(n),
+                                             byref(A), byref(k), _ptr(vl), _stream()))
+        return list(out[: n.value]), A.value, k.value, vl
+
+    def decode_multistep(self, prefix_dev, B, steps, tau, max_len):
+        out = _i32(max(max_len, 1))
+        n = ctypes.c_int32()
+        st = L.SsbStats()
+        L.check(self.lib.ssb_decode_multistep(self.model.h, self.h, _ptr(prefix_dev), prefix_dev.shape[0], B, steps,
+                                              float(tau), max_len, out, byref(n), byref(st), _stream()))
+        return list(out[: n.value]), st
+
     def dd_block(self, B, tau, max_commit=None, write_cache=True, want_steps=False, want_logits=False):
         """One direct block-diffusion block.
 

@@ -161,3 +161,55 @@ def test_dd_decode_matches_oracle_eos_and_budget(tiny):
             p2.close()
             m2.close()
     assert agree >= 6 and eos_checked
+
+
+# ---- multi-step draft schedule ----
+
+def test_multistep_one_step_is_gpu_round(tiny):
+    wl, cfg, w, model, pool, orc = tiny
+    B = wl.block
+    for s in range(4):
+        pre = model.prefix_tensor(prefix_embeddings(wl.wid, s, wl.prefix_len, cfg.hidden))
+        a, b = _kv(pool), _kv(pool)
+        a.prefill(pre)
+        b.prefill(pre)
+        for k in range(3):
+            c1, A1, k1, v1 = a.round_multistep(B, 1, 0.5, want_logits=True)
+            c2, A2, _, v2 = b.round(B, want_logits=True)
+            assert (c1, A1, k1) == (c2, A2, 1)
+            assert torch.equal(v1, v2)
+            assert a.state()[:2] == b.state()[:2]
+        a.close()
+        b.close()
+
+
+def test_multistep_decode_is_gpu_ar_and_matches_oracle(tiny):
+    from oracle import spec_round_multistep
+    wl, cfg, w, model, pool, orc = tiny
+    B = wl.block
+    checked = 0
+    for s in range(4):
+        pre_np = prefix_embeddings(wl.wid, s, wl.prefix_len, cfg.hidden)
+        pre = model.prefix_tensor(pre_np)
+        tau = _mid_tau(orc, pre_np, B)
+        kv = _kv(pool)
+        ar, _ = kv.decode_ar(pre, 40)
+        for steps in (2, 4):
+            kv.reset()
+            out, st = kv.decode_multistep(pre, B, steps, tau, 40)
+            assert out == ar, (s, steps)
+            assert st.rounds <= st.forwards - st.rounds <= steps * st.rounds
+        # round by round against the oracle while no draft decision is near the threshold
+        kv.reset()
+        kv.prefill(pre)
+        ost, _, _ = prefill(orc, pre_np, wl.prefix_len + 5 * (B + 2))
+        for k in range(3):
+            c, A, nf, vl = kv.round_multistep(B, 3, tau, want_logits=True)
+            r = spec_round_multistep(orc, ost, B, 3, tau, keep_logits=True)
+            if (c, A, nf) != (r.committed, r.A, r.draft_forwards):
+                break          # a draft decision within rounding of the threshold
+            assert np.abs(vl.cpu().numpy() - r.verify_logits).max() < 1e-4
+            assert kv.state()[:2] == (ost.n, ost.x0)
+            checked += 1
+        kv.close()
+    assert checked >= 6

@@ -263,3 +263,22 @@ def test_stochastic_round_full_width(full, T):
             if rows:
                 assert np.abs(vl[:rows] - r.verify_logits[:rows]).max() < full["tol"]
     kv.rewind(P, y1)
+
+
+def test_multistep_draft_full_width(full):
+    """Draft schedules at full width: one step equals the one-shot round exactly
+    (tokens and verify logits), and three steps decode AR-identically."""
+    cfg, P, kv, pre_dev = full["cfg"], full["P"], full["kv"], full["pre_dev"]
+    y1 = full["y1"]
+    kv.rewind(P, y1)
+    c1, A1, k1, v1 = kv.round_multistep(B, 1, 0.5, want_logits=True)
+    kv.rewind(P, y1)
+    c2, A2, _, v2 = kv.round(B, want_logits=True)
+    assert (c1, A1, k1) == (c2, A2, 1) and torch.equal(v1, v2)
+    kv.reset()
+    ar, _ = kv.decode_ar(pre_dev, 48)
+    kv.reset()
+    out, st = kv.decode_multistep(pre_dev, B, 3, 0.5, 48)
+    assert out == ar and st.forwards <= 4 * st.rounds
+    kv.reset()
+    assert kv.prefill(pre_dev) == y1
