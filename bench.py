@@ -404,6 +404,63 @@ def sample_workload(args):
     print(json.dumps(line))
 
 
+def multistep_workload(args):
+    """Greedy self-speculative decoding of the text regions (config 3 shapes) with draft
+    schedules of 1, 2 and 4 steps, B = 32, batch 1.  The draft-side threshold is the median of
+    the first draft step's confidences on the first region.  Outputs are checked equal to AR.
+    The random-init decoder's drafts rarely match the verifier, so acceptance stays near zero
+    here; the line measures what each extra draft forward costs per round."""
+    import numpy as np
+    import torch
+    from ssb_inputs import generate_weights, prefix_embeddings, workload
+    from ssb_inputs.schedule import target_lengths
+    from self_speculative_block_amd.engine import KV, Model, Pool
+
+    wl = workload(3)
+    cfg, B, P = wl.model, wl.block, wl.prefix_len
+    lengths = target_lengths(wl)
+    n = min(args.regions or 32, wl.n_regions)
+    cap = max(lengths[:n])
+    torch.cuda.set_device(0)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8)
+    pool = Pool(model, n_pages=(P + cap + 2 * B + 8) // 16 + 8)
+    kv = KV(pool, P + cap + 2 * B + 8)
+    pres = [model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden)) for i in range(n)]
+    kv.reset()
+    kv.prefill(pres[0])
+    _, _, _, ex = kv.dd_block(B, 0.0, write_cache=False, want_steps=True)
+    tau = float(np.median(ex["conf"][0]))
+    ars = []
+    for i in range(n):
+        kv.reset()
+        ars.append(kv.decode_ar(pres[i], lengths[i])[0])
+    res = {}
+    for steps in (1, 2, 4):
+        toks = fw = rounds = acc = 0
+        us = 0.0
+        for i in range(n):
+            kv.reset()
+            out, st = kv.decode_multistep(pres[i], B, steps, tau, lengths[i])
+            assert out == ars[i], f"region {i}: output differs from AR"
+            toks += st.tokens - 1
+            fw += st.forwards
+            rounds += st.rounds
+            acc += st.accepted
+            us += st.decode_us
+        res[str(steps)] = {"tokens_per_s": toks / (us * 1e-6), "tpf": toks / max(fw, 1),
+                           "mean_accept": acc / max(rounds, 1), "draft_forwards_per_round": (fw - rounds) / rounds,
+                           "round_ms_mean": us / rounds / 1e3, "rounds": rounds}
+    line = {
+        "metric": "decode-only tokens/s, self-speculative decoding with a multi-step draft schedule (B=32, batch 1)",
+        "value": res["1"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + "_draft_schedule", "regions": n, "prefix": P, "block_B": B,
+                   "draft_tau": tau},
+        "by_steps": res, "outputs_identical_to_ar": True,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -411,11 +468,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=20)
-    ap.add_argument("--workload", choices=["round", "text", "table", "batched", "direct", "sample"], default="round",
+    ap.add_argument("--workload", choices=["round", "text", "table", "batched", "direct", "sample", "multistep"], default="round",
                     help="round: the round microbenchmark (the headline line); text / table: decode "
                          "of text or table regions; batched: the 16-request page; direct: direct "
                          "block-diffusion decoding of the text regions; sample: stochastic decoding "
-                         "of the text regions")
+                         "of the text regions; multistep: draft schedules of 1, 2, 4 steps")
     ap.add_argument("--regions", type=int, default=0, help="text / table: number of regions (0 = all)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -433,6 +490,8 @@ def main():
         return direct_workload(args)
     if args.workload == "sample":
         return sample_workload(args)
+    if args.workload == "multistep":
+        return multistep_workload(args)
 
     import numpy as np
     import torch
