@@ -461,6 +461,70 @@ def multistep_workload(args):
     print(json.dumps(line))
 
 
+def sweep_workload(args):
+    """Throughput against the cap on running requests (GravityOCR review, section 4.3, Figure 6;
+    Appendix C: a full client queue and a running-request cap).  A queue of text regions (config 3
+    shapes: prefix 1088, lengths of mean ~68) is served by continuous batching at caps 1..64, with
+    greedy AR steps and with self-speculative rounds (B = 32, drafts planted from the AR output with
+    the config's accept-length schedule).  Reports tokens/s over the whole queue (prefills
+    included, as a server's clock runs) and decode-only, per cap, and their ratio."""
+    import numpy as np
+    import torch
+    from ssb_inputs import generate_weights, plant_accept_lengths, prefix_embeddings, workload
+    from ssb_inputs.schedule import target_lengths
+    from self_speculative_block_amd.engine import KV, Model, Pool, serve
+    from self_speculative_block_amd._lib import SSB_SERVE_AR, SSB_SERVE_SPEC
+
+    wl = workload(3)
+    cfg, B, P = wl.model, wl.block, wl.prefix_len
+    lengths = target_lengths(wl)
+    n = min(args.regions or 128, wl.n_regions)
+    caps = (1, 2, 4, 8, 16, 32, 64)
+    cap_len = max(lengths[:n])
+    max_tokens = P + cap_len + 2 * B + 8
+    torch.cuda.set_device(0)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=max(caps) * (B + 1), max_positions=max_tokens)
+    pool = Pool(model, n_pages=(max(caps) + 1) * (max_tokens // 16 + 2))
+    reqs = [{"prefix_dev": model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden)), "max_len": lengths[i]}
+            for i in range(n)]
+    # AR reference outputs (they plant the drafts), one request at a time
+    kv = KV(pool, max_tokens)
+    ref = []
+    for q in reqs:
+        kv.reset()
+        ref.append(kv.decode_ar(q["prefix_dev"], q["max_len"])[0])
+    kv.close()
+    planted = [dict(q, cont_dev=torch.tensor(ref[i], dtype=torch.int32, device="cuda"),
+                    astar=[int(a) for a in plant_accept_lengths(wl.wid, i, q["max_len"], B, wl.plant_p)])
+               for i, q in enumerate(reqs)]
+    toks = sum(len(o) - 1 for o in ref)
+    res = {}
+    for cap in caps:
+        row = {}
+        for name, mode, qs in (("ar", SSB_SERVE_AR, reqs), ("spec", SSB_SERVE_SPEC, planted)):
+            out, info, st = serve(model, pool, qs, cap, mode, B=B if mode == SSB_SERVE_SPEC else 0,
+                                  max_tokens=max_tokens)
+            assert out == ref, f"cap {cap} {name}: output differs from AR"
+            row[name] = {"tokens_per_s": toks / (st["total_us"] * 1e-6),
+                         "decode_tokens_per_s": toks / (st["decode_us"] * 1e-6),
+                         "launches": st["steps"], "mean_running": st["mean_running"],
+                         "total_ms": st["total_us"] / 1e3, "prefill_ms": st["prefill_us"] / 1e3}
+        row["speedup"] = row["spec"]["tokens_per_s"] / row["ar"]["tokens_per_s"]
+        row["decode_speedup"] = row["spec"]["decode_tokens_per_s"] / row["ar"]["decode_tokens_per_s"]
+        res[str(cap)] = row
+        print(f"cap {cap}: ar {row['ar']['tokens_per_s']:.0f} spec {row['spec']['tokens_per_s']:.0f} tok/s "
+              f"(x{row['speedup']:.2f}; decode-only x{row['decode_speedup']:.2f})", file=sys.stderr, flush=True)
+    line = {
+        "metric": "tokens/s over a queue of text regions under continuous batching, self-speculative vs AR",
+        "value": res["64"]["spec"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + "_batch_sweep", "requests": n, "prefix": P, "block_B": B,
+                   "caps": list(caps), "output_tokens": toks},
+        "by_cap": res, "outputs_identical_to_ar": True,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -468,11 +532,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=20)
-    ap.add_argument("--workload", choices=["round", "text", "table", "batched", "direct", "sample", "multistep"], default="round",
+    ap.add_argument("--workload", choices=["round", "text", "table", "batched", "direct", "sample", "multistep", "sweep"], default="round",
                     help="round: the round microbenchmark (the headline line); text / table: decode "
                          "of text or table regions; batched: the 16-request page; direct: direct "
                          "block-diffusion decoding of the text regions; sample: stochastic decoding "
-                         "of the text regions; multistep: draft schedules of 1, 2, 4 steps")
+                         "of the text regions; multistep: draft schedules of 1, 2, 4 steps; sweep: "
+                         "continuous batching at running caps 1..64, AR vs self-speculative")
     ap.add_argument("--regions", type=int, default=0, help="text / table: number of regions (0 = all)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -492,6 +557,8 @@ def main():
         return sample_workload(args)
     if args.workload == "multistep":
         return multistep_workload(args)
+    if args.workload == "sweep":
+        return sweep_workload(args)
 
     import numpy as np
     import torch

@@ -48,7 +48,7 @@ extern "C" {
 #define SSB_F32 0
 #define SSB_BF16 1
 
-#define SSB_MAX_BATCH 16 /* requests per ssb_round_batch call */
+#define SSB_MAX_BATCH 64 /* requests per batched call */
 #define SSB_MAX_BLOCK 64 /* largest block size B */
 
 /* Decoder shape. Pre-norm Llama-style block: RMSNorm, RoPE (rotate-half
@@ -292,6 +292,49 @@ int ssb_dd_block(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, int
  * forwards = denoising forwards, cache_forwards = cache-write forwards. */
 int ssb_decode_dd(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int B, float tau, int max_len,
                   int32_t* out, int32_t* n_out, ssb_stats* stats, void* stream);
+
+/* One greedy AR step for R <= SSB_MAX_BATCH requests (distinct prefilled
+ * kvs of one pool), one launch per stage: request r feeds its boundary token
+ * and gets the next one in tokens (host [R]). */
+int ssb_ar_step_batch(ssb_model* m, ssb_kv* const* kvs, int R, int32_t* tokens, void* stream);
+
+/* Continuous batching over a request queue (GravityOCR review, section 4.3,
+ * Figure 6 "Throughput Scaling with Batch Size", and Appendix C: a full
+ * client queue served under a cap on running requests). All n_reqs requests
+ * are queued at the start, in array order. At most max_running run at once;
+ * a free slot admits the next queued request, whose prefill runs between
+ * decode launches. Each decode launch advances every running request by one
+ * greedy AR step (mode SSB_SERVE_AR) or one self-speculative round of block
+ * B (mode SSB_SERVE_SPEC). A request leaves at EOS or after max_len tokens.
+ * The engine creates max_running kvs of max_tokens positions in `pool` and
+ * frees them before returning; the pool needs the pages for them.
+ * Per request (in): prefix_dev (device [P][hidden]), P, max_len, out (host
+ * [max_len]); optional planting as in ssb_decode (cont_dev, cont_len, astar,
+ * n_astar; SPEC mode only). Per request (out): n_out, rounds (decode
+ * launches it took part in), finish_us (completion time from the call's
+ * start). */
+#define SSB_SERVE_AR 0
+#define SSB_SERVE_SPEC 1
+typedef struct ssb_request {
+  const void* prefix_dev;
+  int P, max_len;
+  const int32_t* cont_dev;
+  int cont_len;
+  const int32_t* astar;
+  int n_astar;
+  int32_t* out;
+  int n_out, rounds;
+  double finish_us;
+} ssb_request;
+typedef struct ssb_serve_stats {
+  int steps;             /* decode launches */
+  int prefills;
+  long long tokens;      /* output tokens of all requests, y1 included */
+  double total_us, prefill_us, decode_us;
+  double mean_running;   /* running requests per decode launch, averaged */
+} ssb_serve_stats;
+int ssb_serve(ssb_model* m, ssb_pool* pool, ssb_request* reqs, int n_reqs, int max_running, int mode, int B,
+              int max_tokens, ssb_serve_stats* stats, void* stream);
 
 /* Teacher-forced causal forward over tokens (host [M], M <= max_rows) at
  * positions p..p+M-1 of the kv. Writes their KV but does not change the

@@ -7,7 +7,7 @@ from .build import LIB
 
 SSB_OK, SSB_EINVAL, SSB_ENOKV, SSB_EHIP, SSB_ESTATE, SSB_ENOMEM = 0, -1, -2, -3, -4, -5
 SSB_F32, SSB_BF16 = 0, 1
-SSB_MAX_BATCH = 16
+SSB_MAX_BATCH = 64
 SSB_MAX_BLOCK = 64
 KERNEL_KINDS = {"qkv": 0, "attention": 1, "combine": 2, "o": 3, "gate_up": 4, "down": 5, "lm_head": 6, "argmax": 7,
                 "reduce": 8}
@@ -37,6 +37,20 @@ class SsbWeights(ctypes.Structure):
 class SsbStats(ctypes.Structure):
     _fields_ = [("rounds", c_int), ("forwards", c_int), ("tokens", c_int), ("accepted", c_int),
                 ("decode_us", c_double), ("prefill_us", c_double), ("cache_forwards", c_int)]
+
+
+SSB_SERVE_AR, SSB_SERVE_SPEC = 0, 1
+
+
+class SsbRequest(ctypes.Structure):
+    _fields_ = [("prefix_dev", c_void_p), ("P", c_int), ("max_len", c_int), ("cont_dev", c_void_p),
+                ("cont_len", c_int), ("astar", c_void_p), ("n_astar", c_int), ("out", c_void_p),
+                ("n_out", c_int), ("rounds", c_int), ("finish_us", c_double)]
+
+
+class SsbServeStats(ctypes.Structure):
+    _fields_ = [("steps", c_int), ("prefills", c_int), ("tokens", ctypes.c_longlong), ("total_us", c_double),
+                ("prefill_us", c_double), ("decode_us", c_double), ("mean_running", c_double)]
 
 
 # name -> (restype, argtypes)
@@ -75,6 +89,9 @@ SIGNATURES = {
                                     c_void_p, c_void_p]),
     "ssb_decode_multistep": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_float, c_int, P_i32,
                                      P_i32, ctypes.POINTER(SsbStats), c_void_p]),
+    "ssb_ar_step_batch": (c_int, [c_void_p, ctypes.POINTER(c_void_p), c_int, P_i32, c_void_p]),
+    "ssb_serve": (c_int, [c_void_p, c_void_p, ctypes.POINTER(SsbRequest), c_int, c_int, c_int, c_int, c_int,
+                          ctypes.POINTER(SsbServeStats), c_void_p]),
     "ssb_dd_block": (c_int, [c_void_p, c_void_p, c_int, c_float, c_int, c_int, P_i32, P_i32, P_i32, P_i32,
                              P_f32, P_i32, c_void_p, c_void_p]),
     "ssb_decode_dd": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_float, c_int, P_i32, P_i32,

@@ -23,7 +23,7 @@ constexpr int kWave = 64;
 constexpr int kThreads = 256;      // 4 waves per workgroup
 constexpr int kKeyChunk = 64;      // fixed key chunk of attention (absolute positions)
 constexpr int kPage = 16;          // tokens per KV page
-constexpr int kMaxReq = 16;        // requests per batched launch
+constexpr int kMaxReq = 64;        // requests per batched launch
 constexpr int kMaxTasks = 64;      // attention row tasks per launch
 constexpr int kTaskRows = 48;      // rows per attention task (3 MFMA row tiles)
 constexpr int kMaxNormParts = 128; // per-16-column norm partials (hidden <= 2048)

@@ -607,6 +607,37 @@ void kv_trim(ssb_kv* kv, int keep_tokens) {
   }
 }
 
+ssb_kv* kv_new(ssb_pool* p, int max_tokens) {
+  if (max_tokens < 2) fail(SSB_EINVAL, "max_tokens must be >= 2");
+  if (max_tokens > p->m->c.max_positions) fail(SSB_EINVAL, "max_tokens exceeds max_positions");
+  hip_check(hipSetDevice(p->m->device), "hipSetDevice");
+  auto* kv = new ssb_kv();
+  std::unique_ptr<ssb_kv> hold(kv);
+  kv->pool = p;
+  kv->max_tokens = max_tokens;
+  kv->max_pages = (max_tokens + kPage - 1) / kPage;
+  kv->seq_len = 0;
+  kv->x0 = -1;
+  if (hipMalloc(reinterpret_cast<void**>(&kv->pt_dev), (size_t)kv->max_pages * 4) != hipSuccess)
+    fail(SSB_ENOMEM, "page table allocation failed");
+  if (hipHostMalloc(reinterpret_cast<void**>(&kv->pt_host), (size_t)kv->max_pages * 4, hipHostMallocDefault) !=
+      hipSuccess) {
+    (void)hipFree(kv->pt_dev);
+    fail(SSB_ENOMEM, "pinned page table allocation failed");
+  }
+  return hold.release();
+}
+
+void kv_delete(ssb_kv* kv) {
+  if (!kv) return;
+  (void)hipSetDevice(kv->pool->m->device);
+  (void)hipDeviceSynchronize();
+  kv_trim(kv, 0);
+  (void)hipFree(kv->pt_dev);
+  (void)hipHostFree(kv->pt_host);
+  delete kv;
+}
+
 hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
 
@@ -731,7 +762,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
   const ssb_config& c = m->c;
   check_sample(smp, R);
   if (smp && (planted || cont)) fail(SSB_EINVAL, "planted drafts apply to greedy rounds only");
-  if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, 16]");
+  if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
   if (B < 0 || B > c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
   if (R * (B + 1) > c.max_rows) fail(SSB_EINVAL, "R*(B+1) exceeds max_rows");
   if ((dlog || vlog) && R != 1) fail(SSB_EINVAL, "logits output needs R == 1");
@@ -746,7 +777,6 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
       if (kvs[q] == kvs[r]) fail(SSB_EINVAL, "the same kv appears twice in a batch");
   }
   for (int r = 0; r < R; ++r) kv_ensure(kvs[r], kvs[r]->seq_len + B + 2, st);
-  if (cont && R != 1) fail(SSB_EINVAL, "planting from a continuation needs R == 1");
   ReqArgs ra{};
   ra.n = R;
   ra.B = B;
@@ -875,6 +905,195 @@ void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_
   kv->seq_len += 1;
   kv->x0 = y;
   if (token) *token = y;
+}
+
+double now_us() {
+  return std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+// One greedy AR step for R requests, one launch per stage: request r's row is
+// [x0_r] at p_r, keys <= p_r (the window of a round with no masks).
+void ar_step_batch_impl(ssb_model* m, ssb_kv* const* kvs, int R, int32_t* tokens, hipStream_t st) {
+  const ssb_config& c = m->c;
+  if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
+  if (R > c.max_rows) fail(SSB_EINVAL, "R exceeds max_rows");
+  ssb_pool* pool = kvs[0]->pool;
+  for (int r = 0; r < R; ++r) {
+    check_model_kv(m, kvs[r]);
+    if (kvs[r]->pool != pool) fail(SSB_EINVAL, "batched kvs must share one pool");
+    if (kvs[r]->x0 < 0) fail(SSB_ESTATE, "AR step needs a prefilled kv (no boundary token)");
+    if (kvs[r]->seq_len + 1 > c.max_positions) fail(SSB_ENOKV, "position exceeds max_positions");
+    for (int q = 0; q < r; ++q)
+      if (kvs[q] == kvs[r]) fail(SSB_EINVAL, "the same kv appears twice in a batch");
+  }
+  for (int r = 0; r < R; ++r) kv_ensure(kvs[r], kvs[r]->seq_len + 1, st);
+  ReqArgs ra{};
+  ra.n = R;
+  ra.B = 0;
+  int maxpos = 0;
+  for (int r = 0; r < R; ++r) {
+    ra.p[r] = kvs[r]->seq_len;
+    ra.x0[r] = kvs[r]->x0;
+    ra.row0[r] = r;
+    ra.max_commit[r] = 1;
+    ra.pt[r] = kvs[r]->pt_dev;
+    ra.npg[r] = (int)kvs[r]->pages.size();
+    maxpos = std::max(maxpos, ra.p[r] + 1);
+  }
+  upload_req(m, ra, st);
+  auto body = [&](hipStream_t s, bool graph) {
+    FwdSpec f{};
+    f.mode = PREP_DRAFT;
+    f.M = R;
+    f.ra = ra;
+    f.max_pos = maxpos;
+    f.graph = graph;
+    run_forward(m, pool, f, s);
+    hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, (size_t)R * 4, hipMemcpyDeviceToHost, s), "copy tokens");
+  };
+  if (m->prof_kind >= 0) {
+    body(st, false);
+  } else {
+    hipGraphExec_t ex = get_graph(m, 1, pool, R, 0, [&](hipStream_t s) { body(s, true); });
+    hip_check(hipGraphLaunch(ex, st), "AR graph launch");
+  }
+  hip_check(hipStreamSynchronize(st), "ar sync");
+  prof_collect(m);
+  for (int r = 0; r < R; ++r) {
+    const int32_t y = m->pin_i32[r];
+    if (y < 0 || y >= c.vocab) fail(SSB_EHIP, "AR step produced no valid token (NaN logits?)");
+    tokens[r] = y;
+  }
+  for (int r = 0; r < R; ++r) {
+    kvs[r]->seq_len += 1;
+    kvs[r]->x0 = tokens[r];
+  }
+}
+
+// Continuous batching over a queue of requests, all present at the start
+// (the batch-size throughput setting of the GravityOCR review, section 4.3 /
+// Figure 6: a full client queue and a cap on running requests).  Up to
+// max_running requests run at once; a free slot admits the next request in
+// queue order (its prefill runs between decode launches); every decode launch
+// advances all running requests by one greedy AR step or one round; a request
+// leaves at EOS or its max_len.
+void serve_impl(ssb_model* m, ssb_pool* pool, ssb_request* reqs, int n_reqs, int max_running, int mode, int B,
+                int max_tokens, ssb_serve_stats* stats, hipStream_t st) {
+  const ssb_config& c = m->c;
+  if (!pool || pool->m != m) fail(SSB_EINVAL, "pool belongs to another model");
+  if (n_reqs < 0 || (n_reqs > 0 && !reqs)) fail(SSB_EINVAL, "bad request array");
+  if (mode != SSB_SERVE_AR && mode != SSB_SERVE_SPEC) fail(SSB_EINVAL, "unknown serve mode");
+  if (max_running < 1 || max_running > SSB_MAX_BATCH) fail(SSB_EINVAL, "max_running must be in [1, SSB_MAX_BATCH]");
+  if (mode == SSB_SERVE_SPEC) {
+    if (B < 0 || B > c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
+    if (max_running * (B + 1) > c.max_rows) fail(SSB_EINVAL, "max_running * (B + 1) exceeds max_rows");
+  } else if (max_running > c.max_rows) {
+    fail(SSB_EINVAL, "max_running exceeds max_rows");
+  }
+  const int W = mode == SSB_SERVE_SPEC ? B + 2 : 1;
+  for (int i = 0; i < n_reqs; ++i) {
+    const ssb_request& q = reqs[i];
+    if (!q.prefix_dev || q.P < 1 || q.max_len < 0 || (q.max_len > 0 && !q.out))
+      fail(SSB_EINVAL, "bad request " + std::to_string(i));
+    if (q.P + q.max_len + W + 1 > max_tokens) fail(SSB_EINVAL, "request exceeds max_tokens");
+    if (q.cont_dev && (q.cont_len < 0 || (q.n_astar > 0 && !q.astar))) fail(SSB_EINVAL, "bad planting");
+  }
+  struct Slot { ssb_kv* kv = nullptr; int req = -1, k = 0, n = 0; };
+  std::vector<Slot> slots(max_running);
+  struct Hold {
+    std::vector<Slot>& s;
+    ~Hold() { for (auto& x : s) kv_delete(x.kv); }
+  } hold{slots};
+  for (auto& x : slots) x.kv = kv_new(pool, max_tokens);
+  ssb_serve_stats S0{};
+  const double t0 = now_us();
+  int next = 0;
+  double running_sum = 0;
+  auto finish = [&](Slot& x) {
+    ssb_request& q = reqs[x.req];
+    q.n_out = x.n;
+    q.rounds = x.k;
+    q.finish_us = now_us() - t0;
+    S0.tokens += x.n;
+    x.req = -1;
+  };
+  std::vector<ssb_kv*> kvs;
+  std::vector<Slot*> run;
+  std::vector<int32_t> toks;
+  std::vector<int> mc, cl, cc, as;
+  std::vector<const int32_t*> conts;
+  std::vector<RoundOut> outs;
+  for (;;) {
+    for (auto& x : slots) {
+      while (x.req < 0 && next < n_reqs) {
+        x.req = next++;
+        x.k = 0;
+        x.n = 0;
+        ssb_request& q = reqs[x.req];
+        if (q.max_len == 0) { finish(x); continue; }
+        kv_trim(x.kv, 0);
+        x.kv->seq_len = 0;
+        x.kv->x0 = -1;
+        const double tp = now_us();
+        int32_t y1 = 0;
+        prefill(m, x.kv, q.prefix_dev, q.P, &y1, st);
+        S0.prefill_us += now_us() - tp;
+        S0.prefills += 1;
+        q.out[x.n++] = y1;
+        if (y1 == c.eos_id || x.n >= q.max_len) finish(x);
+      }
+    }
+    run.clear();
+    kvs.clear();
+    for (auto& x : slots)
+      if (x.req >= 0) { run.push_back(&x); kvs.push_back(x.kv); }
+    if (run.empty()) break;
+    const int R = (int)run.size();
+    const double td = now_us();
+    if (mode == SSB_SERVE_AR) {
+      toks.assign(R, 0);
+      ar_step_batch_impl(m, kvs.data(), R, toks.data(), st);
+      for (int r = 0; r < R; ++r) {
+        Slot& x = *run[r];
+        ssb_request& q = reqs[x.req];
+        q.out[x.n++] = toks[r];
+        x.k += 1;
+        if (toks[r] == c.eos_id || x.n >= q.max_len) finish(x);
+      }
+    } else {
+      mc.assign(R, 0); cl.assign(R, 0); cc.assign(R, 0); as.assign(R, 0);
+      conts.assign(R, nullptr);
+      outs.assign(R, RoundOut{});
+      bool any_plant = false;
+      for (int r = 0; r < R; ++r) {
+        const Slot& x = *run[r];
+        const ssb_request& q = reqs[x.req];
+        mc[r] = q.max_len - x.n;
+        if (q.cont_dev && x.k < q.n_astar) {
+          conts[r] = q.cont_dev;
+          cl[r] = q.cont_len;
+          cc[r] = x.n;
+          as[r] = q.astar[x.k];
+          any_plant = true;
+        }
+      }
+      round_impl(m, kvs.data(), R, B, mc.data(), nullptr, any_plant ? conts.data() : nullptr, cl.data(), cc.data(),
+                 as.data(), nullptr, nullptr, outs.data(), st);
+      for (int r = 0; r < R; ++r) {
+        Slot& x = *run[r];
+        ssb_request& q = reqs[x.req];
+        for (int i = 0; i < outs[r].n; ++i) q.out[x.n++] = outs[r].tok[i];
+        x.k += 1;
+        if (outs[r].eos || x.n >= q.max_len) finish(x);
+      }
+    }
+    S0.decode_us += now_us() - td;
+    S0.steps += 1;
+    running_sum += R;
+  }
+  S0.total_us = now_us() - t0;
+  S0.mean_running = S0.steps ? running_sum / S0.steps : 0.0;
+  if (stats) *stats = S0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1086,9 +1305,6 @@ void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau,
   kv_trim(kv, kv->seq_len + B + 2);
 }
 
-double now_us() {
-  return std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now().time_since_epoch()).count();
-}
 
 }  // namespace
 
@@ -1160,36 +1376,11 @@ int ssb_pool_free_pages(const ssb_pool* p, int* n_free) {
 int ssb_kv_create(ssb_pool* p, int max_tokens, ssb_kv** out) {
   return guard([&] {
     if (!p || !out) fail(SSB_EINVAL, "null argument");
-    if (max_tokens < 2) fail(SSB_EINVAL, "max_tokens must be >= 2");
-    if (max_tokens > p->m->c.max_positions) fail(SSB_EINVAL, "max_tokens exceeds max_positions");
-    hip_check(hipSetDevice(p->m->device), "hipSetDevice");
-    auto* kv = new ssb_kv();
-    std::unique_ptr<ssb_kv> hold(kv);
-    kv->pool = p;
-    kv->max_tokens = max_tokens;
-    kv->max_pages = (max_tokens + kPage - 1) / kPage;
-    kv->seq_len = 0;
-    kv->x0 = -1;
-    if (hipMalloc(reinterpret_cast<void**>(&kv->pt_dev), (size_t)kv->max_pages * 4) != hipSuccess)
-      fail(SSB_ENOMEM, "page table allocation failed");
-    if (hipHostMalloc(reinterpret_cast<void**>(&kv->pt_host), (size_t)kv->max_pages * 4, hipHostMallocDefault) !=
-        hipSuccess) {
-      (void)hipFree(kv->pt_dev);
-      fail(SSB_ENOMEM, "pinned page table allocation failed");
-    }
-    *out = hold.release();
+    *out = kv_new(p, max_tokens);
   });
 }
 
-void ssb_kv_free(ssb_kv* kv) {
-  if (!kv) return;
-  (void)hipSetDevice(kv->pool->m->device);
-  (void)hipDeviceSynchronize();
-  kv_trim(kv, 0);
-  (void)hipFree(kv->pt_dev);
-  (void)hipHostFree(kv->pt_host);
-  delete kv;
-}
+void ssb_kv_free(ssb_kv* kv) { kv_delete(kv); }
 
 int ssb_kv_reset(ssb_kv* kv) {
   return guard([&] {
@@ -1323,7 +1514,7 @@ int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_
                     void* stream) {
   return guard([&] {
     if (!m || !kvs || !max_commit) fail(SSB_EINVAL, "null argument");
-    if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, 16]");
+    if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
     for (int r = 0; r < R; ++r)
       if (!kvs[r]) fail(SSB_EINVAL, "null kv in batch");
     std::vector<RoundOut> ro(R);
@@ -1484,6 +1675,25 @@ int ssb_decode_multistep(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P
     st.tokens = n;
     if (n_out) *n_out = n;
     if (stats) *stats = st;
+  });
+}
+
+int ssb_ar_step_batch(ssb_model* m, ssb_kv* const* kvs, int R, int32_t* tokens, void* stream) {
+  return guard([&] {
+    if (!m || !kvs || !tokens) fail(SSB_EINVAL, "null argument");
+    if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
+    for (int r = 0; r < R; ++r)
+      if (!kvs[r]) fail(SSB_EINVAL, "null kv in batch");
+    ar_step_batch_impl(m, kvs, R, tokens, S(stream));
+  });
+}
+
+int ssb_serve(ssb_model* m, ssb_pool* pool, ssb_request* reqs, int n_reqs, int max_running, int mode, int B,
+              int max_tokens, ssb_serve_stats* stats, void* stream) {
+  return guard([&] {
+    if (!m || !pool) fail(SSB_EINVAL, "null argument");
+    hip_check(hipSetDevice(m->device), "hipSetDevice");
+    serve_impl(m, pool, reqs, n_reqs, max_running, mode, B, max_tokens, stats, S(stream));
   });
 }
 

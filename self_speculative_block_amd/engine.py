@@ -320,3 +320,47 @@ def round_batch(model, kvs, B, max_commit, planted_dev=None):
     A = _i32(R)
     L.check(model.lib.ssb_round_batch(model.h, hs, R, B, mc, _ptr(planted_dev), out, n, A, _stream()))
     return [(list(out[r * (B + 2): r * (B + 2) + n[r]]), A[r]) for r in range(R)]
+
+
+def ar_step_batch(model, kvs):
+    """One greedy AR step for every kv in one launch per stage; returns the tokens."""
+    R = len(kvs)
+    hs = (ctypes.c_void_p * R)(*[kv.h.value for kv in kvs])
+    out = _i32(R)
+    L.check(model.lib.ssb_ar_step_batch(model.h, hs, R, out, _stream()))
+    return list(out[:R])
+
+
+def serve(model, pool, requests, max_running, mode, B=0, max_tokens=None):
+    """Continuous batching over a queue of requests.
+
+    requests: list of dicts with prefix_dev (device tensor [P][hidden]), max_len and, optionally,
+    cont_dev (device int32 AR continuation) and astar (planted accept lengths per round).
+    Returns (outputs, per-request info dicts, stats dict).
+    """
+    n = len(requests)
+    reqs = (L.SsbRequest * max(n, 1))()
+    outs, keep = [], []
+    for i, q in enumerate(requests):
+        r = reqs[i]
+        r.prefix_dev = _ptr(q["prefix_dev"])
+        r.P = q["prefix_dev"].shape[0]
+        r.max_len = q["max_len"]
+        o = _i32(max(q["max_len"], 1))
+        outs.append(o)
+        r.out = ctypes.cast(o, ctypes.c_void_p)
+        if q.get("cont_dev") is not None:
+            r.cont_dev = _ptr(q["cont_dev"])
+            r.cont_len = q["cont_dev"].shape[0]
+            a = (ctypes.c_int32 * max(len(q["astar"]), 1))(*[int(x) for x in q["astar"]])
+            keep.append(a)
+            r.astar = ctypes.cast(a, ctypes.c_void_p)
+            r.n_astar = len(q["astar"])
+    if max_tokens is None:
+        max_tokens = max(q["prefix_dev"].shape[0] + q["max_len"] for q in requests) + 2 * B + 8
+    st = L.SsbServeStats()
+    L.check(model.lib.ssb_serve(model.h, pool.h, reqs, n, max_running, mode, B, max_tokens, byref(st), _stream()))
+    res = [list(outs[i][: reqs[i].n_out]) for i in range(n)]
+    info = [{"rounds": reqs[i].rounds, "finish_us": reqs[i].finish_us} for i in range(n)]
+    stats = {k: getattr(st, k) for k, _ in L.SsbServeStats._fields_}
+    return res, info, stats

@@ -73,3 +73,33 @@ def test_null_arguments_are_rejected_without_a_gpu(lib):
     lib.ssb_free_model(None)
     lib.ssb_kv_free(None)
     lib.ssb_pool_free(None)
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of the header's structs have the C compiler's sizes and offsets."""
+    import subprocess
+    from self_speculative_block_amd import _lib
+    structs = {"ssb_config": _lib.SsbConfig, "ssb_stats": _lib.SsbStats, "ssb_request": _lib.SsbRequest,
+               "ssb_serve_stats": _lib.SsbServeStats, "ssb_weights": _lib.SsbWeights}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def test_serve_rejects_bad_arguments_without_a_gpu(lib):
+    from self_speculative_block_amd._lib import SSB_EINVAL
+    assert lib.ssb_serve(None, None, None, 0, 1, 0, 0, 16, None, None) == SSB_EINVAL
+    assert lib.ssb_ar_step_batch(None, None, 1, None, None) == SSB_EINVAL
