@@ -463,7 +463,12 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   at.fwd_pt = m->fwd_pt; at.pt_ld = m->pt_ld;
   at.row_lim = m->row_lim; at.part = m->apart; at.max_chunks = m->max_chunks;
   at.out = m->attn; at.out_ld = qd;
-  at.fold = M > m->max_decode_rows ? 1 : 0;
+  // rows of a prefill or teacher-forced forward fold their key chunks in one workgroup (no
+  // records, no combine launch); decode windows split keys over workgroups and combine
+  const bool tall = f.mode == PREP_PREFILL || f.mode == PREP_TOKENS;
+  at.fold = (tall || M > m->max_decode_rows) ? 1 : 0;
+  // tall bf16 forwards use the large-tile GEMM (no decode row is computed there)
+  const bool big = tall && m->elem == 2 && M >= 128;
   at.scale = 1.0f / std::sqrt((float)c.head_dim);
   // row tasks: windows of each request (draft/verify) or one request's rows
   at.tasks.n = 0;
@@ -490,7 +495,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       set_w(a, m->qkv[l]);
       a.x = m->xg; a.ldx = H;
       prof_begin(m, SSB_K_QKV, st);
-      hip_check(launch_gemm<T>(a, EPI_QKV, st), "qkv gemm");
+      hip_check(big ? launch_gemm_big(a, EPI_QKV, st) : launch_gemm<T>(a, EPI_QKV, st), "qkv gemm");
       prof_end(m, SSB_K_QKV, st);
     }
     at.layer = l;
@@ -509,7 +514,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       a.x = m->attn; a.ldx = qd;
       a.gain_next = m->mlp_norm[l];
       prof_begin(m, SSB_K_O, st);
-      hip_check(launch_gemm<T>(a, EPI_RESID, st), "o gemm");
+      hip_check(big ? launch_gemm_big(a, EPI_RESID, st) : launch_gemm<T>(a, EPI_RESID, st), "o gemm");
       prof_end(m, SSB_K_O, st);
     }
     {  // gate|up + SwiGLU
@@ -517,7 +522,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       set_w(a, m->gu[l]);
       a.x = m->xg; a.ldx = H;
       prof_begin(m, SSB_K_GATEUP, st);
-      hip_check(launch_gemm<T>(a, EPI_SWIGLU, st), "gate/up gemm");
+      hip_check(big ? launch_gemm_big(a, EPI_SWIGLU, st) : launch_gemm<T>(a, EPI_SWIGLU, st), "gate/up gemm");
       prof_end(m, SSB_K_GATEUP, st);
     }
     {  // down + residual; next input xg = h * (next attn_norm | final_norm)
@@ -526,9 +531,10 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       a.x = m->act; a.ldx = c.ffn;
       a.gain_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
       prof_begin(m, SSB_K_DOWN, st);
-      hip_check(launch_gemm<T>(a, a.S > 1 ? EPI_PARTIAL : EPI_RESID, st), "down gemm");
+      if (big) hip_check(launch_gemm_big(a, EPI_RESID, st), "down gemm");
+      else hip_check(launch_gemm<T>(a, a.S > 1 ? EPI_PARTIAL : EPI_RESID, st), "down gemm");
       prof_end(m, SSB_K_DOWN, st);
-      if (a.S > 1) {
+      if (a.S > 1 && !big) {
         prof_begin(m, SSB_K_REDUCE, st);
         hip_check(launch_resid_reduce<T>(a, st), "down reduce");
         prof_end(m, SSB_K_REDUCE, st);

@@ -542,6 +542,192 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-M GEMM for prefill and teacher-forced forwards (M >= 128 rows, bf16):
+// the same packed weight fragments and fused epilogues as k_gemm (QKV + RoPE +
+// KV write, residual + next norm input, SwiGLU), tiled for operand reuse.  A
+// workgroup of 4 waves (2 x 2) owns a (32 RT) x (32 CT) output block and walks
+// the whole K range in 32-wide steps.  Each step's fragments (2CT weight
+// fragments of 1 KiB, 2RT activation fragments of 1 KiB in MFMA operand
+// layout) go straight from global memory to LDS (16 B per lane), NS steps in
+// flight, one barrier per step; each wave multiplies its RT x CT 16x16 tiles
+// from LDS.  Used only for forwards without decode rows, so the row-count
+// independence of k_gemm is not needed here.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt immediate: vmcnt[3:0] and [15:14]; expcnt and lgkmcnt left at "no wait"
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane (lds_base is
+// wave-uniform; it goes through M0).  Issued as inline assembly so the compiler does not pair
+// every later LDS read with a wait for all outstanding loads; the caller waits with wait_vmcnt
+// and a barrier before reading the destination.
+__device__ __forceinline__ void load_lds16(const void* gptr, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(gptr)
+               : "memory", "m0");
+}
+
+template <int EPI, int RT, int CT, int NS>
+__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
+  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
+  constexpr int NF = 2 * CT + 2 * RT;      // 1 KiB fragments per step: weights first, then activations
+  constexpr int FPW = NF / 4;              // fragments each wave stages per step
+  constexpr int BM = 32 * RT;
+  static_assert(NF % 4 == 0 && NS >= 2, "tile shape");
+  extern __shared__ __align__(16) unsigned char smem[];   // [NS][NF][1 KiB], then 1/rms [BM]
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wr = wave / 2, wc = wave % 2;
+  const int tn0 = blockIdx.x * 2 * CT;     // first 16-column tile of the block
+  const int m0 = blockIdx.y * BM;          // first row of the block
+  const int ksteps = a.K / Ty<bf16_t>::kStepK;
+  float* s_inv = reinterpret_cast<float*>(smem + NS * NF * 1024);
+  const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)smem;   // LDS byte address of the staging area
+
+  // this wave's fragments of a step: f = wave + 4i; weights for f < 2CT, activations after
+  const uint4* src[FPW];
+  int stride[FPW];
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    const int f = wave + 4 * i;
+    if (f < 2 * CT) {
+      src[i] = a.W + (size_t)(tn0 + f) * ksteps * kWave + lane;
+      stride[i] = kWave;
+    } else {
+      const int row = min(m0 + 16 * (f - 2 * CT) + lane % 16, a.M - 1);   // rows past M: any valid row
+      src[i] = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.x) + (size_t)row * a.ldx +
+                                              (lane / 16) * 8);
+      stride[i] = Ty<bf16_t>::kStepK / 8;   // uint4 per 32 K
+    }
+  }
+  auto issue = [&](int s) {
+    const int ss = min(s, ksteps - 1);      // steps past the end reload the last one (never read)
+    const unsigned buf = lds0 + (s % NS) * NF * 1024;
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) load_lds16(src[i] + (size_t)ss * stride[i], buf + (wave + 4 * i) * 1024);
+  };
+
+  if constexpr (NORM) {
+    // 1/rms of the block's rows from the per-16-column sums of squares, two threads per row
+    const int r = threadIdx.x / 2, h2 = threadIdx.x % 2;
+    float sum = 0.f;
+    if (r < BM) {
+      const int m = min(m0 + r, a.M - 1);
+      const float* sp = a.ssq + (size_t)m * a.ssq_ld + h2 * (a.n_ssq / 2);
+      for (int k = 0; k < a.n_ssq / 2; ++k) sum += sp[k];
+    }
+    sum += __shfl_xor(sum, 1);
+    if (r < BM && h2 == 0) s_inv[r] = 1.0f / sqrtf(sum / (float)a.hidden + a.eps);
+  }
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  f32x4_t acc[CT][RT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[c][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < ksteps; ++s) {
+    wait_vmcnt<FPW * (NS - 2)>();           // this wave's fragments of step s have landed
+    __syncthreads();                        // everyone's have; everyone is done with step s - 1
+    issue(s + NS - 1);                      // into the buffer step s - 1 used
+    const unsigned char* buf = smem + (s % NS) * NF * 1024;
+    uint4 wf[CT], xf[RT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) wf[c] = *reinterpret_cast<const uint4*>(buf + (wc * CT + c) * 1024 + lane * 16);
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+      xf[r] = *reinterpret_cast<const uint4*>(buf + (2 * CT + wr * RT + r) * 1024 + lane * 16);
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) mma_step(acc[c][r], wf[c], xf[r], bf16_t());
+  }
+  wait_vmcnt<0>();
+
+  // epilogue: element i of lane l of tile (c, r) is row 16 r' + l%16, column 16 tg + 4(l/16) + i
+  const int q = lane / 16;
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int tg = tn0 + wc * CT + c;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int rl = 16 * (wr * RT + r) + lane % 16;     // row within the block
+      const int m = m0 + rl;
+      const bool ok = m < a.M;
+      const int mc = ok ? m : a.M - 1;
+      float z[4], zo[4];
+      if constexpr (EPI == EPI_QKV) {
+        const int hd = a.head_dim, half = hd / 2, tph = hd / 16;
+        const int hh = tg / tph, jj = tg % tph;
+        const int kind = hh < a.n_heads ? 0 : (hh < a.n_heads + a.n_kv ? 1 : 2);
+        const int head = kind == 0 ? hh : (kind == 1 ? hh - a.n_heads : hh - a.n_heads - a.n_kv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = acc[c][r][i] * s_inv[rl];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zo[i] = __shfl_xor(z[i], 32);   // the rotary partner column (c +- 8)
+        const int qq = q & 1;
+        {
+          bf16_t* dst;
+          if (kind == 0) {
+            dst = reinterpret_cast<bf16_t*>(a.q) + (size_t)mc * a.q_ld + head * hd;
+          } else {
+            const int sl = a.row_slot[mc];
+            const size_t base = (((size_t)a.layer * a.n_pages + sl / kPage) * 2 + (kind - 1)) * a.n_kv + head;
+            dst = reinterpret_cast<bf16_t*>(a.kv_pool) + (base * kPage + sl % kPage) * hd;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pr = 8 * jj + 4 * qq + i;                      // rotary pair index
+            const int dim = (q < 2 ? 0 : half) + pr;
+            float o = z[i];
+            if (kind != 2) {
+              const float2 cs = a.row_cs[(size_t)mc * half + pr];
+              o = q < 2 ? z[i] * cs.x - zo[i] * cs.y : z[i] * cs.x + zo[i] * cs.y;
+            }
+            if (ok) dst[dim] = f2bf(o);
+          }
+        }
+      } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = acc[c][r][i] * s_inv[rl];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zo[i] = __shfl_xor(z[i], 32);   // up (columns 8..15) for gate lanes
+        if (ok && q < 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            reinterpret_cast<bf16_t*>(a.act)[(size_t)m * a.act_ld + tg * 8 + 4 * q + i] = f2bf(silu_f(z[i]) * zo[i]);
+        }
+      } else {  // EPI_RESID
+        const int n0 = tg * 16 + 4 * q;
+        float sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = a.h[(size_t)mc * a.hidden + n0 + i] + acc[c][r][i];
+          z[i] = v;
+          sq += v * v;
+        }
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        if (ok) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a.h[(size_t)m * a.hidden + n0 + i] = z[i];
+            reinterpret_cast<bf16_t*>(a.xg_out)[(size_t)m * a.hidden + n0 + i] = f2bf(z[i] * a.gain_next[n0 + i]);
+          }
+          if (q == 0) a.ssq_out[(size_t)m * a.ssq_ld + tg] = sq;
+        }
+      }
+    }
+  }
+}
+
 // Residual update after a K-split GEMM: h += sum of the S partial sums (in
 // split order), then the next GEMM's input xg = h * gain_next and the
 // per-16-column sums of squares of h.  Grid (M, hidden / 64), 64 threads.
@@ -1303,6 +1489,39 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
 }
 template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
 template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
+
+template <int EPI, int RT, int CT, int NS>
+static hipError_t launch_gemm_big_cfg(const GemmArgs& a, hipStream_t st) {
+  constexpr int NF = 2 * CT + 2 * RT;
+  const dim3 grid(a.n_tiles / (2 * CT), (a.M + 32 * RT - 1) / (32 * RT));
+  const int shm = NS * NF * 1024 + 32 * RT * 4;
+  SSB_LAUNCH((k_gemm_big<EPI, RT, CT, NS>), grid, dim3(256), shm, st, a);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_gemm_big_epi(const GemmArgs& a, hipStream_t st) {
+  // the largest tile that still gives about one workgroup per CU
+  const int rb4 = (a.M + 127) / 128;
+  // (LDS: 4 steps of 16 KiB, 5 of 12 KiB, 8 of 8 KiB: two workgroups per CU; deeper pipelines
+  // with one workgroup per CU measured slower)
+  if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 4>(a, st);
+  if (a.n_tiles % 4 == 0 && (a.n_tiles / 4) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 2, 5>(a, st);
+  if (a.n_tiles % 4 == 0) return launch_gemm_big_cfg<EPI, 2, 2, 8>(a, st);
+  return hipErrorInvalidValue;
+}
+
+// Prefill / teacher-forced GEMM (bf16, M >= 1): epilogues QKV, RESID (no K split) and SWIGLU.
+hipError_t launch_gemm_big(const GemmArgs& a, int epi, hipStream_t st) {
+  if (a.M < 1 || a.K % Ty<bf16_t>::kStepK != 0 || a.n_tiles % 4 != 0) return hipErrorInvalidValue;
+  if ((epi == EPI_QKV || epi == EPI_SWIGLU) && (a.n_ssq % 2 != 0 || a.n_ssq < 2)) return hipErrorInvalidValue;
+  switch (epi) {
+    case EPI_QKV: return launch_gemm_big_epi<EPI_QKV>(a, st);
+    case EPI_RESID: return launch_gemm_big_epi<EPI_RESID>(a, st);
+    case EPI_SWIGLU: return launch_gemm_big_epi<EPI_SWIGLU>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 
 template <typename T>
