@@ -626,28 +626,40 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
     if (r < BM && h2 == 0) s_inv[r] = 1.0f / sqrtf(sum / (float)a.hidden + a.eps);
   }
 
+  // NS steps in flight; step s+1's operands are read from LDS into registers while step s
+  // multiplies (register double buffer), one barrier per step
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s);
+  for (int s = 0; s < NS; ++s) issue(s);
   f32x4_t acc[CT][RT];
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
     for (int r = 0; r < RT; ++r) acc[c][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ksteps; ++s) {
-    wait_vmcnt<FPW * (NS - 2)>();           // this wave's fragments of step s have landed
-    __syncthreads();                        // everyone's have; everyone is done with step s - 1
-    issue(s + NS - 1);                      // into the buffer step s - 1 used
+  auto rd = [&](int s, uint4* w, uint4* x) {
     const unsigned char* buf = smem + (s % NS) * NF * 1024;
-    uint4 wf[CT], xf[RT];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) wf[c] = *reinterpret_cast<const uint4*>(buf + (wc * CT + c) * 1024 + lane * 16);
+    for (int c = 0; c < CT; ++c) w[c] = *reinterpret_cast<const uint4*>(buf + (wc * CT + c) * 1024 + lane * 16);
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
-      xf[r] = *reinterpret_cast<const uint4*>(buf + (2 * CT + wr * RT + r) * 1024 + lane * 16);
+    for (int r = 0; r < RT; ++r) x[r] = *reinterpret_cast<const uint4*>(buf + (2 * CT + wr * RT + r) * 1024 + lane * 16);
+  };
+  uint4 wf[CT], xf[RT];
+  wait_vmcnt<FPW * (NS - 1)>();            // step 0 has landed
+  __syncthreads();
+  rd(0, wf, xf);
+  for (int s = 0; s < ksteps; ++s) {
+    wait_vmcnt<FPW * (NS - 2)>();          // step s+1 has landed (steps past the end reload the last)
+    __syncthreads();                       // and every wave holds step s in registers
+    issue(s + NS);                         // into step s's buffer
+    uint4 wn[CT], xn[RT];
+    rd(s + 1, wn, xn);
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int r = 0; r < RT; ++r) mma_step(acc[c][r], wf[c], xf[r], bf16_t());
+#pragma unroll
+    for (int c = 0; c < CT; ++c) wf[c] = wn[c];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) xf[r] = xn[r];
   }
   wait_vmcnt<0>();
 
@@ -1503,11 +1515,11 @@ template <int EPI>
 static hipError_t launch_gemm_big_epi(const GemmArgs& a, hipStream_t st) {
   // the largest tile that still gives about one workgroup per CU
   const int rb4 = (a.M + 127) / 128;
-  // (LDS: 4 steps of 16 KiB, 5 of 12 KiB, 8 of 8 KiB: two workgroups per CU; deeper pipelines
-  // with one workgroup per CU measured slower)
-  if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 4>(a, st);
-  if (a.n_tiles % 4 == 0 && (a.n_tiles / 4) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 2, 5>(a, st);
-  if (a.n_tiles % 4 == 0) return launch_gemm_big_cfg<EPI, 2, 2, 8>(a, st);
+  // (LDS: 3 steps of 16 KiB, 4 of 12 KiB, 6 of 8 KiB: two or three workgroups per CU; deeper
+  // pipelines with one workgroup per CU measured slower)
+  if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3>(a, st);
+  if (a.n_tiles % 4 == 0 && (a.n_tiles / 4) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 2, 4>(a, st);
+  if (a.n_tiles % 4 == 0) return launch_gemm_big_cfg<EPI, 2, 2, 6>(a, st);
   return hipErrorInvalidValue;
 }
 

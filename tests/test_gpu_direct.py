@@ -213,3 +213,53 @@ def test_multistep_decode_is_gpu_ar_and_matches_oracle(tiny):
             checked += 1
         kv.close()
     assert checked >= 6
+
+
+def test_error_paths_of_the_decoding_modes(tiny):
+    """Bad arguments of the direct-diffusion, stochastic and draft-schedule calls fail with a
+    code and leave the committed state unchanged."""
+    from self_speculative_block_amd import SsbError, SSB_EINVAL, SSB_ENOKV, SSB_ESTATE
+    from self_speculative_block_amd.engine import KV, ar_step_batch, serve
+    from self_speculative_block_amd._lib import SSB_SERVE_SPEC
+    wl, cfg, w, model, pool, orc = tiny
+    B = wl.block
+    pre = model.prefix_tensor(prefix_embeddings(wl.wid, 0, wl.prefix_len, cfg.hidden))
+    kv = _kv(pool)
+
+    def code(fn):
+        with pytest.raises(SsbError) as e:
+            fn()
+        return e.value.code
+
+    u = torch.rand(2 * B + 2, device="cuda")
+    assert code(lambda: kv.dd_block(B, 0.5)) == SSB_ESTATE          # no prefill yet
+    assert code(lambda: kv.round_sample(B, u)) == SSB_ESTATE
+    assert code(lambda: kv.round_multistep(B, 2, 0.5)) == SSB_ESTATE
+    kv.prefill(pre)
+    st0 = kv.state()
+    assert code(lambda: kv.dd_block(0, 0.5)) == SSB_EINVAL
+    assert code(lambda: kv.dd_block(B + 1, 0.5)) == SSB_EINVAL
+    assert code(lambda: kv.dd_block(B, float("nan"))) == SSB_EINVAL
+    assert code(lambda: kv.dd_block(B, 0.5, max_commit=0)) == SSB_EINVAL
+    assert code(lambda: kv.round_sample(B, u, temperature=0.0)) == SSB_EINVAL
+    assert code(lambda: kv.round_sample(B, u, temperature=float("inf"))) == SSB_EINVAL
+    assert code(lambda: kv.round_sample(B, None)) == SSB_EINVAL
+    assert code(lambda: kv.round_multistep(B, 0, 0.5)) == SSB_EINVAL
+    assert code(lambda: kv.round_multistep(0, 1, 0.5)) == SSB_EINVAL
+    assert code(lambda: kv.decode_sample(pre, B, 40, torch.rand((1, 2 * B + 2), device="cuda"))) == SSB_ESTATE
+    assert kv.state() == st0
+    # the sampling decode runs out of uniforms: an error, not a read past the array
+    kv.reset()
+    assert code(lambda: kv.decode_sample(pre, B, 40, torch.rand((1, 2 * B + 2), device="cuda"))) == SSB_EINVAL
+    kv.close()
+    small = KV(pool, wl.prefix_len + 4)
+    small.prefill(pre)
+    assert code(lambda: small.dd_block(B, 0.5)) == SSB_ENOKV
+    assert code(lambda: small.round_multistep(B, 2, 0.5)) == SSB_ENOKV
+    assert small.state()[0] == wl.prefix_len
+    assert code(lambda: ar_step_batch(model, [small, small])) == SSB_EINVAL   # the same kv twice
+    small.close()
+    reqs = [{"prefix_dev": pre, "max_len": 10}]
+    assert code(lambda: serve(model, pool, reqs, 0, SSB_SERVE_SPEC, B=B)) == SSB_EINVAL
+    assert code(lambda: serve(model, pool, reqs, 2, 7, B=B)) == SSB_EINVAL
+    assert code(lambda: serve(model, pool, reqs, 2, SSB_SERVE_SPEC, B=B, max_tokens=wl.prefix_len + 4)) == SSB_EINVAL
