@@ -97,45 +97,97 @@ def event_pair_overhead_us(torch, n=200):
     return statistics.median(vals)
 
 
-def cpu_baseline(cfg, weights, prefix, planted_rows, B, committed_per_round, target_s=15.0):
-    """The oracle (float64 numpy) timed on the host on a bounded sample of the same rounds.
+class no_gc:
+    """Collect garbage before a timed loop and keep the collector off during it (as timeit does):
+    a full collection over the heap of torch and numpy takes tens of milliseconds and would land
+    on one arbitrary round."""
+
+    def __enter__(self):
+        import gc
+        gc.collect()
+        self.was = gc.isenabled()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        import gc
+        if self.was:
+            gc.enable()
+        return False
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, weights, prefix, planted_rows, B, committed_per_round, reps=10, budget_s=12.0):
+    """The oracle timed on the host on a bounded sample of the same rounds: numpy in float32 on
+    every BLAS thread (the reported value), then float32 on one thread and float64 (the parity
+    reference) as side notes.
 
     Each timed call is one full round (draft forward, verify forward, accept, rollback) from the
-    same state with the same planted drafts as the GPU's rounds.  The drafts are planted from the
-    GPU's AR continuation; where the float64 oracle's own greedy path departs from it at a near-tie
-    the oracle accepts fewer of them, although it does the same work per round.  So the oracle's
-    rate is stated in rounds/s and converted to tokens/s with the committed tokens per round of
-    the GPU line (the planted schedule); the oracle's own committed count is reported beside it.
+    same state with the same planted drafts as the GPU's rounds; the rate is the median over up
+    to ``reps`` rounds (fewer if ``budget_s`` of CPU time runs out first).  The drafts are planted
+    from the GPU's AR continuation; where the oracle's own greedy path departs from it at a
+    near-tie the oracle accepts fewer of them, although it does the same work per round.  So the
+    oracle's rate is stated in rounds/s and converted to tokens/s with the committed tokens per
+    round of the GPU line (the planted schedule); the oracle's own committed count is reported
+    beside it.
     """
     import numpy as np
     from oracle import Decoder, prefill, spec_round
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
+        threadpool_limits = None
         cores = os.cpu_count()
-    model = Decoder(cfg, weights)
+
     P = prefix.shape[0]
-    st, y1, _ = prefill(model, prefix, P + B + 4)
-    committed = 0
-    t_total = 0.0
-    rounds = 0
-    for planted in planted_rows:
-        st.n, st.x0 = P, y1
-        t0 = time.perf_counter()
-        r = spec_round(model, st, B, planted=[int(x) for x in planted])
-        t_total += time.perf_counter() - t0
-        committed += len(r.committed)
-        rounds += 1
-        if t_total >= target_s and rounds >= 3:
-            break
-    rps = rounds / t_total
-    return {"value": rps * committed_per_round, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "rounds_per_s": rps,
-            "sample": f"{rounds} rounds of the round microbenchmark (float64 numpy oracle, n=1280, B=32, "
-                      f"same states and planted drafts), {t_total:.1f} s of CPU time, prefill excluded; "
-                      f"tokens/s = rounds/s x {committed_per_round:.2f} committed tokens per round of the "
-                      f"planted schedule (the oracle itself committed {committed / rounds:.2f} per round)"}
+
+    def setup(dtype):
+        model = Decoder(cfg, weights, dtype=dtype)
+        st, y1, _ = prefill(model, np.asarray(prefix, dtype=dtype), P + B + 4)
+        return model, st, y1
+
+    def timed(setup_out, n_reps, budget):
+        model, st, y1 = setup_out
+        times, committed = [], 0
+        for planted in planted_rows[:n_reps]:
+            st.n, st.x0 = P, y1
+            t0 = time.perf_counter()
+            r = spec_round(model, st, B, planted=[int(x) for x in planted])
+            times.append(time.perf_counter() - t0)
+            committed += len(r.committed)
+            if sum(times) >= budget:
+                break
+        return len(times), statistics.median(times), committed / len(times)
+
+    f32 = setup(np.float32)
+    n32, t32, c32 = timed(f32, reps, budget_s)
+    out = {"value": committed_per_round / t32, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "cpu": host_cpu_model(), "rounds_per_s": 1.0 / t32}
+    note = ""
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            n1, t1, _ = timed(f32, 3, budget_s / 3)
+        out["rounds_per_s_1core"] = 1.0 / t1
+        note += f"; float32 on 1 thread: median of {n1} rounds {t1:.2f} s"
+    del f32
+    n64, t64, _ = timed(setup(np.float64), 3, budget_s / 3)
+    out["rounds_per_s_float64"] = 1.0 / t64
+    note += f"; float64 on {cores} threads: median of {n64} rounds {t64:.2f} s"
+    out["sample"] = (f"median of {n32} rounds of the round microbenchmark (numpy float32 oracle on {cores} "
+                     f"threads, n=1280, B=32, same states and planted drafts), {t32:.2f} s per round, prefill "
+                     f"excluded; tokens/s = rounds/s x {committed_per_round:.2f} committed tokens per round of "
+                     f"the planted schedule (the oracle itself committed {c32:.2f} per round)" + note)
+    return out
 
 
 def plant_rows(cont, c, astar, B, vocab):
@@ -249,20 +301,21 @@ def batched_workload(args):
         rounds = [0] * R
         n_launch = 0
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        while True:
-            act = [r for r in range(R) if len(outs[r]) < lengths[r] and outs[r][-1] != cfg.eos_id]
-            if not act:
-                break
-            rows = [plant_rows(ars[r], len(outs[r]), int(astars[r][rounds[r]]), B, cfg.vocab) for r in act]
-            planted = torch.tensor(rows, dtype=torch.int32, device="cuda")
-            res = round_batch(model, [kvs[r] for r in act], B, [lengths[r] - len(outs[r]) for r in act],
-                              planted_dev=planted)
-            for r, (c, _A) in zip(act, res):
-                outs[r] += c
-                rounds[r] += 1
-            n_launch += 1
-        t = time.perf_counter() - t0
+        with no_gc():
+            t0 = time.perf_counter()
+            while True:
+                act = [r for r in range(R) if len(outs[r]) < lengths[r] and outs[r][-1] != cfg.eos_id]
+                if not act:
+                    break
+                rows = [plant_rows(ars[r], len(outs[r]), int(astars[r][rounds[r]]), B, cfg.vocab) for r in act]
+                planted = torch.tensor(rows, dtype=torch.int32, device="cuda")
+                res = round_batch(model, [kvs[r] for r in act], B, [lengths[r] - len(outs[r]) for r in act],
+                                  planted_dev=planted)
+                for r, (c, _A) in zip(act, res):
+                    outs[r] += c
+                    rounds[r] += 1
+                n_launch += 1
+            t = time.perf_counter() - t0
         for r in range(R):
             assert outs[r] == ars[r], f"request {r}: batched self-speculative output differs from AR"
         toks = sum(len(o) - 1 for o in outs)
@@ -622,20 +675,21 @@ def main():
     per_round = []
     events = []
     st = torch.cuda.current_stream()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        ts = time.perf_counter()
-        e0.record(st)
-        n, A = run(args.warmup + k)
-        e1.record(st)
-        per_round.append(time.perf_counter() - ts)
-        events.append((e0, e1))
-        committed += n
-        accepts.append(A)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with no_gc():
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            ts = time.perf_counter()
+            e0.record(st)
+            n, A = run(args.warmup + k)
+            e1.record(st)
+            per_round.append(time.perf_counter() - ts)
+            events.append((e0, e1))
+            committed += n
+            accepts.append(A)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     dev_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in events)
 
     # rounds without planting (the draft's own proposals), same state
@@ -714,6 +768,8 @@ def main():
                    "cached_positions": P, "batch": 1, "mean_accept": float(np.mean(accepts)),
                    "committed_per_round": committed / args.steps},
         "round_us_median": t_med * 1e6,
+        "round_us_wall": {"p90": sorted(per_round)[len(per_round) * 9 // 10] * 1e6, "max": max(per_round) * 1e6,
+                          "mean": elapsed / args.steps * 1e6},
         "round_device_us": {"median": statistics.median(dev_us), "p10": dev_us[len(dev_us) // 10],
                             "p90": dev_us[(len(dev_us) * 9) // 10]},
         "round_us_unplanted_median": statistics.median(unplanted) * 1e6,
