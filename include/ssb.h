@@ -198,10 +198,14 @@ int ssb_decode_ar(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int m
 /* R <= SSB_MAX_BATCH concurrent requests, one launch per stage. Each
  * request has its own kv, state, budget and page table. Every kv needs a
  * boundary token (prefilled). planted_dev: nullable device [R][B].
- * committed: host [R][B+2]. n_committed, accept_len: host [R]. */
+ * committed: host [R][B+2]. n_committed, accept_len: host [R].
+ * draft_logits_dev, verify_logits_dev: nullable, fp32 [R*(B+1)][vocab],
+ * request r's window rows at r*(B+1) .. r*(B+1)+B (the round then runs
+ * without graph replay). A request's results, logits included, are bit-identical
+ * to those of its own single round. */
 int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_t* max_commit,
                     const int32_t* planted_dev, int32_t* committed, int32_t* n_committed,
-                    int32_t* accept_len, void* stream);
+                    int32_t* accept_len, float* draft_logits_dev, float* verify_logits_dev, void* stream);
 
 /* Stochastic self-speculative round (GravityOCR review, section 2
  * "Speculative Decoding"; Trillion Labs blog, the speculative rejection rule

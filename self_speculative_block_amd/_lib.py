@@ -78,7 +78,7 @@ SIGNATURES = {
     "ssb_decode_ar": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, P_i32, P_i32,
                               ctypes.POINTER(SsbStats), c_void_p]),
     "ssb_round_batch": (c_int, [c_void_p, ctypes.POINTER(c_void_p), c_int, c_int, P_i32, c_void_p, P_i32,
-                                P_i32, P_i32, c_void_p]),
+                                P_i32, P_i32, c_void_p, c_void_p, c_void_p]),
     "ssb_round_sample": (c_int, [c_void_p, c_void_p, c_int, c_int, c_float, c_void_p, P_i32, P_i32, P_i32,
                                  c_void_p, c_void_p, c_void_p]),
     "ssb_decode_sample": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_float, c_int, c_void_p, c_int,

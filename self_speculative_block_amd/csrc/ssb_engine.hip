@@ -771,7 +771,6 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
   if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
   if (B < 0 || B > c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
   if (R * (B + 1) > c.max_rows) fail(SSB_EINVAL, "R*(B+1) exceeds max_rows");
-  if ((dlog || vlog) && R != 1) fail(SSB_EINVAL, "logits output needs R == 1");
   ssb_pool* pool = kvs[0]->pool;
   for (int r = 0; r < R; ++r) {
     check_model_kv(m, kvs[r]);
@@ -1517,7 +1516,7 @@ int ssb_decode_ar(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P, int m
 
 int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_t* max_commit,
                     const int32_t* planted_dev, int32_t* committed, int32_t* n_committed, int32_t* accept_len,
-                    void* stream) {
+                    float* draft_logits_dev, float* verify_logits_dev, void* stream) {
   return guard([&] {
     if (!m || !kvs || !max_commit) fail(SSB_EINVAL, "null argument");
     if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
@@ -1525,8 +1524,8 @@ int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_
       if (!kvs[r]) fail(SSB_EINVAL, "null kv in batch");
     std::vector<RoundOut> ro(R);
     std::vector<int> mc(max_commit, max_commit + R);
-    round_impl(m, kvs, R, B, mc.data(), planted_dev, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-               ro.data(), S(stream));
+    round_impl(m, kvs, R, B, mc.data(), planted_dev, nullptr, nullptr, nullptr, nullptr, draft_logits_dev,
+               verify_logits_dev, ro.data(), S(stream));
     for (int r = 0; r < R; ++r) {
       if (committed) std::memcpy(committed + (size_t)r * (B + 2), ro[r].tok, (size_t)ro[r].n * 4);
       if (n_committed) n_committed[r] = ro[r].n;

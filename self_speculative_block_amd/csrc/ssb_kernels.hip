@@ -173,7 +173,10 @@ __device__ __forceinline__ Top2 merge_top2(Top2 a, Top2 b) {
 // ---------------------------------------------------------------------------
 // GEMM with fused epilogues:  out[m][n] = sum_k X[m][k] W[n][k].
 // Grid (n_tiles / NT, S, m_blocks).  A workgroup owns NT 16-column tiles for
-// 16*MT rows and one of S equal K ranges; it has NT*KSL waves.  Wave
+// 16*MT rows and one of S equal K ranges; it has NT*KSL waves.  With many rows
+// (a batched round) the looped form runs one workgroup per tile group over a
+// stride of row blocks, keeping its weight fragments in registers; each row
+// block goes through exactly the per-element operations of the one-block form.  Wave
 // w = t*KSL + j reduces K steps [j*KPW, (j+1)*KPW) of the range for tile t
 // with an MFMA chain in K order.  The workgroup issues every global load it
 // needs before its first MFMA: the weight fragments of each wave, the
@@ -188,7 +191,10 @@ __device__ __forceinline__ Top2 merge_top2(Top2 a, Top2 b) {
 // by 1/rms(h), rms from the per-16-column sums of squares added in column
 // order (review section 3.1: both modes share these layers).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+__device__ __forceinline__ float silu_f(float g) {
+#pragma clang fp contract(off)
+  return g / (1.0f + expf(-g));
+}
 
 // Sum over aligned groups of g lanes (g a power of two, 1..64), result in every lane of the
 // group.  Steps: swap within pairs, within quads (DPP quad permutes), mirror within 8 and 16
@@ -221,6 +227,7 @@ __device__ __forceinline__ float lane_group_sum(float v, int g) {
 template <typename T, int MB>
 __device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, const float* s_pre, int tg, int NT,
                                                int m_base) {
+#pragma clang fp contract(off)
   const float* s_h = s_pre;
   const float* s_g = s_pre + NT * MB * 16;
   for (int e = threadIdx.x; e < NT * MB * 16; e += kGemmThreads) {
@@ -246,8 +253,11 @@ __device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, 
   }
 }
 
-template <typename T, int MT, int EPI, int KPW>
+template <typename T, int MT, int EPI, int KPW, bool MLOOP>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
+  // No multiply-add contraction anywhere in this kernel: both of its forms (one row block per
+  // workgroup, or several) then compute exactly the written operations for every row.
+#pragma clang fp contract(off)
   constexpr int KS = Ty<T>::kStepK;
   constexpr int PER = Ty<T>::kPerFrag;
   constexpr int MB = MT * 16;
@@ -264,14 +274,20 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   float* ctile = reinterpret_cast<float*>(smem + L.ctile);
   __shared__ float s_inv[MB];
 
-  constexpr bool LOOP = (EPI == EPI_LOGITS);         // LM head: persistent over tile groups
+  // Single-block form: one row block (blockIdx.z); the LM head's workgroups are persistent over
+  // tile groups.  Looped form (MLOOP): one tile group per workgroup, which keeps its weight
+  // fragments in registers and walks the row blocks blockIdx.z, blockIdx.z + gridDim.z, ...,
+  // loading the next block's slab while the current one is multiplied.
+  constexpr bool LOOP = (EPI == EPI_LOGITS) && !MLOOP;
   int tg = blockIdx.x;
   const int split = blockIdx.y;
-  const int m_base = blockIdx.z * MB;
+  int mb = blockIdx.z;
+  int m_base = mb * MB;
+  const int m_blocks = (a.M + MB - 1) / MB;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const bool cwave = wave < NT * KSL;               // waves past NT*KSL only help with loads
   const int ksl = wave % KSL;
-  const int tile = tg * NT + (cwave ? wave / KSL : 0);
+  const int tsub = cwave ? wave / KSL : 0;
   const int ksteps = a.K / KS;
   const int kstep0 = split * (KSL * KPW) + ksl * KPW;
   const int m_last = a.M - 1;
@@ -280,7 +296,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   // 1. this wave's weight fragments (HBM)
   uint4 wf[KPW];
   {
-    const uint4* wp = a.W + ((size_t)tile * ksteps + kstep0) * kWave + lane;
+    const uint4* wp = a.W + ((size_t)(tg * NT + tsub) * ksteps + kstep0) * kWave + lane;
 #pragma unroll
     for (int s = 0; s < KPW; ++s) wf[s] = wp[(size_t)s * kWave];
   }
@@ -293,89 +309,115 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0, a.M * a.ldx * (int)sizeof(T), kBufWord3);
   uint4 xs[SB];
+  auto load_slab = [&](int mbase) {
 #pragma unroll
-  for (int b = 0; b < SB; ++b) {
-    const int e = min((int)threadIdx.x + b * NTH, total - 1);
-    const int off = ((m_base + (e >> fsh)) * a.ldx + split * KR + (e & (FPR - 1)) * PER) * (int)sizeof(T);
-    xs[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-  }
+    for (int b = 0; b < SB; ++b) {
+      const int e = min((int)threadIdx.x + b * NTH, total - 1);
+      const int off = ((mbase + (e >> fsh)) * a.ldx + split * KR + (e & (FPR - 1)) * PER) * (int)sizeof(T);
+      xs[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    }
+  };
+  load_slab(m_base);
   // 3. norm partials: G = n_ssq/4 lanes per row, one float4 each, up to 3 passes of rows
   constexpr int NPASS = 3;
   float4 sv[NPASS];
   const int G = a.n_ssq / 4, gsh = 31 - __builtin_clz(G), RP = NTH >> gsh;   // G is a power of two
-  if constexpr (NORM) {
-    const __amdgpu_buffer_rsrc_t sr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.ssq), (short)0, a.M * a.ssq_ld * 4, kBufWord3);
+  const __amdgpu_buffer_rsrc_t sr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.ssq), (short)0, a.M * a.ssq_ld * 4, kBufWord3);
+  auto load_norm = [&](int mbase, float4 (&dst)[NPASS]) {
 #pragma unroll
     for (int k = 0; k < NPASS; ++k) {
       const int row = min(k * RP + ((int)threadIdx.x >> gsh), MB - 1);
-      const int off = ((m_base + row) * a.ssq_ld + ((int)threadIdx.x & (G - 1)) * 4) * 4;
-      sv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+      const int off = ((mbase + row) * a.ssq_ld + ((int)threadIdx.x & (G - 1)) * 4) * 4;
+      dst[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
     }
-  }
+  };
+  if constexpr (NORM) load_norm(m_base, sv);
   // 4. epilogue inputs that do not depend on the product
   float2 pcs = make_float2(0.f, 0.f);
   int pslot = 0;
   float ph[2] = {0.f, 0.f}, pg = 0.f;
-  if constexpr (EPI == EPI_QKV) {   // NT == 1: rotary pairs 8jj..8jj+7 of this tile's head
-    const int half = a.head_dim / 2, jj = tg % (a.head_dim / 16);
-    const int m = min(m_base + min((int)threadIdx.x / 8, MB - 1), m_last);
-    pcs = a.row_cs[(size_t)m * half + 8 * jj + threadIdx.x % 8];
-    pslot = a.row_slot[min(m_base + min((int)threadIdx.x, MB - 1), m_last)];
-  }
-  if constexpr (EPI == EPI_RESID) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int e = min((int)threadIdx.x + b * NTH, NT * MB * 16 - 1);
-      const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
-      ph[b] = a.h[(size_t)min(m_base + r, m_last) * a.hidden + (tg * NT + t) * 16 + n];
+  auto load_epi = [&](int mbase) {
+    if constexpr (EPI == EPI_QKV) {   // NT == 1: rotary pairs 8jj..8jj+7 of this tile's head
+      const int half = a.head_dim / 2, jj = tg % (a.head_dim / 16);
+      const int m = min(mbase + min((int)threadIdx.x / 8, MB - 1), m_last);
+      pcs = a.row_cs[(size_t)m * half + 8 * jj + threadIdx.x % 8];
+      pslot = a.row_slot[min(mbase + min((int)threadIdx.x, MB - 1), m_last)];
     }
-    pg = a.gain_next[tg * NT * 16 + min((int)threadIdx.x, NT * 16 - 1)];
+    if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int e = min((int)threadIdx.x + b * NTH, NT * MB * 16 - 1);
+        const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
+        ph[b] = a.h[(size_t)min(mbase + r, m_last) * a.hidden + (tg * NT + t) * 16 + n];
+      }
+      pg = a.gain_next[tg * NT * 16 + min((int)threadIdx.x, NT * 16 - 1)];
+    }
+  };
+  load_epi(m_base);
+
+  // ---- stores to LDS: the slab and the epilogue inputs of row block m_base ----
+  auto stage = [&]() {
+#pragma unroll
+    for (int b = 0; b < SB; ++b) {
+      const int e = threadIdx.x + b * NTH;
+      if (e < total) *reinterpret_cast<uint4*>(slab + (e >> fsh) * XSTR + (e & (FPR - 1)) * 16) = xs[b];
+    }
+    for (int e = threadIdx.x + SB * NTH; e < total; e += NTH) {   // K ranges above SB*NTH fragments
+      const int r = e >> fsh, q = e & (FPR - 1);
+      *reinterpret_cast<uint4*>(slab + r * XSTR + q * 16) =
+          m_base + r <= m_last ? *reinterpret_cast<const uint4*>(xb + (size_t)(m_base + r) * a.ldx + q * PER)
+                               : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (EPI == EPI_QKV) {
+      float2* s_cs = reinterpret_cast<float2*>(smem + L.pre);
+      int* s_slot = reinterpret_cast<int*>(smem + L.pre + MB * 8 * 8);
+      if (threadIdx.x < MB * 8) s_cs[threadIdx.x] = pcs;
+      if (threadIdx.x < MB) s_slot[threadIdx.x] = pslot;
+    }
+    if constexpr (EPI == EPI_RESID) {
+      float* s_h = reinterpret_cast<float*>(smem + L.pre);
+      float* s_g = s_h + NT * MB * 16;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        if (threadIdx.x + b * NTH < NT * MB * 16) s_h[threadIdx.x + b * NTH] = ph[b];
+      if (threadIdx.x < NT * 16) s_g[threadIdx.x] = pg;
+    }
+  };
+  if constexpr (!MLOOP) {
+    stage();
+    __syncthreads();
   }
 
-  // ---- stores to LDS ----
-#pragma unroll
-  for (int b = 0; b < SB; ++b) {
-    const int e = threadIdx.x + b * NTH;
-    if (e < total) *reinterpret_cast<uint4*>(slab + (e >> fsh) * XSTR + (e & (FPR - 1)) * 16) = xs[b];
-  }
-  for (int e = threadIdx.x + SB * NTH; e < total; e += NTH) {   // K ranges above SB*NTH fragments
-    const int r = e >> fsh, q = e & (FPR - 1);
-    *reinterpret_cast<uint4*>(slab + r * XSTR + q * 16) =
-        m_base + r <= m_last ? *reinterpret_cast<const uint4*>(xb + (size_t)(m_base + r) * a.ldx + q * PER)
-                             : make_uint4(0, 0, 0, 0);
-  }
-  if constexpr (EPI == EPI_QKV) {
-    float2* s_cs = reinterpret_cast<float2*>(smem + L.pre);
-    int* s_slot = reinterpret_cast<int*>(smem + L.pre + MB * 8 * 8);
-    if (threadIdx.x < MB * 8) s_cs[threadIdx.x] = pcs;
-    if (threadIdx.x < MB) s_slot[threadIdx.x] = pslot;
-  }
-  if constexpr (EPI == EPI_RESID) {
-    float* s_h = reinterpret_cast<float*>(smem + L.pre);
-    float* s_g = s_h + NT * MB * 16;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-      if (threadIdx.x + b * NTH < NT * MB * 16) s_h[threadIdx.x + b * NTH] = ph[b];
-    if (threadIdx.x < NT * 16) s_g[threadIdx.x] = pg;
-  }
-  __syncthreads();
-
-  // The LM head's workgroups stay resident: the slab and 1/rms are staged once, then each
-  // workgroup walks its tile groups (stride gridDim.x), loading the next group's weights while
-  // the current one is multiplied and reduced.  Every other GEMM runs the body once.
+  // The LM head's single-block workgroups stage the slab and 1/rms once, then walk their tile
+  // groups (stride gridDim.x), loading the next group's weights while the current one is
+  // multiplied and reduced.  The looped form stages each row block in turn.  Every other GEMM
+  // runs the body once.
   const int n_groups = a.n_tiles / NT;
   bool first = true;
+  float4 svn[NPASS];
   for (;;) {
-  const int tg_next = tg + (int)gridDim.x;
-  const bool more = LOOP && tg_next < n_groups;
+  int tg_next = tg + (int)gridDim.x;
+  bool more = LOOP && tg_next < n_groups;
   uint4 wn[KPW];
   if constexpr (LOOP) {
     // branch-free: past the last group, the current group's lines are read again (L2 hits)
     const int tg_load = more ? tg_next : tg;
-    const uint4* wp = a.W + ((size_t)(tg_load * NT + (cwave ? wave / KSL : 0)) * ksteps + kstep0) * kWave + lane;
+    const uint4* wp = a.W + ((size_t)(tg_load * NT + tsub) * ksteps + kstep0) * kWave + lane;
 #pragma unroll
     for (int s = 0; s < KPW; ++s) wn[s] = wp[(size_t)s * kWave];
+  }
+  int mb_next = mb;
+  if constexpr (MLOOP) {
+    stage();
+    __syncthreads();
+    // branch-free: after the last row block, the current block's lines are read again (L2 hits)
+    mb_next = mb + (int)gridDim.z;
+    more = mb_next < m_blocks;
+    const int mb_load = more ? mb_next : mb;
+    load_slab(mb_load * MB);
+    if constexpr (NORM) load_norm(mb_load * MB, svn);
+    load_epi(mb_load * MB);
   }
   // 5. MFMA chain over this wave's K steps
   f32x4_t acc[MT];
@@ -392,7 +434,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       }
     }
   }
-  if (NORM && first) {
+  if (NORM && (first || MLOOP)) {
     // 1/rms of each row (needed only by the epilogue, so it runs behind the MFMA chain): each
     // lane adds its 4 partials in column order, then a fixed butterfly over the row's G lanes
 #pragma unroll
@@ -534,11 +576,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
     }
   }
   if (!more) break;
-  tg = tg_next;
+  if constexpr (LOOP) {
+    tg = tg_next;
 #pragma unroll
-  for (int s = 0; s < KPW; ++s) wf[s] = wn[s];
+    for (int s = 0; s < KPW; ++s) wf[s] = wn[s];
+  }
+  if constexpr (MLOOP) {
+    mb = mb_next;
+    m_base = mb * MB;
+#pragma unroll
+    for (int k = 0; k < NPASS; ++k) sv[k] = svn[k];
+  }
   first = false;
-  __syncthreads();   // red and ctile are reused by the next group
+  __syncthreads();   // red, ctile, the slab and the staged inputs are reused by the next item
   }
 }
 
@@ -1438,12 +1488,26 @@ static hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
   const GemmLds L = gemm_lds(MT, KR * (int)sizeof(T), a.NT, a.KSL, a.n_ssq, EPI);
   const int m_blocks = (a.M + 16 * MT - 1) / (16 * MT);
   int gx = a.n_tiles / a.NT;
+  if constexpr (MT == 3) {
+    if (m_blocks >= 5) {
+      // many row blocks: one tile group per workgroup, which walks gz-strided row blocks with
+      // its weights held in registers.  One such workgroup fits a CU (LDS and registers), so
+      // the grid stays within one workgroup per CU, with at least two row blocks each.  (With
+      // up to 3 row blocks the parallel grid measured faster; from 5 the loop wins, by 6% at
+      // 198 rows, 13-15% at 264-528 and 18% at 1040.)
+      const int want = kGemmPersistentWgs / (gx * a.S);
+      const int gz = max(1, min(want, m_blocks / 2));
+      const dim3 grid(gx, a.S, gz), block(kGemmThreads);
+      SSB_LAUNCH((k_gemm<T, MT, EPI, KPW, true>), grid, block, L.total, st, a);
+      return hipGetLastError();
+    }
+  }
   if (EPI == EPI_LOGITS) {           // persistent: about one workgroup per CU, equal group counts
     const int per = (gx + kGemmPersistentWgs - 1) / kGemmPersistentWgs;
     gx = (gx + per - 1) / per;
   }
   const dim3 grid(gx, a.S, m_blocks), block(kGemmThreads);
-  SSB_LAUNCH((k_gemm<T, MT, EPI, KPW>), grid, block, L.total, st, a);
+  SSB_LAUNCH((k_gemm<T, MT, EPI, KPW, false>), grid, block, L.total, st, a);
   return hipGetLastError();
 }
 

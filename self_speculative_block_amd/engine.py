@@ -310,16 +310,24 @@ class KV:
         return list(out[: n.value]), st
 
 
-def round_batch(model, kvs, B, max_commit, planted_dev=None):
-    """One batched round over R requests; returns [(committed, A)] per request."""
+def round_batch(model, kvs, B, max_commit, planted_dev=None, want_logits=False):
+    """One batched round over R requests; returns [(committed, A)] per request, and with
+    want_logits also the draft and verify logits [R*(B+1), vocab] (request-major rows)."""
     R = len(kvs)
     hs = (ctypes.c_void_p * R)(*[kv.h.value for kv in kvs])
     mc = (ctypes.c_int32 * R)(*[int(x) for x in max_commit])
     out = _i32(R * (B + 2))
     n = _i32(R)
     A = _i32(R)
-    L.check(model.lib.ssb_round_batch(model.h, hs, R, B, mc, _ptr(planted_dev), out, n, A, _stream()))
-    return [(list(out[r * (B + 2): r * (B + 2) + n[r]]), A[r]) for r in range(R)]
+    dl = vl = None
+    if want_logits:
+        shape = (R * (B + 1), model.cfg.vocab)
+        dl = torch.empty(shape, dtype=torch.float32, device=model.device)
+        vl = torch.empty(shape, dtype=torch.float32, device=model.device)
+    L.check(model.lib.ssb_round_batch(model.h, hs, R, B, mc, _ptr(planted_dev), out, n, A, _ptr(dl), _ptr(vl),
+                                      _stream()))
+    res = [(list(out[r * (B + 2): r * (B + 2) + n[r]]), A[r]) for r in range(R)]
+    return (res, dl, vl) if want_logits else res
 
 
 def ar_step_batch(model, kvs):

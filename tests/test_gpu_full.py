@@ -162,14 +162,16 @@ def test_spec_decode_equals_ar_decode_and_oracle(full):
     assert kv.prefill(pre_dev) == full["y1"]
 
 
-@pytest.mark.parametrize("Bb", [32, 64])
-def test_batched_round_equals_single_rounds(full, Bb):
-    """A ragged batched round (four requests of different lengths, one launch per stage)
-    gives each request exactly what its own single round gives."""
+@pytest.mark.parametrize("Bb,R", [(32, 4), (32, 8), (64, 4)])
+def test_batched_round_equals_single_rounds(full, Bb, R):
+    """A ragged batched round (R requests of different lengths, one launch per stage) gives each
+    request exactly what its own single round gives: tokens, accept length and state, and its
+    draft and verify logits bit for bit.  132 rows run the GEMMs' parallel grid; 260 and 264 rows
+    the looped form (several 48-row blocks per workgroup)."""
     from self_speculative_block_amd.engine import KV, round_batch
     cfg, model, pool = full["cfg"], full["model"], full["pool"]
     wl5 = workload(5)
-    lens = [1088, 1000, 1100, 1200]
+    lens = [1088, 1000, 1100, 1200] if R == 4 else [600, 520, 700, 650, 480, 560, 610, 530]
     kvs, firsts, conts = [], [], []
     for i, P in enumerate(lens):
         pre = prefix_embeddings(wl5.wid, i, P, cfg.hidden)
@@ -183,19 +185,27 @@ def test_batched_round_equals_single_rounds(full, Bb):
         kvs.append(kv)
         firsts.append(y)
         conts.append(c)
-    astars = [0, Bb // 2, Bb, 3]
-    budgets = [Bb + 2, Bb + 2, 5, Bb + 2]
-    plants = [build_plant(conts[r], 1, astars[r], Bb, cfg.vocab, cfg.mask_id) for r in range(4)]
+    astars = [0, Bb // 2, Bb, 3, 5, 1, Bb - 1, 7][:R]
+    budgets = [Bb + 2, Bb + 2, 5, Bb + 2, Bb + 2, 3, Bb + 2, Bb + 2][:R]
+    plants = [build_plant(conts[r], 1, astars[r], Bb, cfg.vocab, cfg.mask_id) for r in range(R)]
     planted = torch.tensor(plants, dtype=torch.int32, device="cuda")
-    got = round_batch(model, kvs, Bb, budgets, planted_dev=planted)
+    got = round_batch(model, kvs, Bb, budgets, planted_dev=planted)          # graph replay
     states = [kv.state() for kv in kvs]
     for r, kv in enumerate(kvs):
         kv.rewind(lens[r], firsts[r])
-        c, A, _, _ = kv.round(Bb, max_commit=budgets[r], planted_dev=planted[r])
+    got_l, dl, vl = round_batch(model, kvs, Bb, budgets, planted_dev=planted, want_logits=True)
+    assert got_l == got
+    assert [kv.state() for kv in kvs] == states
+    for r, kv in enumerate(kvs):
+        kv.rewind(lens[r], firsts[r])
+        c, A, dls, vls = kv.round(Bb, max_commit=budgets[r], planted_dev=planted[r], want_logits=True)
         assert (c, A) == got[r], f"request {r}"
         assert kv.state() == states[r]
         assert A == min(astars[r], Bb)
         assert c == conts[r][1: 1 + min(A + 2, budgets[r])]
+        rows = slice(r * (Bb + 1), (r + 1) * (Bb + 1))
+        assert torch.equal(dl[rows], dls), f"request {r}: draft logits differ from its single round"
+        assert torch.equal(vl[rows], vls), f"request {r}: verify logits differ from its single round"
     for kv in kvs:
         kv.close()
 
