@@ -232,6 +232,79 @@ def plant_rows(cont, c, astar, B, vocab):
     return row
 
 
+def round_vs_n(torch, model, kv, cfg, wid, B, ns, reps=20):
+    """Device time of one round (draft + verify + accept, no planting) from a state with n cached
+    positions, for each n: a synthetic prefix of n embeddings is prefilled, then the same round is
+    repeated from that state; the roofline fraction is the round's algorithmic bytes at that n."""
+    from ssb_inputs import prefix_embeddings
+    out = {}
+    for n in ns:
+        kv.reset()
+        y1 = kv.prefill(model.prefix_tensor(prefix_embeddings(wid, 10_000 + n, n, cfg.hidden)))
+        evs = []
+        with no_gc():
+            for r in range(reps + 3):
+                kv.rewind(n, y1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                kv.round(B)
+                e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+        us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs[3:])
+        ab = alg_bytes_round(cfg, n, B)
+        out[str(n)] = {"round_us": us, "alg_bytes": ab, "roofline_frac": ab / (us * 1e-6) / (PEAK_HBM_GBS * 1e9)}
+    return out
+
+
+def decode_cpu_baseline(wl, weights, lengths, ar_outputs, gpu_tokens_per_round, budget_s=15.0):
+    """The float32 oracle on a bounded sample of the workload's regions: region by region, prefill
+    (not timed), then self-speculative rounds with the GPU line's planted drafts (built from the
+    GPU's AR output and the same planted accept lengths), each round timed, until budget_s of
+    round time.  Where the oracle's own greedy path departs from the GPU's at a near-tie, the
+    planted drafts stop matching and its rounds commit fewer tokens for the same work, so the rate
+    is measured in rounds/s and converted with the GPU line's committed tokens per round; the
+    oracle's own count is reported beside it."""
+    import numpy as np
+    from oracle import Decoder, build_plant, prefill, spec_round
+    from ssb_inputs import plant_accept_lengths, prefix_embeddings
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    cfg, B, P = wl.model, wl.block, wl.prefix_len
+    model = Decoder(cfg, weights, dtype=np.float32)
+    t_rounds, committed, rounds, regions = 0.0, 0, 0, 0
+    for i, L in enumerate(lengths):
+        if t_rounds >= budget_s:
+            break
+        print(f"oracle baseline: region {i}", file=sys.stderr, flush=True)
+        pre = np.asarray(prefix_embeddings(wl.wid, i, P, cfg.hidden), dtype=np.float32)
+        st, y1, _ = prefill(model, pre, P + L + B + 3)
+        astar = plant_accept_lengths(wl.wid, i, L, B, wl.plant_p, wl.full_accept_p)
+        out, k = [y1], 0
+        while out[-1] != cfg.eos_id and len(out) < L and t_rounds < budget_s:
+            plant = build_plant(ar_outputs[i], len(out), int(astar[k]) if k < len(astar) else B, B, cfg.vocab,
+                                cfg.mask_id)
+            t0 = time.perf_counter()
+            r = spec_round(model, st, B, planted=plant, budget=L - len(out))
+            t_rounds += time.perf_counter() - t0
+            out += r.committed
+            committed += len(r.committed)
+            rounds += 1
+            k += 1
+        regions += 1
+    rps = rounds / t_rounds
+    return {"value": rps * gpu_tokens_per_round, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu": host_cpu_model(), "rounds_per_s": rps,
+            "sample": f"numpy float32 oracle on {cores} threads: {rounds} rounds over the first {regions} "
+                      f"regions of the workload, {t_rounds:.1f} s of round time (prefill excluded), drafts "
+                      f"planted from the GPU's AR output with the same accept lengths; tokens/s = rounds/s x "
+                      f"{gpu_tokens_per_round:.2f} committed tokens per round of the GPU line (the oracle "
+                      f"itself committed {committed / max(rounds, 1):.2f} per round)"}
+
+
 def decode_workload(args, wid):
     """Configs 3 and 4: per region, GPU AR decode (its output plants the drafts), then GPU
     self-speculative decode of the same region; decode-only committed tokens/s of both."""
@@ -253,11 +326,15 @@ def decode_workload(args, wid):
     tot = {"spec_tokens": 0, "spec_us": 0.0, "ar_tokens": 0, "ar_us": 0.0, "rounds": 0, "forwards": 0,
            "accepted": 0}
     hist = np.zeros(B + 1, dtype=np.int64)
+    ar_outputs = []
     for i in range(n):
+        if i % 16 == 0:
+            print(f"{wl.name}: region {i} of {n}", file=sys.stderr, flush=True)
         pre_dev = model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden))
         L = lengths[i]
         kv.reset()
         ar, st_ar = kv.decode_ar(pre_dev, L)
+        ar_outputs.append(ar)
         astar = plant_accept_lengths(wl.wid, i, L, B, wl.plant_p, wl.full_accept_p)
         kv.reset()
         spec, st = kv.decode(pre_dev, B, L, cont_dev=torch.tensor(ar, dtype=torch.int32, device="cuda"),
@@ -274,6 +351,15 @@ def decode_workload(args, wid):
             hist[min(int(a), B)] += 1
     spec_tps = tot["spec_tokens"] / (tot["spec_us"] * 1e-6)
     ar_tps = tot["ar_tokens"] / (tot["ar_us"] * 1e-6)
+    # round time against the HBM roofline across the cached lengths the workload reaches
+    top = P + min(max(lengths[:n]), 4096)
+    ns = sorted({P, (P + top) // 2, top} if wid == 3 else {P, 2048, 3072, 4096, top})
+    print(f"{wl.name}: round time against cached length", file=sys.stderr, flush=True)
+    per_n = round_vs_n(torch, model, kv, cfg, wl.wid, B, [x for x in ns if x + B + 2 <= P + cap + 2 * B + 8])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = decode_cpu_baseline(wl, generate_weights(cfg), lengths[:n], ar_outputs,
+                                  tot["spec_tokens"] / max(tot["rounds"], 1))
     line = {
         "metric": "decode-only committed tokens/s, self-speculative (B=32, batch 1), prefill excluded",
         "value": spec_tps, "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
@@ -285,6 +371,8 @@ def decode_workload(args, wid):
         "mean_accept": tot["accepted"] / max(tot["rounds"], 1), "rounds": tot["rounds"],
         "planted_accept_histogram": hist.tolist(),
         "outputs_identical_to_ar": True,
+        "round_vs_n": per_n,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line))
 

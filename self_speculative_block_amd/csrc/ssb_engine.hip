@@ -135,7 +135,7 @@ struct ssb_model {
   ReqArgs* req_dev;   // device request state read by every kernel of a forward
   ReqArgs* req_pin;   // pinned staging of the request state
   hipStream_t cap;    // private stream used only to capture graphs
-  std::map<std::tuple<int, void*, int, int, uint32_t>, hipGraphExec_t> graphs;   // (kind, pool, R, B, T bits)
+  std::map<std::tuple<int, void*, int, int, uint32_t, int>, hipGraphExec_t> graphs;   // (kind, pool, R, B, T bits, slots)
   // kernel timing hook
   int prof_kind = -1;
   std::vector<hipEvent_t> prof_ev;    // pairs (start, end)
@@ -417,6 +417,7 @@ struct FwdSpec {
   const void* prefix; // PREFILL
   ReqArgs ra;         // host copy of the request state (already uploaded to the device)
   int max_pos;        // largest position of any row + 1
+  int slots;          // graph capture: attention chunk slots of the launch (slot_bucket of max_pos)
   bool graph;         // launches are being captured: no round-dependent launch shapes
   float* logits;      // nullable [M][vocab] (all rows) or [1][vocab] (last row only)
   bool lm_last_only;  // LM head on the last row only (prefill)
@@ -486,7 +487,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   } else {
     add_tasks(0, 0, M, 0, f.pos0 + M - 1);
   }
-  const int chunk_slots = f.graph ? m->max_chunks : (f.max_pos - 1) / kKeyChunk + 1;
+  const int chunk_slots = f.graph ? (f.slots > 0 ? f.slots : m->max_chunks) : (f.max_pos - 1) / kKeyChunk + 1;
 
   for (int l = 0; l < c.n_layers; ++l) {
     g.layer = l;
@@ -666,11 +667,19 @@ void upload_req(ssb_model* m, const ReqArgs& ra, hipStream_t st) {
 // Graph of a fixed launch sequence, captured once per (kind, pool, R, B) on a
 // private stream and replayed on the caller's stream.  Launch shapes inside
 // never depend on the round; round state is read from the device.
-hipGraphExec_t get_graph(ssb_model* m, int kind, ssb_pool* pool, int R, int B,
+// Attention chunk slots a captured launch covers for windows ending before max_pos: the chunk
+// count rounded up to a multiple of 8 (so a growing sequence re-captures once per 512 positions),
+// at most the model's chunk capacity.  Slots past a window's last chunk exit at once.
+int slot_bucket(const ssb_model* m, int max_pos) {
+  const int c = (max_pos - 1) / kKeyChunk + 1;
+  return std::min((c + 7) / 8 * 8, m->max_chunks);
+}
+
+hipGraphExec_t get_graph(ssb_model* m, int kind, ssb_pool* pool, int R, int B, int slots,
                          const std::function<void(hipStream_t)>& body, float temperature = 0.f) {
   uint32_t tb = 0;
   std::memcpy(&tb, &temperature, 4);
-  const auto key = std::make_tuple(kind, static_cast<void*>(pool), R, B, tb);
+  const auto key = std::make_tuple(kind, static_cast<void*>(pool), R, B, tb, slots);
   auto it = m->graphs.find(key);
   if (it != m->graphs.end()) return it->second;
   hip_check(hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal), "begin capture");
@@ -802,11 +811,13 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
     maxpos = std::max(maxpos, ra.p[r] + B + 2);
   }
   upload_req(m, ra, st);
+  const int slots = slot_bucket(m, maxpos);
   auto body = [&](hipStream_t s, bool graph) {
     FwdSpec f{};
     f.M = R * (B + 1);
     f.ra = ra;
     f.max_pos = maxpos;
+    f.slots = slots;
     f.graph = graph;
     f.mode = PREP_DRAFT;
     f.logits = dlog;
@@ -846,7 +857,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
   if (dlog || vlog || m->prof_kind >= 0) {
     body(st, false);
   } else {
-    hipGraphExec_t ex = get_graph(m, smp ? 4 : 0, pool, R, B, [&](hipStream_t s) { body(s, true); },
+    hipGraphExec_t ex = get_graph(m, smp ? 4 : 0, pool, R, B, slots, [&](hipStream_t s) { body(s, true); },
                                   smp ? smp->temperature : 0.f);
     hip_check(hipGraphLaunch(ex, st), "round graph launch");
   }
@@ -886,6 +897,7 @@ void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_
     f.M = 1;
     f.ra = ra;
     f.max_pos = kv->seq_len + 1;
+    f.slots = slot_bucket(m, f.max_pos);
     f.graph = graph;
     f.logits = logits;
     if (smp) {
@@ -899,7 +911,8 @@ void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_
   if (logits || m->prof_kind >= 0) {
     body(st, false);
   } else {
-    hipGraphExec_t ex = get_graph(m, smp ? 5 : 1, kv->pool, 1, 0, [&](hipStream_t s) { body(s, true); },
+    hipGraphExec_t ex = get_graph(m, smp ? 5 : 1, kv->pool, 1, 0, slot_bucket(m, kv->seq_len + 1),
+                                  [&](hipStream_t s) { body(s, true); },
                                   smp ? smp->temperature : 0.f);
     hip_check(hipGraphLaunch(ex, st), "AR graph launch");
   }
@@ -952,6 +965,7 @@ void ar_step_batch_impl(ssb_model* m, ssb_kv* const* kvs, int R, int32_t* tokens
     f.M = R;
     f.ra = ra;
     f.max_pos = maxpos;
+    f.slots = slot_bucket(m, maxpos);
     f.graph = graph;
     run_forward(m, pool, f, s);
     hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, (size_t)R * 4, hipMemcpyDeviceToHost, s), "copy tokens");
@@ -959,7 +973,7 @@ void ar_step_batch_impl(ssb_model* m, ssb_kv* const* kvs, int R, int32_t* tokens
   if (m->prof_kind >= 0) {
     body(st, false);
   } else {
-    hipGraphExec_t ex = get_graph(m, 1, pool, R, 0, [&](hipStream_t s) { body(s, true); });
+    hipGraphExec_t ex = get_graph(m, 1, pool, R, 0, slot_bucket(m, maxpos), [&](hipStream_t s) { body(s, true); });
     hip_check(hipGraphLaunch(ex, st), "AR graph launch");
   }
   hip_check(hipStreamSynchronize(st), "ar sync");
@@ -1141,6 +1155,7 @@ void dd_block_impl(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, i
     f.M = B + 1;
     f.ra = ra;
     f.max_pos = p + B + 1;
+    f.slots = slot_bucket(m, f.max_pos);
     f.graph = graph;
     f.logits = logits;
     f.stat_sc = kLog2e;
@@ -1157,7 +1172,8 @@ void dd_block_impl(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, i
     if (eager) {
       step_body(st, false, step_logits ? step_logits + (size_t)steps * (B + 1) * c.vocab : nullptr);
     } else {
-      hipGraphExec_t ex = get_graph(m, 2, pool, 1, B, [&](hipStream_t s) { step_body(s, true, nullptr); });
+      hipGraphExec_t ex = get_graph(m, 2, pool, 1, B, slot_bucket(m, p + B + 1),
+                                    [&](hipStream_t s) { step_body(s, true, nullptr); });
       hip_check(hipGraphLaunch(ex, st), "direct diffusion step graph launch");
     }
     hip_check(hipStreamSynchronize(st), "direct diffusion step sync");
@@ -1199,6 +1215,7 @@ void dd_block_impl(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, i
         f.M = B - 1;
         f.ra = rc;
         f.max_pos = p + B;
+        f.slots = slot_bucket(m, f.max_pos);
         f.graph = graph;
         f.no_head = true;
         run_forward(m, pool, f, s);
@@ -1206,7 +1223,7 @@ void dd_block_impl(ssb_model* m, ssb_kv* kv, int B, float tau, int max_commit, i
       if (eager) {
         cw_body(st, false);
       } else {
-        hipGraphExec_t ex = get_graph(m, 3, pool, 1, B, [&](hipStream_t s) { cw_body(s, true); });
+        hipGraphExec_t ex = get_graph(m, 3, pool, 1, B, slot_bucket(m, p + B), [&](hipStream_t s) { cw_body(s, true); });
         hip_check(hipGraphLaunch(ex, st), "cache-write graph launch");
       }
       hip_check(hipStreamSynchronize(st), "cache-write sync");
@@ -1250,6 +1267,7 @@ void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau,
     f.M = B + 1;
     f.ra = ra;
     f.max_pos = p + B + 1;
+    f.slots = slot_bucket(m, f.max_pos);
     f.graph = graph;
     f.stat_sc = kLog2e;
     run_forward(m, pool, f, s);
@@ -1263,7 +1281,8 @@ void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau,
     if (eager) {
       step_body(st, false);
     } else {
-      hipGraphExec_t ex = get_graph(m, 2, pool, 1, B, [&](hipStream_t s) { step_body(s, true); });
+      hipGraphExec_t ex = get_graph(m, 2, pool, 1, B, slot_bucket(m, p + B + 1),
+                                    [&](hipStream_t s) { step_body(s, true); });
       hip_check(hipGraphLaunch(ex, st), "draft step graph launch");
     }
     hip_check(hipStreamSynchronize(st), "draft step sync");
@@ -1282,6 +1301,7 @@ void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau,
     f.M = B + 1;
     f.ra = ra;
     f.max_pos = p + B + 2;
+    f.slots = slot_bucket(m, f.max_pos);
     f.graph = graph;
     f.logits = vlog;
     run_forward(m, pool, f, s);
@@ -1292,7 +1312,8 @@ void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau,
   if (eager) {
     verify_body(st, false);
   } else {
-    hipGraphExec_t ex = get_graph(m, 6, pool, 1, B, [&](hipStream_t s) { verify_body(s, true); });
+    hipGraphExec_t ex = get_graph(m, 6, pool, 1, B, slot_bucket(m, p + B + 2),
+                                  [&](hipStream_t s) { verify_body(s, true); });
     hip_check(hipGraphLaunch(ex, st), "verify graph launch");
   }
   hip_check(hipStreamSynchronize(st), "verify sync");
