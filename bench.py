@@ -318,7 +318,8 @@ def decode_workload(args, wid):
     cfg, B, P = wl.model, wl.block, wl.prefix_len
     lengths = target_lengths(wl)
     n = min(args.regions or wl.n_regions, wl.n_regions)
-    cap = max(lengths[:n])
+    # room for the longest region; for tables, for the length cap (round_vs_n reaches prefix + 4096)
+    cap = max(max(lengths[:n]), 4096 if wid == 4 else 0)
     torch.cuda.set_device(0)
     model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8)
     pool = Pool(model, n_pages=(P + cap + 2 * B + 8) // 16 + 8)
@@ -352,7 +353,7 @@ def decode_workload(args, wid):
     spec_tps = tot["spec_tokens"] / (tot["spec_us"] * 1e-6)
     ar_tps = tot["ar_tokens"] / (tot["ar_us"] * 1e-6)
     # round time against the HBM roofline across the cached lengths the workload reaches
-    top = P + min(max(lengths[:n]), 4096)
+    top = P + min(cap, 4096)
     ns = sorted({P, (P + top) // 2, top} if wid == 3 else {P, 2048, 3072, 4096, top})
     print(f"{wl.name}: round time against cached length", file=sys.stderr, flush=True)
     per_n = round_vs_n(torch, model, kv, cfg, wl.wid, B, [x for x in ns if x + B + 2 <= P + cap + 2 * B + 8])
