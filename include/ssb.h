@@ -370,6 +370,26 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
 int ssb_profile_kernel(ssb_model* m, int kind);
 int ssb_profile_read(ssb_model* m, double* total_us, long long* launches, int reset);
 
+/* Debug check of the in-place KV overwrite and of rollback (GravityOCR
+ * review, Appendix B.2: verify overwrites the draft's window slots, and only
+ * causal state survives a round). With SSB_DEBUG_POISON set, every greedy or
+ * stochastic round (single, batched, inside decode and serve) writes NaN into
+ * every layer's K and V at positions p+1 .. p+B+1 of each request between its
+ * draft and verify forwards, and at p+A+2 .. p+B+1 after accept. A correct
+ * engine reads none of them before rewriting them, so results are unchanged
+ * bit for bit; a stale read surfaces as NaN logits (SSB_EHIP from the round).
+ * Rounds then run without graph replay. flags: 0 or SSB_DEBUG_POISON;
+ * SSB_EINVAL for other bits or a null model. */
+#define SSB_DEBUG_POISON 1
+int ssb_set_debug(ssb_model* m, int flags);
+
+/* Debug: writes NaN into every layer's K and V at positions [lo, hi) of the
+ * kv's pages (a test hook for the poisoning above: poisoning a slot the next
+ * round reads makes that round fail with SSB_EHIP; poisoning slots the next
+ * window rewrites first changes nothing). SSB_EINVAL if the range is outside
+ * the pages the kv holds. Synchronous on stream. */
+int ssb_kv_poison(ssb_kv* kv, int lo, int hi, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

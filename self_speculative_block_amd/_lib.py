@@ -40,6 +40,7 @@ class SsbStats(ctypes.Structure):
 
 
 SSB_SERVE_AR, SSB_SERVE_SPEC = 0, 1
+SSB_DEBUG_POISON = 1
 
 
 class SsbRequest(ctypes.Structure):
@@ -77,6 +78,8 @@ SIGNATURES = {
                            c_int, P_i32, P_i32, ctypes.POINTER(SsbStats), c_void_p]),
     "ssb_decode_ar": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, P_i32, P_i32,
                               ctypes.POINTER(SsbStats), c_void_p]),
+    "ssb_set_debug": (c_int, [c_void_p, c_int]),
+    "ssb_kv_poison": (c_int, [c_void_p, c_int, c_int, c_void_p]),
     "ssb_round_batch": (c_int, [c_void_p, ctypes.POINTER(c_void_p), c_int, c_int, P_i32, c_void_p, P_i32,
                                 P_i32, P_i32, c_void_p, c_void_p, c_void_p]),
     "ssb_round_sample": (c_int, [c_void_p, c_void_p, c_int, c_int, c_float, c_void_p, P_i32, P_i32, P_i32,

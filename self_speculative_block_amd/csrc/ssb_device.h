@@ -223,6 +223,9 @@ template <typename T> hipError_t launch_attn(const AttnArgs& a, int n_chunk_slot
 template <typename T>
 hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, int n_heads, int head_dim,
                                const int32_t* row_lim, int M, void* out, int out_ld, hipStream_t st);
+template <typename T>
+hipError_t launch_poison_kv(const ReqArgs* req, int R, const int32_t* acc, int acc_stride, int lo_abs, int hi_abs,
+                            void* kv_pool, int n_layers, int n_pages, int n_kv, int hd, hipStream_t st);
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
                          int32_t* out, int out_stride, hipStream_t st);
 hipError_t launch_dd_init(const ReqArgs* ra, int n_req, int mask_id, int32_t* rec, int rec_stride, hipStream_t st);

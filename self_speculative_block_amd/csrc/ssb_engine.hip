@@ -131,6 +131,7 @@ struct ssb_model {
   int max_chunks;
   int max_decode_rows;
   int32_t* accept_dev;
+  bool debug_poison = false;   // NaN-poison KV slots no correct read reaches (rounds run eagerly)
   int32_t* tok_dev;
   ReqArgs* req_dev;   // device request state read by every kernel of a forward
   ReqArgs* req_pin;   // pinned staging of the request state
@@ -771,6 +772,18 @@ struct RoundOut {
 };
 
 // Runs draft + verify + accept for R requests (row windows concatenated).
+// Debug: NaN into the KV slots [lo, p + B + 2) of every request of the launch (lo = p + 1 with no
+// accept record, p + A + 2 with one).
+void poison_kv(ssb_model* m, ssb_pool* pool, int R, const int32_t* acc, hipStream_t s, int lo = -1, int hi = -1) {
+  const ssb_config& c = m->c;
+  if (m->elem == 2)
+    hip_check(launch_poison_kv<bf16_t>(m->req_dev, R, acc, kOutStride, lo, hi, pool->base, c.n_layers, pool->n_pages,
+                                       c.n_kv_heads, c.head_dim, s), "poison kv");
+  else
+    hip_check(launch_poison_kv<float>(m->req_dev, R, acc, kOutStride, lo, hi, pool->base, c.n_layers, pool->n_pages,
+                                      c.n_kv_heads, c.head_dim, s), "poison kv");
+}
+
 void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_commit, const int32_t* planted,
                 const int32_t* const* cont, const int* cont_len, const int* cont_c, const int* astar,
                 float* dlog, float* vlog, RoundOut* out, hipStream_t st, const SampleSpec* smp = nullptr) {
@@ -830,6 +843,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
       f.st_z = m->sz_d;
     }
     run_forward(m, pool, f, s);
+    if (m->debug_poison) poison_kv(m, pool, R, nullptr, s);   // the window slots verify rewrites
     f.mode = PREP_VERIFY;
     f.logits = vlog;
     if (smp) {
@@ -851,10 +865,11 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
       hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, R, c.eos_id, m->accept_dev, kOutStride, s),
                 "accept");
     }
+    if (m->debug_poison) poison_kv(m, pool, R, m->accept_dev, s);   // the rolled-back slots
     hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)R * kOutStride * 4, hipMemcpyDeviceToHost, s),
               "copy accept");
   };
-  if (dlog || vlog || m->prof_kind >= 0) {
+  if (dlog || vlog || m->prof_kind >= 0 || m->debug_poison) {
     body(st, false);
   } else {
     hipGraphExec_t ex = get_graph(m, smp ? 4 : 0, pool, R, B, slots, [&](hipStream_t s) { body(s, true); },
@@ -1552,6 +1567,28 @@ int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_
       if (n_committed) n_committed[r] = ro[r].n;
       if (accept_len) accept_len[r] = ro[r].A;
     }
+  });
+}
+
+int ssb_kv_poison(ssb_kv* kv, int lo, int hi, void* stream) {
+  return guard([&] {
+    if (!kv) fail(SSB_EINVAL, "null kv");
+    if (lo < 0 || hi < lo || hi > (int)kv->pages.size() * kPage) fail(SSB_EINVAL, "range outside the kv's pages");
+    if (hi == lo) return;
+    ssb_model* m = kv->pool->m;
+    hipStream_t st = S(stream);
+    ReqArgs ra = single_req(kv, 0, 1);
+    upload_req(m, ra, st);
+    poison_kv(m, kv->pool, 1, nullptr, st, lo, hi);
+    hip_check(hipStreamSynchronize(st), "poison sync");
+  });
+}
+
+int ssb_set_debug(ssb_model* m, int flags) {
+  return guard([&] {
+    if (!m) fail(SSB_EINVAL, "null model");
+    if (flags & ~SSB_DEBUG_POISON) fail(SSB_EINVAL, "unknown debug flag");
+    m->debug_poison = (flags & SSB_DEBUG_POISON) != 0;
   });
 }
 

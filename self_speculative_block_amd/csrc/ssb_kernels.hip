@@ -1203,6 +1203,35 @@ __global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int
 }
 
 // ---------------------------------------------------------------------------
+// Debug poisoning of KV slots that no correct read may reach (a test of the
+// in-place overwrite and of rollback): NaN into every layer's K and V at the
+// positions [lo, p + B + 2) of each request, lo = p + 1 between the draft and
+// the verify forward (the verify rewrites them before any read), or
+// lo = p + A + 2 after accept (rolled back; the next window rewrites them).
+// lo_abs >= 0 gives the range [lo_abs, hi_abs) explicitly (a test hook).
+// Grid (requests x layers), 256 threads; vector stores only.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_poison_kv(const ReqArgs* rap, const int32_t* acc, int acc_stride,
+                                                   int lo_abs, int hi_abs, void* kv_pool, int n_layers, int n_pages,
+                                                   int n_kv, int hd) {
+  const ReqArgs& ra = *rap;
+  const int r = blockIdx.x / n_layers, layer = blockIdx.x % n_layers;
+  const int p = ra.p[r];
+  const int lo = lo_abs >= 0 ? lo_abs : acc ? p + acc[(size_t)r * acc_stride] + 2 : p + 1;
+  const int hi = lo_abs >= 0 ? hi_abs : p + ra.B + 2;
+  const int per = 2 * n_kv * hd;                    // K and V values of one position
+  T* pool = reinterpret_cast<T*>(kv_pool);
+  for (int e = threadIdx.x; e < (hi - lo) * per; e += blockDim.x) {
+    const int s = lo + e / per, rem = e % per;
+    const int kv = rem / (n_kv * hd), h = (rem / hd) % n_kv, d = rem % hd;
+    const int pg = ra.pt[r][s / kPage];
+    const size_t base = (((size_t)layer * n_pages + pg) * 2 + kv) * n_kv + h;
+    pool[(base * kPage + s % kPage) * hd + d] = Ty<T>::from_f(NAN);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Direct block-diffusion step (GravityOCR review, Appendix B.1; Trillion Labs
 // blog, the "confidence threshold" entry): one wave per request.  Lane j owns
 // block position j + 1, whose prediction is window row j.  Every undecided
@@ -1659,6 +1688,18 @@ template hipError_t launch_attn_combine<bf16_t>(const float*, int, int, int, int
                                                 hipStream_t);
 template hipError_t launch_attn_combine<float>(const float*, int, int, int, int, const int32_t*, int, void*, int,
                                                hipStream_t);
+
+template <typename T>
+hipError_t launch_poison_kv(const ReqArgs* req, int R, const int32_t* acc, int acc_stride, int lo_abs, int hi_abs,
+                            void* kv_pool, int n_layers, int n_pages, int n_kv, int hd, hipStream_t st) {
+  hipLaunchKernelGGL((k_poison_kv<T>), dim3(R * n_layers), dim3(256), 0, st, req, acc, acc_stride, lo_abs, hi_abs,
+                     kv_pool, n_layers, n_pages, n_kv, hd);
+  return hipGetLastError();
+}
+template hipError_t launch_poison_kv<bf16_t>(const ReqArgs*, int, const int32_t*, int, int, int, void*, int, int, int,
+                                             int, hipStream_t);
+template hipError_t launch_poison_kv<float>(const ReqArgs*, int, const int32_t*, int, int, int, void*, int, int, int,
+                                            int, hipStream_t);
 
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
                          int32_t* out, int out_stride, hipStream_t st) {

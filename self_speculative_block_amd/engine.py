@@ -90,6 +90,11 @@ class Model:
         return torch.from_numpy(np.ascontiguousarray(prefix, dtype=np.float32)).to(self.device).to(
             torch_dtype(self.cfg))
 
+    def set_debug(self, poison):
+        """NaN-poison the KV slots no correct read reaches (window slots between draft and verify,
+        rolled-back slots after accept); rounds then run without graph replay."""
+        L.check(self.lib.ssb_set_debug(self.h, L.SSB_DEBUG_POISON if poison else 0))
+
     def profile_kernel(self, kind):
         """Start timing every launch of one kernel kind (name in KERNEL_KINDS), or stop (None)."""
         L.check(self.lib.ssb_profile_kernel(self.h, -1 if kind is None else L.KERNEL_KINDS[kind]))
@@ -148,6 +153,10 @@ class KV:
 
     def reset(self):
         L.check(self.lib.ssb_kv_reset(self.h))
+
+    def poison(self, lo, hi):
+        """Debug: NaN into every layer's K and V at positions [lo, hi) of this kv's pages."""
+        L.check(self.lib.ssb_kv_poison(self.h, lo, hi, _stream()))
 
     def rewind(self, n, x0):
         L.check(self.lib.ssb_kv_rewind(self.h, n, x0))
