@@ -155,18 +155,18 @@ def test_eos_and_max_len(tiny):
         kv.reset()
         assert spec == full[:max_len]
     kv.close()
-    eos = full[9]
-    cfg2 = dataclasses.replace(cfg, eos_id=eos)
-    m2 = Model(cfg2, w, block_B=wl.block, max_rows=64, max_positions=256)
-    p2 = Pool(m2, n_pages=16)
-    kv2 = KV(p2, 200)
-    for B in (0, 1, 4, 8):
-        spec, _ = kv2.decode(m2.prefix_tensor(pre), B, 40)
-        kv2.reset()
-        assert spec == full[: full.index(eos) + 1]
-    kv2.close()
-    p2.close()
-    m2.close()
+    for eos in (full[9], full[0]):            # EOS mid-output, and the prefill's own token
+        cfg2 = dataclasses.replace(cfg, eos_id=eos)
+        m2 = Model(cfg2, w, block_B=wl.block, max_rows=64, max_positions=256)
+        p2 = Pool(m2, n_pages=16)
+        kv2 = KV(p2, 200)
+        for B in (0, 1, 4, 8):
+            spec, _ = kv2.decode(m2.prefix_tensor(pre), B, 40)
+            kv2.reset()
+            assert spec == full[: full.index(eos) + 1]
+        kv2.close()
+        p2.close()
+        m2.close()
 
 
 def test_error_paths(tiny):
@@ -190,6 +190,10 @@ def test_error_paths(tiny):
     assert e.value.code == SSB_EINVAL
     n0 = kv.state()
     assert n0[0] == wl.prefix_len
+    with pytest.raises(SsbError) as e:          # [M] can never be a boundary token
+        kv.rewind(wl.prefix_len, cfg.mask_id)
+    assert e.value.code == SSB_EINVAL
+    assert kv.state() == n0
     kv.close()
     small = KV(pool, wl.prefix_len + 4)
     small.prefill(pre_dev)
