@@ -128,6 +128,9 @@ void ssb_free_model(ssb_model* m);
  * [token][head_dim]. */
 int ssb_pool_bytes(const ssb_model* m, int n_pages, size_t* bytes);
 int ssb_pool_init(ssb_model* m, void* dev_buf, size_t bytes, int n_pages, ssb_pool** out);
+/* Frees the pool (not its caller-owned buffer) after the device is idle; the
+ * model's captured launch graphs that use this pool are destroyed with it.
+ * Free every kv of the pool first. */
 void ssb_pool_free(ssb_pool* p);
 int ssb_pool_free_pages(const ssb_pool* p, int* n_free);
 

@@ -1405,7 +1405,23 @@ int ssb_pool_init(ssb_model* m, void* dev_buf, size_t bytes, int n_pages, ssb_po
   });
 }
 
-void ssb_pool_free(ssb_pool* p) { delete p; }
+void ssb_pool_free(ssb_pool* p) {
+  if (!p) return;
+  // Captured graphs bake in this pool's device buffer: drop them, so that a pool created later
+  // at the same host address can never replay them.
+  ssb_model* m = p->m;
+  (void)hipSetDevice(m->device);
+  (void)hipDeviceSynchronize();
+  for (auto it = m->graphs.begin(); it != m->graphs.end();) {
+    if (std::get<1>(it->first) == static_cast<void*>(p)) {
+      (void)hipGraphExecDestroy(it->second);
+      it = m->graphs.erase(it);
+    } else {
+      ++it;
+    }
+  }
+  delete p;
+}
 
 int ssb_pool_free_pages(const ssb_pool* p, int* n_free) {
   return guard([&] {

@@ -194,3 +194,26 @@ def test_poison_hook_control(setup):
     assert kv.state()[:2] == (P, s["y1"])
     kv.reset()                               # drop the poisoned cache; later tests prefill again
     assert kv.prefill(s["pre_dev"]) == s["y1"]
+
+
+def test_graphs_do_not_outlive_their_pool():
+    """Captured round graphs bake in the pool's device buffer.  A pool freed and followed by a new
+    pool (often at the same host address, with a different buffer) must not replay them: rounds in
+    the new pool give the same results as in the first one."""
+    from self_speculative_block_amd.engine import KV, Model, Pool
+    wl = workload(1)
+    cfg, B, P = wl.model, wl.block, wl.prefix_len
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=64, max_positions=256)
+    pre_dev = model.prefix_tensor(prefix_embeddings(wl.wid, 5, P, cfg.hidden))
+    results = []
+    for n_pages in (40, 24, 40):
+        pool = Pool(model, n_pages=n_pages)
+        kv = KV(pool, 200)
+        kv.prefill(pre_dev)
+        got = [kv.round(B)[:2] for _ in range(3)]        # graph capture, then replays
+        got.append(kv.ar_step()[0])
+        results.append(got)
+        kv.close()
+        pool.close()
+    assert results[1] == results[0] and results[2] == results[0]
+    model.close()
