@@ -217,3 +217,61 @@ def test_graphs_do_not_outlive_their_pool():
         pool.close()
     assert results[1] == results[0] and results[2] == results[0]
     model.close()
+
+
+def _other_token(t, cfg):
+    u = (t + 7) % cfg.vocab
+    return (u + 1) % cfg.vocab if u == cfg.mask_id else u
+
+
+def test_verify_rows_see_only_earlier_window_rows(setup):
+    """Causal verify visibility on the GPU (GravityOCR review, section 3.2: verify row i attends
+    to the cache and window rows <= i).  Changing the planted draft d_j leaves verify rows
+    0..j-1 bit-identical and changes row j; the draft forward runs before planting and is
+    unchanged."""
+    s = setup
+    kv, cfg, B, P = s["kv"], s["cfg"], s["B"], s["P"]
+    base = build_plant(s["cont"], 1, B, B, cfg.vocab, cfg.mask_id)
+    for j in sorted({1, B // 2, B}):
+        pert = list(base)
+        pert[j - 1] = _other_token(pert[j - 1], cfg)
+        outs = []
+        for plant in (base, pert):
+            kv.rewind(P, s["y1"])
+            outs.append(kv.round(B, planted_dev=torch.tensor(plant, dtype=torch.int32, device="cuda"),
+                                 want_logits=True))
+        (_, _, d0, v0), (_, _, d1, v1) = outs
+        assert torch.equal(d0, d1)
+        assert torch.equal(v0[:j], v1[:j]), f"a verify row before {j} saw d_{j}"
+        assert not torch.equal(v0[j], v1[j])
+
+
+def test_batched_requests_are_isolated(setup):
+    """In a batched round, changing one request's planted drafts changes nothing, bit for bit, in
+    another request's draft and verify logits."""
+    from self_speculative_block_amd.engine import KV, round_batch
+    s = setup
+    model, pool, cfg, B, P = s["model"], s["pool"], s["cfg"], s["B"], s["P"]
+    kvs, firsts, plants = [], [], []
+    for i in range(2):
+        kv = KV(pool, P + 2 * B + 8)
+        y = kv.prefill(model.prefix_tensor(prefix_embeddings(s["wl"].wid, 40 + i, P, cfg.hidden)))
+        cont = [y] + [kv.ar_step()[0] for _ in range(B + 2)]
+        kv.rewind(P, y)
+        kvs.append(kv)
+        firsts.append(y)
+        plants.append(build_plant(cont, 1, B, B, cfg.vocab, cfg.mask_id))
+    pert = [list(plants[0]), [_other_token(t, cfg) for t in plants[1]]]
+    outs = []
+    for pl in (plants, pert):
+        for kv, y in zip(kvs, firsts):
+            kv.rewind(P, y)
+        res, dl, vl = round_batch(model, kvs, B, [B + 2] * 2, planted_dev=torch.tensor(pl, dtype=torch.int32,
+                                                                                      device="cuda"), want_logits=True)
+        outs.append((res, dl, vl))
+    rows0 = slice(0, B + 1)
+    assert outs[0][0][0] == outs[1][0][0]
+    assert torch.equal(outs[0][1][rows0], outs[1][1][rows0]) and torch.equal(outs[0][2][rows0], outs[1][2][rows0])
+    assert not torch.equal(outs[0][2][B + 2:], outs[1][2][B + 2:])   # request 1's verify rows did change
+    for kv in kvs:
+        kv.close()
