@@ -48,8 +48,8 @@ def alg_bytes_kernel(kind, cfg, M, n_keys):
         return H * qd * e + M * qd * e + M * H * (4 + 4 + e)
     if kind == "gate_up":
         return 2 * F * H * e + M * H * e + M * F * e
-    if kind == "down":      # K-split into fp32 partial sums: weights + input + S partial outputs
-        return H * F * e + M * F * e + 4 * M * H * 4
+    if kind == "down":      # one K range: weights + input + residual in and out, next input
+        return H * F * e + M * F * e + M * H * (4 + 4 + e)
     if kind == "reduce":    # S partials + residual in, residual + next input + norm partials out
         return 4 * M * H * 4 + M * H * 4 + M * H * (4 + e) + M * (H // 16) * 4
     if kind == "lm_head":
@@ -857,8 +857,9 @@ def main():
         for k in range(args.profile_steps):
             run(args.warmup + k)
         us, launches = model.profile_read(reset=True)
-        n = max(launches, 1)
-        breakdown[kind] = {"avg_us": us / n, "us_per_round": us / args.profile_steps,
+        if launches == 0:       # a kind this model's shapes never launch (the K-split reduce)
+            continue
+        breakdown[kind] = {"avg_us": us / launches, "us_per_round": us / args.profile_steps,
                            "launches_per_round": launches / args.profile_steps}
     model.profile_kernel(None)
     dom = max(breakdown, key=lambda k: breakdown[k]["us_per_round"])

@@ -55,7 +55,9 @@ extern "C" {
  * pairing), grouped-query attention, SwiGLU MLP, no biases, untied LM head.
  * Constraints:
  *   - hidden, n_heads*head_dim and ffn are multiples of 128. The reduction
- *     lengths hidden, n_heads*head_dim and ffn are 128 times a power of two.
+ *     lengths hidden, n_heads*head_dim and ffn are 128 times a power of two;
+ *     hidden <= 2048, n_heads*head_dim <= 4096 (bf16) / 2048 (f32), and
+ *     ffn <= 8192 (bf16) / 4096 (f32).
  *   - head_dim is 32 or 64.
  *   - n_heads/n_kv_heads is 1 or 4.
  *   - page_tokens == 16.

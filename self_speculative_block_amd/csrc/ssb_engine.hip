@@ -176,10 +176,11 @@ void prof_collect(ssb_model* m) {
 }
 
 // Workgroup shape of a GEMM: NT 16-column tiles per workgroup, KSL K slices
-// per tile (8 waves in all), and S K ranges over the grid's y axis for a GEMM
-// with too few tiles to cover the CUs (its epilogue then runs in
-// k_resid_reduce).  Each wave chains 4..16 K steps (bf16) or 1..4 (f32).
-// The shape depends on the GEMM's dimensions only, never on the row count.
+// per tile (8 waves in all), and, for a residual GEMM whose K is too long for
+// one workgroup (EPI_PARTIAL requested), S K ranges over the grid's y axis
+// (its epilogue then runs in k_resid_reduce).  Each wave chains 4..16 K steps
+// (bf16) or 1..4 (f32).  The shape depends on the GEMM's dimensions only,
+// never on the row count.
 GemmShape plan_gemm(int K, int n_tiles, int elem, int epi) {
   const int KS = elem == 2 ? 32 : 16, ksteps = K / KS;
   const int kmin = elem == 2 ? 4 : 1, kmax = elem == 2 ? 16 : 4;
@@ -189,12 +190,11 @@ GemmShape plan_gemm(int K, int n_tiles, int elem, int epi) {
   g.KSL = epi == EPI_SWIGLU ? 4 : epi == EPI_LOGITS ? 2 : 8;
   g.S = 1;
   g.n_tiles = (n_tiles + g.NT - 1) / g.NT * g.NT;
-  if (epi == EPI_PARTIAL)
-    while (g.n_tiles / g.NT * g.S < 256 && g.S < 8 && ksteps / (2 * g.S * g.KSL) >= kmin) g.S *= 2;
   while (g.KSL > 1 && ksteps / (g.S * g.KSL) < kmin) g.KSL /= 2;
   while (ksteps / (g.S * g.KSL) > kmax) {
     if (g.NT * g.KSL < 8) g.KSL *= 2;
     else if (g.NT > 1 && n_tiles % (g.NT / 2) == 0) { g.NT /= 2; g.KSL *= 2; g.n_tiles = (n_tiles + g.NT - 1) / g.NT * g.NT; }
+    else if (epi == EPI_PARTIAL && g.S < 8) g.S *= 2;   // split K over workgroups, reduced afterwards
     else fail(SSB_EINVAL, "reduction length too large for the GEMM kernel");
   }
   const int kpw = ksteps / (g.S * g.KSL);
@@ -216,9 +216,10 @@ void check_config(const ssb_config* c) {
       "n_heads*head_dim must be 128 * 2^k");
   req(c->ffn % 128 == 0 && pow2(c->ffn / 128), "ffn must be 128 * 2^k");
   req(c->hidden <= 16 * kMaxNormParts, "hidden above 2048 is not supported");
-  req(c->ffn <= (c->dtype == SSB_BF16 ? 4096 : 2048) && c->hidden <= (c->dtype == SSB_BF16 ? 4096 : 2048) &&
-          c->n_heads * c->head_dim <= (c->dtype == SSB_BF16 ? 4096 : 2048),
-      "reduction lengths above 4096 (bf16) / 2048 (f32) are not supported");
+  req(c->hidden <= (c->dtype == SSB_BF16 ? 4096 : 2048) && c->n_heads * c->head_dim <= (c->dtype == SSB_BF16 ? 4096 : 2048),
+      "hidden and n_heads*head_dim above 4096 (bf16) / 2048 (f32) are not supported");
+  // the down projection (reduction length ffn) splits K over workgroups when one cannot hold it
+  req(c->ffn <= (c->dtype == SSB_BF16 ? 8192 : 4096), "ffn above 8192 (bf16) / 4096 (f32) is not supported");
   req(c->vocab >= 2, "vocab must be >= 2");
   req(c->mask_id >= 0 && c->mask_id < c->vocab, "mask_id out of range");
   req(c->eos_id >= 0 && c->eos_id < c->vocab && c->eos_id != c->mask_id, "eos_id out of range or == mask_id");

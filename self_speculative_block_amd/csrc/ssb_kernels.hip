@@ -308,10 +308,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   const T* xb = reinterpret_cast<const T*>(a.x) + split * KR;
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0, a.M * a.ldx * (int)sizeof(T), kBufWord3);
-  uint4 xs[SB];
+  // a 16-row slab of a 4096-long K range (the down projection) has 8192 fragments: 16 per thread
+  constexpr int SBX = SB + ((MT == 1 && KPW == 16) ? 4 : 0);
+  uint4 xs[SBX];
   auto load_slab = [&](int mbase) {
 #pragma unroll
-    for (int b = 0; b < SB; ++b) {
+    for (int b = 0; b < SBX; ++b) {
       const int e = min((int)threadIdx.x + b * NTH, total - 1);
       const int off = ((mbase + (e >> fsh)) * a.ldx + split * KR + (e & (FPR - 1)) * PER) * (int)sizeof(T);
       xs[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
@@ -359,11 +361,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   // ---- stores to LDS: the slab and the epilogue inputs of row block m_base ----
   auto stage = [&]() {
 #pragma unroll
-    for (int b = 0; b < SB; ++b) {
+    for (int b = 0; b < SBX; ++b) {
       const int e = threadIdx.x + b * NTH;
       if (e < total) *reinterpret_cast<uint4*>(slab + (e >> fsh) * XSTR + (e & (FPR - 1)) * 16) = xs[b];
     }
-    for (int e = threadIdx.x + SB * NTH; e < total; e += NTH) {   // K ranges above SB*NTH fragments
+    for (int e = threadIdx.x + SBX * NTH; e < total; e += NTH) {   // K ranges above SBX*NTH fragments
       const int r = e >> fsh, q = e & (FPR - 1);
       *reinterpret_cast<uint4*>(slab + r * XSTR + q * 16) =
           m_base + r <= m_last ? *reinterpret_cast<const uint4*>(xb + (size_t)(m_base + r) * a.ldx + q * PER)
@@ -1517,15 +1519,16 @@ static hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
   const GemmLds L = gemm_lds(MT, KR * (int)sizeof(T), a.NT, a.KSL, a.n_ssq, EPI);
   const int m_blocks = (a.M + 16 * MT - 1) / (16 * MT);
   int gx = a.n_tiles / a.NT;
-  if constexpr (MT == 3) {
+  if constexpr (MT == 3 || MT == 1) {
     if (m_blocks >= 5) {
       // many row blocks: one tile group per workgroup, which walks gz-strided row blocks with
       // its weights held in registers.  One such workgroup fits a CU (LDS and registers), so
-      // the grid stays within one workgroup per CU, with at least two row blocks each.  (With
-      // up to 3 row blocks the parallel grid measured faster; from 5 the loop wins, by 6% at
-      // 198 rows, 13-15% at 264-528 and 18% at 1040.)
+      // the grid stays within one workgroup per CU; 48-row blocks keep at least two per
+      // workgroup.  (With up to 3 row blocks the parallel grid measured faster; from 5 the loop
+      // wins, by 6% at 198 rows, 13-15% at 264-528 and 18% at 1040.  The 16-row blocks of the
+      // 4096-long down projection spread as widely as the CUs allow.)
       const int want = kGemmPersistentWgs / (gx * a.S);
-      const int gz = max(1, min(want, m_blocks / 2));
+      const int gz = max(1, min(want, MT == 1 ? m_blocks : m_blocks / 2));
       const dim3 grid(gx, a.S, gz), block(kGemmThreads);
       SSB_LAUNCH((k_gemm<T, MT, EPI, KPW, true>), grid, block, L.total, st, a);
       return hipGetLastError();

@@ -51,11 +51,12 @@ def test_config_validation(lib):
     bad = [dict(head_dim=48), dict(hidden=1000), dict(hidden=384), dict(n_kv_heads=3), dict(n_kv_heads=8),
            dict(ffn=3000), dict(mask_id=60000), dict(eos_id=59999), dict(block_B=65), dict(page_tokens=32),
            dict(max_rows=0), dict(max_rows=4000), dict(max_rows=16, block_B=32), dict(dtype=7),
-           dict(max_positions=1), dict(n_layers=0)]
+           dict(max_positions=1), dict(n_layers=0), dict(ffn=16384), dict(n_heads=128, n_kv_heads=32)]
     for kw in bad:
         assert lib.ssb_check_config(ctypes.byref(_cfg(**kw))) == SSB_EINVAL, kw
         assert lib.ssb_last_error()
     assert lib.ssb_check_config(None) == SSB_EINVAL
+    assert lib.ssb_check_config(ctypes.byref(_cfg(ffn=8192))) == SSB_OK     # split down projection
     tiny = _cfg(n_layers=2, hidden=128, n_heads=4, n_kv_heads=4, head_dim=32, ffn=512, vocab=512, mask_id=511,
                 eos_id=510, block_B=8, dtype=0)
     assert lib.ssb_check_config(ctypes.byref(tiny)) == SSB_OK
