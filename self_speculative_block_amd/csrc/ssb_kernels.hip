@@ -1576,7 +1576,11 @@ static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t st) {
   if (fit == 0 || a.NT * a.KSL > kGemmThreads / kWave || a.n_tiles % a.NT != 0 || a.n_ssq > kMaxNormParts ||
       a.n_ssq % 8 != 0)
     return hipErrorInvalidValue;
-  const int want = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 3;
+  // Row tile height never changes a row's arithmetic (each row's K slices are summed in the same
+  // order), only the launch shape.  Up to 64 rows the residual GEMMs (O projection) run fastest
+  // in 16-row blocks: three or four times the workgroups, each staging a third of the slab;
+  // the QKV and gate|up GEMMs measured slower that way and keep the taller tiles.
+  const int want = (EPI == EPI_RESID && a.M <= 64) ? 1 : a.M <= 16 ? 1 : a.M <= 32 ? 2 : 3;
   const int MT = want < fit ? want : fit;
   if (EPI == EPI_RESID && a.NT * MT * 16 * 16 > 2 * kGemmThreads) return hipErrorInvalidValue;
   if (EPI == EPI_PARTIAL && (a.S < 2 || a.S > 8)) return hipErrorInvalidValue;
