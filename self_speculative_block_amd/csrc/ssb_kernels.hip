@@ -720,6 +720,32 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     const int tg = tn0 + wc * CT + c;
+    // QKV: this tile column's rotary factors and KV slots for all RT row tiles, loaded before
+    // any is used (loads inside the per-tile branches below were each awaited on the spot)
+    const int qq = q & 1;
+    int slr[RT];
+    float4 csr[RT][2];
+    float4 hr[RT], gn;                   // RESID: residual rows and next-norm gains, likewise
+    if constexpr (EPI == EPI_RESID) {
+      const int n0 = tg * 16 + 4 * q;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int mcr = min(m0 + 16 * (wr * RT + r) + lane % 16, a.M - 1);
+        hr[r] = *reinterpret_cast<const float4*>(a.h + (size_t)mcr * a.hidden + n0);
+      }
+      gn = *reinterpret_cast<const float4*>(a.gain_next + n0);
+    }
+    if constexpr (EPI == EPI_QKV) {
+      const int half = a.head_dim / 2, jj = tg % (a.head_dim / 16);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int mcr = min(m0 + 16 * (wr * RT + r) + lane % 16, a.M - 1);
+        slr[r] = a.row_slot[mcr];
+        const float4* cp = reinterpret_cast<const float4*>(a.row_cs + (size_t)mcr * half + 8 * jj + 4 * qq);
+        csr[r][0] = cp[0];
+        csr[r][1] = cp[1];
+      }
+    }
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const int rl = 16 * (wr * RT + r) + lane % 16;     // row within the block
@@ -736,24 +762,25 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
         for (int i = 0; i < 4; ++i) z[i] = acc[c][r][i] * s_inv[rl];
 #pragma unroll
         for (int i = 0; i < 4; ++i) zo[i] = __shfl_xor(z[i], 32);   // the rotary partner column (c +- 8)
-        const int qq = q & 1;
         {
           bf16_t* dst;
           if (kind == 0) {
             dst = reinterpret_cast<bf16_t*>(a.q) + (size_t)mc * a.q_ld + head * hd;
           } else {
-            const int sl = a.row_slot[mc];
+            const int sl = slr[r];
             const size_t base = (((size_t)a.layer * a.n_pages + sl / kPage) * 2 + (kind - 1)) * a.n_kv + head;
             dst = reinterpret_cast<bf16_t*>(a.kv_pool) + (base * kPage + sl % kPage) * hd;
           }
+          const float csv[8] = {csr[r][0].x, csr[r][0].y, csr[r][0].z, csr[r][0].w,
+                                csr[r][1].x, csr[r][1].y, csr[r][1].z, csr[r][1].w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int pr = 8 * jj + 4 * qq + i;                      // rotary pair index
             const int dim = (q < 2 ? 0 : half) + pr;
             float o = z[i];
             if (kind != 2) {
-              const float2 cs = a.row_cs[(size_t)mc * half + pr];
-              o = q < 2 ? z[i] * cs.x - zo[i] * cs.y : z[i] * cs.x + zo[i] * cs.y;
+              const float cx = csv[2 * i], cy = csv[2 * i + 1];
+              o = q < 2 ? z[i] * cx - zo[i] * cy : z[i] * cx + zo[i] * cy;
             }
             if (ok) dst[dim] = f2bf(o);
           }
@@ -770,10 +797,12 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
         }
       } else {  // EPI_RESID
         const int n0 = tg * 16 + 4 * q;
+        const float hv[4] = {hr[r].x, hr[r].y, hr[r].z, hr[r].w};
+        const float gv[4] = {gn.x, gn.y, gn.z, gn.w};
         float sq = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = a.h[(size_t)mc * a.hidden + n0 + i] + acc[c][r][i];
+          const float v = hv[i] + acc[c][r][i];
           z[i] = v;
           sq += v * v;
         }
@@ -783,7 +812,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             a.h[(size_t)m * a.hidden + n0 + i] = z[i];
-            reinterpret_cast<bf16_t*>(a.xg_out)[(size_t)m * a.hidden + n0 + i] = f2bf(z[i] * a.gain_next[n0 + i]);
+            reinterpret_cast<bf16_t*>(a.xg_out)[(size_t)m * a.hidden + n0 + i] = f2bf(z[i] * gv[i]);
           }
           if (q == 0) a.ssq_out[(size_t)m * a.ssq_ld + tg] = sq;
         }
@@ -921,7 +950,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   constexpr int REC = HD + 4;
   constexpr int FPK = HD / PER;            // 16-byte fragments per key row
   constexpr int NKF = 2 * kKeyChunk * FPK; // K and V fragments of one chunk
-  constexpr int KVF = (NKF + NTH - 1) / NTH;
+  constexpr int KVF = NKF / NTH;
+  static_assert(NKF % NTH == 0, "every thread loads the same number of K/V fragments");
   __shared__ __align__(16) unsigned char ks[kKeyChunk * KSTR];
   __shared__ __align__(16) unsigned char vts[HD * VSTR];
   __shared__ int s_lim[16];
@@ -939,30 +969,31 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   // scores are kept in log2 units: s * scale * log2(e), so the softmax uses exp2
   const float qscale = a.scale * kLog2e;
 
-  // ---- first memory round trip: limits, query fragments, page ids ----
-  const int lim_v = threadIdx.x < 16 && mt * 16 + (int)threadIdx.x < task.nrows
-                        ? a.row_lim[task.row0 + mt * 16 + threadIdx.x] : -1;
-  uint4 qf[QKS];
-#pragma unroll
-  for (int st = 0; st < QKS; ++st) {
-    qf[st] = make_uint4(0, 0, 0, 0);
-    if (active && row_local < task.nrows)
-      qf[st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.q) +
-                                               (size_t)(task.row0 + row_local) * a.q_ld + head * HD + st * KS +
-                                               PER * (lane / 16));
-  }
+  // ---- first memory round trip: page ids, limits, query fragments (loads complete in issue
+  //      order, so the K/V addresses wait for the page ids only) ----
   const int cbeg = a.fold ? 0 : blockIdx.x;
   int pg[KVF];
 #pragma unroll
   for (int q = 0; q < KVF; ++q) {
-    const int f = min((int)threadIdx.x + q * NTH, NKF - 1);
+    const int f = (int)threadIdx.x + q * NTH;
     pg[q] = pt[(cbeg * kKeyChunk + (f % (kKeyChunk * FPK)) / FPK) / kPage];
+  }
+  // Branch-free as well (clamped to the task's last row and the last head): rows past the task
+  // and idle waves read real data that never reaches a written result (rows stay independent in
+  // both products; idle waves skip them).
+  const int lim_row = mt * 16 + (int)threadIdx.x % 16;
+  const int lim_ld = a.row_lim[task.row0 + min(lim_row, task.nrows - 1)];
+  uint4 qf[QKS];
+  {
+    const T* qp = reinterpret_cast<const T*>(a.q) + (size_t)(task.row0 + min(row_local, task.nrows - 1)) * a.q_ld +
+                  min(head, a.n_heads - 1) * HD + PER * (lane / 16);
+#pragma unroll
+    for (int st = 0; st < QKS; ++st) qf[st] = *reinterpret_cast<const uint4*>(qp + st * KS);
   }
   // largest visibility limit of the task's rows
   const int maxlim = task.lim_mode == 0 ? task.max_lim : a.req->p[task.req] + a.req->B + (task.lim_mode == 2 ? 1 : 0);
   const int cend = a.fold ? maxlim / kKeyChunk + 1 : cbeg + 1;
   if (cbeg * kKeyChunk > maxlim) return;     // no visible key in this chunk slot
-  if (threadIdx.x < 16) s_lim[threadIdx.x] = lim_v;
 
   float run_m = -INFINITY, run_l = 0.f;
   f32x4_t run_o[DT];
@@ -973,32 +1004,34 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     if (c != cbeg) {
 #pragma unroll
       for (int q = 0; q < KVF; ++q) {
-        const int f = min((int)threadIdx.x + q * NTH, NKF - 1);
+        const int f = (int)threadIdx.x + q * NTH;
         pg[q] = pt[(c * kKeyChunk + (f % (kKeyChunk * FPK)) / FPK) / kPage];
       }
     }
-    // ---- second round trip: K and V of keys [c*64, c*64+64) that a row of the task may see ----
     uint4 kvv[KVF];
+    // ---- second round trip: K and V of keys [c*64, c*64+64) ----
+    // Unconditional loads: a conditional load makes the compiler wait for it inside its branch,
+    // which serialised the KVF round trips.  Every address is in the pool: the page list holds
+    // page 0 past the request's pages.  Keys past the task's limit are zeroed below (their
+    // scores are masked; a zero V keeps 0 * P finite).
 #pragma unroll
     for (int q = 0; q < KVF; ++q) {
       const int f = threadIdx.x + q * NTH;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
-      const int key = c * kKeyChunk + rem / FPK;
-      kvv[q] = make_uint4(0, 0, 0, 0);
-      if (f < NKF && key <= maxlim) {
-        const size_t base = (((size_t)a.layer * a.n_pages + pg[q]) * 2 + kv) * a.n_kv + g;
-        kvv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kv_pool) +
-                                                 (base * kPage + key % kPage) * HD + (rem % FPK) * PER);
-      }
+      const size_t base = (((size_t)a.layer * a.n_pages + pg[q]) * 2 + kv) * a.n_kv + g;
+      kvv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kv_pool) +
+                                               (base * kPage + rem / FPK % kPage) * HD + (rem % FPK) * PER);
     }
+    // (the row limits are stored once the K/V loads are in flight)
+    if (threadIdx.x < 16) s_lim[threadIdx.x] = lim_row < task.nrows ? lim_ld : -1;
 #pragma unroll
     for (int q = 0; q < KVF; ++q) {
       const int f = threadIdx.x + q * NTH;
-      if (f >= NKF) continue;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
       const int kk = rem / FPK, d0 = (rem % FPK) * PER;
+      if (c * kKeyChunk + kk > maxlim) kvv[q] = make_uint4(0, 0, 0, 0);
       if (kv == 0) {
         *reinterpret_cast<uint4*>(ks + kk * KSTR + d0 * (int)sizeof(T)) = kvv[q];
       } else {
@@ -1141,7 +1174,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, in
       mc[b] = ml.x; lc[b] = ml.y;
       oc[b] = rec[c * REC + min(lane, HD - 1)];
     }
-    const int nvis = lim / kKeyChunk + 1;          // chunks that hold a visible key of this row
+    // chunks that hold a visible key of this row; the empty asm keeps this (loop-invariant) use of
+    // the limit inside the loop, so the record loads above are issued before the limit is awaited
+    int limv = lim;
+    asm volatile("" : "+v"(limv));
+    const int nvis = limv / kKeyChunk + 1;
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
@@ -1182,20 +1219,25 @@ __global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int
   const ReqArgs& ra = *rap;
   const int r = blockIdx.x, j = threadIdx.x;
   const int B = ra.B, row0 = ra.row0[r];
-  const bool mismatch = j < B && row_tok[row0 + 1 + j] != am[row0 + j];
-  const unsigned long long bal = __ballot(mismatch);
+  // Every load is unconditional (indices clamped into the request's B + 1 rows), so the few
+  // round trips overlap instead of each being awaited inside its own branch.
+  const int dj = row_tok[min(row0 + 1 + j, row0 + B)], aj = am[min(row0 + j, row0 + B)];
+  const unsigned long long bal = __ballot(j < B && dj != aj);
   const int A = bal ? __builtin_ctzll(bal) : B;
   int32_t* o = out + (size_t)r * out_stride;
-  // candidate commit list: k = 0 -> a0, k >= 1 -> a_k = am[row0 + k - 1]
+  // candidate commit list: k = 0 -> a0, k >= 1 -> a_k = am[row0 + k - 1]; lane j holds
+  // candidates j and j + 64, the first EOS among them cuts the list
   const int ncand = A + 2;
-  int eos_at = ncand;
-  for (int k = 0; k < ncand; ++k) {
-    const int tk = k == 0 ? row_tok[row0] : am[row0 + k - 1];
-    if (tk == eos_id) { eos_at = k; break; }
-  }
+  auto cand = [&](int k) { return k == 0 ? row_tok[row0] : am[row0 + k - 1]; };
+  const int k1 = j, k2 = j + 64;
+  const int t1 = cand(min(k1, ncand - 1)), t2 = cand(min(k2, ncand - 1));
+  const unsigned long long e1 = __ballot(k1 < ncand && t1 == eos_id);
+  const unsigned long long e2 = __ballot(k2 < ncand && t2 == eos_id);
+  const int eos_at = e1 ? __builtin_ctzll(e1) : (e2 ? 64 + __builtin_ctzll(e2) : ncand);
   int n = min(ncand, eos_at + 1);
   n = min(n, ra.max_commit[r]);
-  for (int k = j; k < n; k += 64) o[4 + k] = k == 0 ? row_tok[row0] : am[row0 + k - 1];
+  if (k1 < n) o[4 + k1] = t1;
+  if (k2 < n) o[4 + k2] = t2;
   if (j == 0) {
     o[0] = A;
     o[1] = n;
