@@ -211,7 +211,7 @@ hipError_t launch_pack(uint4* dst, int n_tiles, int K, int mode, const void* s0,
 template <typename T> hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
 template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
 template <typename T> hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st);
-hipError_t launch_gemm_big(const GemmArgs& a, int epi, hipStream_t st);
+hipError_t launch_gemm_big(const GemmArgs& a, int epi, bool exact, hipStream_t st);
 int gemm_max_mt(int elem, int K, int S, int NT, int KSL, int n_ssq, int epi);
 // gs (nullable, then zs too): per-group exp-sums of the LM head at scale sc = log2(e) / T;
 // zs [M] gets the row's sum of exp((z - top1) / T) over the vocabulary without [M].

@@ -181,6 +181,12 @@ void prof_collect(ssb_model* m) {
 // (its epilogue then runs in k_resid_reduce).  Each wave chains 4..16 K steps
 // (bf16) or 1..4 (f32).  The shape depends on the GEMM's dimensions only,
 // never on the row count.
+// Decode forwards of many rows (batched rounds) run a layer GEMM in the large-tile kernel's
+// exact form from these row counts on (measured crossovers against k_gemm's looped form at
+// 132 / 264 / 528 / 1040 rows: QKV 17 vs 26 us at 528 rows, O and down 15 vs 23 and 38 vs 60 us
+// at 1040, gate|up 75 vs 79 us at 1040 but 49 vs 43 at 528).
+constexpr int kExactRowsQkv = 384, kExactRowsO = 768, kExactRowsGateUp = 1024, kExactRowsDown = 768;
+
 GemmShape plan_gemm(int K, int n_tiles, int elem, int epi) {
   const int KS = elem == 2 ? 32 : 16, ksteps = K / KS;
   const int kmin = elem == 2 ? 4 : 1, kmax = elem == 2 ? 16 : 4;
@@ -470,8 +476,13 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   // records, no combine launch); decode windows split keys over workgroups and combine
   const bool tall = f.mode == PREP_PREFILL || f.mode == PREP_TOKENS;
   at.fold = (tall || M > m->max_decode_rows) ? 1 : 0;
-  // tall bf16 forwards use the large-tile GEMM (no decode row is computed there)
+  // tall bf16 forwards use the large-tile GEMM (no decode row is computed there); decode
+  // forwards of many rows (batched rounds) use its exact form, which reproduces k_gemm's
+  // arithmetic bit for bit (k_gemm keeps the small-M shapes it is fast at)
   const bool big = tall && m->elem == 2 && M >= 128;
+  const bool dec_big = !tall && m->elem == 2;
+  const bool x_qkv = dec_big && M >= kExactRowsQkv, x_o = dec_big && M >= kExactRowsO;
+  const bool x_gu = dec_big && M >= kExactRowsGateUp, x_down = dec_big && M >= kExactRowsDown;
   at.scale = 1.0f / std::sqrt((float)c.head_dim);
   // row tasks: windows of each request (draft/verify) or one request's rows
   at.tasks.n = 0;
@@ -498,7 +509,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       set_w(a, m->qkv[l]);
       a.x = m->xg; a.ldx = H;
       prof_begin(m, SSB_K_QKV, st);
-      hip_check(big ? launch_gemm_big(a, EPI_QKV, st) : launch_gemm<T>(a, EPI_QKV, st), "qkv gemm");
+      hip_check(big || x_qkv ? launch_gemm_big(a, EPI_QKV, x_qkv, st) : launch_gemm<T>(a, EPI_QKV, st), "qkv gemm");
       prof_end(m, SSB_K_QKV, st);
     }
     at.layer = l;
@@ -517,7 +528,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       a.x = m->attn; a.ldx = qd;
       a.gain_next = m->mlp_norm[l];
       prof_begin(m, SSB_K_O, st);
-      hip_check(big ? launch_gemm_big(a, EPI_RESID, st) : launch_gemm<T>(a, EPI_RESID, st), "o gemm");
+      hip_check(big || x_o ? launch_gemm_big(a, EPI_RESID, x_o, st) : launch_gemm<T>(a, EPI_RESID, st), "o gemm");
       prof_end(m, SSB_K_O, st);
     }
     {  // gate|up + SwiGLU
@@ -525,7 +536,8 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       set_w(a, m->gu[l]);
       a.x = m->xg; a.ldx = H;
       prof_begin(m, SSB_K_GATEUP, st);
-      hip_check(big ? launch_gemm_big(a, EPI_SWIGLU, st) : launch_gemm<T>(a, EPI_SWIGLU, st), "gate/up gemm");
+      hip_check(big || x_gu ? launch_gemm_big(a, EPI_SWIGLU, x_gu, st) : launch_gemm<T>(a, EPI_SWIGLU, st),
+                "gate/up gemm");
       prof_end(m, SSB_K_GATEUP, st);
     }
     {  // down + residual; next input xg = h * (next attn_norm | final_norm)
@@ -534,7 +546,8 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       a.x = m->act; a.ldx = c.ffn;
       a.gain_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
       prof_begin(m, SSB_K_DOWN, st);
-      if (big) hip_check(launch_gemm_big(a, EPI_RESID, st), "down gemm");
+      const bool dexact = x_down && a.S == 1;   // a K-split down projection stays on k_gemm
+      if (big || dexact) hip_check(launch_gemm_big(a, EPI_RESID, dexact, st), "down gemm");
       else hip_check(launch_gemm<T>(a, a.S > 1 ? EPI_PARTIAL : EPI_RESID, st), "down gemm");
       prof_end(m, SSB_K_DOWN, st);
       if (a.S > 1 && !big) {

@@ -603,8 +603,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
 // fragments of 1 KiB, 2RT activation fragments of 1 KiB in MFMA operand
 // layout) go straight from global memory to LDS (16 B per lane), NS steps in
 // flight, one barrier per step; each wave multiplies its RT x CT 16x16 tiles
-// from LDS.  Used only for forwards without decode rows, so the row-count
-// independence of k_gemm is not needed here.
+// from LDS.  Forwards without decode rows (prefill, teacher forcing) use it as
+// is.  EXACT: the per-element arithmetic of k_gemm, for tall decode forwards
+// (batched rounds): each K slice of k_gemm's plan (a.KSL slices of
+// ksteps/a.KSL steps) gets its own MFMA chain from zero and the slices are
+// added in order; 1/rms, RoPE, SwiGLU and the residual sums of squares follow
+// k_gemm's operation order; no multiply-add contraction.  A row's results are
+// then bit-identical to k_gemm's, whatever the row count or tile shape.
 // ---------------------------------------------------------------------------
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -626,8 +631,9 @@ __device__ __forceinline__ void load_lds16(const void* gptr, unsigned lds_base) 
                : "memory", "m0");
 }
 
-template <int EPI, int RT, int CT, int NS>
+template <int EPI, int RT, int CT, int NS, bool EXACT>
 __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
+#pragma clang fp contract(off)
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
   constexpr int NF = 2 * CT + 2 * RT;      // 1 KiB fragments per step: weights first, then activations
   constexpr int FPW = NF / 4;              // fragments each wave stages per step
@@ -665,7 +671,18 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
     for (int i = 0; i < FPW; ++i) load_lds16(src[i] + (size_t)ss * stride[i], buf + (wave + 4 * i) * 1024);
   };
 
-  if constexpr (NORM) {
+  if constexpr (NORM && EXACT) {
+    // k_gemm's order: G = n_ssq/4 lanes per row each add their 4 partials in column order,
+    // then the same fixed butterfly over the row's G lanes
+    const int G = a.n_ssq / 4, gsh = 31 - __builtin_clz(G), RP = 256 >> gsh;
+    for (int k = 0; k * RP < BM; ++k) {
+      const int row = k * RP + ((int)threadIdx.x >> gsh);
+      const int m = min(m0 + min(row, BM - 1), a.M - 1);
+      const float4 sv = *reinterpret_cast<const float4*>(a.ssq + (size_t)m * a.ssq_ld + ((int)threadIdx.x & (G - 1)) * 4);
+      const float sum = lane_group_sum(((sv.x + sv.y) + sv.z) + sv.w, G);
+      if (((int)threadIdx.x & (G - 1)) == 0 && row < BM) s_inv[row] = 1.0f / sqrtf(sum / (float)a.hidden + a.eps);
+    }
+  } else if constexpr (NORM) {
     // 1/rms of the block's rows from the per-16-column sums of squares, two threads per row
     const int r = threadIdx.x / 2, h2 = threadIdx.x % 2;
     float sum = 0.f;
@@ -695,6 +712,11 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
     for (int r = 0; r < RT; ++r) x[r] = *reinterpret_cast<const uint4*>(buf + (2 * CT + wr * RT + r) * 1024 + lane * 16);
   };
   uint4 wf[CT], xf[RT];
+  // EXACT: acc holds the current K slice's chain, tot the slices so far (added in slice order)
+  f32x4_t tot[CT][RT];
+  const int kpw = EXACT ? ksteps / a.KSL : ksteps;
+  int left = kpw;
+  bool first_slice = true;
   wait_vmcnt<FPW * (NS - 1)>();            // step 0 has landed
   __syncthreads();
   rd(0, wf, xf);
@@ -708,12 +730,31 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int r = 0; r < RT; ++r) mma_step(acc[c][r], wf[c], xf[r], bf16_t());
+    if constexpr (EXACT) {
+      if (--left == 0) {                   // end of a K slice (uniform)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            tot[c][r] = first_slice ? acc[c][r] : tot[c][r] + acc[c][r];
+            acc[c][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        first_slice = false;
+        left = kpw;
+      }
+    }
 #pragma unroll
     for (int c = 0; c < CT; ++c) wf[c] = wn[c];
 #pragma unroll
     for (int r = 0; r < RT; ++r) xf[r] = xn[r];
   }
   wait_vmcnt<0>();
+  if constexpr (EXACT) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[c][r] = tot[c][r];
+  }
 
   // epilogue: element i of lane l of tile (c, r) is row 16 r' + l%16, column 16 tg + 4(l/16) + i
   const int q = lane / 16;
@@ -806,8 +847,20 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
           z[i] = v;
           sq += v * v;
         }
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
+        if constexpr (EXACT) {
+          // k_gemm's order: the tile row's 16 squares added one after another
+          sq = 0.f;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float v = __shfl(z[i], lane % 16 + 16 * qq);
+              sq += v * v;
+            }
+        } else {
+          sq += __shfl_xor(sq, 16);
+          sq += __shfl_xor(sq, 32);
+        }
         if (ok) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -1644,35 +1697,49 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
 template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
 template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
 
-template <int EPI, int RT, int CT, int NS>
+template <int EPI, int RT, int CT, int NS, bool EXACT>
 static hipError_t launch_gemm_big_cfg(const GemmArgs& a, hipStream_t st) {
   constexpr int NF = 2 * CT + 2 * RT;
   const dim3 grid(a.n_tiles / (2 * CT), (a.M + 32 * RT - 1) / (32 * RT));
   const int shm = NS * NF * 1024 + 32 * RT * 4;
-  SSB_LAUNCH((k_gemm_big<EPI, RT, CT, NS>), grid, dim3(256), shm, st, a);
+  SSB_LAUNCH((k_gemm_big<EPI, RT, CT, NS, EXACT>), grid, dim3(256), shm, st, a);
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool EXACT>
 static hipError_t launch_gemm_big_epi(const GemmArgs& a, hipStream_t st) {
   // the largest tile that still gives about one workgroup per CU
   const int rb4 = (a.M + 127) / 128;
   // (LDS: 3 steps of 16 KiB, 4 of 12 KiB, 6 of 8 KiB: two or three workgroups per CU; deeper
   // pipelines with one workgroup per CU measured slower)
-  if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3>(a, st);
-  if (a.n_tiles % 4 == 0 && (a.n_tiles / 4) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 2, 4>(a, st);
-  if (a.n_tiles % 4 == 0) return launch_gemm_big_cfg<EPI, 2, 2, 6>(a, st);
+  if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3, EXACT>(a, st);
+  if (a.n_tiles % 4 == 0 && (a.n_tiles / 4) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 2, 4, EXACT>(a, st);
+  if (a.n_tiles % 4 == 0) return launch_gemm_big_cfg<EPI, 2, 2, 6, EXACT>(a, st);
   return hipErrorInvalidValue;
 }
 
-// Prefill / teacher-forced GEMM (bf16, M >= 1): epilogues QKV, RESID (no K split) and SWIGLU.
-hipError_t launch_gemm_big(const GemmArgs& a, int epi, hipStream_t st) {
+// Large-tile GEMM (bf16, M >= 1): epilogues QKV, RESID (no K split) and SWIGLU.  exact: the
+// arithmetic of k_gemm for the same plan (a.S == 1, a.KSL slices), for tall decode forwards.
+hipError_t launch_gemm_big(const GemmArgs& a, int epi, bool exact, hipStream_t st) {
   if (a.M < 1 || a.K % Ty<bf16_t>::kStepK != 0 || a.n_tiles % 4 != 0) return hipErrorInvalidValue;
   if ((epi == EPI_QKV || epi == EPI_SWIGLU) && (a.n_ssq % 2 != 0 || a.n_ssq < 2)) return hipErrorInvalidValue;
+  if (exact) {
+    const int ksteps = a.K / Ty<bf16_t>::kStepK;
+    const int G = a.n_ssq / 4;
+    if (a.S != 1 || a.KSL < 1 || ksteps % a.KSL != 0) return hipErrorInvalidValue;
+    if ((epi == EPI_QKV || epi == EPI_SWIGLU) && (a.n_ssq % 4 != 0 || G > 64 || (G & (G - 1)) != 0))
+      return hipErrorInvalidValue;
+    switch (epi) {
+      case EPI_QKV: return launch_gemm_big_epi<EPI_QKV, true>(a, st);
+      case EPI_RESID: return launch_gemm_big_epi<EPI_RESID, true>(a, st);
+      case EPI_SWIGLU: return launch_gemm_big_epi<EPI_SWIGLU, true>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (epi) {
-    case EPI_QKV: return launch_gemm_big_epi<EPI_QKV>(a, st);
-    case EPI_RESID: return launch_gemm_big_epi<EPI_RESID>(a, st);
-    case EPI_SWIGLU: return launch_gemm_big_epi<EPI_SWIGLU>(a, st);
+    case EPI_QKV: return launch_gemm_big_epi<EPI_QKV, false>(a, st);
+    case EPI_RESID: return launch_gemm_big_epi<EPI_RESID, false>(a, st);
+    case EPI_SWIGLU: return launch_gemm_big_epi<EPI_SWIGLU, false>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

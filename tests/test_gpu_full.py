@@ -162,16 +162,18 @@ def test_spec_decode_equals_ar_decode_and_oracle(full):
     assert kv.prefill(pre_dev) == full["y1"]
 
 
-@pytest.mark.parametrize("Bb,R", [(32, 4), (32, 8), (64, 4)])
+@pytest.mark.parametrize("Bb,R", [(32, 4), (32, 8), (64, 4), (32, 16), (64, 16)])
 def test_batched_round_equals_single_rounds(full, Bb, R):
     """A ragged batched round (R requests of different lengths, one launch per stage) gives each
     request exactly what its own single round gives: tokens, accept length and state, and its
     draft and verify logits bit for bit.  132 rows run the GEMMs' parallel grid; 260 and 264 rows
-    the looped form (several 48-row blocks per workgroup)."""
+    the looped form (several 48-row blocks per workgroup); 528 rows the large-tile exact form for
+    QKV, 1040 rows for all four layer GEMMs."""
     from self_speculative_block_amd.engine import KV, round_batch
     cfg, model, pool = full["cfg"], full["model"], full["pool"]
     wl5 = workload(5)
-    lens = [1088, 1000, 1100, 1200] if R == 4 else [600, 520, 700, 650, 480, 560, 610, 530]
+    lens = {4: [1088, 1000, 1100, 1200], 8: [600, 520, 700, 650, 480, 560, 610, 530],
+            16: [300, 260, 340, 280, 320, 250, 310, 270, 330, 290, 260, 350, 240, 300, 280, 320]}[R]
     kvs, firsts, conts = [], [], []
     for i, P in enumerate(lens):
         pre = prefix_embeddings(wl5.wid, i, P, cfg.hidden)
@@ -185,8 +187,8 @@ def test_batched_round_equals_single_rounds(full, Bb, R):
         kvs.append(kv)
         firsts.append(y)
         conts.append(c)
-    astars = [0, Bb // 2, Bb, 3, 5, 1, Bb - 1, 7][:R]
-    budgets = [Bb + 2, Bb + 2, 5, Bb + 2, Bb + 2, 3, Bb + 2, Bb + 2][:R]
+    astars = ([0, Bb // 2, Bb, 3, 5, 1, Bb - 1, 7] * 2)[:R]
+    budgets = ([Bb + 2, Bb + 2, 5, Bb + 2, Bb + 2, 3, Bb + 2, Bb + 2] * 2)[:R]
     plants = [build_plant(conts[r], 1, astars[r], Bb, cfg.vocab, cfg.mask_id) for r in range(R)]
     planted = torch.tensor(plants, dtype=torch.int32, device="cuda")
     got = round_batch(model, kvs, Bb, budgets, planted_dev=planted)          # graph replay
