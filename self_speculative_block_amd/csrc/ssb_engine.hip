@@ -186,6 +186,7 @@ void prof_collect(ssb_model* m) {
 // 132 / 264 / 528 / 1040 rows: QKV 17 vs 26 us at 528 rows, O and down 15 vs 23 and 38 vs 60 us
 // at 1040, gate|up 75 vs 79 us at 1040 but 49 vs 43 at 528).
 constexpr int kExactRowsQkv = 384, kExactRowsO = 768, kExactRowsGateUp = 1024, kExactRowsDown = 768;
+constexpr int kExactRowsLm = 256;   // LM head (records only; softmax-sum launches stay on k_gemm)
 
 GemmShape plan_gemm(int K, int n_tiles, int elem, int epi) {
   const int KS = elem == 2 ? 32 : 16, ksteps = K / KS;
@@ -575,7 +576,9 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       rows = 1;
     }
     prof_begin(m, SSB_K_LMHEAD, st);
-    hip_check(launch_gemm<T>(a, EPI_LOGITS, st), "lm head gemm");
+    const bool x_lm = dec_big && rows >= kExactRowsLm && !a.am_s && a.NT == 4 && a.n_tiles % 8 == 0;
+    if (x_lm) hip_check(launch_gemm_big(a, EPI_LOGITS, true, st), "lm head gemm");
+    else hip_check(launch_gemm<T>(a, EPI_LOGITS, st), "lm head gemm");
     prof_end(m, SSB_K_LMHEAD, st);
     prof_begin(m, SSB_K_ARGMAX, st);
     float* top1 = f.st_max ? f.st_max : m->am_top1;

@@ -634,7 +634,8 @@ __device__ __forceinline__ void load_lds16(const void* gptr, unsigned lds_base) 
 template <int EPI, int RT, int CT, int NS, bool EXACT>
 __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 #pragma clang fp contract(off)
-  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU);
+  constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
+  static_assert(EPI != EPI_LOGITS || (EXACT && CT == 4), "LM head: exact form, one 4-tile group per wave");
   constexpr int NF = 2 * CT + 2 * RT;      // 1 KiB fragments per step: weights first, then activations
   constexpr int FPW = NF / 4;              // fragments each wave stages per step
   constexpr int BM = 32 * RT;
@@ -758,6 +759,46 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 
   // epilogue: element i of lane l of tile (c, r) is row 16 r' + l%16, column 16 tg + 4(l/16) + i
   const int q = lane / 16;
+  if constexpr (EPI == EPI_LOGITS) {
+    // LM head: a wave's 4 tiles are one 64-column group of k_gemm's plan.  Its (top1, id, top2)
+    // record per row is a function of the group's values alone (lowest id among equal maxima,
+    // second value of the multiset, NaN if any counted value is NaN), so the row's 4 lanes scan
+    // their columns in increasing order and merge.
+    const int grp = (tn0 + wc * CT) / 4;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int rl = 16 * (wr * RT + r) + lane % 16;
+      const int m = m0 + rl;
+      const float inv = s_inv[rl];
+      Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
+      bool nan = false;
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = (tn0 + wc * CT + c) * 16 + 4 * q + i;
+          const float z = acc[c][r][i] * inv;
+          if (a.logits && m < a.M && col < a.vocab) a.logits[(size_t)m * a.vocab + col] = z;
+          if (col >= a.vocab || col == a.mask_id) continue;
+          if (z != z) { nan = true; continue; }
+          if (z > best.v1) { best.v2 = best.v1; best.v1 = z; best.i1 = col; }
+          else if (z > best.v2) { best.v2 = z; }
+        }
+      if (nan) best = Top2{NAN, -1, NAN};
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) {
+        const Top2 other{__shfl_xor(best.v1, o), __shfl_xor(best.i1, o), __shfl_xor(best.v2, o)};
+        best = merge_top2(best, other);
+      }
+      if (q == 0 && m < a.M) {
+        const size_t o = (size_t)m * a.am_ld + grp;
+        a.am_v1[o] = best.v1;
+        a.am_i1[o] = best.i1;
+        a.am_v2[o] = best.v2;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     const int tg = tn0 + wc * CT + c;
@@ -1708,18 +1749,24 @@ static hipError_t launch_gemm_big_cfg(const GemmArgs& a, hipStream_t st) {
 
 template <int EPI, bool EXACT>
 static hipError_t launch_gemm_big_epi(const GemmArgs& a, hipStream_t st) {
-  // the largest tile that still gives about one workgroup per CU
-  const int rb4 = (a.M + 127) / 128;
-  // (LDS: 3 steps of 16 KiB, 4 of 12 KiB, 6 of 8 KiB: two or three workgroups per CU; deeper
-  // pipelines with one workgroup per CU measured slower)
-  if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3, EXACT>(a, st);
-  if (a.n_tiles % 4 == 0 && (a.n_tiles / 4) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 2, 4, EXACT>(a, st);
-  if (a.n_tiles % 4 == 0) return launch_gemm_big_cfg<EPI, 2, 2, 6, EXACT>(a, st);
-  return hipErrorInvalidValue;
+  if constexpr (EPI == EPI_LOGITS) {
+    // 128 x 128 blocks: each wave's 64 columns are one LM head group
+    return a.n_tiles % 8 == 0 ? launch_gemm_big_cfg<EPI, 4, 4, 3, true>(a, st) : hipErrorInvalidValue;
+  } else {
+    // the largest tile that still gives about one workgroup per CU
+    const int rb4 = (a.M + 127) / 128;
+    // (LDS: 3 steps of 16 KiB, 4 of 12 KiB, 6 of 8 KiB: two or three workgroups per CU; deeper
+    // pipelines with one workgroup per CU measured slower)
+    if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3, EXACT>(a, st);
+    if (a.n_tiles % 4 == 0 && (a.n_tiles / 4) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 2, 4, EXACT>(a, st);
+    if (a.n_tiles % 4 == 0) return launch_gemm_big_cfg<EPI, 2, 2, 6, EXACT>(a, st);
+    return hipErrorInvalidValue;
+  }
 }
 
 // Large-tile GEMM (bf16, M >= 1): epilogues QKV, RESID (no K split) and SWIGLU.  exact: the
-// arithmetic of k_gemm for the same plan (a.S == 1, a.KSL slices), for tall decode forwards.
+// arithmetic of k_gemm for the same plan (a.S == 1, a.KSL slices), for tall decode forwards;
+// it also has the LM head's records (LOGITS, without the softmax sums).
 hipError_t launch_gemm_big(const GemmArgs& a, int epi, bool exact, hipStream_t st) {
   if (a.M < 1 || a.K % Ty<bf16_t>::kStepK != 0 || a.n_tiles % 4 != 0) return hipErrorInvalidValue;
   if ((epi == EPI_QKV || epi == EPI_SWIGLU) && (a.n_ssq % 2 != 0 || a.n_ssq < 2)) return hipErrorInvalidValue;
@@ -1733,6 +1780,8 @@ hipError_t launch_gemm_big(const GemmArgs& a, int epi, bool exact, hipStream_t s
       case EPI_QKV: return launch_gemm_big_epi<EPI_QKV, true>(a, st);
       case EPI_RESID: return launch_gemm_big_epi<EPI_RESID, true>(a, st);
       case EPI_SWIGLU: return launch_gemm_big_epi<EPI_SWIGLU, true>(a, st);
+      case EPI_LOGITS:   // records of 4-tile groups only (no softmax sums)
+        return a.am_s || a.NT != 4 ? hipErrorInvalidValue : launch_gemm_big_epi<EPI_LOGITS, true>(a, st);
       default: return hipErrorInvalidValue;
     }
   }
