@@ -1713,11 +1713,17 @@ static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t st) {
       a.n_ssq % 8 != 0)
     return hipErrorInvalidValue;
   // Row tile height never changes a row's arithmetic (each row's K slices are summed in the same
-  // order), only the launch shape.  Up to 64 rows the residual GEMMs (O projection) run fastest
-  // in 16-row blocks: three or four times the workgroups, each staging a third of the slab;
-  // the QKV and gate|up GEMMs measured slower that way and keep the taller tiles.
-  const int want = (EPI == EPI_RESID && a.M <= 64) ? 1 : a.M <= 16 ? 1 : a.M <= 32 ? 2 : 3;
-  const int MT = want < fit ? want : fit;
+  // order), only the launch shape.  The smallest tile whose grid still fits one workgroup per CU
+  // runs fastest: more, shorter blocks spread the slab staging over more CUs, while a grid past
+  // one workgroup per CU (the slab leaves room for one) runs in two rounds.  At 33 rows: QKV in
+  // 32-row blocks (192 workgroups; 7.8 -> 7.3 us against 48-row blocks, 7.9 in 16-row blocks),
+  // O in 16-row blocks (192; 7.3 -> 6.4 us), gate|up in 48-row blocks (256; 13.3 us in 32-row).
+  // (Never taller than the rows need: one block covers up to 16 * cap rows.)
+  const int gx = a.n_tiles / a.NT;
+  const int cap = min(fit, max(1, (a.M + 15) / 16));
+  int MT = cap;
+  for (int mt = 1; mt < cap; ++mt)
+    if ((long)gx * a.S * ((a.M + 16 * mt - 1) / (16 * mt)) <= kGemmPersistentWgs) { MT = mt; break; }
   if (EPI == EPI_RESID && a.NT * MT * 16 * 16 > 2 * kGemmThreads) return hipErrorInvalidValue;
   if (EPI == EPI_PARTIAL && (a.S < 2 || a.S > 8)) return hipErrorInvalidValue;
   if (MT == 1) return launch_gemm_mt<T, EPI, 1>(a, st);
