@@ -966,21 +966,29 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) t = merge_top2(t, rec[b]);
   }
-  sh[threadIdx.x] = t;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) sh[threadIdx.x] = merge_top2(sh[threadIdx.x], sh[threadIdx.x + s]);
-    __syncthreads();
+  // The merged record depends on the set of records only (largest value, lowest id among equal
+  // maxima, second value of the multiset, NaN if any is NaN), so the merge runs in any order:
+  // across each wave by shuffles, then across the waves in LDS (one barrier).
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    const Top2 other{__shfl_xor(t.v1, o), __shfl_xor(t.i1, o), __shfl_xor(t.v2, o)};
+    t = merge_top2(t, other);
   }
+  if (threadIdx.x % kWave == 0) sh[threadIdx.x / kWave] = t;
+  __syncthreads();
   if (threadIdx.x == 0) {
-    tok[m] = sh[0].i1;
-    top1[m] = sh[0].v1;
-    top2[m] = sh[0].v2;
+    Top2 r = sh[0];
+    for (int w = 1; w < kThreads / kWave; ++w) r = merge_top2(r, sh[w]);
+    sh[0] = r;
+    tok[m] = r.i1;
+    top1[m] = r.v1;
+    top2[m] = r.v2;
   }
   if (gs) {
     // the row's softmax denominator relative to its max, [M] excluded: the sum over groups of
     // gs_g * exp((v1_g - max) / T), groups in a fixed thread order and tree.  At T = 1 its
     // inverse is the greedy token's softmax probability.
+    __syncthreads();   // the merged record in sh[0]
     const float mx = sh[0].v1;
     float part = 0.f;
     for (int g = threadIdx.x; g < n_groups; g += kThreads) {
@@ -1247,13 +1255,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 // chunks: m* = max m_c, then l = sum l_c 2^(m_c - m*) and
 // o = sum o_c 2^(m_c - m*) in chunk order (maxima in log2 units); batches fold online.
 template <typename T, int HD>
-__global__ __launch_bounds__(kThreads) void k_attn_combine(const float* part, int max_chunks, int n_slots,
+__global__ __launch_bounds__(kWave) void k_attn_combine(const float* part, int max_chunks, int n_slots,
                                                           int n_heads, const int32_t* row_lim, int M, void* out,
                                                           int out_ld) {
   constexpr int REC = HD + 4;
   constexpr int BATCH = 32;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int idx = blockIdx.x * 4 + wave;
+  const int lane = threadIdx.x;
+  const int idx = blockIdx.x;
   if (idx >= M * n_heads) return;
   const int row = idx / n_heads, head = idx % n_heads;
   const int lim = row_lim[row];
@@ -1846,12 +1854,14 @@ template <typename T>
 hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, int n_heads, int head_dim,
                                const int32_t* row_lim, int M, void* out, int out_ld, hipStream_t st) {
   if (n_slots < 1 || n_slots > max_chunks) return hipErrorInvalidValue;
-  const int blocks = (M * n_heads + 3) / 4;
+  // one single-wave workgroup per (row, head): spread over every CU (4-wave workgroups on half
+  // the CUs measured 0.2-0.3 us slower per launch, 2-wave ones slower still)
+  const int blocks = M * n_heads;
   if (head_dim == 64)
-    SSB_LAUNCH((k_attn_combine<T, 64>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks, n_slots,
+    SSB_LAUNCH((k_attn_combine<T, 64>), dim3(blocks), dim3(kWave), 0, st, part, max_chunks, n_slots,
                        n_heads, row_lim, M, out, out_ld);
   else
-    SSB_LAUNCH((k_attn_combine<T, 32>), dim3(blocks), dim3(kThreads), 0, st, part, max_chunks, n_slots,
+    SSB_LAUNCH((k_attn_combine<T, 32>), dim3(blocks), dim3(kWave), 0, st, part, max_chunks, n_slots,
                        n_heads, row_lim, M, out, out_ld);
   return hipGetLastError();
 }
