@@ -162,7 +162,23 @@ def test_spec_decode_equals_ar_decode_and_oracle(full):
     assert kv.prefill(pre_dev) == full["y1"]
 
 
-@pytest.mark.parametrize("Bb,R", [(32, 4), (32, 8), (64, 4), (32, 16), (64, 16)])
+@pytest.mark.parametrize("Bs", [16, 24])
+def test_spec_decode_other_block_sizes_equal_ar(full, Bs):
+    """Windows of 17 and 25 rows take other GEMM row tiles than the 33-row window (QKV and O in
+    16-row blocks, gate|up in one 32-row block): self-speculative decoding still equals AR
+    decoding token for token."""
+    kv, pre_dev = full["kv"], full["pre_dev"]
+    kv.reset()
+    spec, stats = kv.decode(pre_dev, Bs, 64)
+    kv.reset()
+    ar, _ = kv.decode_ar(pre_dev, 64)
+    assert spec == ar
+    assert stats.rounds >= 1
+    kv.reset()
+    assert kv.prefill(pre_dev) == full["y1"]
+
+
+@pytest.mark.parametrize("Bb,R", [(32, 4), (32, 8), (64, 4), (32, 16), (64, 16), (24, 8)])
 def test_batched_round_equals_single_rounds(full, Bb, R):
     """A ragged batched round (R requests of different lengths, one launch per stage) gives each
     request exactly what its own single round gives: tokens, accept length and state, and its
