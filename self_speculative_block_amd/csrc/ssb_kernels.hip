@@ -439,11 +439,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   if (NORM && (first || MLOOP)) {
     // 1/rms of each row (needed only by the epilogue, so it runs behind the MFMA chain): each
     // lane adds its 4 partials in column order, then a fixed butterfly over the row's G lanes
+    // hidden is a power of two, so the product with its reciprocal is the quotient exactly; passes
+    // past the block's rows are skipped
+    const float rh = 1.0f / (float)a.hidden;
 #pragma unroll
     for (int k = 0; k < NPASS; ++k) {
+      if (k * RP >= MB) break;
       const float sum = lane_group_sum(((sv[k].x + sv[k].y) + sv[k].z) + sv[k].w, G);
       const int row = k * RP + ((int)threadIdx.x >> gsh);
-      if (((int)threadIdx.x & (G - 1)) == 0 && row < MB) s_inv[row] = 1.0f / sqrtf(sum / (float)a.hidden + a.eps);
+      if (((int)threadIdx.x & (G - 1)) == 0 && row < MB) s_inv[row] = 1.0f / sqrtf(sum * rh + a.eps);
     }
   }
   // 6. K-slice partial tiles added in slice order: element i of lane l of a tile is
@@ -676,12 +680,13 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
     // k_gemm's order: G = n_ssq/4 lanes per row each add their 4 partials in column order,
     // then the same fixed butterfly over the row's G lanes
     const int G = a.n_ssq / 4, gsh = 31 - __builtin_clz(G), RP = 256 >> gsh;
+    const float rh = 1.0f / (float)a.hidden;   // a power of two: x * rh == x / hidden
     for (int k = 0; k * RP < BM; ++k) {
       const int row = k * RP + ((int)threadIdx.x >> gsh);
       const int m = min(m0 + min(row, BM - 1), a.M - 1);
       const float4 sv = *reinterpret_cast<const float4*>(a.ssq + (size_t)m * a.ssq_ld + ((int)threadIdx.x & (G - 1)) * 4);
       const float sum = lane_group_sum(((sv.x + sv.y) + sv.z) + sv.w, G);
-      if (((int)threadIdx.x & (G - 1)) == 0 && row < BM) s_inv[row] = 1.0f / sqrtf(sum / (float)a.hidden + a.eps);
+      if (((int)threadIdx.x & (G - 1)) == 0 && row < BM) s_inv[row] = 1.0f / sqrtf(sum * rh + a.eps);
     }
   } else if constexpr (NORM) {
     // 1/rms of the block's rows from the per-16-column sums of squares, two threads per row
