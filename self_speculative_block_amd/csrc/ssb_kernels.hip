@@ -226,7 +226,7 @@ __device__ __forceinline__ float lane_group_sum(float v, int g) {
 // prefetched h tile [NT][MB][16] and the next gain [NT*16].
 template <typename T, int MB>
 __device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, const float* s_pre, int tg, int NT,
-                                               int m_base) {
+                                               int m_base, int m_end) {
 #pragma clang fp contract(off)
   const float* s_h = s_pre;
   const float* s_g = s_pre + NT * MB * 16;
@@ -236,7 +236,7 @@ __device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, 
     float* ct = ctile + (t * MB + r) * 17;
     const float v = s_h[e] + ct[n];
     ct[n] = v;
-    if (m >= a.M) continue;
+    if (m >= m_end) continue;
     const int col = (tg * NT + t) * 16 + n;
     a.h[(size_t)m * a.hidden + col] = v;
     reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * s_g[t * 16 + n]);
@@ -245,7 +245,7 @@ __device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, 
   for (int e = threadIdx.x; e < NT * MB; e += kGemmThreads) {
     const int t = e / MB, r = e % MB;
     const int m = m_base + r;
-    if (m >= a.M) continue;
+    if (m >= m_end) continue;
     const float* ct = ctile + (t * MB + r) * 17;
     float sum = 0.f;
     for (int n = 0; n < 16; ++n) sum += ct[n] * ct[n];
@@ -279,10 +279,22 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   // fragments in registers and walks the row blocks blockIdx.z, blockIdx.z + gridDim.z, ...,
   // loading the next block's slab while the current one is multiplied.
   constexpr bool LOOP = (EPI == EPI_LOGITS) && !MLOOP;
+  // DIRECT (one row block, one tile per workgroup, short K slices: QKV and O): no two waves share
+  // a K slice of the activations, so each wave loads its own MFMA operand fragments straight into
+  // registers (same bounded buffer resource) and the slab is not staged in LDS.  (O: 6.5 -> 6.0 us;
+  // the down projection's 16-step slices, 16 rows of 64 B per load, measured 0.4 us slower.)
+  constexpr bool DIRECT =
+      !MLOOP && !LOOP && KPW <= 4 && (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_PARTIAL);
   int tg = blockIdx.x;
   const int split = blockIdx.y;
   int mb = blockIdx.z;
-  int m_base = mb * MB;
+  // DIRECT GEMMs balance their row blocks (ceil(M / blocks) rows each, at most MB): at 33 rows in
+  // 16-row tiles 11 + 11 + 11 rows instead of 16 + 16 + 1, so no wave loads a full block's rows
+  // (QKV 7.2 -> 7.0 us).  A block's rows past its end read as zero and are left to the block that
+  // owns them.  (The down projection, which stages the whole slab anyway, measured slower so.)
+  const int rpb = DIRECT ? min(MB, (a.M + (int)gridDim.z - 1) / (int)gridDim.z) : MB;
+  int m_base = mb * rpb;
+  int m_end = min(a.M, m_base + rpb);
   const int m_blocks = (a.M + MB - 1) / MB;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const bool cwave = wave < NT * KSL;               // waves past NT*KSL only help with loads
@@ -307,7 +319,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   const int total = MB * FPR;
   const T* xb = reinterpret_cast<const T*>(a.x) + split * KR;
   const __amdgpu_buffer_rsrc_t xr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0, a.M * a.ldx * (int)sizeof(T), kBufWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0,
+                                        (DIRECT ? m_end : a.M) * a.ldx * (int)sizeof(T), kBufWord3);
   // a 16-row slab of a 4096-long K range (the down projection) has 8192 fragments: 16 per thread
   constexpr int SBX = SB + ((MT == 1 && KPW == 16) ? 4 : 0);
   uint4 xs[SBX];
@@ -319,12 +332,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       xs[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
     }
   };
-  // DIRECT (one row block, one tile per workgroup, short K slices: QKV and O): no two waves share
-  // a K slice of the activations, so each wave loads its own MFMA operand fragments straight into
-  // registers (same bounded buffer resource) and the slab is not staged in LDS.  (O: 6.5 -> 6.0 us;
-  // the down projection's 16-step slices, 16 rows of 64 B per load, measured 0.4 us slower.)
-  constexpr bool DIRECT =
-      !MLOOP && !LOOP && KPW <= 4 && (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_PARTIAL);
   uint4 bx[DIRECT ? KPW : 1][DIRECT ? MT : 1];
   if constexpr (DIRECT) {
 #pragma unroll
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       for (int e = threadIdx.x + SBX * NTH; e < total; e += NTH) {   // K ranges above SBX*NTH fragments
         const int r = e >> fsh, q = e & (FPR - 1);
         *reinterpret_cast<uint4*>(slab + r * XSTR + q * 16) =
-            m_base + r <= m_last ? *reinterpret_cast<const uint4*>(xb + (size_t)(m_base + r) * a.ldx + q * PER)
+            m_base + r < m_end ? *reinterpret_cast<const uint4*>(xb + (size_t)(m_base + r) * a.ldx + q * PER)
                                  : make_uint4(0, 0, 0, 0);
       }
     }
@@ -501,7 +508,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
     for (int e = threadIdx.x; e < MB * 8; e += NTH) {
       const int r = e / 8, c = e % 8;
       const int m = m_base + r;
-      if (m >= a.M) continue;
+      if (m >= m_end) continue;
       const float inv = s_inv[r];
       const float* ct = ctile + r * 17;
       float x1 = ct[c] * inv, x2 = ct[c + 8] * inv;
@@ -524,12 +531,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       dst[i + half] = Ty<T>::from_f(x2);
     }
   } else if constexpr (EPI == EPI_RESID) {
-    resid_epilogue<T, MB>(a, ctile, reinterpret_cast<const float*>(smem + L.pre), tg, NT, m_base);
+    resid_epilogue<T, MB>(a, ctile, reinterpret_cast<const float*>(smem + L.pre), tg, NT, m_base, m_end);
   } else if constexpr (EPI == EPI_PARTIAL) {
     for (int e = threadIdx.x; e < NT * MB * 16; e += NTH) {
       const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
       const int m = m_base + r;
-      if (m >= a.M) continue;
+      if (m >= m_end) continue;
       const int col = (tg * NT + t) * 16 + n;
       a.part[((size_t)split * a.M + m) * a.part_ld + col] = ctile[(t * MB + r) * 17 + n];
     }
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
     for (int e = threadIdx.x; e < NT * MB * 8; e += NTH) {
       const int t = e / (MB * 8), r = (e / 8) % MB, c = e % 8;
       const int m = m_base + r;
-      if (m >= a.M) continue;
+      if (m >= m_end) continue;
       const float* ct = ctile + (t * MB + r) * 17;
       const float g = ct[c] * s_inv[r];
       const float u = ct[c + 8] * s_inv[r];
@@ -551,7 +558,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       const float z = ct[n] * s_inv[r];
       ct[n] = z;
       const int col = (tg * NT + t) * 16 + n;
-      if (a.logits && m < a.M && col < a.vocab) a.logits[(size_t)m * a.vocab + col] = z;
+      if (a.logits && m < m_end && col < a.vocab) a.logits[(size_t)m * a.vocab + col] = z;
     }
     __syncthreads();
     // one (top1, id, top2) record per row over the workgroup's NT*16 columns:
@@ -580,7 +587,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
         best = merge_top2(best, other);
       }
       const int m = m_base + r;
-      if (sub == 0 && r < MB && m < a.M) {
+      if (sub == 0 && r < MB && m < m_end) {
         const size_t o = (size_t)m * a.am_ld + tg;
         a.am_v1[o] = best.v1;
         a.am_i1[o] = best.i1;
@@ -600,7 +607,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
         }
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) se += __shfl_xor(se, o);
-        if (sub == 0 && r < MB && m < a.M) a.am_s[(size_t)m * a.am_ld + tg] = best.i1 >= 0 ? se : NAN;
+        if (sub == 0 && r < MB && m < m_end) a.am_s[(size_t)m * a.am_ld + tg] = best.i1 >= 0 ? se : NAN;
       }
     }
   }
@@ -613,6 +620,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   if constexpr (MLOOP) {
     mb = mb_next;
     m_base = mb * MB;
+    m_end = min(a.M, m_base + MB);
 #pragma unroll
     for (int k = 0; k < NPASS; ++k) sv[k] = svn[k];
   }
