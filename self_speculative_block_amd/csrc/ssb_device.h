@@ -37,8 +37,8 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
-// Storage-type traits.  A "fragment" is the 16 bytes one lane feeds to the
-// matrix core per step: 8 bf16 or 4 f32 values along K.
+// Storage-type traits of the weights.  A "fragment" is the 16 bytes one lane feeds to the
+// matrix core per step: 8 16-bit or 4 f32 values along K.
 template <typename T> struct Ty;
 template <> struct Ty<bf16_t> {
   static constexpr int kStepK = 32;   // K covered by one 16-byte-per-lane step
@@ -53,21 +53,64 @@ template <> struct Ty<float> {
   static __device__ __forceinline__ float from_f(float v) { return v; }
 };
 
+// Activations of a model whose weights are bf16 are stored as IEEE fp16 in the same 16 bits:
+// GEMM inputs, q, the KV cache, attention probabilities and outputs, SwiGLU outputs.  fp16 keeps
+// 11 significant bits against bf16's 8, so each rounding of an activation costs 8x less; the
+// 24-layer decoder then stays within a few 1e-3 of exact arithmetic in its logits, where bf16
+// activations (and a bf16 KV cache) had drifted to about 6e-2.  The range condition is that
+// every activation stays below 65504 in magnitude; an overflow becomes inf and then NaN logits,
+// which the engine reports.  Weights stay bf16 in memory and are widened to fp16 in registers
+// right before the matrix core (exact for |w| >= 2^-17 and |w| < 65504).  f32 models keep f32
+// activations.
+// The empty asm materializes f as an fp32 register value: without it the compiler may fuse a
+// preceding multiply with the conversion (v_fma_mixlo_f16, one rounding of the exact product)
+// in one kernel and not in another, and rows would no longer be bit-identical across kernels.
+__device__ __forceinline__ uint16_t f2h(float f) {
+  asm("" : "+v"(f));
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+template <typename T> struct Act;
+template <> struct Act<bf16_t> {
+  static __device__ __forceinline__ float to_f(uint16_t v) { return h2f(v); }
+  static __device__ __forceinline__ uint16_t from_f(float v) { return f2h(v); }
+};
+template <> struct Act<float> {
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+// Two bf16 values (low half first) widened to two fp16 values, packed the same way.
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t w) {
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  const f2v f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, h2v));
+}
+__device__ __forceinline__ uint4 bf8_to_h8(uint4 w) {
+  return make_uint4(bf2_to_h2(w.x), bf2_to_h2(w.y), bf2_to_h2(w.z), bf2_to_h2(w.w));
+}
+
 // One 16x16 output tile step: acc[n][m] += sum_k A[n][k] * B[k][m].
 // Lane l supplies A row (l % 16) and B column (l % 16), and the K values
 // [kStepK/4 * (l/16), kStepK/4 * (l/16 + 1)) of the step; A and B use the
 // same lane->K map, so any fixed K permutation inside a step is harmless.
 // Result layout: lane l, element i holds acc[4*(l/16) + i][l % 16].
-__device__ __forceinline__ void mma_step(f32x4_t& acc, uint4 a, uint4 b, bf16_t) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+// mma_aa: both operands are activations (fp16 for a bf16 model).
+__device__ __forceinline__ void mma_aa(f32x4_t& acc, uint4 a, uint4 b, bf16_t) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), acc,
+                                               0, 0, 0);
 }
-__device__ __forceinline__ void mma_step(f32x4_t& acc, uint4 a, uint4 b, float) {
+__device__ __forceinline__ void mma_aa(f32x4_t& acc, uint4 a, uint4 b, float) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
+// mma_wa: A is a weight fragment (bf16, widened to fp16 here), B an activation fragment.
+__device__ __forceinline__ void mma_wa(f32x4_t& acc, uint4 w, uint4 x, bf16_t) { mma_aa(acc, bf8_to_h8(w), x, bf16_t()); }
+__device__ __forceinline__ void mma_wa(f32x4_t& acc, uint4 w, uint4 x, float) { mma_aa(acc, w, x, float()); }
 
 // Per-request launch arguments (passed by value).
 struct ReqArgs {

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(64) void k_prep_embed(PrepArgs a) {
                           : reinterpret_cast<const T*>(a.prefix) + (size_t)pos * a.hidden;
   const float v = Ty<T>::to_f(src[col]);
   a.h[(size_t)m * a.hidden + col] = v;
-  reinterpret_cast<T*>(a.xg)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * a.gain[col]);
+  reinterpret_cast<T*>(a.xg)[(size_t)m * a.hidden + col] = Act<T>::from_f(v * a.gain[col]);
   float s = v * v;
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
@@ -239,7 +239,7 @@ __device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, 
     if (m >= m_end) continue;
     const int col = (tg * NT + t) * 16 + n;
     a.h[(size_t)m * a.hidden + col] = v;
-    reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * s_g[t * 16 + n]);
+    reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Act<T>::from_f(v * s_g[t * 16 + n]);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < NT * MB; e += kGemmThreads) {
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
         uint4 b;
         if constexpr (DIRECT) b = bx[s][mt];
         else b = *reinterpret_cast<const uint4*>(slab + (mt * 16 + lane % 16) * XSTR + kb);
-        mma_step(acc[mt], wf[s], b, T());
+        mma_wa(acc[mt], wf[s], b, T());
       }
     }
   }
@@ -527,8 +527,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
         const size_t base = (((size_t)a.layer * a.n_pages + sl / kPage) * 2 + (kind - 1)) * a.n_kv + head;
         dst = reinterpret_cast<T*>(a.kv_pool) + (base * kPage + sl % kPage) * hd;
       }
-      dst[i] = Ty<T>::from_f(x1);
-      dst[i + half] = Ty<T>::from_f(x2);
+      dst[i] = Act<T>::from_f(x1);
+      dst[i + half] = Act<T>::from_f(x2);
     }
   } else if constexpr (EPI == EPI_RESID) {
     resid_epilogue<T, MB>(a, ctile, reinterpret_cast<const float*>(smem + L.pre), tg, NT, m_base, m_end);
@@ -548,7 +548,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       const float* ct = ctile + (t * MB + r) * 17;
       const float g = ct[c] * s_inv[r];
       const float u = ct[c + 8] * s_inv[r];
-      reinterpret_cast<T*>(a.act)[(size_t)m * a.act_ld + (tg * NT + t) * 8 + c] = Ty<T>::from_f(silu_f(g) * u);
+      reinterpret_cast<T*>(a.act)[(size_t)m * a.act_ld + (tg * NT + t) * 8 + c] = Act<T>::from_f(silu_f(g) * u);
     }
   } else {  // EPI_LOGITS
     for (int e = threadIdx.x; e < NT * MB * 16; e += NTH) {
@@ -766,7 +766,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int r = 0; r < RT; ++r) mma_step(acc[c][r], wf[c], xf[r], bf16_t());
+      for (int r = 0; r < RT; ++r) mma_wa(acc[c][r], wf[c], xf[r], bf16_t());
     if constexpr (EXACT) {
       if (--left == 0) {                   // end of a K slice (uniform)
 #pragma unroll
@@ -900,7 +900,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
               const float cx = csv[2 * i], cy = csv[2 * i + 1];
               o = q < 2 ? z[i] * cx - zo[i] * cy : z[i] * cx + zo[i] * cy;
             }
-            if (ok) dst[dim] = f2bf(o);
+            if (ok) dst[dim] = f2h(o);
           }
         }
       } else if constexpr (EPI == EPI_SWIGLU) {
@@ -911,7 +911,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
         if (ok && q < 2) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            reinterpret_cast<bf16_t*>(a.act)[(size_t)m * a.act_ld + tg * 8 + 4 * q + i] = f2bf(silu_f(z[i]) * zo[i]);
+            reinterpret_cast<bf16_t*>(a.act)[(size_t)m * a.act_ld + tg * 8 + 4 * q + i] = f2h(silu_f(z[i]) * zo[i]);
         }
       } else {  // EPI_RESID
         const int n0 = tg * 16 + 4 * q;
@@ -942,7 +942,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             a.h[(size_t)m * a.hidden + n0 + i] = z[i];
-            reinterpret_cast<bf16_t*>(a.xg_out)[(size_t)m * a.hidden + n0 + i] = f2bf(z[i] * gv[i]);
+            reinterpret_cast<bf16_t*>(a.xg_out)[(size_t)m * a.hidden + n0 + i] = f2h(z[i] * gv[i]);
           }
           if (q == 0) a.ssq_out[(size_t)m * a.ssq_ld + tg] = sq;
         }
@@ -969,7 +969,7 @@ __global__ __launch_bounds__(64) void k_resid_reduce(GemmArgs a) {
     if (s < a.S) v += p[s];
   v = h0 + v;
   a.h[(size_t)m * a.hidden + col] = v;
-  reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Ty<T>::from_f(v * g);
+  reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Act<T>::from_f(v * g);
   float sq = v * v;
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
@@ -1062,12 +1062,12 @@ __device__ __forceinline__ void fold_coef(float m, float mc, float& mn, float& a
   al = __builtin_amdgcn_exp2f(m - mn);     // m = -inf (empty running state) gives 0
   be = __builtin_amdgcn_exp2f(mc - mn);
 }
-// Two fp32 values rounded to bf16 (nearest even) and packed, low half first.
-__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
-  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// Two fp32 values rounded to fp16 (nearest even) and packed, low half first.
+__device__ __forceinline__ uint32_t pack_h2(float x, float y) {
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
   typedef float f32x2v __attribute__((ext_vector_type(2)));
   const f32x2v f = {x, y};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, h2v));
 }
 __device__ __forceinline__ float fold_val(float v, float al, float vc, float be) {
   return __fadd_rn(__fmul_rn(v, al), __fmul_rn(vc, be));
@@ -1190,7 +1190,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         for (int st = 0; st < QKS; ++st) {
           const uint4 kf = *reinterpret_cast<const uint4*>(
               ks + (kt * 16 + lane % 16) * KSTR + (st * KS + PER * (lane / 16)) * (int)sizeof(T));
-          mma_step(s[kt], kf, qf[st], T());
+          mma_aa(s[kt], kf, qf[st], T());
         }
       }
       const int lim = s_lim[lane % 16];
@@ -1229,10 +1229,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         if constexpr (sizeof(T) == 2) {
           // keys 32st + 4(l/16) + {0..3} from tile 2st, then the same +16 from tile 2st+1
           const f32x4_t p0 = s[2 * st], p1 = s[2 * st + 1];
-          pf.x = pack_bf16x2(p0[0], p0[1]);
-          pf.y = pack_bf16x2(p0[2], p0[3]);
-          pf.z = pack_bf16x2(p1[0], p1[1]);
-          pf.w = pack_bf16x2(p1[2], p1[3]);
+          pf.x = pack_h2(p0[0], p0[1]);
+          pf.y = pack_h2(p0[2], p0[3]);
+          pf.z = pack_h2(p1[0], p1[1]);
+          pf.w = pack_h2(p1[2], p1[3]);
         } else {
           const f32x4_t p0 = s[st];
           pf = make_uint4(__float_as_uint(p0[0]), __float_as_uint(p0[1]), __float_as_uint(p0[2]),
@@ -1249,7 +1249,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
           } else {
             vf = *reinterpret_cast<const uint4*>(vrow + (16 * st + 4 * (lane / 16)) * 4);
           }
-          mma_step(o[dt], vf, pf, T());
+          mma_aa(o[dt], vf, pf, T());
         }
       }
       // o[dt][i] = o_c[d = dt*16 + 4*(lane/16) + i] of row_local; the record's max is mref
@@ -1280,7 +1280,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[dt * 16 + 4 * (lane / 16) + i] = Ty<T>::from_f(run_o[dt][i] / run_l);
+      for (int i = 0; i < 4; ++i) dst[dt * 16 + 4 * (lane / 16) + i] = Act<T>::from_f(run_o[dt][i] / run_l);
   }
 }
 
@@ -1341,7 +1341,7 @@ __global__ __launch_bounds__(kWave) void k_attn_combine(const float* part, int m
       m = mn;
     }
   }
-  if (lane < HD) reinterpret_cast<T*>(out)[(size_t)row * out_ld + head * HD + lane] = Ty<T>::from_f(o / l);
+  if (lane < HD) reinterpret_cast<T*>(out)[(size_t)row * out_ld + head * HD + lane] = Act<T>::from_f(o / l);
 }
 
 // ---------------------------------------------------------------------------
@@ -1409,7 +1409,7 @@ __global__ __launch_bounds__(256) void k_poison_kv(const ReqArgs* rap, const int
     const int kv = rem / (n_kv * hd), h = (rem / hd) % n_kv, d = rem % hd;
     const int pg = ra.pt[r][s / kPage];
     const size_t base = (((size_t)layer * n_pages + pg) * 2 + kv) * n_kv + h;
-    pool[(base * kPage + s % kPage) * hd + d] = Ty<T>::from_f(NAN);
+    pool[(base * kPage + s % kPage) * hd + d] = Act<T>::from_f(NAN);
   }
 }
 

@@ -1,24 +1,23 @@
-"""GPU parity of the full-width bf16 decoder against the float64 oracle, at the
-round microbenchmark's shape: hidden 1024, 16 query heads over 4 KV heads of
-64, SwiGLU 4096, vocab 60000; n = 1280 cached positions; B = 32; batch 1 (the
-launch configuration bench.py times), plus ragged batched rounds.  Stacks of 1
-and 24 layers.
+"""GPU parity of the full-width decoder (bf16 weights, fp16 activations and KV cache, fp32
+accumulation) against the float64 oracle, at the round microbenchmark's shape: hidden 1024, 16
+query heads over 4 KV heads of 64, SwiGLU 4096, vocab 60000; n = 1280 cached positions; B = 32;
+batch 1 (the launch configuration bench.py times), plus ragged batched rounds.  Stacks of 1 and
+24 layers.
 
-Bars (bf16 operands and KV cache, fp32 accumulation, against float64):
-  * logits within max-abs 2e-2 * sqrt(L) of the oracle.  One layer at full
-    width exercises every kernel at its real shape (attention over 1313 keys,
-    the LM head over 60000 ids) and meets the 2e-2 bar itself; the rounding
-    errors of successive layers' bf16 inputs are independent, so the
-    end-to-end error of an L-layer stack grows as sqrt(L);
-  * argmax decisions (a0, d_j, a_j, y1) equal wherever the oracle's top-2
-    margin exceeds twice the observed max logit error (a flip needs a margin
-    below that); accept lengths and committed tokens exact when no decision
-    on the accepted path is that close;
+Bars, the same at every stack depth:
+  * logits within max-abs 2e-2 of the oracle;
+  * argmax decisions (a0, d_j, a_j, y1) equal wherever the oracle's top-2 margin exceeds twice
+    the logit error measured on the same rows (a flip needs a smaller margin), and at least 1e-2;
+    accept lengths and committed tokens exact when no decision on the accepted path is that close;
+  * teacher-forced tokens: every position where a GPU-decoded sequence departs from the oracle's
+    prediction for it sits at an oracle top-2 margin below 1e-2 (GravityOCR review, Appendix B.3:
+    divergences are traced to near-ties);
   * GPU self-speculative decoding identical to GPU AR decoding (exact);
-  * a batched round identical, request by request, to single rounds (exact).
+  * a batched round identical, request by request, to single rounds (exact), and each request's
+    logits, accept length and tokens against the oracle at its own ragged state (one layer).
 
-The oracle's 1280-position prefill of the 24-layer stack takes 10-20 s on the
-host, so each stack is one module fixture.
+The oracle's 1280-position prefill of the 24-layer stack takes 10-20 s on the host, so each
+stack is one module fixture.
 """
 
 import numpy as np
@@ -26,14 +25,16 @@ import pytest
 import torch
 
 from ssb_inputs import generate_weights, prefix_embeddings, workload
-from oracle import Decoder, ar_step, build_plant, dd_fill, prefill, spec_round
+from oracle import Decoder, ar_step, build_plant, dd_fill, prefill, spec_round, teacher_forced_argmax
 from oracle.model import argmax_excluding
 from dd_checks import check_block_against_own_outputs
 from sample_checks import replay_round
+from round_checks import check_round
 
 pytestmark = pytest.mark.gpu
 
-LOGIT_TOL = 2e-2      # per layer stack of one; an L-layer stack: LOGIT_TOL * sqrt(L)
+LOGIT_TOL = 2e-2      # max-abs logit bar at every stack depth
+NEAR_TIE = 1e-2       # oracle top-2 margin below which either token is acceptable
 B = 32
 
 
@@ -71,16 +72,28 @@ def full(request):
         y, mg = ar_step(orc, st_ar)
         cont.append(y)
         margins.append(mg)
+    # the logit error measured on one unplanted round (draft rows, the oracle's own state) sets the
+    # near-tie threshold of the decision checks: max(1e-2, twice the measured error)
+    kv.rewind(P, y1_orc)
+    _, _, dl0, _ = kv.round(B, want_logits=True)
+    r0 = spec_round(orc, _copy_state(st), B, keep_logits=True)
+    meas = float(np.abs(dl0.cpu().numpy() - r0.draft_logits).max())
+    print(f"\n[{cfg.n_layers} layers] draft-logit max-abs error vs the oracle {meas:.5f}", flush=True)
+    kv.rewind(P, y1)
     yield dict(wl=wl, cfg=cfg, P=P, orc=orc, model=model, pool=pool, pre=pre, pre_dev=pre_dev, kv=kv,
                y1=y1, st=st, y1_orc=y1_orc, cont=cont, cont_margins=margins, st_ar=st_ar,
-               tol=LOGIT_TOL * np.sqrt(cfg.n_layers))
+               tol=LOGIT_TOL, meas=meas, tie=max(NEAR_TIE, 2 * meas))
     kv.close()
     pool.close()
     model.close()
 
 
+def test_draft_logit_error_within_bar(full):
+    assert full["meas"] < LOGIT_TOL, full["meas"]
+
+
 def test_prefill_first_token_matches_oracle(full):
-    if full["cont_margins"][0] >= 2 * full["tol"]:
+    if full["cont_margins"][0] >= full["tie"]:
         assert full["y1"] == full["y1_orc"]
 
 
@@ -95,52 +108,14 @@ def test_round_logits_accept_and_commit_match_oracle(full, astar):
     kv.rewind(P, y1)
     planted = torch.tensor(plant, dtype=torch.int32, device="cuda")     # -1 keeps the draft's token
     committed, A, dl, vl = kv.round(B, planted_dev=planted, want_logits=True)
-    # oracle: same state, same plant
     st = full["st"]
     st.n, st.x0 = P, y1
-    r = spec_round(orc, st, B, planted=plant, keep_logits=True)
-    dl, vl = dl.cpu().numpy(), vl.cpu().numpy()
-    derr = np.abs(dl - r.draft_logits).max()
-    assert derr < full["tol"], (derr, full["tol"])
-    # verify row k sees a0, d_1..d_k: its logits are comparable while both sides fed the same
-    # tokens (an unplanted draft token at an oracle near-tie may differ, and with it every later row)
-    g_in = [_am(dl[0], cfg.mask_id)[0]] + [plant[j - 1] if plant[j - 1] >= 0 else _am(dl[j], cfg.mask_id)[0]
-                                           for j in range(1, B + 1)]
-    o_in = [r.a0] + list(r.d)
-    same = 0
-    while same < B + 1 and g_in[same] == o_in[same]:
-        same += 1
-    for j in range(same, min(same + 1, B + 1)):
-        t, t1, t2 = _am(r.draft_logits[j], cfg.mask_id)
-        assert t1 - t2 <= 2 * derr, f"draft row {j} differs away from a near-tie"
-    verr = np.abs(vl[:same] - r.verify_logits[:same]).max() if same else 0.0
-    assert verr < full["tol"], (verr, full["tol"])
-    if g_in[0] == o_in[0]:
-        assert same > min(astar, B)         # planted rows always agree
-    err = max(derr, verr)
-    # argmax decisions wherever the oracle margin exceeds twice the observed error
-    close = 2 * err
-    tie = False
-    for j in range(B + 1):
-        t, t1, t2 = _am(r.draft_logits[j], cfg.mask_id)
-        if t1 - t2 > close:
-            assert _am(dl[j], cfg.mask_id)[0] == t, f"draft row {j}"
-        elif j == 0:
-            tie = True
-    for j in range(B + 1):
-        if j >= same:
-            tie = tie or j <= r.A
-            break
-        t, t1, t2 = _am(r.verify_logits[j], cfg.mask_id)
-        if t1 - t2 > close:
-            assert _am(vl[j], cfg.mask_id)[0] == t, f"verify row {j}"
-        elif j <= r.A:
-            tie = True
-    if not tie:
-        assert A == r.A == min(astar, B)
-        assert committed == r.committed
-        n, x0, _ = kv.state()
-        assert (n, x0) == (st.n, st.x0)
+    res = check_round(cfg, orc, st, B, plant, committed, A, dl.cpu().numpy(), vl.cpu().numpy(), full["tol"])
+    if full["y1"] == y1 and res["same_rows"] >= 1:
+        assert res["same_rows"] > min(astar, B)       # planted rows always agree
+    if not res["tie"]:
+        assert A == min(astar, B)
+        assert kv.state()[:2] == (st.n, st.x0)
 
 
 def test_spec_decode_equals_ar_decode_and_oracle(full):
@@ -155,7 +130,7 @@ def test_spec_decode_equals_ar_decode_and_oracle(full):
     # the oracle's greedy continuation agrees up to the first oracle near-tie
     ref, margins = full["cont"], full["cont_margins"]
     for k, (g, o) in enumerate(zip(ar, ref)):
-        if margins[k] <= 2 * full["tol"]:
+        if margins[k] <= full["tie"]:
             break
         assert g == o, f"AR token {k}"
     kv.reset()
@@ -224,8 +199,64 @@ def test_batched_round_equals_single_rounds(full, Bb, R):
         rows = slice(r * (Bb + 1), (r + 1) * (Bb + 1))
         assert torch.equal(dl[rows], dls), f"request {r}: draft logits differ from its single round"
         assert torch.equal(vl[rows], vls), f"request {r}: verify logits differ from its single round"
+    if cfg.n_layers == 1 and R == 16:
+        # each request against the oracle at its own ragged state (lengths 240-350, one layer)
+        orc = full["orc"]
+        dl_np, vl_np = dl.cpu().numpy(), vl.cpu().numpy()
+        for r in range(R):
+            st = _oracle_prefill_cached(full, wl5.wid, r, lens[r], Bb)
+            if st.x0 != firsts[r]:
+                assert full["batch_margins"][(wl5.wid, r)] < full["tie"], f"request {r}: prefill token"
+                continue
+            rows = slice(r * (Bb + 1), (r + 1) * (Bb + 1))
+            check_round(cfg, orc, st, Bb, plants[r], got[r][0], got[r][1], dl_np[rows], vl_np[rows], full["tol"],
+                        budget=budgets[r])
     for kv in kvs:
         kv.close()
+
+
+def _oracle_prefill_cached(full, wid, i, P, Bb):
+    """The oracle's state after prefilling request i's prefix (cached per prefix; a copy)."""
+    cache = full.setdefault("batch_states", {})
+    key = (wid, i)
+    if key not in cache or cache[key].cache.K.shape[1] < P + 2 * Bb + 8:
+        pre = prefix_embeddings(wid, i, P, full["cfg"].hidden)
+        st, _, margin = prefill(full["orc"], pre, P + 2 * 64 + 8)
+        cache[key] = st
+        full.setdefault("batch_margins", {})[key] = margin
+    return _copy_state(cache[key])
+
+
+def test_teacher_forced_tokens_match_oracle(full):
+    """GravityOCR review, Appendix B.3: a decoded sequence is judged position by position; a
+    position where the GPU's token differs from the oracle's greedy prediction for it (given the
+    same history) must sit at an oracle top-2 margin below 1e-2.  Eight seeded prefixes: the
+    microbenchmark's 1280 positions and seven 256-position prefixes; 64 tokens each, decoded by
+    GPU self-speculative rounds (B = 32).  A sequence with no such position is exactly what the
+    oracle's own greedy decode produces; the share of such sequences is the identity rate."""
+    from self_speculative_block_amd.engine import KV
+    cfg, model, pool, orc = full["cfg"], full["model"], full["pool"], full["orc"]
+    N = 64
+    prefixes = [full["pre"]] + [prefix_embeddings(3, 1000 + i, 256, cfg.hidden) for i in range(7)]
+    identical, positions, flips = 0, 0, []
+    kv = KV(pool, full["P"] + N + 2 * B + 8)
+    for i, pre in enumerate(prefixes):
+        kv.reset()
+        toks, _ = kv.decode(model.prefix_tensor(pre), B, N)
+        preds, margins = teacher_forced_argmax(orc, pre, toks)
+        bad = [(t, toks[t], preds[t], margins[t]) for t in range(len(toks)) if toks[t] != preds[t]]
+        for t, g, o, mg in bad:
+            flips.append((i, t, mg))
+            assert mg < NEAR_TIE, f"prefix {i} position {t}: GPU {g} vs oracle {o} at margin {mg:.4f}"
+        identical += not bad
+        positions += len(toks)
+    kv.close()
+    print(f"\n[{cfg.n_layers} layers] teacher-forced: {positions} positions over {len(prefixes)} prefixes, "
+          f"{len(flips)} departures (margins {[round(m, 4) for _, _, m in flips]}), "
+          f"identical sequences {identical}/{len(prefixes)}", flush=True)
+    kv = full["kv"]
+    kv.reset()
+    assert kv.prefill(full["pre_dev"]) == full["y1"]
 
 
 def test_direct_diffusion_block(full):
