@@ -29,6 +29,13 @@ PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA peak of MI355X
 COPY_CALIB_BYTES = 64 << 20
 
 
+def expected_committed(B, p):
+    """E[committed tokens per round] of the planted schedule: A* = min(G, B) with G geometric on
+    {0, 1, ...} (P(G >= k) = (1 - p)^k), and every round commits A* + 2 tokens (no EOS, no budget
+    cut in the microbenchmark): E[A*] = sum_{k=1..B} (1 - p)^k."""
+    return 2.0 + sum((1.0 - p) ** k for k in range(1, B + 1))
+
+
 def alg_bytes_round(cfg, n, B):
     """Algorithmic bytes of one round: weights streamed twice, KV read by both
     forwards, KV written for B+1 rows by each forward (bf16)."""
@@ -108,18 +115,37 @@ def traffic_from_profiles(kind):
     return None
 
 
-def event_pair_overhead_us(torch, n=200):
-    """Median time between two HIP events recorded back to back on the current stream."""
-    st = torch.cuda.current_stream()
-    vals = []
-    for _ in range(n):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        e1.record(st)
-        e1.synchronize()
-        vals.append(e0.elapsed_time(e1) * 1e3)
-    return statistics.median(vals)
+KERNEL_LABELS = {   # (kernel template, EPI, KPW) of the GEMMs at the benchmark's shapes
+    ("k_gemm", "0", "4"): "QKV GEMM + RoPE + KV write", ("k_gemm", "1", "4"): "O GEMM + residual",
+    ("k_gemm", "2", "8"): "gate|up GEMM + SwiGLU", ("k_gemm", "1", "16"): "down GEMM + residual",
+    ("k_gemm", "3", "16"): "LM head GEMM + top-2 records",
+}
+
+
+def summarize_trace(path):
+    """Group a rocprofv3 kernel trace (CSV) by kernel name and grid: the decode GEMMs of a round
+    (33 rows) and of an AR step (1 row) share a kernel and differ in their grid."""
+    import collections
+    import csv
+    import re
+    groups = collections.defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name", "")
+            grid = tuple(row.get(f"Grid_Size_{a}", "") for a in "XYZ")
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
+            groups[(name, grid)].append(dur)
+    total = sum(sum(v) for v in groups.values())
+    out = [f"{'kernel':58s} {'grid':>16s} {'calls':>7s} {'avg us':>8s} {'min us':>8s} {'% time':>7s}"]
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        m = re.search(r"ssb::(k_\w+)<[^,]+, (\d+), (\d+), (\d+)", name)
+        label = name
+        if m and m.group(1) == "k_gemm":
+            label = KERNEL_LABELS.get(("k_gemm", m.group(3), m.group(4)), name)
+        label = re.sub(r"^void ", "", label)[:58]
+        out.append(f"{label:58s} {'x'.join(grid):>16s} {len(v):7d} {sum(v) / len(v):8.2f} {min(v):8.2f} "
+                   f"{100 * sum(v) / total:7.2f}")
+    return "\n".join(out)
 
 
 class no_gc:
@@ -321,7 +347,8 @@ def decode_workload(args, wid):
     # room for the longest region; for tables, for the length cap (round_vs_n reaches prefix + 4096)
     cap = max(max(lengths[:n]), 4096 if wid == 4 else 0)
     torch.cuda.set_device(0)
-    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8,
+                  max_batch=1, sampling=False)
     pool = Pool(model, n_pages=(P + cap + 2 * B + 8) // 16 + 8)
     kv = KV(pool, P + cap + 2 * B + 8)
     tot = {"spec_tokens": 0, "spec_us": 0.0, "ar_tokens": 0, "ar_us": 0.0, "rounds": 0, "forwards": 0,
@@ -394,7 +421,8 @@ def batched_workload(args):
     torch.cuda.set_device(0)
     Bmax = max((wl.block,) + tuple(wl.blocks_extra))
     cap = max(lengths) + 2 * Bmax + 8
-    model = Model(cfg, generate_weights(cfg), block_B=Bmax, max_rows=2048, max_positions=P + cap)
+    model = Model(cfg, generate_weights(cfg), block_B=Bmax, max_rows=2048, max_positions=P + cap,
+                  max_batch=16, sampling=False)
     pool = Pool(model, n_pages=R * ((P + cap) // 16 + 2))
     kvs = [KV(pool, P + cap) for _ in range(R)]
     pres = [model.prefix_tensor(prefix_embeddings(wl.wid, r, P, cfg.hidden)) for r in range(R)]
@@ -491,7 +519,8 @@ def direct_workload(args):
     n = min(args.regions or wl.n_regions, wl.n_regions)
     cap = max(lengths[:n])
     torch.cuda.set_device(0)
-    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8,
+                  max_batch=1, sampling=False)
     pool = Pool(model, n_pages=(P + cap + 2 * B + 8) // 16 + 8)
     kv = KV(pool, P + cap + 2 * B + 8)
     pres = [model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden)) for i in range(n)]
@@ -570,7 +599,8 @@ def sample_workload(args):
     n = min(args.regions or 64, wl.n_regions)
     cap = max(lengths[:n])
     torch.cuda.set_device(0)
-    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8,
+                  max_batch=1)
     pool = Pool(model, n_pages=(P + cap + 2 * B + 8) // 16 + 8)
     kv = KV(pool, P + cap + 2 * B + 8)
     pres = [model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden)) for i in range(n)]
@@ -625,7 +655,8 @@ def multistep_workload(args):
     n = min(args.regions or 32, wl.n_regions)
     cap = max(lengths[:n])
     torch.cuda.set_device(0)
-    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=2048, max_positions=P + cap + 2 * B + 8,
+                  max_batch=1, sampling=False)
     pool = Pool(model, n_pages=(P + cap + 2 * B + 8) // 16 + 8)
     kv = KV(pool, P + cap + 2 * B + 8)
     pres = [model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden)) for i in range(n)]
@@ -686,7 +717,8 @@ def sweep_workload(args):
     cap_len = max(lengths[:n])
     max_tokens = P + cap_len + 2 * B + 8
     torch.cuda.set_device(0)
-    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=max(caps) * (B + 1), max_positions=max_tokens)
+    model = Model(cfg, generate_weights(cfg), block_B=B, max_rows=max(caps) * (B + 1), max_positions=max_tokens,
+                  sampling=False)
     pool = Pool(model, n_pages=(max(caps) + 1) * (max_tokens // 16 + 2))
     reqs = [{"prefix_dev": model.prefix_tensor(prefix_embeddings(wl.wid, i, P, cfg.hidden)), "max_len": lengths[i]}
             for i in range(n)]
@@ -742,7 +774,12 @@ def main():
                          "of the text regions; multistep: draft schedules of 1, 2, 4 steps; sweep: "
                          "continuous batching at running caps 1..64, AR vs self-speculative")
     ap.add_argument("--regions", type=int, default=0, help="text / table: number of regions (0 = all)")
+    ap.add_argument("--summarize-trace", default=None,
+                    help="print a rocprofv3 kernel trace (CSV) grouped by kernel and grid, then exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the round engine is a single-GPU path "
               "(requests would shard across GPUs with no exchange step); run with --gpus 1",
@@ -775,7 +812,8 @@ def main():
     P = wl.prefix_len
     torch.cuda.set_device(0)
     weights = generate_weights(cfg)
-    model = Model(cfg, weights, block_B=B, max_rows=2048, max_positions=P + 256)
+    # one request, greedy rounds only: the workspace holds one window's rows
+    model = Model(cfg, weights, block_B=B, max_rows=2048, max_positions=P + 256, max_batch=1, sampling=False)
     pool = Pool(model, n_pages=(P + 256) // 16 + 8)
     kv = KV(pool, P + 200)
     prefix = prefix_embeddings(wl.wid, 0, P, cfg.hidden)
@@ -839,20 +877,23 @@ def main():
         unplanted.append(time.perf_counter() - ts)
     for k in range(args.steps):
         assert accepts[k] == min(int(astar[args.warmup + k]), B), "planted accept length not realized"
-    value = committed / elapsed
+    assert cfg.eos_id not in cont[1:B + 3], "the planted continuation holds EOS (rounds would be cut)"
     ms_step = elapsed * 1e3 / args.steps
     t_med = statistics.median(per_round)
+    # headline: the schedule's expected committed tokens per round over the median round time (the
+    # realised mean of the timed sample is reported beside it; it moves with --steps)
+    e_committed = expected_committed(B, wl.plant_p)
+    value = e_committed / t_med
     bytes_round = alg_bytes_round(cfg, P, B)
 
-    # per-kernel timing with HIP events: the engine launches every kernel of one kind with
-    # hipExtLaunchKernel and a start/stop event pair attached to the dispatch (the dispatch's
-    # own begin/end timestamps, the basis rocprofv3 reports); an empty event pair recorded on
-    # the stream is given for reference only
-    ev_over = event_pair_overhead_us(torch)
+    # per-kernel timing of graph-replayed launches (as in the timed region): for each kernel kind
+    # the engine replays a round graph in which every launch of that kind stamps, on the device's
+    # real-time counter, its earliest workgroup start and its latest workgroup end
     kinds = ["qkv", "attention", "combine", "o", "gate_up", "down", "reduce", "lm_head", "argmax"]
     breakdown = {}
     for kind in kinds:
-        model.profile_kernel(kind)
+        model.profile_kernel(kind, in_graph=True)
+        run(args.warmup)                    # capture the timing graph outside the sample
         model.profile_read(reset=True)
         for k in range(args.profile_steps):
             run(args.warmup + k)
@@ -887,7 +928,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, weights, prefix, planted[args.warmup:], B, committed / args.steps)
+        cpu = cpu_baseline(cfg, weights, prefix, planted[args.warmup:], B, e_committed)
 
     line = {
         "metric": "committed tokens/s (B=32, batch 1) + round time as % of HBM roofline",
@@ -904,8 +945,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": cfg.n_layers, "hidden": cfg.hidden, "heads": cfg.n_heads,
                    "kv_heads": cfg.n_kv_heads, "ffn": cfg.ffn, "vocab": cfg.vocab, "block_B": B,
-                   "cached_positions": P, "batch": 1, "mean_accept": float(np.mean(accepts)),
-                   "committed_per_round": committed / args.steps},
+                   "cached_positions": P, "batch": 1},
+        "committed_per_round_expected": e_committed,
+        "committed_per_round_realised": committed / args.steps,
+        "mean_accept_realised": float(np.mean(accepts)),
+        "tokens_per_s_realised": committed / elapsed,
         "round_us_median": t_med * 1e6,
         "round_us_wall": {"p90": sorted(per_round)[len(per_round) * 9 // 10] * 1e6, "max": max(per_round) * 1e6,
                           "mean": elapsed / args.steps * 1e6},
@@ -915,9 +959,12 @@ def main():
         "copy_probe_GBs": copy_gbs,
         "round_roofline_frac": bytes_round / t_med / (PEAK_HBM_GBS * 1e9),
         "round_alg_bytes": bytes_round,
+        "device_memory_MB": {k: v / 2 ** 20 for k, v in zip(("packed_weights", "workspace"), model.memory())},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles(dom), "alg_bytes_per_launch": ab,
-                     "avg_launch_us": breakdown[dom]["avg_us"], "empty_event_pair_us": ev_over},
+                     "avg_launch_us": breakdown[dom]["avg_us"],
+                     "timing": "graph-replayed launches, device real-time stamps (first workgroup start to last "
+                               "workgroup end)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

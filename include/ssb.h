@@ -71,8 +71,14 @@ typedef struct ssb_config {
   int max_rows;       /* rows per forward pass: prefill chunk, batched windows */
   int max_positions;  /* largest position + 1 any sequence reaches */
   float rms_eps, rope_theta;
-  int dtype;          /* SSB_BF16 or SSB_F32: weights, KV cache and GEMM inputs */
+  int dtype;          /* SSB_BF16: bf16 weights, fp16 activations and KV cache; SSB_F32: all f32 */
+  int max_batch;      /* requests per batched call (rounds, AR steps, serving cap): 1..SSB_MAX_BATCH,
+                         0 = SSB_MAX_BATCH; sizes the per-row workspace of decode forwards */
+  int features;       /* SSB_FEAT_SAMPLE: workspace for stochastic rounds (two fp32 logit planes of
+                         max_batch * (block_B + 1) rows); without it the sampling calls fail with
+                         SSB_EINVAL */
 } ssb_config;
+#define SSB_FEAT_SAMPLE 1
 
 /* Weights: device pointers, row-major [out_features][in_features] in the
  * config dtype (bf16 as raw uint16 bits); norm gains are float32 [hidden].
@@ -123,6 +129,12 @@ int ssb_check_config(const ssb_config* cfg);
  * afterwards. *out is owned by the caller; release it with ssb_free_model. */
 int ssb_init_model(const ssb_config* cfg, const ssb_weights* w, void* stream, ssb_model** out);
 void ssb_free_model(ssb_model* m);
+
+/* Device bytes the model holds: its packed weights (and RoPE table) and its
+ * fixed workspace (activations of max_rows rows, per-row attention records of
+ * max_batch windows, LM-head group records, stochastic logit planes with
+ * SSB_FEAT_SAMPLE). Either output may be null. SSB_EINVAL for a null model. */
+int ssb_model_memory(const ssb_model* m, size_t* weight_bytes, size_t* workspace_bytes);
 
 /* KV page pool, in caller-owned device memory. ssb_pool_bytes returns the
  * size of n_pages pages: each page holds page_tokens positions of K and V
@@ -358,7 +370,12 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
  * launch of that kernel kind is issued with hipExtLaunchKernel and a start /
  * stop event pair that the runtime attaches to the dispatch itself, on the
  * stream it is launched on. Rounds and AR steps then run without graph
- * replay. ssb_profile_read returns the summed event time and the launch
+ * replay. With SSB_PROFILE_IN_GRAPH or'ed into kind, greedy and stochastic
+ * rounds (single and batched) and AR steps keep replaying launch graphs
+ * instead: a separate graph per timed kind carries an event-record node
+ * before and after each launch of that kind, so the times are those of
+ * graph-replayed launches (the other calls run eagerly as above).
+ * ssb_profile_read returns the summed event time and the launch
  * count since the last reset; reset != 0 clears them.
  * kind: one of SSB_K_*, or -1 to stop timing. SSB_K_DOWN is the down
  * projection GEMM; SSB_K_REDUCE its K-split reduce (absent when the down
@@ -372,6 +389,7 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
 #define SSB_K_LMHEAD 6
 #define SSB_K_ARGMAX 7
 #define SSB_K_REDUCE 8
+#define SSB_PROFILE_IN_GRAPH 0x100
 int ssb_profile_kernel(ssb_model* m, int kind);
 int ssb_profile_read(ssb_model* m, double* total_us, long long* launches, int reset);
 

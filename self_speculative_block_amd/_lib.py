@@ -7,8 +7,10 @@ from .build import LIB
 
 SSB_OK, SSB_EINVAL, SSB_ENOKV, SSB_EHIP, SSB_ESTATE, SSB_ENOMEM = 0, -1, -2, -3, -4, -5
 SSB_F32, SSB_BF16 = 0, 1
+SSB_FEAT_SAMPLE = 1
 SSB_MAX_BATCH = 64
 SSB_MAX_BLOCK = 64
+SSB_PROFILE_IN_GRAPH = 0x100
 KERNEL_KINDS = {"qkv": 0, "attention": 1, "combine": 2, "o": 3, "gate_up": 4, "down": 5, "lm_head": 6, "argmax": 7,
                 "reduce": 8}
 
@@ -22,7 +24,8 @@ class SsbConfig(ctypes.Structure):
     _fields_ = [(n, c_int) for n in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn",
                                       "vocab", "mask_id", "eos_id", "block_B", "page_tokens",
                                       "max_rows", "max_positions")] + \
-               [("rms_eps", c_float), ("rope_theta", c_float), ("dtype", c_int)]
+               [("rms_eps", c_float), ("rope_theta", c_float), ("dtype", c_int), ("max_batch", c_int),
+                ("features", c_int)]
 
 
 class SsbWeights(ctypes.Structure):
@@ -61,6 +64,7 @@ SIGNATURES = {
     "ssb_init_model": (c_int, [ctypes.POINTER(SsbConfig), ctypes.POINTER(SsbWeights), c_void_p,
                                ctypes.POINTER(c_void_p)]),
     "ssb_free_model": (None, [c_void_p]),
+    "ssb_model_memory": (c_int, [c_void_p, ctypes.POINTER(c_size_t), ctypes.POINTER(c_size_t)]),
     "ssb_pool_bytes": (c_int, [c_void_p, c_int, ctypes.POINTER(c_size_t)]),
     "ssb_pool_init": (c_int, [c_void_p, c_void_p, c_size_t, c_int, ctypes.POINTER(c_void_p)]),
     "ssb_pool_free": (None, [c_void_p]),

@@ -112,6 +112,30 @@ __device__ __forceinline__ void mma_aa(f32x4_t& acc, uint4 a, uint4 b, float) {
 __device__ __forceinline__ void mma_wa(f32x4_t& acc, uint4 w, uint4 x, bf16_t) { mma_aa(acc, bf8_to_h8(w), x, bf16_t()); }
 __device__ __forceinline__ void mma_wa(f32x4_t& acc, uint4 w, uint4 x, float) { mma_aa(acc, w, x, float()); }
 
+// Kernel timing stamps of one launch (measurement only), on the device's real-time counter:
+// word 0 is the start of workgroup 0 (dispatched first), word 1 + w the end of workgroup w
+// (w < kStampWgs).  Plain stores to distinct words: atomics from hundreds of workgroups finishing
+// together would queue on one address and slow the very kernel being timed.  Slots are not reset
+// between launches: the host keeps the end words at or after the launch's own start.  A null
+// pointer disables the stamps.
+constexpr int kStampWgs = 2047;
+struct ProfStamp { unsigned long long t[1 + kStampWgs]; };
+__device__ __forceinline__ int stamp_wg() {
+  return (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+}
+__device__ __forceinline__ void stamp_begin(ProfStamp* s) {
+  if (s && threadIdx.x == 0 && stamp_wg() == 0) s->t[0] = __builtin_amdgcn_s_memrealtime();
+}
+// Every thread of the workgroup calls it at the kernel's end (s is uniform): once each thread's
+// memory operations have completed, one thread records the time.
+__device__ __forceinline__ void stamp_end(ProfStamp* s) {
+  if (!s) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int w = stamp_wg();
+  if (threadIdx.x == 0 && w < kStampWgs) s->t[1 + w] = __builtin_amdgcn_s_memrealtime();
+}
+
 // Per-request launch arguments (passed by value).
 struct ReqArgs {
   int n;                              // requests in this launch
@@ -181,6 +205,7 @@ struct GemmArgs {
   float* am_v1; int32_t* am_i1; float* am_v2; int am_ld;   // LOGITS: records [M][am_ld]
   float* am_s;                                  // LOGITS, nullable: sum of exp((z - group max) / T) [M][am_ld]
   float am_scale;                               // log2(e) / T for am_s
+  ProfStamp* stamp;                             // nullable timing stamps of this launch
 };
 
 // Inverse-CDF sampling of window rows from their LM-head records and logits.
@@ -240,6 +265,7 @@ struct AttnArgs {
   void* out; int out_ld;                   // fold: [rows][n_heads*hd]
   int fold;
   float scale;
+  ProfStamp* stamp;                        // nullable timing stamps of this launch
   AttnTasks tasks;
 };
 
@@ -259,13 +285,15 @@ int gemm_max_mt(int elem, int K, int S, int NT, int KSL, int n_ssq, int epi);
 // gs (nullable, then zs too): per-group exp-sums of the LM head at scale sc = log2(e) / T;
 // zs [M] gets the row's sum of exp((z - top1) / T) over the vocabulary without [M].
 hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, float sc, int n_groups,
-                         int ld, int M, int32_t* tok, float* top1, float* top2, float* zs, hipStream_t st);
+                         int ld, int M, int32_t* tok, float* top1, float* top2, float* zs, hipStream_t st,
+                         ProfStamp* stamp = nullptr);
 hipError_t launch_sample_rows(const SampleArgs& a, int rows_per_req, int n_req, hipStream_t st);
 hipError_t launch_accept_sample(const AcceptSampleArgs& a, int n_req, hipStream_t st);
 template <typename T> hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipStream_t st);
 template <typename T>
 hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, int n_heads, int head_dim,
-                               const int32_t* row_lim, int M, void* out, int out_ld, hipStream_t st);
+                               const int32_t* row_lim, int M, void* out, int out_ld, hipStream_t st,
+                               ProfStamp* stamp = nullptr);
 template <typename T>
 hipError_t launch_poison_kv(const ReqArgs* req, int R, const int32_t* acc, int acc_stride, int lo_abs, int hi_abs,
                             void* kv_pool, int n_layers, int n_pages, int n_kv, int hd, hipStream_t st);

@@ -98,6 +98,7 @@ struct ssb_model {
   int elem;
   // packed weights
   void* wmem;
+  size_t wmem_bytes = 0, ws_bytes = 0;
   const void* embed;
   const float* final_norm;
   std::vector<const float*> attn_norm, mlp_norm;
@@ -130,6 +131,8 @@ struct ssb_model {
   float* apart;
   int max_chunks;
   int max_decode_rows;
+  int max_batch;      // requests per batched call
+  bool sampling;      // stochastic-round workspace allocated
   int32_t* accept_dev;
   bool debug_poison = false;   // NaN-poison KV slots no correct read reaches (rounds run eagerly)
   int32_t* tok_dev;
@@ -139,6 +142,13 @@ struct ssb_model {
   std::map<std::tuple<int, void*, int, int, uint32_t, int>, hipGraphExec_t> graphs;   // (kind, pool, R, B, T bits, slots)
   // kernel timing hook
   int prof_kind = -1;
+  bool prof_graph = false;            // time launches of prof_kind inside graph replays (event nodes)
+  bool capturing = false;             // a launch graph is being captured on m->cap
+  std::map<hipGraphExec_t, int> graph_prof_pairs;   // stamp slots written by each profiled graph
+  ProfStamp* prof_stamps = nullptr;   // device slots of graph-replayed launches [prof_slots]
+  int prof_slots = 0;
+  int prof_stamp_used = 0;            // slots the last replayed graph wrote
+  double wallclock_mhz = 100.0;       // device real-time counter
   std::vector<hipEvent_t> prof_ev;    // pairs (start, end)
   int prof_used = 0;                  // pairs recorded since the last collect
   double prof_us = 0;
@@ -152,18 +162,33 @@ namespace {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Kernel timing hook: an event pair around each launch of the selected kind.
-void prof_begin(ssb_model* m, int kind, hipStream_t) {
-  if (m->prof_kind != kind) return;
+// Kernel timing hook around each launch of the selected kind.  Eager launches carry a start /
+// stop event pair on the dispatch itself (hipExtLaunchKernel).  A graph captured for timing
+// gives each such launch a device stamp slot instead (earliest workgroup start, latest
+// workgroup end on the real-time counter; HIP cannot time events recorded by graph nodes).
+ProfStamp* prof_begin(ssb_model* m, int kind, hipStream_t) {
+  if (m->prof_kind != kind) return nullptr;
+  if (m->capturing) {
+    if (!m->prof_graph) return nullptr;
+    if (m->prof_stamp_used >= m->prof_slots) fail(SSB_EINVAL, "kernel timing: too many launches per graph");
+    return m->prof_stamps + m->prof_stamp_used;
+  }
   if (m->prof_used * 2 + 2 > (int)m->prof_ev.size()) fail(SSB_EINVAL, "kernel timing: too many launches per call");
   g_prof_ev[0] = m->prof_ev[2 * m->prof_used];
   g_prof_ev[1] = m->prof_ev[2 * m->prof_used + 1];
+  return nullptr;
 }
 void prof_end(ssb_model* m, int kind, hipStream_t) {
   if (m->prof_kind != kind) return;
+  if (m->capturing) {
+    if (m->prof_graph) ++m->prof_stamp_used;
+    return;
+  }
   g_prof_ev[0] = g_prof_ev[1] = nullptr;
   ++m->prof_used;
 }
+// Rounds replay graphs unless a kind is timed eagerly.
+bool prof_eager(const ssb_model* m) { return m->prof_kind >= 0 && !m->prof_graph; }
 // Called after the stream has been synchronized.
 void prof_collect(ssb_model* m) {
   for (int i = 0; i < m->prof_used; ++i) {
@@ -173,6 +198,21 @@ void prof_collect(ssb_model* m) {
   }
   m->prof_launches += m->prof_used;
   m->prof_used = 0;
+  if (m->prof_stamp_used > 0) {
+    const int n = m->prof_stamp_used;
+    std::vector<ProfStamp> st(n);
+    hip_check(hipMemcpy(st.data(), m->prof_stamps, n * sizeof(ProfStamp), hipMemcpyDeviceToHost), "read stamps");
+    for (const ProfStamp& x : st) {
+      // end words older than this launch's start belong to earlier launches of the slot
+      unsigned long long t1 = 0;
+      for (int w = 1; w <= kStampWgs; ++w)
+        if (x.t[w] >= x.t[0] && x.t[w] > t1) t1 = x.t[w];
+      if (t1 == 0) continue;   // every workgroup left at once
+      m->prof_us += (double)(t1 - x.t[0]) / m->wallclock_mhz;
+      ++m->prof_launches;
+    }
+    m->prof_stamp_used = 0;
+  }
 }
 
 // Workgroup shape of a GEMM: NT 16-column tiles per workgroup, KSL K slices
@@ -236,6 +276,8 @@ void check_config(const ssb_config* c) {
   req(c->max_rows >= c->block_B + 1, "max_rows must hold one window (block_B + 1 rows)");
   req(c->max_positions >= 2, "max_positions must be >= 2");
   req(c->rms_eps >= 0.f && c->rope_theta > 0.f, "bad rms_eps or rope_theta");
+  req(c->max_batch >= 0 && c->max_batch <= SSB_MAX_BATCH, "max_batch must be in [0, SSB_MAX_BATCH]");
+  req((c->features & ~SSB_FEAT_SAMPLE) == 0, "unknown feature bits");
 }
 
 template <typename T>
@@ -300,6 +342,7 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const size_t o_lm = take((size_t)lm_tiles * 16 * H * E);
   const size_t o_rope = take((size_t)c.max_positions * (c.head_dim / 2) * sizeof(float2));
   if (hipMalloc(&m->wmem, off) != hipSuccess) fail(SSB_ENOMEM, "hipMalloc of packed weights failed");
+  m->wmem_bytes = off;
   char* wb = static_cast<char*>(m->wmem);
   m->embed = wb + o_embed;
   m->final_norm = reinterpret_cast<const float*>(wb + o_fnorm);
@@ -341,7 +384,9 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
 
   // ---- workspace ----
   const int MR = c.max_rows;
-  m->max_decode_rows = std::min(MR, SSB_MAX_BATCH * (std::max(c.block_B, 1) + 1));
+  m->max_batch = c.max_batch ? c.max_batch : SSB_MAX_BATCH;
+  m->sampling = (c.features & SSB_FEAT_SAMPLE) != 0;
+  m->max_decode_rows = std::min(MR, m->max_batch * (std::max(c.block_B, 1) + 1));
   m->max_chunks = (c.max_positions + kKeyChunk - 1) / kKeyChunk;
   off = 0;
   const size_t w_h = take((size_t)MR * H * 4);
@@ -359,7 +404,7 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const size_t w_amp = take((size_t)(lm_tiles / p_lm.NT) * MR * 12);
   const size_t w_ams = take((size_t)(lm_tiles / p_lm.NT) * MR * 4);
   const size_t w_conf = take((size_t)MR * 4);
-  const size_t w_slog = take((size_t)2 * m->max_decode_rows * V * 4);
+  const size_t w_slog = take(m->sampling ? (size_t)2 * m->max_decode_rows * V * 4 : 0);
   const size_t w_sst = take((size_t)4 * MR * 4);
   const size_t w_ddw = take((size_t)kMaxReq * (SSB_MAX_BLOCK + 1) * 4);
   const size_t w_ddr = take((size_t)kMaxReq * kDDRec * 4);
@@ -368,6 +413,7 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const size_t w_tok = take((size_t)MR * 4);
   const size_t w_req = take(sizeof(ReqArgs));
   if (hipMalloc(&m->ws, off) != hipSuccess) fail(SSB_ENOMEM, "hipMalloc of workspace failed");
+  m->ws_bytes = off;
   char* wsb = static_cast<char*>(m->ws);
   m->h = reinterpret_cast<float*>(wsb + w_h);
   m->xg = wsb + w_xg;
@@ -391,8 +437,8 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   m->ami1 = reinterpret_cast<int32_t*>(m->amv2 + (size_t)(lm_tiles / p_lm.NT) * MR);
   m->ams = reinterpret_cast<float*>(wsb + w_ams);
   m->am_z = reinterpret_cast<float*>(wsb + w_conf);
-  m->slog_d = reinterpret_cast<float*>(wsb + w_slog);
-  m->slog_v = m->slog_d + (size_t)m->max_decode_rows * V;
+  m->slog_d = m->sampling ? reinterpret_cast<float*>(wsb + w_slog) : nullptr;
+  m->slog_v = m->sampling ? m->slog_d + (size_t)m->max_decode_rows * V : nullptr;
   m->smax_d = reinterpret_cast<float*>(wsb + w_sst);
   m->sz_d = m->smax_d + MR;
   m->smax_v = m->sz_d + MR;
@@ -509,18 +555,18 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       GemmArgs a = g;
       set_w(a, m->qkv[l]);
       a.x = m->xg; a.ldx = H;
-      prof_begin(m, SSB_K_QKV, st);
+      a.stamp = prof_begin(m, SSB_K_QKV, st);
       hip_check(big || x_qkv ? launch_gemm_big(a, EPI_QKV, x_qkv, st) : launch_gemm<T>(a, EPI_QKV, st), "qkv gemm");
       prof_end(m, SSB_K_QKV, st);
     }
     at.layer = l;
-    prof_begin(m, SSB_K_ATTN, st);
+    at.stamp = prof_begin(m, SSB_K_ATTN, st);
     hip_check(launch_attn<T>(at, chunk_slots, c.head_dim, st), "attention");
     prof_end(m, SSB_K_ATTN, st);
     if (!at.fold) {
-      prof_begin(m, SSB_K_COMBINE, st);
+      ProfStamp* cst = prof_begin(m, SSB_K_COMBINE, st);
       hip_check(launch_attn_combine<T>(m->apart, m->max_chunks, chunk_slots, c.n_heads, c.head_dim, m->row_lim, M,
-                                       m->attn, qd, st), "attention combine");
+                                       m->attn, qd, st, cst), "attention combine");
       prof_end(m, SSB_K_COMBINE, st);
     }
     {  // O + residual; next input xg = h * mlp_norm[l]
@@ -528,7 +574,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       set_w(a, m->o[l]);
       a.x = m->attn; a.ldx = qd;
       a.gain_next = m->mlp_norm[l];
-      prof_begin(m, SSB_K_O, st);
+      a.stamp = prof_begin(m, SSB_K_O, st);
       hip_check(big || x_o ? launch_gemm_big(a, EPI_RESID, x_o, st) : launch_gemm<T>(a, EPI_RESID, st), "o gemm");
       prof_end(m, SSB_K_O, st);
     }
@@ -536,7 +582,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       GemmArgs a = g;
       set_w(a, m->gu[l]);
       a.x = m->xg; a.ldx = H;
-      prof_begin(m, SSB_K_GATEUP, st);
+      a.stamp = prof_begin(m, SSB_K_GATEUP, st);
       hip_check(big || x_gu ? launch_gemm_big(a, EPI_SWIGLU, x_gu, st) : launch_gemm<T>(a, EPI_SWIGLU, st),
                 "gate/up gemm");
       prof_end(m, SSB_K_GATEUP, st);
@@ -546,13 +592,13 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       set_w(a, m->d[l]);
       a.x = m->act; a.ldx = c.ffn;
       a.gain_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
-      prof_begin(m, SSB_K_DOWN, st);
+      a.stamp = prof_begin(m, SSB_K_DOWN, st);
       const bool dexact = x_down && a.S == 1;   // a K-split down projection stays on k_gemm
       if (big || dexact) hip_check(launch_gemm_big(a, EPI_RESID, dexact, st), "down gemm");
       else hip_check(launch_gemm<T>(a, a.S > 1 ? EPI_PARTIAL : EPI_RESID, st), "down gemm");
       prof_end(m, SSB_K_DOWN, st);
       if (a.S > 1 && !big) {
-        prof_begin(m, SSB_K_REDUCE, st);
+        a.stamp = prof_begin(m, SSB_K_REDUCE, st);
         hip_check(launch_resid_reduce<T>(a, st), "down reduce");
         prof_end(m, SSB_K_REDUCE, st);
       }
@@ -575,16 +621,16 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       a.M = 1;
       rows = 1;
     }
-    prof_begin(m, SSB_K_LMHEAD, st);
+    a.stamp = prof_begin(m, SSB_K_LMHEAD, st);
     const bool x_lm = dec_big && rows >= kExactRowsLm && !a.am_s && a.NT == 4 && a.n_tiles % 8 == 0;
     if (x_lm) hip_check(launch_gemm_big(a, EPI_LOGITS, true, st), "lm head gemm");
     else hip_check(launch_gemm<T>(a, EPI_LOGITS, st), "lm head gemm");
     prof_end(m, SSB_K_LMHEAD, st);
-    prof_begin(m, SSB_K_ARGMAX, st);
+    ProfStamp* ast = prof_begin(m, SSB_K_ARGMAX, st);
     float* top1 = f.st_max ? f.st_max : m->am_top1;
     float* zs = f.st_z ? f.st_z : m->am_z;
     hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, f.stat_sc > 0.f ? m->ams : nullptr, f.stat_sc, n_groups,
-                            n_groups, rows, m->am_tok, top1, m->am_top2, zs, st), "argmax");
+                            n_groups, rows, m->am_tok, top1, m->am_top2, zs, st, ast), "argmax");
     prof_end(m, SSB_K_ARGMAX, st);
     if (f.sample) {
       if (!f.logits || !(f.stat_sc > 0.f)) fail(SSB_EINVAL, "sampling needs logits and row sums");
@@ -697,18 +743,28 @@ hipGraphExec_t get_graph(ssb_model* m, int kind, ssb_pool* pool, int R, int B, i
                          const std::function<void(hipStream_t)>& body, float temperature = 0.f) {
   uint32_t tb = 0;
   std::memcpy(&tb, &temperature, 4);
-  const auto key = std::make_tuple(kind, static_cast<void*>(pool), R, B, tb, slots);
+  // a graph that times one kernel kind (event nodes around its launches) is kept apart
+  const int pk = m->prof_graph ? m->prof_kind + 1 : 0;
+  const auto key = std::make_tuple(kind * 64 + pk, static_cast<void*>(pool), R, B, tb, slots);
   auto it = m->graphs.find(key);
-  if (it != m->graphs.end()) return it->second;
+  if (it != m->graphs.end()) {
+    if (pk) m->prof_stamp_used = m->graph_prof_pairs[it->second];   // read back after the replay
+    return it->second;
+  }
+  m->prof_stamp_used = 0;
+  m->capturing = true;
   hip_check(hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal), "begin capture");
   try {
     body(m->cap);
   } catch (...) {
+    m->capturing = false;
+    m->prof_stamp_used = 0;
     hipGraph_t tmp = nullptr;
     (void)hipStreamEndCapture(m->cap, &tmp);
     if (tmp) (void)hipGraphDestroy(tmp);
     throw;
   }
+  m->capturing = false;
   hipGraph_t g = nullptr;
   hip_check(hipStreamEndCapture(m->cap, &g), "end capture");
   hipGraphExec_t ex = nullptr;
@@ -716,6 +772,8 @@ hipGraphExec_t get_graph(ssb_model* m, int kind, ssb_pool* pool, int R, int B, i
   (void)hipGraphDestroy(g);
   hip_check(e, "graph instantiate");
   m->graphs[key] = ex;
+  if (pk) m->graph_prof_pairs[ex] = m->prof_stamp_used;   // slots written by each replay
+  else m->prof_stamp_used = 0;
   return ex;
 }
 
@@ -738,8 +796,9 @@ struct SampleSpec {
   const float* const* u;
 };
 
-void check_sample(const SampleSpec* smp, int R) {
+void check_sample(const ssb_model* m, const SampleSpec* smp, int R) {
   if (!smp) return;
+  if (!m->sampling) fail(SSB_EINVAL, "the model was initialised without SSB_FEAT_SAMPLE");
   if (!(smp->temperature > 0.f) || !(smp->temperature < INFINITY)) fail(SSB_EINVAL, "temperature must be > 0");
   for (int r = 0; r < R; ++r)
     if (!smp->u[r]) fail(SSB_EINVAL, "null uniforms");
@@ -752,7 +811,7 @@ void prefill(ssb_model* m, ssb_kv* kv, const void* prefix, int P, int32_t* first
   if (P < 1) fail(SSB_EINVAL, "P must be >= 1");
   if (kv->seq_len != 0 || kv->x0 >= 0) fail(SSB_ESTATE, "prefill needs an empty kv");
   if (P + 1 > m->c.max_positions) fail(SSB_EINVAL, "P exceeds max_positions");
-  check_sample(smp, 1);
+  check_sample(m, smp, 1);
   kv_ensure(kv, P, st);
   ReqArgs ra = single_req(kv, 0, 1);
   if (smp) ra.u[0] = smp->u[0];
@@ -805,9 +864,9 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
                 const int32_t* const* cont, const int* cont_len, const int* cont_c, const int* astar,
                 float* dlog, float* vlog, RoundOut* out, hipStream_t st, const SampleSpec* smp = nullptr) {
   const ssb_config& c = m->c;
-  check_sample(smp, R);
+  check_sample(m, smp, R);
   if (smp && (planted || cont)) fail(SSB_EINVAL, "planted drafts apply to greedy rounds only");
-  if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
+  if (R < 1 || R > m->max_batch) fail(SSB_EINVAL, "R must be in [1, max_batch]");
   if (B < 0 || B > c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
   if (R * (B + 1) > c.max_rows) fail(SSB_EINVAL, "R*(B+1) exceeds max_rows");
   ssb_pool* pool = kvs[0]->pool;
@@ -886,7 +945,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
     hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)R * kOutStride * 4, hipMemcpyDeviceToHost, s),
               "copy accept");
   };
-  if (dlog || vlog || m->prof_kind >= 0 || m->debug_poison) {
+  if (dlog || vlog || prof_eager(m) || m->debug_poison) {
     body(st, false);
   } else {
     hipGraphExec_t ex = get_graph(m, smp ? 4 : 0, pool, R, B, slots, [&](hipStream_t s) { body(s, true); },
@@ -915,7 +974,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
 void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_t st,
              const SampleSpec* smp = nullptr) {
   check_model_kv(m, kv);
-  check_sample(smp, 1);
+  check_sample(m, smp, 1);
   if (kv->x0 < 0) fail(SSB_ESTATE, "AR step needs a prefilled kv (no boundary token)");
   if (kv->seq_len + 1 > m->c.max_positions) fail(SSB_ENOKV, "position exceeds max_positions");
   kv_ensure(kv, kv->seq_len + 1, st);
@@ -940,7 +999,7 @@ void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_
     run_forward(m, kv->pool, f, s);
     hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, 4, hipMemcpyDeviceToHost, s), "copy token");
   };
-  if (logits || m->prof_kind >= 0) {
+  if (logits || prof_eager(m)) {
     body(st, false);
   } else {
     hipGraphExec_t ex = get_graph(m, smp ? 5 : 1, kv->pool, 1, 0, slot_bucket(m, kv->seq_len + 1),
@@ -965,7 +1024,7 @@ double now_us() {
 // [x0_r] at p_r, keys <= p_r (the window of a round with no masks).
 void ar_step_batch_impl(ssb_model* m, ssb_kv* const* kvs, int R, int32_t* tokens, hipStream_t st) {
   const ssb_config& c = m->c;
-  if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
+  if (R < 1 || R > m->max_batch) fail(SSB_EINVAL, "R must be in [1, max_batch]");
   if (R > c.max_rows) fail(SSB_EINVAL, "R exceeds max_rows");
   ssb_pool* pool = kvs[0]->pool;
   for (int r = 0; r < R; ++r) {
@@ -1002,7 +1061,7 @@ void ar_step_batch_impl(ssb_model* m, ssb_kv* const* kvs, int R, int32_t* tokens
     run_forward(m, pool, f, s);
     hip_check(hipMemcpyAsync(m->pin_i32, m->am_tok, (size_t)R * 4, hipMemcpyDeviceToHost, s), "copy tokens");
   };
-  if (m->prof_kind >= 0) {
+  if (prof_eager(m)) {
     body(st, false);
   } else {
     hipGraphExec_t ex = get_graph(m, 1, pool, R, 0, slot_bucket(m, maxpos), [&](hipStream_t s) { body(s, true); });
@@ -1034,7 +1093,7 @@ void serve_impl(ssb_model* m, ssb_pool* pool, ssb_request* reqs, int n_reqs, int
   if (!pool || pool->m != m) fail(SSB_EINVAL, "pool belongs to another model");
   if (n_reqs < 0 || (n_reqs > 0 && !reqs)) fail(SSB_EINVAL, "bad request array");
   if (mode != SSB_SERVE_AR && mode != SSB_SERVE_SPEC) fail(SSB_EINVAL, "unknown serve mode");
-  if (max_running < 1 || max_running > SSB_MAX_BATCH) fail(SSB_EINVAL, "max_running must be in [1, SSB_MAX_BATCH]");
+  if (max_running < 1 || max_running > m->max_batch) fail(SSB_EINVAL, "max_running must be in [1, max_batch]");
   if (mode == SSB_SERVE_SPEC) {
     if (B < 0 || B > c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
     if (max_running * (B + 1) > c.max_rows) fail(SSB_EINVAL, "max_running * (B + 1) exceeds max_rows");
@@ -1389,11 +1448,20 @@ void ssb_free_model(ssb_model* m) {
   (void)hipFree(m->ws);
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
   for (hipEvent_t e : m->prof_ev) (void)hipEventDestroy(e);
+  if (m->prof_stamps) (void)hipFree(m->prof_stamps);
   (void)hipStreamDestroy(m->cap);
   (void)hipHostFree(m->req_pin);
   (void)hipHostFree(m->pin_i32);
   (void)hipHostFree(m->pin_f32);
   delete m;
+}
+
+int ssb_model_memory(const ssb_model* m, size_t* weight_bytes, size_t* workspace_bytes) {
+  return guard([&] {
+    if (!m) fail(SSB_EINVAL, "null model");
+    if (weight_bytes) *weight_bytes = m->wmem_bytes;
+    if (workspace_bytes) *workspace_bytes = m->ws_bytes;
+  });
 }
 
 int ssb_pool_bytes(const ssb_model* m, int n_pages, size_t* bytes) {
@@ -1431,6 +1499,7 @@ void ssb_pool_free(ssb_pool* p) {
   (void)hipDeviceSynchronize();
   for (auto it = m->graphs.begin(); it != m->graphs.end();) {
     if (std::get<1>(it->first) == static_cast<void*>(p)) {
+      m->graph_prof_pairs.erase(it->second);
       (void)hipGraphExecDestroy(it->second);
       it = m->graphs.erase(it);
     } else {
@@ -1588,7 +1657,7 @@ int ssb_round_batch(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int32_
                     float* draft_logits_dev, float* verify_logits_dev, void* stream) {
   return guard([&] {
     if (!m || !kvs || !max_commit) fail(SSB_EINVAL, "null argument");
-    if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
+    if (R < 1 || R > m->max_batch) fail(SSB_EINVAL, "R must be in [1, max_batch]");
     for (int r = 0; r < R; ++r)
       if (!kvs[r]) fail(SSB_EINVAL, "null kv in batch");
     std::vector<RoundOut> ro(R);
@@ -1777,7 +1846,7 @@ int ssb_decode_multistep(ssb_model* m, ssb_kv* kv, const void* prefix_dev, int P
 int ssb_ar_step_batch(ssb_model* m, ssb_kv* const* kvs, int R, int32_t* tokens, void* stream) {
   return guard([&] {
     if (!m || !kvs || !tokens) fail(SSB_EINVAL, "null argument");
-    if (R < 1 || R > SSB_MAX_BATCH) fail(SSB_EINVAL, "R must be in [1, SSB_MAX_BATCH]");
+    if (R < 1 || R > m->max_batch) fail(SSB_EINVAL, "R must be in [1, max_batch]");
     for (int r = 0; r < R; ++r)
       if (!kvs[r]) fail(SSB_EINVAL, "null kv in batch");
     ar_step_batch_impl(m, kvs, R, tokens, S(stream));
@@ -1884,6 +1953,8 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
 int ssb_profile_kernel(ssb_model* m, int kind) {
   return guard([&] {
     if (!m) fail(SSB_EINVAL, "null model");
+    const bool in_graph = kind >= 0 && (kind & SSB_PROFILE_IN_GRAPH);
+    if (kind >= 0) kind &= ~SSB_PROFILE_IN_GRAPH;
     if (kind < -1 || kind > SSB_K_REDUCE) fail(SSB_EINVAL, "unknown kernel kind");
     hip_check(hipSetDevice(m->device), "hipSetDevice");
     if (kind >= 0 && m->prof_ev.empty()) {
@@ -1892,8 +1963,19 @@ int ssb_profile_kernel(ssb_model* m, int kind) {
       m->prof_ev.resize(2 * pairs);
       for (auto& e : m->prof_ev) hip_check(hipEventCreate(&e), "event create");
     }
+    if (in_graph && !m->prof_stamps) {
+      m->prof_slots = 8 * (m->c.n_layers + 2);
+      hip_check(hipMalloc(reinterpret_cast<void**>(&m->prof_stamps), m->prof_slots * sizeof(ProfStamp)),
+                "stamp slots");
+      hip_check(hipMemset(m->prof_stamps, 0, m->prof_slots * sizeof(ProfStamp)), "clear stamps");
+      int khz = 0;
+      hip_check(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, m->device), "wall clock rate");
+      if (khz > 0) m->wallclock_mhz = khz / 1000.0;
+    }
     m->prof_kind = kind;
+    m->prof_graph = in_graph;
     m->prof_used = 0;
+    m->prof_stamp_used = 0;
   });
 }
 

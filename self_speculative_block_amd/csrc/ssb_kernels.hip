@@ -304,6 +304,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   const int kstep0 = split * (KSL * KPW) + ksl * KPW;
   const int m_last = a.M - 1;
 
+  stamp_begin(a.stamp);
   // ---- every global load of the prologue is issued before the first wait ----
   // 1. this wave's weight fragments (HBM)
   uint4 wf[KPW];
@@ -627,6 +628,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
   first = false;
   __syncthreads();   // red, ctile, the slab and the staged inputs are reused by the next item
   }
+  stamp_end(a.stamp);
 }
 
 // ---------------------------------------------------------------------------
@@ -683,6 +685,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
   const int ksteps = a.K / Ty<bf16_t>::kStepK;
   float* s_inv = reinterpret_cast<float*>(smem + NS * NF * 1024);
   const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)smem;   // LDS byte address of the staging area
+  stamp_begin(a.stamp);
 
   // this wave's fragments of a step: f = wave + 4i; weights for f < 2CT, activations after
   const uint4* src[FPW];
@@ -833,6 +836,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
         a.am_v2[o] = best.v2;
       }
     }
+    stamp_end(a.stamp);
     return;
   }
 #pragma unroll
@@ -949,6 +953,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
       }
     }
   }
+  stamp_end(a.stamp);
 }
 
 // Residual update after a K-split GEMM: h += sum of the S partial sums (in
@@ -957,6 +962,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 template <typename T>
 __global__ __launch_bounds__(64) void k_resid_reduce(GemmArgs a) {
   constexpr int SMAX = 8;
+  stamp_begin(a.stamp);
   const int m = blockIdx.x, col = blockIdx.y * 64 + threadIdx.x;
   float p[SMAX];
 #pragma unroll
@@ -974,6 +980,7 @@ __global__ __launch_bounds__(64) void k_resid_reduce(GemmArgs a) {
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
   if (threadIdx.x % 16 == 0) a.ssq_out[(size_t)m * a.ssq_ld + col / 16] = sq;
+  stamp_end(a.stamp);
 }
 
 // ---------------------------------------------------------------------------
@@ -985,7 +992,8 @@ __global__ __launch_bounds__(64) void k_resid_reduce(GemmArgs a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int32_t* i1, const float* v2,
                                                     const float* gs, float sc, int n_groups, int ld, int32_t* tok,
-                                                    float* top1, float* top2, float* zs) {
+                                                    float* top1, float* top2, float* zs, ProfStamp* stamp) {
+  stamp_begin(stamp);
   __shared__ Top2 sh[kThreads];
   __shared__ float ssum[kThreads];
   const int m = blockIdx.x;
@@ -1039,6 +1047,7 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
     }
     if (threadIdx.x == 0) zs[m] = sh[0].i1 >= 0 ? ssum[0] : NAN;
   }
+  stamp_end(stamp);
 }
 
 // ---------------------------------------------------------------------------
@@ -1094,6 +1103,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   __shared__ __align__(16) unsigned char vts[HD * VSTR];
   __shared__ int s_lim[16];
 
+  stamp_begin(a.stamp);
   const AttnTask task = a.tasks.t[blockIdx.z / TILES];
   const int mt = blockIdx.z % TILES;       // this workgroup's 16-row tile of the task
   if (mt * 16 >= task.nrows) return;
@@ -1282,6 +1292,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[dt * 16 + 4 * (lane / 16) + i] = Act<T>::from_f(run_o[dt][i] / run_l);
   }
+  stamp_end(a.stamp);
 }
 
 // Combine the per-chunk records of each (row, head).  One wave per (row,
@@ -1293,7 +1304,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 template <typename T, int HD>
 __global__ __launch_bounds__(kWave) void k_attn_combine(const float* part, int max_chunks, int n_slots,
                                                           int n_heads, const int32_t* row_lim, int M, void* out,
-                                                          int out_ld) {
+                                                          int out_ld, ProfStamp* stamp) {
+  stamp_begin(stamp);
   constexpr int REC = HD + 4;
   constexpr int BATCH = 32;
   const int lane = threadIdx.x;
@@ -1342,6 +1354,7 @@ __global__ __launch_bounds__(kWave) void k_attn_combine(const float* part, int m
     }
   }
   if (lane < HD) reinterpret_cast<T*>(out)[(size_t)row * out_ld + head * HD + lane] = Act<T>::from_f(o / l);
+  stamp_end(stamp);
 }
 
 // ---------------------------------------------------------------------------
@@ -1854,9 +1867,10 @@ template hipError_t launch_resid_reduce<bf16_t>(const GemmArgs&, hipStream_t);
 template hipError_t launch_resid_reduce<float>(const GemmArgs&, hipStream_t);
 
 hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, float sc, int n_groups,
-                         int ld, int M, int32_t* tok, float* top1, float* top2, float* zs, hipStream_t st) {
+                         int ld, int M, int32_t* tok, float* top1, float* top2, float* zs, hipStream_t st,
+                         ProfStamp* stamp) {
   if (gs && !zs) return hipErrorInvalidValue;
-  SSB_LAUNCH(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, gs, sc, n_groups, ld, tok, top1, top2, zs);
+  SSB_LAUNCH(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, gs, sc, n_groups, ld, tok, top1, top2, zs, stamp);
   return hipGetLastError();
 }
 
@@ -1888,23 +1902,24 @@ template hipError_t launch_attn<float>(const AttnArgs&, int, int, hipStream_t);
 
 template <typename T>
 hipError_t launch_attn_combine(const float* part, int max_chunks, int n_slots, int n_heads, int head_dim,
-                               const int32_t* row_lim, int M, void* out, int out_ld, hipStream_t st) {
+                               const int32_t* row_lim, int M, void* out, int out_ld, hipStream_t st,
+                               ProfStamp* stamp) {
   if (n_slots < 1 || n_slots > max_chunks) return hipErrorInvalidValue;
   // one single-wave workgroup per (row, head): spread over every CU (4-wave workgroups on half
   // the CUs measured 0.2-0.3 us slower per launch, 2-wave ones slower still)
   const int blocks = M * n_heads;
   if (head_dim == 64)
     SSB_LAUNCH((k_attn_combine<T, 64>), dim3(blocks), dim3(kWave), 0, st, part, max_chunks, n_slots,
-                       n_heads, row_lim, M, out, out_ld);
+                       n_heads, row_lim, M, out, out_ld, stamp);
   else
     SSB_LAUNCH((k_attn_combine<T, 32>), dim3(blocks), dim3(kWave), 0, st, part, max_chunks, n_slots,
-                       n_heads, row_lim, M, out, out_ld);
+                       n_heads, row_lim, M, out, out_ld, stamp);
   return hipGetLastError();
 }
 template hipError_t launch_attn_combine<bf16_t>(const float*, int, int, int, int, const int32_t*, int, void*, int,
-                                                hipStream_t);
+                                                hipStream_t, ProfStamp*);
 template hipError_t launch_attn_combine<float>(const float*, int, int, int, int, const int32_t*, int, void*, int,
-                                               hipStream_t);
+                                               hipStream_t, ProfStamp*);
 
 template <typename T>
 hipError_t launch_poison_kv(const ReqArgs* req, int R, const int32_t* acc, int acc_stride, int lo_abs, int hi_abs,

@@ -34,8 +34,13 @@ def torch_dtype(cfg):
 class Model:
     """A decoder on the GPU: packed weights plus the engine's fixed workspace."""
 
-    def __init__(self, cfg, weights, block_B, max_rows=2048, max_positions=8192, device="cuda:0"):
+    def __init__(self, cfg, weights, block_B, max_rows=2048, max_positions=8192, device="cuda:0", max_batch=None,
+                 sampling=True):
+        """max_batch: requests per batched call (None: the library's limit); sampling: allocate the
+        workspace of stochastic rounds."""
         self.lib = L.load()
+        self.max_batch = max_batch or L.SSB_MAX_BATCH
+        self.sampling = sampling
         self.cfg = cfg
         self.device = torch.device(device)
         self.block_B = block_B
@@ -63,7 +68,7 @@ class Model:
                       for k in ("attn_norm", "mlp_norm", "wq", "wk", "wv", "wo", "wg", "wu", "wd")}
             for k, v in arrays.items():
                 setattr(w, k, ctypes.cast(v, ctypes.POINTER(ctypes.c_void_p)))
-            self.config = self.make_config(cfg, block_B, max_rows, max_positions)
+            self.config = self.make_config(cfg, block_B, max_rows, max_positions, self.max_batch, sampling)
             h = ctypes.c_void_p()
             L.check(self.lib.ssb_init_model(byref(self.config), byref(w), _stream(), byref(h)))
             torch.cuda.current_stream().synchronize()
@@ -71,7 +76,7 @@ class Model:
         self.h = h
 
     @staticmethod
-    def make_config(cfg, block_B, max_rows, max_positions):
+    def make_config(cfg, block_B, max_rows, max_positions, max_batch=0, sampling=False):
         c = L.SsbConfig()
         for k in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
                   "mask_id", "eos_id"):
@@ -83,6 +88,8 @@ class Model:
         c.rms_eps = cfg.rms_eps
         c.rope_theta = cfg.rope_theta
         c.dtype = L.SSB_BF16 if cfg.dtype == "bf16" else L.SSB_F32
+        c.max_batch = max_batch
+        c.features = L.SSB_FEAT_SAMPLE if sampling else 0
         return c
 
     def prefix_tensor(self, prefix):
@@ -90,14 +97,22 @@ class Model:
         return torch.from_numpy(np.ascontiguousarray(prefix, dtype=np.float32)).to(self.device).to(
             torch_dtype(self.cfg))
 
+    def memory(self):
+        """(packed weight bytes, workspace bytes) the model holds on the device."""
+        wb, ws = ctypes.c_size_t(), ctypes.c_size_t()
+        L.check(self.lib.ssb_model_memory(self.h, byref(wb), byref(ws)))
+        return wb.value, ws.value
+
     def set_debug(self, poison):
         """NaN-poison the KV slots no correct read reaches (window slots between draft and verify,
         rolled-back slots after accept); rounds then run without graph replay."""
         L.check(self.lib.ssb_set_debug(self.h, L.SSB_DEBUG_POISON if poison else 0))
 
-    def profile_kernel(self, kind):
-        """Start timing every launch of one kernel kind (name in KERNEL_KINDS), or stop (None)."""
-        L.check(self.lib.ssb_profile_kernel(self.h, -1 if kind is None else L.KERNEL_KINDS[kind]))
+    def profile_kernel(self, kind, in_graph=False):
+        """Start timing every launch of one kernel kind (name in KERNEL_KINDS), or stop (None).
+        in_graph: rounds keep replaying launch graphs, with event nodes around the timed launches."""
+        code = -1 if kind is None else L.KERNEL_KINDS[kind] | (L.SSB_PROFILE_IN_GRAPH if in_graph else 0)
+        L.check(self.lib.ssb_profile_kernel(self.h, code))
 
     def profile_read(self, reset=True):
         us, n = ctypes.c_double(), ctypes.c_longlong()

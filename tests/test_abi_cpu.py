@@ -51,7 +51,8 @@ def test_config_validation(lib):
     bad = [dict(head_dim=48), dict(hidden=1000), dict(hidden=384), dict(n_kv_heads=3), dict(n_kv_heads=8),
            dict(ffn=3000), dict(mask_id=60000), dict(eos_id=59999), dict(block_B=65), dict(page_tokens=32),
            dict(max_rows=0), dict(max_rows=4000), dict(max_rows=16, block_B=32), dict(dtype=7),
-           dict(max_positions=1), dict(n_layers=0), dict(ffn=16384), dict(n_heads=128, n_kv_heads=32)]
+           dict(max_positions=1), dict(n_layers=0), dict(ffn=16384), dict(n_heads=128, n_kv_heads=32),
+           dict(max_batch=65), dict(max_batch=-1), dict(features=2)]
     for kw in bad:
         assert lib.ssb_check_config(ctypes.byref(_cfg(**kw))) == SSB_EINVAL, kw
         assert lib.ssb_last_error()
@@ -71,6 +72,7 @@ def test_null_arguments_are_rejected_without_a_gpu(lib):
     assert lib.ssb_pool_init(None, None, 0, 1, None) == SSB_EINVAL
     assert lib.ssb_kv_create(None, 16, None) == SSB_EINVAL
     assert lib.ssb_init_model(ctypes.byref(_cfg()), None, None, None) == SSB_EINVAL
+    assert lib.ssb_model_memory(None, ctypes.byref(size), None) == SSB_EINVAL
     lib.ssb_free_model(None)
     lib.ssb_kv_free(None)
     lib.ssb_pool_free(None)
