@@ -61,6 +61,8 @@ def alg_bytes_kernel(kind, cfg, M, n_keys):
         return 4 * M * H * 4 + M * H * 4 + M * H * (4 + e) + M * (H // 16) * 4
     if kind == "lm_head":
         return V * H * e + M * H * e + M * 12
+    if kind == "tail":      # the fused O + gate|up + down of one layer
+        return sum(alg_bytes_kernel(k, cfg, M, n_keys) for k in ("o", "gate_up", "down"))
     if kind == "attention":
         return n_keys * 2 * kvd * e + M * qd * e
     if kind == "combine":
@@ -868,6 +870,25 @@ def main():
         elapsed = time.perf_counter() - t0
     dev_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in events)
 
+    # the same rounds with each layer's O, gate|up and down as three launches instead of the fused
+    # layer tail (bit-identical results; device time only, for comparison)
+    def device_median(n):
+        evs = []
+        with no_gc():
+            for k in range(n):
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(st)
+                run(args.warmup + k)
+                a1.record(st)
+                evs.append((a0, a1))
+            torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs)
+    model.set_debug(False, unfused=True)
+    run(args.warmup)
+    unfused_us = device_median(min(args.steps, 50))
+    model.set_debug(False, unfused=False)
+    run(args.warmup)
+
     # rounds without planting (the draft's own proposals), same state
     unplanted = []
     for k in range(min(args.steps, 50)):
@@ -889,7 +910,7 @@ def main():
     # per-kernel timing of graph-replayed launches (as in the timed region): for each kernel kind
     # the engine replays a round graph in which every launch of that kind stamps, on the device's
     # real-time counter, its earliest workgroup start and its latest workgroup end
-    kinds = ["qkv", "attention", "combine", "o", "gate_up", "down", "reduce", "lm_head", "argmax"]
+    kinds = ["qkv", "attention", "combine", "o", "gate_up", "down", "reduce", "tail", "lm_head", "argmax"]
     breakdown = {}
     for kind in kinds:
         model.profile_kernel(kind, in_graph=True)
@@ -956,6 +977,7 @@ def main():
         "round_device_us": {"median": statistics.median(dev_us), "p10": dev_us[len(dev_us) // 10],
                             "p90": dev_us[(len(dev_us) * 9) // 10]},
         "round_us_unplanted_median": statistics.median(unplanted) * 1e6,
+        "round_device_us_unfused_tail_median": unfused_us,
         "copy_probe_GBs": copy_gbs,
         "round_roofline_frac": bytes_round / t_med / (PEAK_HBM_GBS * 1e9),
         "round_alg_bytes": bytes_round,

@@ -379,7 +379,8 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
  * count since the last reset; reset != 0 clears them.
  * kind: one of SSB_K_*, or -1 to stop timing. SSB_K_DOWN is the down
  * projection GEMM; SSB_K_REDUCE its K-split reduce (absent when the down
- * projection is not split). */
+ * projection is not split); SSB_K_TAIL the fused layer tail that replaces
+ * the O, gate|up and down launches of decode windows of at most 48 rows. */
 #define SSB_K_QKV 0
 #define SSB_K_ATTN 1
 #define SSB_K_COMBINE 2
@@ -389,6 +390,7 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
 #define SSB_K_LMHEAD 6
 #define SSB_K_ARGMAX 7
 #define SSB_K_REDUCE 8
+#define SSB_K_TAIL 9   /* the fused layer tail: O, gate|up and down of a decode window of <= 48 rows */
 #define SSB_PROFILE_IN_GRAPH 0x100
 int ssb_profile_kernel(ssb_model* m, int kind);
 int ssb_profile_read(ssb_model* m, double* total_us, long long* launches, int reset);
@@ -401,9 +403,15 @@ int ssb_profile_read(ssb_model* m, double* total_us, long long* launches, int re
  * draft and verify forwards, and at p+A+2 .. p+B+1 after accept. A correct
  * engine reads none of them before rewriting them, so results are unchanged
  * bit for bit; a stale read surfaces as NaN logits (SSB_EHIP from the round).
- * Rounds then run without graph replay. flags: 0 or SSB_DEBUG_POISON;
+ * Rounds then run without graph replay.
+ * With SSB_DEBUG_UNFUSED set, decode windows of at most 48 rows run each
+ * layer's O, gate|up and down projections as three GEMM launches instead of
+ * the fused layer tail (the same per-row arithmetic, so results are bit-
+ * identical: a test and measurement switch). Changing it drops the captured
+ * launch graphs. flags: any or of SSB_DEBUG_POISON and SSB_DEBUG_UNFUSED;
  * SSB_EINVAL for other bits or a null model. */
 #define SSB_DEBUG_POISON 1
+#define SSB_DEBUG_UNFUSED 2
 int ssb_set_debug(ssb_model* m, int flags);
 
 /* Debug: writes NaN into every layer's K and V at positions [lo, hi) of the

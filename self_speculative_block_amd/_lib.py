@@ -12,7 +12,7 @@ SSB_MAX_BATCH = 64
 SSB_MAX_BLOCK = 64
 SSB_PROFILE_IN_GRAPH = 0x100
 KERNEL_KINDS = {"qkv": 0, "attention": 1, "combine": 2, "o": 3, "gate_up": 4, "down": 5, "lm_head": 6, "argmax": 7,
-                "reduce": 8}
+                "reduce": 8, "tail": 9}
 
 c_int, c_float, c_double, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
 c_void_p = ctypes.c_void_p
@@ -44,6 +44,7 @@ class SsbStats(ctypes.Structure):
 
 SSB_SERVE_AR, SSB_SERVE_SPEC = 0, 1
 SSB_DEBUG_POISON = 1
+SSB_DEBUG_UNFUSED = 2
 
 
 class SsbRequest(ctypes.Structure):

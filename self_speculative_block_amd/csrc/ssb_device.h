@@ -226,6 +226,7 @@ struct AcceptSampleArgs {
   const ReqArgs* req;
   int32_t* acc;                                               // [kMaxReq] accepted count A
   int32_t* out; int out_stride;                               // commit records (as k_accept)
+  const int* err;                                             // nullable: layer-tail barrier failure flag
 };
 
 // Dynamic LDS layout of k_gemm (byte offsets), shared by the kernel and its launcher:
@@ -269,6 +270,17 @@ struct AttnArgs {
   AttnTasks tasks;
 };
 
+// Fused layer tail (O, gate|up, down) of decode forwards of at most 48 rows: one launch of
+// kTailWgs workgroups, one per CU, with two grid barriers (see k_layer_tail).
+constexpr int kTailWgs = 256;
+constexpr int kTailSyncWords = 16 * 19;   // generation word + 2 barriers x (global + 8 partitions), 128 B apart
+struct TailArgs {
+  GemmArgs o, gu, d;                 // the three GEMMs as k_gemm runs them
+  unsigned long long* sync;          // [kTailSyncWords] barrier counters, zero at model creation
+  int* err;                          // set to 1 when a barrier wait exceeds its bound
+  ProfStamp* stamp;                  // nullable timing stamps of this launch
+};
+
 // Timing hook of the launchers: while g_prof_ev[0] is set, launches use hipExtLaunchKernel with
 // this start/stop pair (single-threaded use, set and cleared by the engine around one launch).
 extern hipEvent_t g_prof_ev[2];
@@ -281,12 +293,13 @@ template <typename T> hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
 template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
 template <typename T> hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_big(const GemmArgs& a, int epi, bool exact, hipStream_t st);
+hipError_t launch_layer_tail(const TailArgs& a, hipStream_t st);
 int gemm_max_mt(int elem, int K, int S, int NT, int KSL, int n_ssq, int epi);
 // gs (nullable, then zs too): per-group exp-sums of the LM head at scale sc = log2(e) / T;
 // zs [M] gets the row's sum of exp((z - top1) / T) over the vocabulary without [M].
 hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, float sc, int n_groups,
                          int ld, int M, int32_t* tok, float* top1, float* top2, float* zs, hipStream_t st,
-                         ProfStamp* stamp = nullptr);
+                         ProfStamp* stamp = nullptr, const int* err = nullptr);
 hipError_t launch_sample_rows(const SampleArgs& a, int rows_per_req, int n_req, hipStream_t st);
 hipError_t launch_accept_sample(const AcceptSampleArgs& a, int n_req, hipStream_t st);
 template <typename T> hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipStream_t st);
@@ -298,7 +311,7 @@ template <typename T>
 hipError_t launch_poison_kv(const ReqArgs* req, int R, const int32_t* acc, int acc_stride, int lo_abs, int hi_abs,
                             void* kv_pool, int n_layers, int n_pages, int n_kv, int hd, hipStream_t st);
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
-                         int32_t* out, int out_stride, hipStream_t st);
+                         int32_t* out, int out_stride, hipStream_t st, const int* err = nullptr);
 hipError_t launch_dd_init(const ReqArgs* ra, int n_req, int mask_id, int32_t* rec, int rec_stride, hipStream_t st);
 hipError_t launch_dd_select(const int32_t* am, const float* zs, const ReqArgs* ra, int n_req, int mask_id,
                             int vocab, int32_t* rec, int rec_stride, hipStream_t st);

@@ -135,6 +135,11 @@ struct ssb_model {
   bool sampling;      // stochastic-round workspace allocated
   int32_t* accept_dev;
   bool debug_poison = false;   // NaN-poison KV slots no correct read reaches (rounds run eagerly)
+  // fused layer tail (O, gate|up, down in one launch) for decode forwards of <= 48 rows
+  bool tail_ok = false;        // the model's shapes and the device allow it
+  bool no_fused = false;       // debug: always run the three GEMM launches
+  unsigned long long* tail_sync = nullptr;   // barrier counters and generation [kTailSyncWords]
+  int* tail_err = nullptr;     // set by a layer-tail barrier that timed out
   int32_t* tok_dev;
   ReqArgs* req_dev;   // device request state read by every kernel of a forward
   ReqArgs* req_pin;   // pinned staging of the request state
@@ -412,6 +417,7 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   const size_t w_acc = take((size_t)kMaxReq * kOutStride * 4);
   const size_t w_tok = take((size_t)MR * 4);
   const size_t w_req = take(sizeof(ReqArgs));
+  const size_t w_tail = take((size_t)kTailSyncWords * 8 + 256);
   if (hipMalloc(&m->ws, off) != hipSuccess) fail(SSB_ENOMEM, "hipMalloc of workspace failed");
   m->ws_bytes = off;
   char* wsb = static_cast<char*>(m->ws);
@@ -449,6 +455,19 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   m->accept_dev = reinterpret_cast<int32_t*>(wsb + w_acc);
   m->tok_dev = reinterpret_cast<int32_t*>(wsb + w_tok);
   m->req_dev = reinterpret_cast<ReqArgs*>(wsb + w_req);
+  m->tail_sync = reinterpret_cast<unsigned long long*>(wsb + w_tail);
+  m->tail_err = reinterpret_cast<int*>(wsb + w_tail + (size_t)kTailSyncWords * 8);
+  hip_check(hipMemsetAsync(m->tail_sync, 0, (size_t)kTailSyncWords * 8 + 256, st), "clear layer-tail state");
+  {
+    // the fused layer tail needs one workgroup per CU for kTailWgs workgroups, and the GEMM plans it is
+    // written for (O and down: one tile, 8 K slices of 4 and 16 steps; gate|up: two tiles, 4 slices of 8)
+    int cus = 0;
+    hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, m->device), "CU count");
+    const GemmShape &o = m->o[0], &g = m->gu[0], &d = m->d[0];
+    m->tail_ok = c.dtype == SSB_BF16 && cus >= kTailWgs && o.NT == 1 && o.KSL == 8 && o.S == 1 && o.K == 1024 &&
+                 g.NT == 2 && g.KSL == 4 && g.K == 1024 && g.n_tiles == 2 * kTailWgs && d.NT == 1 && d.KSL == 8 &&
+                 d.S == 1 && d.K == 4096 && o.n_tiles == d.n_tiles && o.n_tiles * 3 <= kTailWgs;
+  }
   if (hipHostMalloc(reinterpret_cast<void**>(&m->req_pin), sizeof(ReqArgs), hipHostMallocDefault) != hipSuccess)
     fail(SSB_ENOMEM, "pinned host allocation failed");
   hip_check(hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking), "capture stream");
@@ -548,6 +567,10 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     add_tasks(0, 0, M, 0, f.pos0 + M - 1);
   }
   const int chunk_slots = f.graph ? (f.slots > 0 ? f.slots : m->max_chunks) : (f.max_pos - 1) / kKeyChunk + 1;
+  // decode windows of at most 48 rows run each layer's O, gate|up and down as one fused launch
+  // (same per-row arithmetic as the three GEMM launches); forwards without an LM head keep the
+  // three launches, since the argmax is what reports a failed layer-tail barrier
+  const bool tail = m->tail_ok && !m->no_fused && !tall && M <= 48 && !f.no_head;
 
   for (int l = 0; l < c.n_layers; ++l) {
     g.layer = l;
@@ -568,6 +591,19 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
       hip_check(launch_attn_combine<T>(m->apart, m->max_chunks, chunk_slots, c.n_heads, c.head_dim, m->row_lim, M,
                                        m->attn, qd, st, cst), "attention combine");
       prof_end(m, SSB_K_COMBINE, st);
+    }
+    if (tail) {  // O + residual, gate|up + SwiGLU, down + residual in one launch
+      TailArgs ta{};
+      ta.o = g; set_w(ta.o, m->o[l]); ta.o.x = m->attn; ta.o.ldx = qd; ta.o.gain_next = m->mlp_norm[l];
+      ta.gu = g; set_w(ta.gu, m->gu[l]); ta.gu.x = m->xg; ta.gu.ldx = H;
+      ta.d = g; set_w(ta.d, m->d[l]); ta.d.x = m->act; ta.d.ldx = c.ffn;
+      ta.d.gain_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
+      ta.sync = m->tail_sync;
+      ta.err = m->tail_err;
+      ta.stamp = prof_begin(m, SSB_K_TAIL, st);
+      hip_check(launch_layer_tail(ta, st), "layer tail");
+      prof_end(m, SSB_K_TAIL, st);
+      continue;
     }
     {  // O + residual; next input xg = h * mlp_norm[l]
       GemmArgs a = g;
@@ -630,7 +666,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     float* top1 = f.st_max ? f.st_max : m->am_top1;
     float* zs = f.st_z ? f.st_z : m->am_z;
     hip_check(launch_argmax(m->amv1, m->ami1, m->amv2, f.stat_sc > 0.f ? m->ams : nullptr, f.stat_sc, n_groups,
-                            n_groups, rows, m->am_tok, top1, m->am_top2, zs, st, ast), "argmax");
+                            n_groups, rows, m->am_tok, top1, m->am_top2, zs, st, ast, m->tail_err), "argmax");
     prof_end(m, SSB_K_ARGMAX, st);
     if (f.sample) {
       if (!f.logits || !(f.stat_sc > 0.f)) fail(SSB_EINVAL, "sampling needs logits and row sums");
@@ -935,10 +971,11 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
       aa.lg_d = dlog ? dlog : m->slog_d; aa.dmax = m->smax_d; aa.dz = m->sz_d;
       aa.lg_v = vlog ? vlog : m->slog_v; aa.vmax = m->smax_v; aa.vz = m->sz_v;
       aa.vocab = c.vocab; aa.mask_id = c.mask_id; aa.eos_id = c.eos_id; aa.sc = kLog2e / smp->temperature;
-      aa.req = m->req_dev; aa.out = m->accept_dev; aa.out_stride = kOutStride;
+      aa.req = m->req_dev; aa.out = m->accept_dev; aa.out_stride = kOutStride; aa.err = m->tail_err;
       hip_check(launch_accept_sample(aa, R, s), "stochastic accept");
     } else {
-      hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, R, c.eos_id, m->accept_dev, kOutStride, s),
+      hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, R, c.eos_id, m->accept_dev, kOutStride, s,
+                              m->tail_err),
                 "accept");
     }
     if (m->debug_poison) poison_kv(m, pool, R, m->accept_dev, s);   // the rolled-back slots
@@ -1396,7 +1433,8 @@ void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau,
     f.graph = graph;
     f.logits = vlog;
     run_forward(m, pool, f, s);
-    hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, 1, c.eos_id, m->accept_dev, kOutStride, s), "accept");
+    hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, 1, c.eos_id, m->accept_dev, kOutStride, s,
+                            m->tail_err), "accept");
     hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)kOutStride * 4, hipMemcpyDeviceToHost, s),
               "copy accept");
   };
@@ -1689,8 +1727,17 @@ int ssb_kv_poison(ssb_kv* kv, int lo, int hi, void* stream) {
 int ssb_set_debug(ssb_model* m, int flags) {
   return guard([&] {
     if (!m) fail(SSB_EINVAL, "null model");
-    if (flags & ~SSB_DEBUG_POISON) fail(SSB_EINVAL, "unknown debug flag");
+    if (flags & ~(SSB_DEBUG_POISON | SSB_DEBUG_UNFUSED)) fail(SSB_EINVAL, "unknown debug flag");
     m->debug_poison = (flags & SSB_DEBUG_POISON) != 0;
+    const bool no_fused = (flags & SSB_DEBUG_UNFUSED) != 0;
+    if (no_fused != m->no_fused) {
+      // captured graphs hold the other form of the layer tail
+      hip_check(hipDeviceSynchronize(), "sync before dropping graphs");
+      for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+      m->graphs.clear();
+      m->graph_prof_pairs.clear();
+      m->no_fused = no_fused;
+    }
   });
 }
 
@@ -1955,7 +2002,7 @@ int ssb_profile_kernel(ssb_model* m, int kind) {
     if (!m) fail(SSB_EINVAL, "null model");
     const bool in_graph = kind >= 0 && (kind & SSB_PROFILE_IN_GRAPH);
     if (kind >= 0) kind &= ~SSB_PROFILE_IN_GRAPH;
-    if (kind < -1 || kind > SSB_K_REDUCE) fail(SSB_EINVAL, "unknown kernel kind");
+    if (kind < -1 || kind > SSB_K_TAIL) fail(SSB_EINVAL, "unknown kernel kind");
     hip_check(hipSetDevice(m->device), "hipSetDevice");
     if (kind >= 0 && m->prof_ev.empty()) {
       // two forwards of a round launch each kind at most n_layers + 1 times, plus prefill chunks

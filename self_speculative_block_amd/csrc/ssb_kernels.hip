@@ -224,7 +224,18 @@ __device__ __forceinline__ float lane_group_sum(float v, int g) {
 // Residual epilogue of a [MB x 16*NT] output tile held in LDS (row stride 17): h += tile,
 // next input xg = h * gain_next, per-16-column sums of squares of h.  s_pre holds the
 // prefetched h tile [NT][MB][16] and the next gain [NT*16].
-template <typename T, int MB>
+// Device-coherent (agent-scope) stores and loads: written through to, and read from, the memory
+// side, so another workgroup of the same kernel on another XCD sees them after a grid barrier
+// with no cache flush (the workgroup that stores waits for their completion before arriving).
+template <typename V>
+__device__ __forceinline__ void st_coh(V* p, V v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename V>
+__device__ __forceinline__ V ld_coh(const V* p) {
+  return __hip_atomic_load(const_cast<V*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr int kCoh = 16;   // cache-policy bit sc1 of a buffer load: device-coherent
+
+template <typename T, int MB, bool COH = false>
 __device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, const float* s_pre, int tg, int NT,
                                                int m_base, int m_end) {
 #pragma clang fp contract(off)
@@ -238,8 +249,14 @@ __device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, 
     ct[n] = v;
     if (m >= m_end) continue;
     const int col = (tg * NT + t) * 16 + n;
-    a.h[(size_t)m * a.hidden + col] = v;
-    reinterpret_cast<T*>(a.xg_out)[(size_t)m * a.hidden + col] = Act<T>::from_f(v * s_g[t * 16 + n]);
+    T* xo = reinterpret_cast<T*>(a.xg_out) + (size_t)m * a.hidden + col;
+    if constexpr (COH) {
+      st_coh(a.h + (size_t)m * a.hidden + col, v);
+      st_coh(xo, Act<T>::from_f(v * s_g[t * 16 + n]));
+    } else {
+      a.h[(size_t)m * a.hidden + col] = v;
+      *xo = Act<T>::from_f(v * s_g[t * 16 + n]);
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < NT * MB; e += kGemmThreads) {
@@ -249,7 +266,8 @@ __device__ __forceinline__ void resid_epilogue(const GemmArgs& a, float* ctile, 
     const float* ct = ctile + (t * MB + r) * 17;
     float sum = 0.f;
     for (int n = 0; n < 16; ++n) sum += ct[n] * ct[n];
-    a.ssq_out[(size_t)m * a.ssq_ld + tg * NT + t] = sum;
+    if constexpr (COH) st_coh(a.ssq_out + (size_t)m * a.ssq_ld + tg * NT + t, sum);
+    else a.ssq_out[(size_t)m * a.ssq_ld + tg * NT + t] = sum;
   }
 }
 
@@ -632,6 +650,316 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Fused tail of one decoder layer for decode forwards of at most 48 rows: O + residual, gate|up
+// + SwiGLU and down + residual in one kernel of kTailWgs workgroups (one per CU), separated by
+// two grid barriers.  Every workgroup issues the loads of all three of its weight slices at
+// entry (O: 32 KB, gate|up: 64 KB, down: 128 KB), so the gate|up and down weights stream in from
+// HBM while the O stage and the first barrier run, instead of each GEMM starting cold after a
+// kernel boundary.  The data that crosses a barrier inside the kernel (the residual h, the next
+// GEMM input xg and the norm partials from O; the SwiGLU output from gate|up) is written and read
+// device-coherently (write-through stores, sc1 loads), so the barrier needs no cache flush.
+//
+// Each stage performs, for every row, exactly the operations of k_gemm with the same plan (O and
+// down: one 16-column tile, 8 K slices; gate|up: 2 tiles, 4 K slices; slice partial tiles added
+// in slice order, the same 1/rms butterfly and epilogues, no contraction), so rows stay
+// bit-identical to the unfused kernels whatever kernel computes them.  Waves 0-7 own the K slices
+// as in k_gemm.  A wave's memory operations complete in issue order, so every load is placed by
+// what it must not wait behind: the gate|up weights go out right after the O stage's own loads,
+// the down weights once the gate|up activations are in.  A ninth wave (kStoreWave) makes every
+// store that crosses a barrier and loads nothing, so it alone waits for its stores before the
+// workgroup arrives, and the other waves keep their weight loads in flight across the barriers.
+//
+// Barriers: arrivals count on 8 partition counters (workgroup w in partition w % 8) whose last
+// arrival bumps a global counter; counters grow monotonically, a launch reading the generation
+// word at entry and waiting for (generation + 1) x its arrivals; the last workgroup through the
+// second barrier advances the generation.  Waits are bounded: past kSpinMax polls a workgroup sets
+// *err and leaves (results are then invalid, and the argmax and accept kernels report it).
+// ---------------------------------------------------------------------------
+constexpr int kTailParts = 8;
+constexpr int kSpinMax = 1 << 16;
+constexpr int kStoreWave = kGemmThreads / kWave;        // the ninth wave
+constexpr int kTailThreads = kGemmThreads + kWave;
+
+// Arrival and polling are the store wave's: it holds no load that could delay its atomics (a
+// wave's memory operations complete in issue order, and the other waves have weight loads in
+// flight), and no other wave has a store in flight.  Returns whether every workgroup arrived;
+// *last tells the workgroup whose arrival completed the barrier.
+__device__ __forceinline__ bool tail_barrier(unsigned long long* sync, int b, unsigned long long gen, int* err,
+                                             int* s_flag, bool* last) {
+  if ((int)threadIdx.x == kStoreWave * kWave) {
+    __builtin_amdgcn_s_waitcnt(0);   // this workgroup's coherent stores have completed
+    const int p = blockIdx.x % kTailParts;
+    const unsigned long long per = kTailWgs / kTailParts;
+    unsigned long long* gc = sync + 16 * (1 + 9 * b);
+    unsigned long long* pc = sync + 16 * (2 + 9 * b + p);
+    bool lst = false;
+    const unsigned long long old = __hip_atomic_fetch_add(pc, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == (gen + 1) * per) {
+      const unsigned long long g = __hip_atomic_fetch_add(gc, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lst = g + 1 == (gen + 1) * kTailParts;
+    }
+    int spins = 0;
+    while (ld_coh(gc) < (gen + 1) * kTailParts && ++spins < kSpinMax) __builtin_amdgcn_s_sleep(1);
+    const bool ok = spins < kSpinMax;
+    if (!ok) st_coh(err, 1);
+    s_flag[0] = ok;
+    s_flag[1] = lst;
+  }
+  __syncthreads();
+  *last = s_flag[1] != 0;
+  return s_flag[0] != 0;
+}
+
+template <int KPW_O, int KPW_G, int KPW_D>
+__global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
+#pragma clang fp contract(off)
+  using T = bf16_t;
+  constexpr int KS = Ty<T>::kStepK, PER = Ty<T>::kPerFrag, NTH = kGemmThreads;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float s_inv[48];
+  __shared__ int s_flag[2];
+  __shared__ unsigned long long s_gen;
+  stamp_begin(ta.stamp);
+  const GemmArgs& ao = ta.o;
+  const GemmArgs& ag = ta.gu;
+  const GemmArgs& ad = ta.d;
+  const int w = blockIdx.x;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const bool cw = wave < kStoreWave;                 // waves 0-7: the K slices
+  const int M = ao.M, m_last = M - 1;
+  if ((int)threadIdx.x == kStoreWave * kWave) s_gen = ld_coh(ta.sync);
+
+  // ---- O stage item (k_gemm's DIRECT form: balanced 16-row blocks); its loads first ----
+  const int nrb = (M + 15) / 16;
+  const int rpb_o = min(16, (M + nrb - 1) / nrb);
+  const bool has_o = w < ao.n_tiles * nrb;
+  const int to = w % ao.n_tiles, mb_o = w / ao.n_tiles;
+  const int mbase_o = mb_o * rpb_o, mend_o = min(M, mbase_o + rpb_o);
+  const bool has_d = w < ad.n_tiles * nrb;
+  const int td = w % ad.n_tiles, mb_d = w / ad.n_tiles;
+  uint4 wo[KPW_O], bxo[KPW_O], wgf[KPW_G], wdf[KPW_D];
+  float pho = 0.f, pgo = 0.f;
+  if (cw) {
+    if (has_o) {
+      const uint4* wp = ao.W + ((size_t)to * (ao.K / KS) + wave * KPW_O) * kWave + lane;
+#pragma unroll
+      for (int s = 0; s < KPW_O; ++s) wo[s] = wp[(size_t)s * kWave];
+      const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ao.x), (short)0,
+                                                                          mend_o * ao.ldx * (int)sizeof(T), kBufWord3);
+#pragma unroll
+      for (int s = 0; s < KPW_O; ++s) {
+        const int off = ((mbase_o + lane % 16) * ao.ldx + (wave * KPW_O + s) * KS + PER * (lane / 16)) * (int)sizeof(T);
+        bxo[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+      }
+      const int e = min((int)threadIdx.x, 255), r = (e / 16) % 16, n = e % 16;
+      pho = ao.h[(size_t)min(mbase_o + r, m_last) * ao.hidden + to * 16 + n];
+      pgo = ao.gain_next[to * 16 + min((int)threadIdx.x, 15)];
+    }
+    asm volatile("" ::: "memory");   // the gate|up weights go out after the O stage's loads
+    const uint4* gp = ag.W + ((size_t)(w * 2 + wave / 4) * (ag.K / KS) + (wave % 4) * KPW_G) * kWave + lane;
+#pragma unroll
+    for (int s = 0; s < KPW_G; ++s) wgf[s] = gp[(size_t)s * kWave];
+  }
+  __syncthreads();
+  const unsigned long long gen = s_gen;
+  bool last = false;
+
+  // ---- stage 1: O + residual (h, xg, norm partials written coherently by the store wave) ----
+  if (has_o) {
+    const GemmLds L = gemm_lds(1, 8 * KPW_O * KS * (int)sizeof(T), 1, 8, ao.n_ssq, EPI_RESID);
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + L.red);
+    float* ctile = reinterpret_cast<float*>(smem + L.ctile);
+    float* s_h = reinterpret_cast<float*>(smem + L.pre);
+    if (cw) {
+      if (threadIdx.x < 256) s_h[threadIdx.x] = pho;
+      if (threadIdx.x < 16) s_h[256 + threadIdx.x] = pgo;
+      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KPW_O; ++s) mma_wa(acc, wo[s], bxo[s], T());
+      red[wave * kWave + lane] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      const int l = threadIdx.x;
+      f32x4_t v = red[l];
+      for (int j = 1; j < 8; ++j) v = v + red[j * kWave + l];
+      float* dst = ctile + (l % 16) * 17 + 4 * (l / 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = v[i];
+    }
+    __syncthreads();
+    if (wave == kStoreWave) {
+      // k_gemm's residual epilogue: v = h + tile, xg = v * gain, each row's 16 squares in order
+      for (int e = lane; e < 256; e += kWave) {
+        const int r = e / 16, n = e % 16, m = mbase_o + r;
+        if (m >= mend_o) continue;
+        const float v = s_h[e] + ctile[r * 17 + n];
+        const int col = to * 16 + n;
+        st_coh(ao.h + (size_t)m * ao.hidden + col, v);
+        st_coh(reinterpret_cast<T*>(ao.xg_out) + (size_t)m * ao.hidden + col, Act<T>::from_f(v * s_h[256 + n]));
+      }
+      if (lane < 16 && mbase_o + lane < mend_o) {
+        float sum = 0.f;
+        for (int n = 0; n < 16; ++n) {
+          const float v = s_h[lane * 16 + n] + ctile[lane * 17 + n];
+          sum += v * v;
+        }
+        st_coh(ao.ssq_out + (size_t)(mbase_o + lane) * ao.ssq_ld + to, sum);
+      }
+    }
+  }
+  if (!tail_barrier(ta.sync, 0, gen, ta.err, s_flag, &last)) return;
+
+  // ---- stage 2: gate|up + SwiGLU over all rows (one 48-row block; SwiGLU output coherent) ----
+  {
+    constexpr int MT = 3, MB = 48, KR = 4 * KPW_G * KS, XSTR = KR * (int)sizeof(T) + 16;
+    constexpr int FPR = KR / PER, TOTAL = MB * FPR, SB = 12;
+    static_assert(TOTAL == SB * NTH, "the gate|up slab is 12 fragments per thread");
+    constexpr int fsh = __builtin_ctz(FPR);
+    const GemmLds L = gemm_lds(MT, KR * (int)sizeof(T), 2, 4, ag.n_ssq, EPI_SWIGLU);
+    unsigned char* slab = smem;
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + L.red);
+    float* ctile = reinterpret_cast<float*>(smem + L.ctile);
+    constexpr int NPASS = 3;
+    const int G = ag.n_ssq / 4, gsh = 31 - __builtin_clz(G), RP = NTH >> gsh;
+    float4 sv[NPASS];
+    if (cw) {
+      const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ag.x), (short)0,
+                                                                          M * ag.ldx * (int)sizeof(T), kBufWord3);
+      uint4 xs[SB];
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int e = threadIdx.x + b * NTH;
+        const int off = ((e >> fsh) * ag.ldx + (e & (FPR - 1)) * PER) * (int)sizeof(T);
+        xs[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, kCoh));
+      }
+      const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ag.ssq), (short)0,
+                                                                          M * ag.ssq_ld * 4, kBufWord3);
+#pragma unroll
+      for (int k = 0; k < NPASS; ++k) {
+        const int row = min(k * RP + ((int)threadIdx.x >> gsh), MB - 1);
+        const int off = (row * ag.ssq_ld + ((int)threadIdx.x & (G - 1)) * 4) * 4;
+        sv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, kCoh));
+      }
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int e = threadIdx.x + b * NTH;
+        *reinterpret_cast<uint4*>(slab + (e >> fsh) * XSTR + (e & (FPR - 1)) * 16) = xs[b];
+      }
+      asm volatile("" ::: "memory");   // the down weights go out once the activations are in
+      if (has_d) {
+        const uint4* dp = ad.W + ((size_t)td * (ad.K / KS) + wave * KPW_D) * kWave + lane;
+#pragma unroll
+        for (int s = 0; s < KPW_D; ++s) wdf[s] = dp[(size_t)s * kWave];
+      }
+    }
+    __syncthreads();
+    if (cw) {
+      const int ksl = wave % 4;
+      f32x4_t acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KPW_G; ++s) {
+        const int kb = ((ksl * KPW_G + s) * KS + PER * (lane / 16)) * (int)sizeof(T);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          mma_wa(acc[mt], wgf[s], *reinterpret_cast<const uint4*>(slab + (mt * 16 + lane % 16) * XSTR + kb), T());
+      }
+      const float rh = 1.0f / (float)ag.hidden;
+#pragma unroll
+      for (int k = 0; k < NPASS; ++k) {
+        if (k * RP >= MB) break;
+        const float sum = lane_group_sum(((sv[k].x + sv[k].y) + sv[k].z) + sv[k].w, G);
+        const int row = k * RP + ((int)threadIdx.x >> gsh);
+        if (((int)threadIdx.x & (G - 1)) == 0 && row < MB) s_inv[row] = 1.0f / sqrtf(sum * rh + ag.eps);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * kWave + lane] = acc[mt];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 2 * MT * kWave; e += NTH) {
+      const int t = e / (MT * kWave), mt = (e / kWave) % MT, l = e % kWave;
+      f32x4_t v = red[((t * 4) * MT + mt) * kWave + l];
+      for (int j = 1; j < 4; ++j) v = v + red[((t * 4 + j) * MT + mt) * kWave + l];
+      float* dst = ctile + (t * MB + mt * 16 + l % 16) * 17 + 4 * (l / 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = v[i];
+    }
+    __syncthreads();
+    for (int e = lane; wave == kStoreWave && e < 2 * MB * 8; e += kWave) {
+      const int t = e / (MB * 8), r = (e / 8) % MB, c = e % 8;
+      if (r >= M) continue;
+      const float* ct = ctile + (t * MB + r) * 17;
+      const float g = ct[c] * s_inv[r];
+      const float u = ct[c + 8] * s_inv[r];
+      st_coh(reinterpret_cast<T*>(ag.act) + (size_t)r * ag.act_ld + (w * 2 + t) * 8 + c, Act<T>::from_f(silu_f(g) * u));
+    }
+  }
+  if (!tail_barrier(ta.sync, 1, gen, ta.err, s_flag, &last)) return;
+
+  // ---- stage 3: down + residual (16-row blocks; its outputs feed the next kernel) ----
+  if (has_d) {
+    constexpr int MB = 16, KR = 8 * KPW_D * KS, XSTR = KR * (int)sizeof(T) + 16;
+    constexpr int FPR = KR / PER, TOTAL = MB * FPR, SB = 16;
+    static_assert(TOTAL == SB * NTH, "the down slab is 16 fragments per thread");
+    constexpr int fsh = __builtin_ctz(FPR);
+    const GemmLds L = gemm_lds(1, KR * (int)sizeof(T), 1, 8, ad.n_ssq, EPI_RESID);
+    unsigned char* slab = smem;
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + L.red);
+    float* ctile = reinterpret_cast<float*>(smem + L.ctile);
+    float* s_h = reinterpret_cast<float*>(smem + L.pre);
+    const int m_base = mb_d * MB, m_end = min(M, m_base + MB);
+    if (cw) {
+      const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ad.x), (short)0,
+                                                                          M * ad.ldx * (int)sizeof(T), kBufWord3);
+      uint4 xs[SB];
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int e = threadIdx.x + b * NTH;
+        const int off = ((m_base + (e >> fsh)) * ad.ldx + (e & (FPR - 1)) * PER) * (int)sizeof(T);
+        xs[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, kCoh));
+      }
+      const int e0 = min((int)threadIdx.x, 255), r0 = (e0 / 16) % 16, n0 = e0 % 16;
+      const float ph = ld_coh(ad.h + (size_t)min(m_base + r0, m_last) * ad.hidden + td * 16 + n0);
+      const float pg = ad.gain_next[td * 16 + min((int)threadIdx.x, 15)];
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int e = threadIdx.x + b * NTH;
+        *reinterpret_cast<uint4*>(slab + (e >> fsh) * XSTR + (e & (FPR - 1)) * 16) = xs[b];
+      }
+      if (threadIdx.x < 256) s_h[threadIdx.x] = ph;
+      if (threadIdx.x < 16) s_h[256 + threadIdx.x] = pg;
+    }
+    __syncthreads();
+    if (cw) {
+      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KPW_D; ++s) {
+        const int kb = ((wave * KPW_D + s) * KS + PER * (lane / 16)) * (int)sizeof(T);
+        mma_wa(acc, wdf[s], *reinterpret_cast<const uint4*>(slab + (lane % 16) * XSTR + kb), T());
+      }
+      red[wave * kWave + lane] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      const int l = threadIdx.x;
+      f32x4_t v = red[l];
+      for (int j = 1; j < 8; ++j) v = v + red[j * kWave + l];
+      float* dst = ctile + (l % 16) * 17 + 4 * (l / 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = v[i];
+    }
+    __syncthreads();
+    resid_epilogue<T, 16, false>(ad, ctile, s_h, td, 1, m_base, m_end);
+  }
+  // every workgroup has read the generation word and passed both barriers: the next launch may go
+  if (last && (int)threadIdx.x == kStoreWave * kWave)
+    __hip_atomic_fetch_add(ta.sync, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  stamp_end(ta.stamp);
+}
+
+// ---------------------------------------------------------------------------
 // Large-M GEMM for prefill and teacher-forced forwards (M >= 128 rows, bf16):
 // the same packed weight fragments and fused epilogues as k_gemm (QKV + RoPE +
 // KV write, residual + next norm input, SwiGLU), tiled for operand reuse.  A
@@ -992,7 +1320,8 @@ __global__ __launch_bounds__(64) void k_resid_reduce(GemmArgs a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int32_t* i1, const float* v2,
                                                     const float* gs, float sc, int n_groups, int ld, int32_t* tok,
-                                                    float* top1, float* top2, float* zs, ProfStamp* stamp) {
+                                                    float* top1, float* top2, float* zs, ProfStamp* stamp,
+                                                    const int* err) {
   stamp_begin(stamp);
   __shared__ Top2 sh[kThreads];
   __shared__ float ssum[kThreads];
@@ -1024,7 +1353,7 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float* v1, const int3
     Top2 r = sh[0];
     for (int w = 1; w < kThreads / kWave; ++w) r = merge_top2(r, sh[w]);
     sh[0] = r;
-    tok[m] = r.i1;
+    tok[m] = (err && *err) ? -1 : r.i1;   // a failed layer-tail barrier: no valid token
     top1[m] = r.v1;
     top2[m] = r.v2;
   }
@@ -1366,7 +1695,7 @@ __global__ __launch_bounds__(kWave) void k_attn_combine(const float* part, int m
 // Output per request: [A, n_committed, next_x0, eos_seen, committed...].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* rap,
-                                               int eos_id, int32_t* out, int out_stride) {
+                                               int eos_id, int32_t* out, int out_stride, const int* err) {
   const ReqArgs& ra = *rap;
   const int r = blockIdx.x, j = threadIdx.x;
   const int B = ra.B, row0 = ra.row0[r];
@@ -1390,7 +1719,7 @@ __global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int
   if (k1 < n) o[4 + k1] = t1;
   if (k2 < n) o[4 + k2] = t2;
   if (j == 0) {
-    o[0] = A;
+    o[0] = (err && *err) ? -1 : A;   // a failed layer-tail barrier: the host rejects the round
     o[1] = n;
     o[2] = am[row0 + A];
     o[3] = (eos_at < ncand && eos_at < n) ? 1 : 0;
@@ -1676,7 +2005,7 @@ __global__ __launch_bounds__(kThreads) void k_accept_sample(AcceptSampleArgs a) 
     int n = min(ncand, eos_at + 1);
     n = min(n, ra.max_commit[r]);
     for (int k = 0; k < n; ++k) o[4 + k] = k <= A ? a.row_tok[row0 + k] : tk;
-    o[0] = A;
+    o[0] = (a.err && *a.err) ? -1 : A;   // a failed layer-tail barrier: the host rejects the round
     o[1] = n;
     o[2] = tk;
     o[3] = (eos_at < ncand && eos_at < n) ? 1 : 0;
@@ -1868,9 +2197,10 @@ template hipError_t launch_resid_reduce<float>(const GemmArgs&, hipStream_t);
 
 hipError_t launch_argmax(const float* v1, const int32_t* i1, const float* v2, const float* gs, float sc, int n_groups,
                          int ld, int M, int32_t* tok, float* top1, float* top2, float* zs, hipStream_t st,
-                         ProfStamp* stamp) {
+                         ProfStamp* stamp, const int* err) {
   if (gs && !zs) return hipErrorInvalidValue;
-  SSB_LAUNCH(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, gs, sc, n_groups, ld, tok, top1, top2, zs, stamp);
+  SSB_LAUNCH(k_argmax, dim3(M), dim3(kThreads), 0, st, v1, i1, v2, gs, sc, n_groups, ld, tok, top1, top2, zs, stamp,
+             err);
   return hipGetLastError();
 }
 
@@ -1934,8 +2264,8 @@ template hipError_t launch_poison_kv<float>(const ReqArgs*, int, const int32_t*,
                                             int, hipStream_t);
 
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
-                         int32_t* out, int out_stride, hipStream_t st) {
-  SSB_LAUNCH(k_accept, dim3(n_req), dim3(64), 0, st, row_tok, am, ra, eos_id, out, out_stride);
+                         int32_t* out, int out_stride, hipStream_t st, const int* err) {
+  SSB_LAUNCH(k_accept, dim3(n_req), dim3(64), 0, st, row_tok, am, ra, eos_id, out, out_stride, err);
   return hipGetLastError();
 }
 
@@ -1951,6 +2281,32 @@ hipError_t launch_dd_select(const int32_t* am, const float* zs, const ReqArgs* r
                             int vocab, int32_t* rec, int rec_stride, hipStream_t st) {
   if (n_req < 1 || n_req > kMaxReq || rec_stride < 4 + 4 * kWave) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_dd_select, dim3(n_req), dim3(kWave), 0, st, am, zs, ra, mask_id, vocab, rec, rec_stride);
+  return hipGetLastError();
+}
+
+// One launch per decode layer: kTailWgs workgroups of nine waves, one per CU (the slab of the down
+// stage keeps a second one off a CU).  Shapes must be those the fused kernel is written for; anything else is
+// hipErrorInvalidValue and the engine runs the three GEMM launches instead.
+int layer_tail_lds(int n_ssq) {
+  const int o = gemm_lds(1, 8 * 4 * 32 * 2, 1, 8, n_ssq, EPI_RESID).total;
+  const int g = gemm_lds(3, 4 * 8 * 32 * 2, 2, 4, n_ssq, EPI_SWIGLU).total;
+  const int d = gemm_lds(1, 8 * 16 * 32 * 2, 1, 8, n_ssq, EPI_RESID).total;
+  return max(o, max(g, d));
+}
+
+hipError_t launch_layer_tail(const TailArgs& a, hipStream_t st) {
+  const int M = a.o.M, nrb = (M + 15) / 16;
+  const bool ok = M >= 1 && M <= 48 && a.gu.M == M && a.d.M == M && a.o.S == 1 && a.d.S == 1 &&
+                  a.o.NT == 1 && a.o.KSL == 8 && a.o.K == 8 * 4 * 32 &&
+                  a.gu.NT == 2 && a.gu.KSL == 4 && a.gu.K == 4 * 8 * 32 && a.gu.n_tiles == 2 * kTailWgs &&
+                  a.d.NT == 1 && a.d.KSL == 8 && a.d.K == 8 * 16 * 32 &&
+                  a.o.n_tiles * nrb <= kTailWgs && a.d.n_tiles * nrb <= kTailWgs && a.o.n_tiles == a.d.n_tiles &&
+                  a.o.hidden == a.o.n_tiles * 16 && a.gu.n_ssq == a.o.hidden / 16 && a.gu.n_ssq % 4 == 0 &&
+                  a.gu.n_ssq / 4 <= 64 && ((a.gu.n_ssq / 4) & (a.gu.n_ssq / 4 - 1)) == 0 && a.sync && a.err;
+  if (!ok) return hipErrorInvalidValue;
+  const int shm = layer_tail_lds(a.gu.n_ssq);
+  if (shm > kGemmMaxLds) return hipErrorInvalidValue;
+  SSB_LAUNCH((k_layer_tail<4, 8, 16>), dim3(kTailWgs), dim3(kTailThreads), shm, st, a);
   return hipGetLastError();
 }
 

@@ -103,10 +103,13 @@ class Model:
         L.check(self.lib.ssb_model_memory(self.h, byref(wb), byref(ws)))
         return wb.value, ws.value
 
-    def set_debug(self, poison):
-        """NaN-poison the KV slots no correct read reaches (window slots between draft and verify,
-        rolled-back slots after accept); rounds then run without graph replay."""
-        L.check(self.lib.ssb_set_debug(self.h, L.SSB_DEBUG_POISON if poison else 0))
+    def set_debug(self, poison, unfused=False):
+        """poison: NaN-poison the KV slots no correct read reaches (window slots between draft and
+        verify, rolled-back slots after accept); rounds then run without graph replay.
+        unfused: run each layer's O, gate|up and down as three launches instead of the fused layer
+        tail (bit-identical; a test and measurement switch)."""
+        flags = (L.SSB_DEBUG_POISON if poison else 0) | (L.SSB_DEBUG_UNFUSED if unfused else 0)
+        L.check(self.lib.ssb_set_debug(self.h, flags))
 
     def profile_kernel(self, kind, in_graph=False):
         """Start timing every launch of one kernel kind (name in KERNEL_KINDS), or stop (None).

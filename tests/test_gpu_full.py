@@ -137,6 +137,32 @@ def test_spec_decode_equals_ar_decode_and_oracle(full):
     assert kv.prefill(pre_dev) == full["y1"]
 
 
+@pytest.mark.parametrize("astar", [20, 32])
+def test_fused_layer_tail_equals_three_launches(full, astar):
+    """Decode windows of at most 48 rows run each layer's O, gate|up and down as one fused launch
+    (two grid barriers inside); the three-launch form must give the same bits: tokens, state and
+    both forwards' logits, for a round and for an AR step."""
+    cfg, P, kv, model = full["cfg"], full["P"], full["kv"], full["model"]
+    y1 = full["y1"]
+    plant = torch.tensor(build_plant(full["cont"], 1, astar, B, cfg.vocab, cfg.mask_id), dtype=torch.int32,
+                         device="cuda")
+    outs = []
+    for unfused in (False, True):
+        model.set_debug(False, unfused=unfused)
+        kv.rewind(P, y1)
+        c, A, dl, vl = kv.round(B, planted_dev=plant, want_logits=True)
+        st = kv.state()
+        kv.rewind(P, y1)
+        tok, lg = kv.ar_step(want_logits=True)
+        outs.append((c, A, dl, vl, st, tok, lg))
+    model.set_debug(False, unfused=False)
+    (c0, A0, d0, v0, s0, t0, l0), (c1, A1, d1, v1, s1, t1, l1) = outs
+    assert (c0, A0, s0, t0) == (c1, A1, s1, t1)
+    assert torch.equal(d0, d1) and torch.equal(v0, v1), "round logits differ between fused and unfused tails"
+    assert torch.equal(l0, l1), "AR-step logits differ between fused and unfused tails"
+    kv.rewind(P, y1)
+
+
 @pytest.mark.parametrize("Bs", [16, 24])
 def test_spec_decode_other_block_sizes_equal_ar(full, Bs):
     """Windows of 17 and 25 rows take other GEMM row tiles than the 33-row window (QKV and O in
