@@ -190,6 +190,22 @@ int ssb_round(ssb_model* m, ssb_kv* kv, int B, int max_commit, const int32_t* pl
               int32_t* committed, int32_t* n_committed, int32_t* accept_len, float* draft_logits_dev,
               float* verify_logits_dev, void* stream);
 
+/* ssb_round for callers that cannot allocate device memory: tight serving
+ * loops and harnesses that forbid allocation. Same arguments and results as
+ * ssb_round without the logits outputs (bit-identical committed tokens,
+ * accept length and kv state), and it calls no hipMalloc, hipFree or other
+ * allocating routine: the forward workspace of the window (B+1 rows, one
+ * request) lives in a file-scope device array of 16 MiB that each GPU holds
+ * until the process ends, and the launches run eagerly, since instantiating
+ * a launch graph allocates. A window that would need more than 16 MiB (for
+ * hidden 1024, 16 heads and vocab 60000: B = 32 up to about 6,900 cached
+ * positions, B = 64 up to about 3,200) fails with SSB_EINVAL, state unchanged. The kv's
+ * pages come from its pool without allocating. Calls on one GPU share the
+ * array: overlapping calls on the same GPU race. Synchronous on stream, like
+ * ssb_round. */
+int ssb_round_noalloc(ssb_model* m, ssb_kv* kv, int B, int max_commit, const int32_t* planted_dev,
+                      int32_t* committed, int32_t* n_committed, int32_t* accept_len, void* stream);
+
 /* One AR step: feed x0 at position p causally. *token gets the argmax,
  * which becomes the new boundary. Length becomes p+1. logits_dev is
  * nullable, fp32 [vocab]. */

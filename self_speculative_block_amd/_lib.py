@@ -76,6 +76,7 @@ SIGNATURES = {
     "ssb_kv_rewind": (c_int, [c_void_p, c_int, ctypes.c_int32]),
     "ssb_kv_state": (c_int, [c_void_p, ctypes.POINTER(c_int), P_i32, ctypes.POINTER(c_int)]),
     "ssb_prefill": (c_int, [c_void_p, c_void_p, c_void_p, c_int, P_i32, c_void_p]),
+    "ssb_round_noalloc": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, P_i32, P_i32, P_i32, c_void_p]),
     "ssb_round": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, P_i32, P_i32, P_i32, c_void_p,
                           c_void_p, c_void_p]),
     "ssb_ar_step": (c_int, [c_void_p, c_void_p, P_i32, c_void_p, c_void_p]),

@@ -17,6 +17,7 @@
 #include <functional>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <tuple>
 #include <new>
 #include <string>
@@ -92,21 +93,10 @@ struct GemmShape {
   int NT, KSL, S;        // tiles per workgroup, K slices per tile, K ranges
 };
 
-struct ssb_model {
-  ssb_config c;
-  int device;
-  int elem;
-  // packed weights
-  void* wmem;
-  size_t wmem_bytes = 0, ws_bytes = 0;
-  const void* embed;
-  const float* final_norm;
-  std::vector<const float*> attn_norm, mlp_norm;
-  std::vector<GemmShape> qkv, o, gu, d;
-  GemmShape lm;
-  float2* rope;
-  // workspace
-  void* ws;
+// Device buffers a forward pass and its accept step read and write, sized for the model's largest
+// forward at init; ssb_round_noalloc lays out the same buffers for one window in the file-scope
+// scratch array instead, for the length of the call.
+struct Workspace {
   float* h;
   void* xg;
   float* ssq;
@@ -128,20 +118,38 @@ struct ssb_model {
   float *smax_d, *sz_d, *smax_v, *sz_v;   // their row max and exp-sum [max_rows]
   int32_t* dd_win;    // block tokens of the direct-diffusion request [kMaxReq][SSB_MAX_BLOCK + 1]
   int32_t* dd_rec;    // step records [kMaxReq][kDDRec]
-  float* apart;
+  float* apart;       // attention chunk records [max_decode_rows][n_heads][max_chunks][hd + 4]
   int max_chunks;
   int max_decode_rows;
+  int32_t* accept_dev;
+  int32_t* tok_dev;
+  ReqArgs* req_dev;   // device request state read by every kernel of a forward
+};
+
+struct ssb_model : Workspace {
+  ssb_config c;
+  int device;
+  int elem;
+  // packed weights
+  void* wmem;
+  size_t wmem_bytes = 0, ws_bytes = 0;
+  const void* embed;
+  const float* final_norm;
+  std::vector<const float*> attn_norm, mlp_norm;
+  std::vector<GemmShape> qkv, o, gu, d;
+  GemmShape lm;
+  float2* rope;
+  // workspace allocation (the Workspace pointers point into it)
+  void* ws;
   int max_batch;      // requests per batched call
   bool sampling;      // stochastic-round workspace allocated
-  int32_t* accept_dev;
+  bool no_graph = false;       // launches run eagerly (ssb_round_noalloc: instantiating a graph allocates)
   bool debug_poison = false;   // NaN-poison KV slots no correct read reaches (rounds run eagerly)
   // fused layer tail (O, gate|up, down in one launch) for decode forwards of <= 48 rows
   bool tail_ok = false;        // the model's shapes and the device allow it
   bool no_fused = false;       // debug: always run the three GEMM launches
   unsigned long long* tail_sync = nullptr;   // barrier counters and generation [kTailSyncWords]
   int* tail_err = nullptr;     // set by a layer-tail barrier that timed out
-  int32_t* tok_dev;
-  ReqArgs* req_dev;   // device request state read by every kernel of a forward
   ReqArgs* req_pin;   // pinned staging of the request state
   hipStream_t cap;    // private stream used only to capture graphs
   std::map<std::tuple<int, void*, int, int, uint32_t, int>, hipGraphExec_t> graphs;   // (kind, pool, R, B, T bits, slots)
@@ -302,6 +310,8 @@ void pack_all(ssb_model* m, const ssb_weights* w, hipStream_t st) {
   hip_check(launch_pack<T>(const_cast<uint4*>(m->lm.W), m->lm.n_tiles, H, 0, w->lm_head, nullptr, nullptr,
                            c.vocab, 0, 0, st), "pack lm_head");
 }
+
+void scratch_setup(int dev);   // the scratch array's device address (defined with the array)
 
 void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb_model** out) {
   check_config(cfg);
@@ -478,6 +488,7 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
       hipSuccess)
     fail(SSB_ENOMEM, "pinned host allocation failed");
   hip_check(hipStreamSynchronize(st), "init sync");
+  scratch_setup(m->device);
   *out = hold.release();
 }
 
@@ -725,6 +736,7 @@ ssb_kv* kv_new(ssb_pool* p, int max_tokens) {
   kv->max_pages = (max_tokens + kPage - 1) / kPage;
   kv->seq_len = 0;
   kv->x0 = -1;
+  kv->pages.reserve(kv->max_pages);   // page pushes on the round path never reallocate
   if (hipMalloc(reinterpret_cast<void**>(&kv->pt_dev), (size_t)kv->max_pages * 4) != hipSuccess)
     fail(SSB_ENOMEM, "page table allocation failed");
   if (hipHostMalloc(reinterpret_cast<void**>(&kv->pt_host), (size_t)kv->max_pages * 4, hipHostMallocDefault) !=
@@ -982,7 +994,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
     hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)R * kOutStride * 4, hipMemcpyDeviceToHost, s),
               "copy accept");
   };
-  if (dlog || vlog || prof_eager(m) || m->debug_poison) {
+  if (dlog || vlog || prof_eager(m) || m->debug_poison || m->no_graph) {
     body(st, false);
   } else {
     hipGraphExec_t ex = get_graph(m, smp ? 4 : 0, pool, R, B, slots, [&](hipStream_t s) { body(s, true); },
@@ -1463,6 +1475,87 @@ void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau,
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Allocation-free rounds (ssb_round_noalloc): the forward workspace of one window laid out in a
+// file-scope device array instead of the model's workspace.  Every GPU the library runs on holds
+// its own copy of the array until the process ends; calls on one GPU share it.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kScratchDevices] = {};   // device address of each device's scratch array
+
+// Once per device, with that device current (from ssb_init_model): the array's device address.
+void scratch_setup(int dev) {
+  if (dev < 0 || dev >= kScratchDevices) return;   // ssb_round_noalloc then reports SSB_ESTATE
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev]) return;
+  void* ptr = nullptr;
+  hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "scratch symbol address");
+  g_scratch[dev] = ptr;
+}
+
+// The workspace of one decode window of M rows (one request) whose attention reaches `chunks` key
+// chunks, laid out from base (null: sizes only).  Returns the bytes it spans.  Every buffer is
+// written before it is read within a round, so nothing needs clearing between calls.
+size_t scratch_layout(const ssb_model* m, int M, int chunks, char* base, Workspace* ws) {
+  const ssb_config& c = m->c;
+  const size_t H = c.hidden, qd = (size_t)c.n_heads * c.head_dim, hd = c.head_dim, E = m->elem;
+  const size_t n_groups = m->lm.n_tiles / m->lm.NT;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return base ? base + o : nullptr;
+  };
+  ws->h = reinterpret_cast<float*>(take(M * H * 4));
+  ws->xg = take(M * H * E);
+  ws->ssq = reinterpret_cast<float*>(take(H / 16 * M * 4));
+  ws->q = take(M * qd * E);
+  ws->attn = take(M * qd * E);
+  ws->act = take(M * (size_t)c.ffn * E);
+  int32_t* meta = reinterpret_cast<int32_t*>(take(5 * (size_t)M * 4));
+  ws->row_tok = meta;
+  ws->row_pos = meta ? meta + M : nullptr;
+  ws->row_lim = meta ? meta + 2 * M : nullptr;
+  ws->row_req = meta ? meta + 3 * M : nullptr;
+  ws->row_slot = meta ? meta + 4 * M : nullptr;
+  ws->row_cs = reinterpret_cast<float2*>(take(M * (hd / 2) * sizeof(float2)));
+  ws->pt_ld = chunks * (kKeyChunk / kPage);
+  ws->fwd_pt = reinterpret_cast<int32_t*>(take((size_t)ws->pt_ld * 4));   // one request
+  ws->part = reinterpret_cast<float*>(take(m->d[0].S > 1 ? (size_t)m->d[0].S * M * H * 4 : 0));
+  float* am = reinterpret_cast<float*>(take(3 * (size_t)M * 4));
+  ws->am_tok = reinterpret_cast<int32_t*>(am);
+  ws->am_top1 = am ? am + M : nullptr;
+  ws->am_top2 = am ? am + 2 * M : nullptr;
+  float* amp = reinterpret_cast<float*>(take(n_groups * M * 12));
+  ws->amv1 = amp;
+  ws->amv2 = amp ? amp + n_groups * M : nullptr;
+  ws->ami1 = amp ? reinterpret_cast<int32_t*>(amp + 2 * n_groups * M) : nullptr;
+  ws->ams = nullptr;        // softmax sums: direct diffusion and sampling only
+  ws->am_z = reinterpret_cast<float*>(take((size_t)M * 4));
+  ws->slog_d = ws->slog_v = nullptr;
+  float* sst = reinterpret_cast<float*>(take(4 * (size_t)M * 4));
+  ws->smax_d = sst;
+  ws->sz_d = sst ? sst + M : nullptr;
+  ws->smax_v = sst ? sst + 2 * M : nullptr;
+  ws->sz_v = sst ? sst + 3 * M : nullptr;
+  ws->dd_win = ws->dd_rec = nullptr;
+  ws->max_chunks = chunks;
+  ws->apart = reinterpret_cast<float*>(take((size_t)M * c.n_heads * chunks * (hd + 4) * 4));
+  ws->max_decode_rows = M;
+  ws->accept_dev = reinterpret_cast<int32_t*>(take((size_t)kOutStride * 4));
+  ws->tok_dev = reinterpret_cast<int32_t*>(take((size_t)M * 4));
+  ws->req_dev = reinterpret_cast<ReqArgs*>(take(sizeof(ReqArgs)));
+  return off;
+}
+}  // namespace
+
 // ===========================================================================
 // C ABI
 // ===========================================================================
@@ -1607,6 +1700,45 @@ int ssb_round(ssb_model* m, ssb_kv* kv, int B, int max_commit, const int32_t* pl
     int mc[1] = {max_commit};
     round_impl(m, kvs, 1, B, mc, planted_dev, nullptr, nullptr, nullptr, nullptr, draft_logits_dev,
                verify_logits_dev, &ro, S(stream));
+    if (committed) std::memcpy(committed, ro.tok, (size_t)ro.n * 4);
+    if (n_committed) *n_committed = ro.n;
+    if (accept_len) *accept_len = ro.A;
+  });
+}
+
+int ssb_round_noalloc(ssb_model* m, ssb_kv* kv, int B, int max_commit, const int32_t* planted_dev,
+                      int32_t* committed, int32_t* n_committed, int32_t* accept_len, void* stream) {
+  return guard([&] {
+    check_model_kv(m, kv);
+    if (B < 0 || B > m->c.block_B) fail(SSB_EINVAL, "B must be in [0, block_B]");
+    char* base = m->device >= 0 && m->device < kScratchDevices ? static_cast<char*>(g_scratch[m->device]) : nullptr;
+    if (!base) fail(SSB_ESTATE, "no scratch array address for this device");
+    const int M = B + 1;
+    const int chunks = (kv->seq_len + B + 2 - 1) / kKeyChunk + 1;   // keys of the verify window's last row
+    Workspace ws{};
+    const size_t need = scratch_layout(m, M, chunks, nullptr, &ws);
+    if (need > kScratchBytes)
+      fail(SSB_EINVAL, "ssb_round_noalloc: a window of " + std::to_string(M) + " rows over " +
+                           std::to_string(kv->seq_len + B + 2) + " positions needs " + std::to_string(need) +
+                           " bytes of scratch; the maximum is " + std::to_string(kScratchBytes));
+    scratch_layout(m, M, chunks, base, &ws);
+    // the model's workspace pointers name the scratch layout for this call only; launches run
+    // eagerly (a captured graph would hold the other layout, and instantiating one allocates)
+    struct Restore {
+      ssb_model* m;
+      Workspace w;
+      bool no_graph;
+      ~Restore() {
+        static_cast<Workspace&>(*m) = w;
+        m->no_graph = no_graph;
+      }
+    } restore{m, static_cast<const Workspace&>(*m), m->no_graph};
+    static_cast<Workspace&>(*m) = ws;
+    m->no_graph = true;
+    RoundOut ro{};
+    ssb_kv* kvs[1] = {kv};
+    int mc[1] = {max_commit};
+    round_impl(m, kvs, 1, B, mc, planted_dev, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, &ro, S(stream));
     if (committed) std::memcpy(committed, ro.tok, (size_t)ro.n * 4);
     if (n_committed) *n_committed = ro.n;
     if (accept_len) *accept_len = ro.A;

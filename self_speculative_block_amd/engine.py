@@ -204,6 +204,16 @@ class KV:
                                    byref(A), _ptr(dl), _ptr(vl), _stream()))
         return list(out[: n.value]), A.value, dl, vl
 
+    def round_noalloc(self, B, max_commit=None, planted_dev=None):
+        """ssb_round_noalloc: the same round with its workspace in the library's scratch array."""
+        max_commit = B + 2 if max_commit is None else max_commit
+        out = _i32(B + 2)
+        n = ctypes.c_int32()
+        A = ctypes.c_int32()
+        L.check(self.lib.ssb_round_noalloc(self.model.h, self.h, B, max_commit, _ptr(planted_dev), out, byref(n),
+                                           byref(A), _stream()))
+        return list(out[: n.value]), A.value
+
     def ar_step(self, want_logits=False):
         y = ctypes.c_int32()
         lg = None
