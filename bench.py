@@ -98,10 +98,7 @@ def traffic_from_profiles(kind):
     """HBM bytes per launch of `kind` from a committed rocprofv3 counter summary
     (profiles/*_traffic.txt), or None when there is none or the kernel source has
     changed since the counters were taken."""
-    import hashlib
-    src = os.path.join(ROOT, "self_speculative_block_amd", "csrc", "ssb_kernels.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = kernel_source_sha()
     pdir = os.path.join(ROOT, "profiles")
     for fn in sorted(os.listdir(pdir)) if os.path.isdir(pdir) else []:
         if not fn.endswith("_traffic.txt"):
@@ -124,30 +121,149 @@ KERNEL_LABELS = {   # (kernel template, EPI, KPW) of the GEMMs at the benchmark'
 }
 
 
-def summarize_trace(path):
-    """Group a rocprofv3 kernel trace (CSV) by kernel name and grid: the decode GEMMs of a round
-    (33 rows) and of an AR step (1 row) share a kernel and differ in their grid."""
-    import collections
-    import csv
+KERNEL_NAMES = {
+    "k_layer_tail": "fused layer tail: O + gate|up + down", "k_attn": "attention (64-key chunks)",
+    "k_attn_combine": "attention combine", "k_argmax": "vocabulary argmax merge",
+    "k_prep_embed": "row prep + embedding gather", "k_accept": "accept + commit",
+    "k_resid_reduce": "K-split residual reduce", "k_gemm_big": "large-tile GEMM",
+}
+
+
+def kernel_label(name, grid, prev=None):
+    """A readable label for a dispatch.  The fused layer tail has one grid for any row count, so its
+    launches are told apart by the grid of the attention combine that precedes them (one wave per
+    row and head: 33 rows x 16 heads x 64 lanes = 33792 in a B=32 round, 1024 in an AR step)."""
     import re
-    groups = collections.defaultdict(list)
+    m = re.search(r"ssb::(k_\w+)(<[^>]*>)?", name)
+    if not m:
+        return re.sub(r"^void ", "", name)
+    k = m.group(1)
+    if k == "k_gemm":
+        g = re.search(r"k_gemm<[^,]+, (\d+), (\d+), (\d+)", name)
+        if g:
+            return KERNEL_LABELS.get(("k_gemm", g.group(2), g.group(3)), name)
+    label = KERNEL_NAMES.get(k, k)
+    if k == "k_gemm_big":
+        label += m.group(2) or ""
+    if k == "k_layer_tail" and prev is not None and "k_attn_combine" in prev[0]:
+        label += f" (after combine {prev[1]})"
+    return label
+
+
+def _dispatches(path, value_cols=False):
+    """Rows of a rocprofv3 CSV (kernel trace or counter collection) as dispatches in launch order:
+    (order key, kernel name, grid, duration in us or None, {counter: value})."""
+    import csv
+    rows = {}
     with open(path) as f:
         for row in csv.DictReader(f):
-            name = row.get("Kernel_Name", "")
-            grid = tuple(row.get(f"Grid_Size_{a}", "") for a in "XYZ")
-            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
-            groups[(name, grid)].append(dur)
-    total = sum(sum(v) for v in groups.values())
-    out = [f"{'kernel':58s} {'grid':>16s} {'calls':>7s} {'avg us':>8s} {'min us':>8s} {'% time':>7s}"]
-    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        m = re.search(r"ssb::(k_\w+)<[^,]+, (\d+), (\d+), (\d+)", name)
-        label = name
-        if m and m.group(1) == "k_gemm":
-            label = KERNEL_LABELS.get(("k_gemm", m.group(3), m.group(4)), name)
-        label = re.sub(r"^void ", "", label)[:58]
-        out.append(f"{label:58s} {'x'.join(grid):>16s} {len(v):7d} {sum(v) / len(v):8.2f} {min(v):8.2f} "
-                   f"{100 * sum(v) / total:7.2f}")
+            did = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            if "Grid_Size_X" in row:
+                grid = "x".join(row.get(f"Grid_Size_{a}", "") for a in "XYZ")
+            else:
+                grid = row.get("Grid_Size", "")
+            d = rows.get(did)
+            if d is None:
+                dur = None
+                if row.get("Start_Timestamp") and row.get("End_Timestamp"):
+                    dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
+                start = int(row.get("Start_Timestamp") or 0)
+                d = rows[did] = [(start, int(did)), row.get("Kernel_Name", ""), grid, dur, {}]
+            if value_cols and row.get("Counter_Name"):
+                c = row["Counter_Name"]
+                d[4][c] = d[4].get(c, 0.0) + float(row["Counter_Value"])
+    return sorted(rows.values(), key=lambda d: d[0])
+
+
+def _grouped(path, value_cols=False):
+    import collections
+    groups = collections.defaultdict(list)
+    prev = None
+    for d in _dispatches(path, value_cols):
+        groups[(kernel_label(d[1], d[2], prev), d[2])].append(d)
+        prev = (d[1], d[2])
+    return groups
+
+
+def summarize_trace(path):
+    """Group a rocprofv3 kernel trace (CSV) by kernel and grid: the decode GEMMs of a round
+    (33 rows) and of an AR step (1 row) share a kernel and differ in their grid."""
+    groups = _grouped(path)
+    dur = {key: [d[3] for d in v] for key, v in groups.items()}
+    total = sum(sum(v) for v in dur.values())
+    out = [f"{'kernel':62s} {'grid':>16s} {'calls':>7s} {'avg us':>8s} {'med us':>8s} {'min us':>8s} {'% time':>7s}"]
+    for (label, grid), v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"{label[:62]:62s} {grid:>16s} {len(v):7d} {sum(v) / len(v):8.2f} "
+                   f"{statistics.median(v):8.2f} {min(v):8.2f} {100 * sum(v) / total:7.2f}")
     return "\n".join(out)
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """HBM bytes per dispatch from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by what the same counter reads for the calibration copy of
+    COPY_CALIB_BYTES (the largest-grid device-to-device copy of the run: it reads and writes that
+    many bytes).  Returns the text of the summary and {label: bytes per launch (median)}."""
+    out, med = [], {}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        groups = _grouped(path, value_cols=True)
+        copies = [(int(g.split("x")[0] or 0), v) for (lab, g), v in groups.items() if "copyBuffer" in lab]
+        if not copies:
+            raise SystemExit(f"{path}: no device-to-device copy to calibrate {counter} with")
+        gmax = max(c[0] for c in copies)
+        cal = statistics.median(d[4][counter] for c in copies if c[0] == gmax for d in c[1])
+        scale = (COPY_CALIB_BYTES / 1024) / cal
+        out.append(f"  calibration copy ({COPY_CALIB_BYTES >> 20} MiB read and written, grid {gmax}): "
+                   f"{counter} {cal:.1f} KiB -> scale {scale:.5f}")
+        for (label, grid), v in groups.items():
+            vals = [d[4].get(counter, 0.0) for d in v]
+            per.setdefault((label, grid), {})[counter] = (statistics.median(vals), scale, len(v))
+    out.append("")
+    out.append(f"  {'kernel':62s} {'grid':>16s} {'calls':>6s} {'FETCH KiB':>10s} {'WRITE KiB':>10s} {'-> MB':>9s}")
+    rows = []
+    for key, c in per.items():
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        f_kib, f_s, n = c["FETCH_SIZE"]
+        w_kib, w_s, _ = c["WRITE_SIZE"]
+        b = (f_kib * f_s + w_kib * w_s) * 1024
+        rows.append((b * n, key, n, f_kib, w_kib, b))
+    for _, (label, grid), n, f_kib, w_kib, b in sorted(rows, reverse=True):
+        if not label.startswith(("__amd", "at::")):
+            out.append(f"  {label[:62]:62s} {grid:>16s} {n:6d} {f_kib:10.1f} {w_kib:10.1f} {b / 1e6:9.3f}")
+        med[(label, grid)] = int(round(b))
+    return "\n".join(out), med
+
+
+KIND_LABELS = {"tail": "fused layer tail", "qkv": "QKV GEMM", "o": "O GEMM", "gate_up": "gate|up GEMM",
+               "down": "down GEMM", "lm_head": "LM head GEMM", "attention": "attention (",
+               "combine": "attention combine", "argmax": "vocabulary argmax"}
+
+
+def kernel_source_sha():
+    import hashlib
+    with open(os.path.join(ROOT, "self_speculative_block_amd", "csrc", "ssb_kernels.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_summary(fetch_csv, write_csv, kind=None):
+    """The text of a profiles/*_traffic.txt record (without its command lines): every kernel's
+    scaled HBM bytes per launch and, for ``kind``, the record that later bench lines read (the
+    group of that kind with the most launches: the round's own, not the AR continuation's)."""
+    text, med = summarize_counters(fetch_csv, write_csv)
+    if kind is None:
+        return text
+    from ssb_inputs import workload
+    wl = workload(2)
+    groups = _grouped(fetch_csv)
+    cands = [key for key in med if key[0].startswith(KIND_LABELS[kind])]
+    if not cands:
+        raise SystemExit(f"no dispatch of kind {kind} in the counter runs")
+    key = max(cands, key=lambda k: len(groups.get(k, ())))
+    ab = alg_bytes_kernel(kind, wl.model, wl.block + 1, wl.prefix_len + wl.block + 1)
+    return (text + f"\n\nkernel {key[0]}, grid {key[1]}: {med[key]} bytes per launch against {ab} "
+            f"algorithmic ({med[key] / ab:.3f}x)\nkernel_kind: {kind}\nsource_sha256: {kernel_source_sha()}\n"
+            f"traffic_bytes_per_launch: {med[key]}")
 
 
 class no_gc:
@@ -778,9 +894,17 @@ def main():
     ap.add_argument("--regions", type=int, default=0, help="text / table: number of regions (0 = all)")
     ap.add_argument("--summarize-trace", default=None,
                     help="print a rocprofv3 kernel trace (CSV) grouped by kernel and grid, then exit")
+    ap.add_argument("--summarize-counters", nargs=2, default=None, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print HBM traffic per dispatch from a FETCH_SIZE run and a WRITE_SIZE run of "
+                         "rocprofv3 --pmc (counter_collection CSVs), then exit; with --traffic-kind, "
+                         "also the lines that give that kernel kind's traffic to later bench lines")
+    ap.add_argument("--traffic-kind", default=None, help="kernel kind of --summarize-counters' record")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_counters:
+        print(traffic_summary(*args.summarize_counters, args.traffic_kind))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the round engine is a single-GPU path "
@@ -908,8 +1032,8 @@ def main():
     bytes_round = alg_bytes_round(cfg, P, B)
 
     # per-kernel timing of graph-replayed launches (as in the timed region): for each kernel kind
-    # the engine replays a round graph in which every launch of that kind stamps, on the device's
-    # real-time counter, its earliest workgroup start and its latest workgroup end
+    # the engine replays a round graph in which every launch stamps its latest workgroup end on the
+    # device's real-time counter; a launch of the kind counts from the end of the launch before it
     kinds = ["qkv", "attention", "combine", "o", "gate_up", "down", "reduce", "tail", "lm_head", "argmax"]
     breakdown = {}
     for kind in kinds:
@@ -985,8 +1109,8 @@ def main():
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles(dom), "alg_bytes_per_launch": ab,
                      "avg_launch_us": breakdown[dom]["avg_us"],
-                     "timing": "graph-replayed launches, device real-time stamps (first workgroup start to last "
-                               "workgroup end)"},
+                     "timing": "graph-replayed launches, device real-time stamps: from the end of the launch "
+                               "before to the last workgroup end (the dispatch interval of a kernel trace)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -388,10 +388,13 @@ int ssb_forward_tokens(ssb_model* m, ssb_kv* kv, const int32_t* tokens, int M, i
  * stream it is launched on. Rounds and AR steps then run without graph
  * replay. With SSB_PROFILE_IN_GRAPH or'ed into kind, greedy and stochastic
  * rounds (single and batched) and AR steps keep replaying launch graphs
- * instead: a separate graph per timed kind carries an event-record node
- * before and after each launch of that kind, so the times are those of
- * graph-replayed launches (the other calls run eagerly as above).
- * ssb_profile_read returns the summed event time and the launch
+ * instead: in a separate graph per timed kind every launch records the
+ * latest end of its workgroups on the device's real-time counter, and a
+ * launch of the timed kind counts from the end of the launch before it to
+ * its own end (back-to-back graph launches start when the previous one
+ * completes, so this is the interval a kernel trace reports for the
+ * dispatch); the other calls run eagerly as above.
+ * ssb_profile_read returns the summed time and the launch
  * count since the last reset; reset != 0 clears them.
  * kind: one of SSB_K_*, or -1 to stop timing. SSB_K_DOWN is the down
  * projection GEMM; SSB_K_REDUCE its K-split reduce (absent when the down

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssb_limits.h"
+
 namespace ssb {
 
 typedef uint16_t bf16_t;
@@ -21,12 +23,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kWave = 64;
 constexpr int kThreads = 256;      // 4 waves per workgroup
-constexpr int kKeyChunk = 64;      // fixed key chunk of attention (absolute positions)
-constexpr int kPage = 16;          // tokens per KV page
-constexpr int kMaxReq = 64;        // requests per batched launch
-constexpr int kMaxTasks = 64;      // attention row tasks per launch
-constexpr int kTaskRows = 48;      // rows per attention task (3 MFMA row tiles)
-constexpr int kMaxNormParts = 128; // per-16-column norm partials (hidden <= 2048)
 constexpr float kLog2e = 1.4426950408889634f;   // exp(x) = exp2(x * log2(e))
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -113,8 +109,9 @@ __device__ __forceinline__ void mma_wa(f32x4_t& acc, uint4 w, uint4 x, bf16_t) {
 __device__ __forceinline__ void mma_wa(f32x4_t& acc, uint4 w, uint4 x, float) { mma_aa(acc, w, x, float()); }
 
 // Kernel timing stamps of one launch (measurement only), on the device's real-time counter:
-// word 0 is the start of workgroup 0 (dispatched first), word 1 + w the end of workgroup w
-// (w < kStampWgs).  Plain stores to distinct words: atomics from hundreds of workgroups finishing
+// word 0 is the start of workgroup 0 (dispatched first), word 1 + w % kStampWgs the end of
+// workgroup w (grids of more workgroups share words; the last store of a word is close to the
+// latest end).  Plain stores to distinct words: atomics from hundreds of workgroups finishing
 // together would queue on one address and slow the very kernel being timed.  Slots are not reset
 // between launches: the host keeps the end words at or after the launch's own start.  A null
 // pointer disables the stamps.
@@ -133,7 +130,7 @@ __device__ __forceinline__ void stamp_end(ProfStamp* s) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int w = stamp_wg();
-  if (threadIdx.x == 0 && w < kStampWgs) s->t[1 + w] = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) s->t[1 + w % kStampWgs] = __builtin_amdgcn_s_memrealtime();
 }
 
 // Per-request launch arguments (passed by value).
@@ -186,6 +183,7 @@ struct PrepArgs {
   int32_t* fwd_pt; int pt_ld;     // page ids of this forward's requests [req][pt_ld] (0 past npg)
   float* h; void* xg; float* ssq; int ssq_ld;   // ssq: per-16-column sums of squares [M][ssq_ld]
   const ReqArgs* req;          // device request state
+  ProfStamp* stamp;            // nullable timing stamps of this launch
 };
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };
@@ -311,7 +309,8 @@ template <typename T>
 hipError_t launch_poison_kv(const ReqArgs* req, int R, const int32_t* acc, int acc_stride, int lo_abs, int hi_abs,
                             void* kv_pool, int n_layers, int n_pages, int n_kv, int hd, hipStream_t st);
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
-                         int32_t* out, int out_stride, hipStream_t st, const int* err = nullptr);
+                         int32_t* out, int out_stride, hipStream_t st, const int* err = nullptr,
+                         ProfStamp* stamp = nullptr);
 hipError_t launch_dd_init(const ReqArgs* ra, int n_req, int mask_id, int32_t* rec, int rec_stride, hipStream_t st);
 hipError_t launch_dd_select(const int32_t* am, const float* zs, const ReqArgs* ra, int n_req, int mask_id,
                             int vocab, int32_t* rec, int rec_stride, hipStream_t st);

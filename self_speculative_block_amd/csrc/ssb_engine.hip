@@ -25,6 +25,7 @@
 
 #include "../../include/ssb.h"
 #include "ssb_device.h"
+#include "ssb_host.h"
 
 
 using namespace ssb;
@@ -33,58 +34,33 @@ namespace {
 
 thread_local std::string g_err;
 
-struct Error {
-  int code;
-  std::string msg;
-};
-
-[[noreturn]] void fail(int code, const std::string& msg) { throw Error{code, msg}; }
-
 void hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) fail(SSB_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
 template <typename F>
 int guard(F&& f) {
-  try {
-    f();
-    return SSB_OK;
-  } catch (const Error& e) {
-    ssb::g_prof_ev[0] = ssb::g_prof_ev[1] = nullptr;   // a launch that failed inside the timing hook
-    g_err = e.msg;
-    return e.code;
-  } catch (const std::bad_alloc&) {
-    g_err = "host allocation failed";
-    return SSB_ENOMEM;
-  } catch (...) {
-    g_err = "unexpected internal error";
-    return SSB_EINVAL;
-  }
+  const int rc = run_guarded(f, &g_err);
+  if (rc != SSB_OK) ssb::g_prof_ev[0] = ssb::g_prof_ev[1] = nullptr;   // a launch that failed inside the timing hook
+  return rc;
 }
 
-bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
-
-constexpr int kOutStride = 4 + SSB_MAX_BLOCK + 2;  // accept record per request
 constexpr int kDDRec = 4 + 4 * SSB_MAX_BLOCK;      // direct-diffusion step record per request
 
 }  // namespace
 
-struct ssb_pool {
+// A pool: the caller's KV buffer and its free page ids.
+struct ssb_pool : PageStack {
   ssb_model* m;
   char* base;
-  int n_pages;
-  std::vector<int> free_pages;  // stack of free page ids
 };
 
-struct ssb_kv {
+// A sequence: its pages (logical page -> pool page), its committed state, and its page table on
+// the device with a pinned host mirror (max_pages entries each).
+struct ssb_kv : PageList, SeqState {
   ssb_pool* pool;
-  int max_tokens;
-  int max_pages;
-  std::vector<int32_t> pages;   // logical page -> pool page
-  int32_t* pt_dev;              // device page table [max_pages]
-  int32_t* pt_host;             // pinned mirror
-  int seq_len;
-  int32_t x0;
+  int32_t* pt_dev;
+  int32_t* pt_host;
 };
 
 struct GemmShape {
@@ -155,12 +131,14 @@ struct ssb_model : Workspace {
   std::map<std::tuple<int, void*, int, int, uint32_t, int>, hipGraphExec_t> graphs;   // (kind, pool, R, B, T bits, slots)
   // kernel timing hook
   int prof_kind = -1;
-  bool prof_graph = false;            // time launches of prof_kind inside graph replays (event nodes)
+  bool prof_graph = false;            // time launches of prof_kind inside graph replays (device stamps)
   bool capturing = false;             // a launch graph is being captured on m->cap
-  std::map<hipGraphExec_t, int> graph_prof_pairs;   // stamp slots written by each profiled graph
+  // kinds of the launches of each graph captured for timing, in launch order (one stamp slot each)
+  std::map<hipGraphExec_t, std::vector<int>> graph_prof_kinds;
   ProfStamp* prof_stamps = nullptr;   // device slots of graph-replayed launches [prof_slots]
   int prof_slots = 0;
   int prof_stamp_used = 0;            // slots the last replayed graph wrote
+  std::vector<int> prof_cap_kinds;    // kinds of the slots of the graph being captured / replayed
   double wallclock_mhz = 100.0;       // device real-time counter
   std::vector<hipEvent_t> prof_ev;    // pairs (start, end)
   int prof_used = 0;                  // pairs recorded since the last collect
@@ -175,28 +153,35 @@ namespace {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Kinds of launches that are never timed themselves but stamp their end in a timing graph (the
+// interval of the launch after them starts there).
+constexpr int kKindPrep = 100, kKindAccept = 101;
+
 // Kernel timing hook around each launch of the selected kind.  Eager launches carry a start /
-// stop event pair on the dispatch itself (hipExtLaunchKernel).  A graph captured for timing
-// gives each such launch a device stamp slot instead (earliest workgroup start, latest
-// workgroup end on the real-time counter; HIP cannot time events recorded by graph nodes).
+// stop event pair on the dispatch itself (hipExtLaunchKernel).  In a graph captured for timing
+// every launch gets a device stamp slot instead (latest workgroup end on the real-time counter;
+// HIP cannot time events recorded by graph nodes), and a launch of the selected kind is timed
+// from the end of the launch before it to its own end: back-to-back graph launches start when
+// the previous one completes, so this is the interval a kernel trace reports for the dispatch.
 ProfStamp* prof_begin(ssb_model* m, int kind, hipStream_t) {
-  if (m->prof_kind != kind) return nullptr;
   if (m->capturing) {
     if (!m->prof_graph) return nullptr;
     if (m->prof_stamp_used >= m->prof_slots) fail(SSB_EINVAL, "kernel timing: too many launches per graph");
+    m->prof_cap_kinds.push_back(kind);
     return m->prof_stamps + m->prof_stamp_used;
   }
+  if (m->prof_kind != kind) return nullptr;
   if (m->prof_used * 2 + 2 > (int)m->prof_ev.size()) fail(SSB_EINVAL, "kernel timing: too many launches per call");
   g_prof_ev[0] = m->prof_ev[2 * m->prof_used];
   g_prof_ev[1] = m->prof_ev[2 * m->prof_used + 1];
   return nullptr;
 }
 void prof_end(ssb_model* m, int kind, hipStream_t) {
-  if (m->prof_kind != kind) return;
   if (m->capturing) {
     if (m->prof_graph) ++m->prof_stamp_used;
     return;
   }
+  if (m->prof_kind != kind) return;
   g_prof_ev[0] = g_prof_ev[1] = nullptr;
   ++m->prof_used;
 }
@@ -215,13 +200,19 @@ void prof_collect(ssb_model* m) {
     const int n = m->prof_stamp_used;
     std::vector<ProfStamp> st(n);
     hip_check(hipMemcpy(st.data(), m->prof_stamps, n * sizeof(ProfStamp), hipMemcpyDeviceToHost), "read stamps");
-    for (const ProfStamp& x : st) {
-      // end words older than this launch's start belong to earlier launches of the slot
+    // latest workgroup end of a slot; end words older than the launch's start belong to earlier
+    // replays of the slot
+    auto end_of = [](const ProfStamp& x) {
       unsigned long long t1 = 0;
       for (int w = 1; w <= kStampWgs; ++w)
         if (x.t[w] >= x.t[0] && x.t[w] > t1) t1 = x.t[w];
-      if (t1 == 0) continue;   // every workgroup left at once
-      m->prof_us += (double)(t1 - x.t[0]) / m->wallclock_mhz;
+      return t1;
+    };
+    for (int i = 1; i < n && i < (int)m->prof_cap_kinds.size(); ++i) {
+      if (m->prof_cap_kinds[i] != m->prof_kind) continue;
+      const unsigned long long e0 = end_of(st[i - 1]), e1 = end_of(st[i]);
+      if (e0 == 0 || e1 <= e0) continue;
+      m->prof_us += (double)(e1 - e0) / m->wallclock_mhz;
       ++m->prof_launches;
     }
     m->prof_stamp_used = 0;
@@ -260,37 +251,6 @@ GemmShape plan_gemm(int K, int n_tiles, int elem, int epi) {
   const int kpw = ksteps / (g.S * g.KSL);
   if (kpw < kmin || g.S * g.KSL * kpw != ksteps) fail(SSB_EINVAL, "reduction length too small for the GEMM kernel");
   return g;
-}
-
-void check_config(const ssb_config* c) {
-  if (!c) fail(SSB_EINVAL, "null config");
-  auto req = [](bool ok, const char* m) { if (!ok) fail(SSB_EINVAL, m); };
-  req(c->dtype == SSB_BF16 || c->dtype == SSB_F32, "dtype must be SSB_BF16 or SSB_F32");
-  req(c->n_layers >= 1, "n_layers must be >= 1");
-  req(c->head_dim == 32 || c->head_dim == 64, "head_dim must be 32 or 64");
-  req(c->n_heads >= 1 && c->n_kv_heads >= 1 && c->n_heads % c->n_kv_heads == 0,
-      "n_heads must be a multiple of n_kv_heads");
-  req(c->n_heads / c->n_kv_heads == 1 || c->n_heads / c->n_kv_heads == 4, "n_heads/n_kv_heads must be 1 or 4");
-  req(c->hidden % 128 == 0 && pow2(c->hidden / 128), "hidden must be 128 * 2^k");
-  req((c->n_heads * c->head_dim) % 128 == 0 && pow2(c->n_heads * c->head_dim / 128),
-      "n_heads*head_dim must be 128 * 2^k");
-  req(c->ffn % 128 == 0 && pow2(c->ffn / 128), "ffn must be 128 * 2^k");
-  req(c->hidden <= 16 * kMaxNormParts, "hidden above 2048 is not supported");
-  req(c->hidden <= (c->dtype == SSB_BF16 ? 4096 : 2048) && c->n_heads * c->head_dim <= (c->dtype == SSB_BF16 ? 4096 : 2048),
-      "hidden and n_heads*head_dim above 4096 (bf16) / 2048 (f32) are not supported");
-  // the down projection (reduction length ffn) splits K over workgroups when one cannot hold it
-  req(c->ffn <= (c->dtype == SSB_BF16 ? 8192 : 4096), "ffn above 8192 (bf16) / 4096 (f32) is not supported");
-  req(c->vocab >= 2, "vocab must be >= 2");
-  req(c->mask_id >= 0 && c->mask_id < c->vocab, "mask_id out of range");
-  req(c->eos_id >= 0 && c->eos_id < c->vocab && c->eos_id != c->mask_id, "eos_id out of range or == mask_id");
-  req(c->block_B >= 0 && c->block_B <= SSB_MAX_BLOCK, "block_B must be in [0, 64]");
-  req(c->page_tokens == kPage, "page_tokens must be 16");
-  req(c->max_rows >= 1 && c->max_rows <= kMaxTasks * kTaskRows, "max_rows must be in [1, 3072]");
-  req(c->max_rows >= c->block_B + 1, "max_rows must hold one window (block_B + 1 rows)");
-  req(c->max_positions >= 2, "max_positions must be >= 2");
-  req(c->rms_eps >= 0.f && c->rope_theta > 0.f, "bad rms_eps or rope_theta");
-  req(c->max_batch >= 0 && c->max_batch <= SSB_MAX_BATCH, "max_batch must be in [0, SSB_MAX_BATCH]");
-  req((c->features & ~SSB_FEAT_SAMPLE) == 0, "unknown feature bits");
 }
 
 template <typename T>
@@ -526,7 +486,9 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   pa.row_slot = m->row_slot; pa.row_cs = m->row_cs; pa.rope = m->rope; pa.half = c.head_dim / 2;
   pa.fwd_pt = m->fwd_pt; pa.pt_ld = m->pt_ld;
   pa.h = m->h; pa.xg = m->xg; pa.ssq = m->ssq; pa.ssq_ld = H / 16; pa.req = m->req_dev;
+  pa.stamp = prof_begin(m, kKindPrep, st);
   hip_check(launch_prep<T>(pa, st), "prep");
+  prof_end(m, kKindPrep, st);
 
   GemmArgs g{};
   g.M = M;
@@ -699,44 +661,25 @@ void run_forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st)
 // ---------------------------------------------------------------------------
 // KV pages
 // ---------------------------------------------------------------------------
+// Pages for positions [0, n_tokens), new page ids uploaded to the device table (stream-ordered).
 void kv_ensure(ssb_kv* kv, int n_tokens, hipStream_t st) {
-  if (n_tokens > kv->max_tokens) fail(SSB_ENOKV, "sequence would exceed the kv's max_tokens");
-  const int need = (n_tokens + kPage - 1) / kPage;
-  const int first_new = (int)kv->pages.size();
-  if (need <= first_new) return;
-  ssb_pool* p = kv->pool;
-  if ((int)p->free_pages.size() < need - first_new) fail(SSB_ENOKV, "KV page pool exhausted");
-  for (int i = first_new; i < need; ++i) {
-    const int pg = p->free_pages.back();
-    p->free_pages.pop_back();
-    kv->pages.push_back(pg);
-    kv->pt_host[i] = pg;
-  }
-  hip_check(hipMemcpyAsync(kv->pt_dev + first_new, kv->pt_host + first_new, (size_t)(need - first_new) * 4,
-                           hipMemcpyHostToDevice, st), "page table upload");
+  const int first = kv->ensure(*kv->pool, n_tokens, kv->pt_host);
+  const int need = (int)kv->pages.size();
+  if (need > first)
+    hip_check(hipMemcpyAsync(kv->pt_dev + first, kv->pt_host + first, (size_t)(need - first) * 4,
+                             hipMemcpyHostToDevice, st), "page table upload");
 }
 
 // Return pages wholly at positions >= keep_tokens.
-void kv_trim(ssb_kv* kv, int keep_tokens) {
-  const int keep = (keep_tokens + kPage - 1) / kPage;
-  while ((int)kv->pages.size() > keep) {
-    kv->pool->free_pages.push_back(kv->pages.back());
-    kv->pages.pop_back();
-  }
-}
+void kv_trim(ssb_kv* kv, int keep_tokens) { kv->trim(*kv->pool, keep_tokens); }
 
 ssb_kv* kv_new(ssb_pool* p, int max_tokens) {
-  if (max_tokens < 2) fail(SSB_EINVAL, "max_tokens must be >= 2");
   if (max_tokens > p->m->c.max_positions) fail(SSB_EINVAL, "max_tokens exceeds max_positions");
   hip_check(hipSetDevice(p->m->device), "hipSetDevice");
   auto* kv = new ssb_kv();
   std::unique_ptr<ssb_kv> hold(kv);
   kv->pool = p;
-  kv->max_tokens = max_tokens;
-  kv->max_pages = (max_tokens + kPage - 1) / kPage;
-  kv->seq_len = 0;
-  kv->x0 = -1;
-  kv->pages.reserve(kv->max_pages);   // page pushes on the round path never reallocate
+  kv->init(max_tokens);
   if (hipMalloc(reinterpret_cast<void**>(&kv->pt_dev), (size_t)kv->max_pages * 4) != hipSuccess)
     fail(SSB_ENOMEM, "page table allocation failed");
   if (hipHostMalloc(reinterpret_cast<void**>(&kv->pt_host), (size_t)kv->max_pages * 4, hipHostMallocDefault) !=
@@ -791,15 +734,19 @@ hipGraphExec_t get_graph(ssb_model* m, int kind, ssb_pool* pool, int R, int B, i
                          const std::function<void(hipStream_t)>& body, float temperature = 0.f) {
   uint32_t tb = 0;
   std::memcpy(&tb, &temperature, 4);
-  // a graph that times one kernel kind (event nodes around its launches) is kept apart
+  // a graph that times one kernel kind (stamps in every launch) is kept apart
   const int pk = m->prof_graph ? m->prof_kind + 1 : 0;
   const auto key = std::make_tuple(kind * 64 + pk, static_cast<void*>(pool), R, B, tb, slots);
   auto it = m->graphs.find(key);
   if (it != m->graphs.end()) {
-    if (pk) m->prof_stamp_used = m->graph_prof_pairs[it->second];   // read back after the replay
+    if (pk) {   // read back after the replay
+      m->prof_cap_kinds = m->graph_prof_kinds[it->second];
+      m->prof_stamp_used = (int)m->prof_cap_kinds.size();
+    }
     return it->second;
   }
   m->prof_stamp_used = 0;
+  m->prof_cap_kinds.clear();
   m->capturing = true;
   hip_check(hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal), "begin capture");
   try {
@@ -820,7 +767,7 @@ hipGraphExec_t get_graph(ssb_model* m, int kind, ssb_pool* pool, int R, int B, i
   (void)hipGraphDestroy(g);
   hip_check(e, "graph instantiate");
   m->graphs[key] = ex;
-  if (pk) m->graph_prof_pairs[ex] = m->prof_stamp_used;   // slots written by each replay
+  if (pk) m->graph_prof_kinds[ex] = m->prof_cap_kinds;   // slots written by each replay
   else m->prof_stamp_used = 0;
   return ex;
 }
@@ -889,11 +836,6 @@ void prefill(ssb_model* m, ssb_kv* kv, const void* prefix, int P, int32_t* first
   kv->x0 = y1;
   if (first) *first = y1;
 }
-
-struct RoundOut {
-  int A, n, next_x0, eos;
-  int32_t tok[SSB_MAX_BLOCK + 2];
-};
 
 // Runs draft + verify + accept for R requests (row windows concatenated).
 // Debug: NaN into the KV slots [lo, p + B + 2) of every request of the launch (lo = p + 1 with no
@@ -986,9 +928,11 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
       aa.req = m->req_dev; aa.out = m->accept_dev; aa.out_stride = kOutStride; aa.err = m->tail_err;
       hip_check(launch_accept_sample(aa, R, s), "stochastic accept");
     } else {
+      ProfStamp* ast = prof_begin(m, kKindAccept, s);
       hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, R, c.eos_id, m->accept_dev, kOutStride, s,
-                              m->tail_err),
+                              m->tail_err, ast),
                 "accept");
+      prof_end(m, kKindAccept, s);
     }
     if (m->debug_poison) poison_kv(m, pool, R, m->accept_dev, s);   // the rolled-back slots
     hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)R * kOutStride * 4, hipMemcpyDeviceToHost, s),
@@ -1003,21 +947,7 @@ void round_impl(ssb_model* m, ssb_kv* const* kvs, int R, int B, const int* max_c
   }
   hip_check(hipStreamSynchronize(st), "round sync");
   prof_collect(m);
-  for (int r = 0; r < R; ++r) {
-    const int32_t* o = m->pin_i32 + (size_t)r * kOutStride;
-    RoundOut& ro = out[r];
-    ro.A = o[0];
-    ro.n = o[1];
-    ro.next_x0 = o[2];
-    ro.eos = o[3];
-    if (ro.A < 0 || ro.A > B || ro.n < 1 || ro.n > B + 2 || ro.next_x0 < 0 || ro.next_x0 >= c.vocab)
-      fail(SSB_EHIP, "round produced an invalid accept record (NaN logits?)");
-    for (int k = 0; k < ro.n; ++k) ro.tok[k] = o[4 + k];
-    ssb_kv* kv = kvs[r];
-    kv->seq_len = ra.p[r] + ro.A + 2;
-    kv->x0 = ro.next_x0;
-    kv_trim(kv, kv->seq_len + B + 2);
-  }
+  commit_batch(kvs, R, *pool, ra.p, m->pin_i32, B, c.vocab, c.mask_id, out);
 }
 
 void ar_step(ssb_model* m, ssb_kv* kv, int32_t* token, float* logits, hipStream_t st,
@@ -1445,8 +1375,10 @@ void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau,
     f.graph = graph;
     f.logits = vlog;
     run_forward(m, pool, f, s);
+    ProfStamp* ast = prof_begin(m, kKindAccept, s);
     hip_check(launch_accept(m->row_tok, m->am_tok, m->req_dev, 1, c.eos_id, m->accept_dev, kOutStride, s,
-                            m->tail_err), "accept");
+                            m->tail_err, ast), "accept");
+    prof_end(m, kKindAccept, s);
     hip_check(hipMemcpyAsync(m->pin_i32, m->accept_dev, (size_t)kOutStride * 4, hipMemcpyDeviceToHost, s),
               "copy accept");
   };
@@ -1459,17 +1391,8 @@ void round_multistep_impl(ssb_model* m, ssb_kv* kv, int B, int steps, float tau,
   }
   hip_check(hipStreamSynchronize(st), "verify sync");
   prof_collect(m);
-  const int32_t* o = m->pin_i32;
-  out->A = o[0];
-  out->n = o[1];
-  out->next_x0 = o[2];
-  out->eos = o[3];
-  if (out->A < 0 || out->A > B || out->n < 1 || out->n > B + 2 || out->next_x0 < 0 || out->next_x0 >= c.vocab)
-    fail(SSB_EHIP, "round produced an invalid accept record (NaN logits?)");
-  for (int i = 0; i < out->n; ++i) out->tok[i] = o[4 + i];
-  kv->seq_len = p + out->A + 2;
-  kv->x0 = out->next_x0;
-  kv_trim(kv, kv->seq_len + B + 2);
+  read_accept(m->pin_i32, B, c.vocab, c.mask_id, out);
+  commit_round(*kv, *kv, *kv->pool, p, *out, B);
 }
 
 
@@ -1612,12 +1535,11 @@ int ssb_pool_init(ssb_model* m, void* dev_buf, size_t bytes, int n_pages, ssb_po
     if (bytes < need) fail(SSB_EINVAL, "pool buffer smaller than ssb_pool_bytes");
     if (reinterpret_cast<uintptr_t>(dev_buf) % 256) fail(SSB_EINVAL, "pool buffer must be 256-byte aligned");
     auto* p = new ssb_pool();
+    std::unique_ptr<ssb_pool> hold(p);
     p->m = m;
     p->base = static_cast<char*>(dev_buf);
-    p->n_pages = n_pages;
-    p->free_pages.reserve(n_pages);
-    for (int i = n_pages - 1; i >= 0; --i) p->free_pages.push_back(i);
-    *out = p;
+    p->init(n_pages);
+    *out = hold.release();
   });
 }
 
@@ -1630,7 +1552,7 @@ void ssb_pool_free(ssb_pool* p) {
   (void)hipDeviceSynchronize();
   for (auto it = m->graphs.begin(); it != m->graphs.end();) {
     if (std::get<1>(it->first) == static_cast<void*>(p)) {
-      m->graph_prof_pairs.erase(it->second);
+      m->graph_prof_kinds.erase(it->second);
       (void)hipGraphExecDestroy(it->second);
       it = m->graphs.erase(it);
     } else {
@@ -1643,7 +1565,7 @@ void ssb_pool_free(ssb_pool* p) {
 int ssb_pool_free_pages(const ssb_pool* p, int* n_free) {
   return guard([&] {
     if (!p || !n_free) fail(SSB_EINVAL, "null argument");
-    *n_free = (int)p->free_pages.size();
+    *n_free = p->n_free();
   });
 }
 
@@ -1668,9 +1590,7 @@ int ssb_kv_reset(ssb_kv* kv) {
 int ssb_kv_rewind(ssb_kv* kv, int n, int32_t x0) {
   return guard([&] {
     if (!kv) fail(SSB_EINVAL, "null kv");
-    if (kv->x0 < 0) fail(SSB_ESTATE, "rewind needs a prefilled kv");
-    if (n < 1 || n > kv->seq_len) fail(SSB_EINVAL, "n must be in [1, current length]");
-    if (x0 < 0 || x0 >= kv->pool->m->c.vocab || x0 == kv->pool->m->c.mask_id) fail(SSB_EINVAL, "bad boundary token");
+    check_rewind(*kv, n, x0, kv->pool->m->c.vocab, kv->pool->m->c.mask_id);
     kv->seq_len = n;
     kv->x0 = x0;
     kv_trim(kv, n + kv->pool->m->c.block_B + 2);
@@ -1867,7 +1787,7 @@ int ssb_set_debug(ssb_model* m, int flags) {
       hip_check(hipDeviceSynchronize(), "sync before dropping graphs");
       for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
       m->graphs.clear();
-      m->graph_prof_pairs.clear();
+      m->graph_prof_kinds.clear();
       m->no_fused = no_fused;
     }
   });
@@ -2143,7 +2063,7 @@ int ssb_profile_kernel(ssb_model* m, int kind) {
       for (auto& e : m->prof_ev) hip_check(hipEventCreate(&e), "event create");
     }
     if (in_graph && !m->prof_stamps) {
-      m->prof_slots = 8 * (m->c.n_layers + 2);
+      m->prof_slots = 32 * (m->c.n_layers + 2);   // every launch of a graph has a slot
       hip_check(hipMalloc(reinterpret_cast<void**>(&m->prof_stamps), m->prof_slots * sizeof(ProfStamp)),
                 "stamp slots");
       hip_check(hipMemset(m->prof_stamps, 0, m->prof_slots * sizeof(ProfStamp)), "clear stamps");

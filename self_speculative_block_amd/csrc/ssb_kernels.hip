@@ -133,6 +133,7 @@ __device__ __forceinline__ void window_row(const PrepArgs& a, int m, int& tok, i
 template <typename T>
 __global__ __launch_bounds__(64) void k_prep_embed(PrepArgs a) {
   const int m = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  stamp_begin(a.stamp);
   int tok, pos, lim, req;
   window_row(a, m, tok, pos, lim, req);
   if (g == 0 && t == 0) {
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(64) void k_prep_embed(PrepArgs a) {
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
   if (t % 16 == 0) a.ssq[(size_t)m * a.ssq_ld + col / 16] = s;
+  stamp_end(a.stamp);
 }
 
 struct Top2 { float v1; int i1; float v2; };
@@ -1695,7 +1697,9 @@ __global__ __launch_bounds__(kWave) void k_attn_combine(const float* part, int m
 // Output per request: [A, n_committed, next_x0, eos_seen, committed...].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* rap,
-                                               int eos_id, int32_t* out, int out_stride, const int* err) {
+                                               int eos_id, int32_t* out, int out_stride, const int* err,
+                                               ProfStamp* stamp) {
+  stamp_begin(stamp);
   const ReqArgs& ra = *rap;
   const int r = blockIdx.x, j = threadIdx.x;
   const int B = ra.B, row0 = ra.row0[r];
@@ -1724,6 +1728,7 @@ __global__ __launch_bounds__(64) void k_accept(const int32_t* row_tok, const int
     o[2] = am[row0 + A];
     o[3] = (eos_at < ncand && eos_at < n) ? 1 : 0;
   }
+  stamp_end(stamp);
 }
 
 // ---------------------------------------------------------------------------
@@ -2264,8 +2269,8 @@ template hipError_t launch_poison_kv<float>(const ReqArgs*, int, const int32_t*,
                                             int, hipStream_t);
 
 hipError_t launch_accept(const int32_t* row_tok, const int32_t* am, const ReqArgs* ra, int n_req, int eos_id,
-                         int32_t* out, int out_stride, hipStream_t st, const int* err) {
-  SSB_LAUNCH(k_accept, dim3(n_req), dim3(64), 0, st, row_tok, am, ra, eos_id, out, out_stride, err);
+                         int32_t* out, int out_stride, hipStream_t st, const int* err, ProfStamp* stamp) {
+  SSB_LAUNCH(k_accept, dim3(n_req), dim3(64), 0, st, row_tok, am, ra, eos_id, out, out_stride, err, stamp);
   return hipGetLastError();
 }
 

@@ -113,7 +113,8 @@ class Model:
 
     def profile_kernel(self, kind, in_graph=False):
         """Start timing every launch of one kernel kind (name in KERNEL_KINDS), or stop (None).
-        in_graph: rounds keep replaying launch graphs, with event nodes around the timed launches."""
+        in_graph: rounds keep replaying launch graphs; a timed launch counts from the end of the launch
+        before it to its own end (device real-time stamps)."""
         code = -1 if kind is None else L.KERNEL_KINDS[kind] | (L.SSB_PROFILE_IN_GRAPH if in_graph else 0)
         L.check(self.lib.ssb_profile_kernel(self.h, code))
 
