@@ -133,6 +133,16 @@ __device__ __forceinline__ void stamp_end(ProfStamp* s) {
   if (threadIdx.x == 0) s->t[1 + w % kStampWgs] = __builtin_amdgcn_s_memrealtime();
 }
 
+// Element offset of one K or V value in the paged KV pool [layer][page][K|V][kv head][block].  A K
+// block is token-major ([16 tokens][hd]: a key row is contiguous, the operand layout of S = K q);
+// a V block is dim-major ([hd][16 tokens]: consecutive tokens of one dimension are contiguous, the
+// operand layout of V^T in the P V product, so it loads without a transpose).
+__host__ __device__ __forceinline__ size_t kv_off(int layer, int n_pages, int page, int kv, int n_kv, int head,
+                                                  int tok, int dim, int hd) {
+  const size_t base = (((size_t)layer * n_pages + page) * 2 + kv) * n_kv + head;
+  return base * kPage * hd + (kv == 0 ? (size_t)tok * hd + dim : (size_t)dim * kPage + tok);
+}
+
 // Per-request launch arguments (passed by value).
 struct ReqArgs {
   int n;                              // requests in this launch

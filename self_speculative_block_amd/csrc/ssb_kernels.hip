@@ -540,16 +540,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
         const float o2 = x2 * cs.x + x1 * cs.y;
         x1 = o1; x2 = o2;
       }
-      T* dst;
       if (kind == 0) {
-        dst = reinterpret_cast<T*>(a.q) + (size_t)m * a.q_ld + head * hd;
+        T* dst = reinterpret_cast<T*>(a.q) + (size_t)m * a.q_ld + head * hd;
+        dst[i] = Act<T>::from_f(x1);
+        dst[i + half] = Act<T>::from_f(x2);
       } else {
         const int sl = s_slot[r];
-        const size_t base = (((size_t)a.layer * a.n_pages + sl / kPage) * 2 + (kind - 1)) * a.n_kv + head;
-        dst = reinterpret_cast<T*>(a.kv_pool) + (base * kPage + sl % kPage) * hd;
+        T* pool = reinterpret_cast<T*>(a.kv_pool);
+        pool[kv_off(a.layer, a.n_pages, sl / kPage, kind - 1, a.n_kv, head, sl % kPage, i, hd)] = Act<T>::from_f(x1);
+        pool[kv_off(a.layer, a.n_pages, sl / kPage, kind - 1, a.n_kv, head, sl % kPage, i + half, hd)] =
+            Act<T>::from_f(x2);
       }
-      dst[i] = Act<T>::from_f(x1);
-      dst[i + half] = Act<T>::from_f(x2);
     }
   } else if constexpr (EPI == EPI_RESID) {
     resid_epilogue<T, MB>(a, ctile, reinterpret_cast<const float*>(smem + L.pre), tg, NT, m_base, m_end);
@@ -1215,13 +1216,16 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zo[i] = __shfl_xor(z[i], 32);   // the rotary partner column (c +- 8)
         {
+          // q row, or the K/V block of the row's slot (dim d at dst[d * dstr])
           bf16_t* dst;
+          int dstr = 1;
           if (kind == 0) {
             dst = reinterpret_cast<bf16_t*>(a.q) + (size_t)mc * a.q_ld + head * hd;
           } else {
             const int sl = slr[r];
-            const size_t base = (((size_t)a.layer * a.n_pages + sl / kPage) * 2 + (kind - 1)) * a.n_kv + head;
-            dst = reinterpret_cast<bf16_t*>(a.kv_pool) + (base * kPage + sl % kPage) * hd;
+            dst = reinterpret_cast<bf16_t*>(a.kv_pool) +
+                  kv_off(a.layer, a.n_pages, sl / kPage, kind - 1, a.n_kv, head, sl % kPage, 0, hd);
+            if (kind == 2) dstr = kPage;
           }
           const float csv[8] = {csr[r][0].x, csr[r][0].y, csr[r][0].z, csr[r][0].w,
                                 csr[r][1].x, csr[r][1].y, csr[r][1].z, csr[r][1].w};
@@ -1234,7 +1238,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
               const float cx = csv[2 * i], cy = csv[2 * i + 1];
               o = q < 2 ? z[i] * cx - zo[i] * cy : z[i] * cx + zo[i] * cy;
             }
-            if (ok) dst[dim] = f2h(o);
+            if (ok) dst[dim * dstr] = f2h(o);
           }
         }
       } else if constexpr (EPI == EPI_SWIGLU) {
@@ -1415,6 +1419,7 @@ __device__ __forceinline__ float fold_val(float v, float al, float vc, float be)
 
 template <typename T, int HD>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
+#pragma clang fp contract(off)
   constexpr int NTH = kAttnThreads;
   constexpr int KS = Ty<T>::kStepK;
   constexpr int PER = Ty<T>::kPerFrag;
@@ -1423,11 +1428,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   constexpr int KT = kKeyChunk / 16;       // key tiles per chunk
   constexpr int PVS = kKeyChunk / KS;      // steps of P V over keys
   constexpr int KSTR = HD * (int)sizeof(T) + 16;              // K rows [key][d]
-  constexpr int VSTR = kKeyChunk * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);   // V^T rows [d][key]
+  constexpr int VSTR = kKeyChunk * (int)sizeof(T) + 16;      // V^T rows [d][key] (16-byte aligned)
   constexpr int TILES = kTaskRows / 16;    // 16-row tiles per task
   constexpr int REC = HD + 4;
   constexpr int FPK = HD / PER;            // 16-byte fragments per key row
   constexpr int NKF = 2 * kKeyChunk * FPK; // K and V fragments of one chunk
+  // Fragment f < kKeyChunk * FPK is K: key f / FPK, dims (f % FPK) * PER.. (token-major blocks).
+  // The rest are V, read from dim-major page blocks in memory order: page pc of the chunk,
+  // dim d, tokens g * PER.. (PER consecutive keys of one dim: a V^T row piece).
+  constexpr int GPP = kPage / PER;         // V fragments per (page, dim)
+  auto frag_key = [](int f) {
+    const int rem = f % (kKeyChunk * FPK);
+    return f < kKeyChunk * FPK ? rem / FPK : rem / (HD * GPP) * kPage + rem % GPP * PER;
+  };
   constexpr int KVF = NKF / NTH;
   static_assert(NKF % NTH == 0, "every thread loads the same number of K/V fragments");
   __shared__ __align__(16) unsigned char ks[kKeyChunk * KSTR];
@@ -1455,7 +1468,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 #pragma unroll
   for (int q = 0; q < KVF; ++q) {
     const int f = (int)threadIdx.x + q * NTH;
-    pg[q] = pt[(cbeg * kKeyChunk + (f % (kKeyChunk * FPK)) / FPK) / kPage];
+    pg[q] = pt[(cbeg * kKeyChunk + frag_key(f)) / kPage];
   }
   // Branch-free as well (clamped to the task's last row and the last head): rows past the task
   // and idle waves read real data that never reaches a written result (rows stay independent in
@@ -1484,7 +1497,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int q = 0; q < KVF; ++q) {
         const int f = (int)threadIdx.x + q * NTH;
-        pg[q] = pt[(c * kKeyChunk + (f % (kKeyChunk * FPK)) / FPK) / kPage];
+        pg[q] = pt[(c * kKeyChunk + frag_key(f)) / kPage];
       }
     }
     uint4 kvv[KVF];
@@ -1498,9 +1511,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
       const int f = threadIdx.x + q * NTH;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
-      const size_t base = (((size_t)a.layer * a.n_pages + pg[q]) * 2 + kv) * a.n_kv + g;
+      const int key = frag_key(f) % kPage, dim = kv == 0 ? (rem % FPK) * PER : rem % (HD * GPP) / GPP;
       kvv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kv_pool) +
-                                               (base * kPage + rem / FPK % kPage) * HD + (rem % FPK) * PER);
+                                               kv_off(a.layer, a.n_pages, pg[q], kv, a.n_kv, g, key, dim, HD));
     }
     // (the row limits are stored once the K/V loads are in flight)
     if (threadIdx.x < 16) s_lim[threadIdx.x] = lim_row < task.nrows ? lim_ld : -1;
@@ -1509,14 +1522,25 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
       const int f = threadIdx.x + q * NTH;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
-      const int kk = rem / FPK, d0 = (rem % FPK) * PER;
-      if (c * kKeyChunk + kk > maxlim) kvv[q] = make_uint4(0, 0, 0, 0);
+      const int kk = frag_key(f);
       if (kv == 0) {
-        *reinterpret_cast<uint4*>(ks + kk * KSTR + d0 * (int)sizeof(T)) = kvv[q];
+        if (c * kKeyChunk + kk > maxlim) kvv[q] = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(ks + kk * KSTR + (rem % FPK) * PER * (int)sizeof(T)) = kvv[q];
       } else {
-        const T* vals = reinterpret_cast<const T*>(&kvv[q]);
+        // zero the values of keys past the limit (PER keys per fragment)
+        const int nv = maxlim - (c * kKeyChunk + kk) + 1;
+        uint32_t* wv = reinterpret_cast<uint32_t*>(&kvv[q]);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) *reinterpret_cast<T*>(vts + (d0 + i) * VSTR + kk * (int)sizeof(T)) = vals[i];
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (sizeof(T) == 2) {
+            if (2 * i >= nv) wv[i] = 0;
+            else if (2 * i + 1 >= nv) wv[i] &= 0xffffu;
+          } else {
+            if (i >= nv) wv[i] = 0;
+          }
+        }
+        const int d = rem % (HD * GPP) / GPP;
+        *reinterpret_cast<uint4*>(vts + d * VSTR + kk * (int)sizeof(T)) = kvv[q];
       }
     }
     __syncthreads();
@@ -1755,8 +1779,7 @@ __global__ __launch_bounds__(256) void k_poison_kv(const ReqArgs* rap, const int
     const int s = lo + e / per, rem = e % per;
     const int kv = rem / (n_kv * hd), h = (rem / hd) % n_kv, d = rem % hd;
     const int pg = ra.pt[r][s / kPage];
-    const size_t base = (((size_t)layer * n_pages + pg) * 2 + kv) * n_kv + h;
-    pool[(base * kPage + s % kPage) * hd + d] = Act<T>::from_f(NAN);
+    pool[kv_off(layer, n_pages, pg, kv, n_kv, h, s % kPage, d, hd)] = Act<T>::from_f(NAN);
   }
 }
 
