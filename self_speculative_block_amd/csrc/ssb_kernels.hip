@@ -1417,8 +1417,9 @@ __device__ __forceinline__ float fold_val(float v, float al, float vc, float be)
   return __fadd_rn(__fmul_rn(v, al), __fmul_rn(vc, be));
 }
 
+// fp16 K/V: at most 128 VGPRs, so four workgroups share a CU (long contexts launch several per CU)
 template <typename T, int HD>
-__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 4 : 1) void k_attn(AttnArgs a) {
 #pragma clang fp contract(off)
   constexpr int NTH = kAttnThreads;
   constexpr int KS = Ty<T>::kStepK;
