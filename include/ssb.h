@@ -126,7 +126,10 @@ int ssb_check_config(const ssb_config* cfg);
 
 /* Builds a model on the current device. Packs the weights and allocates
  * the engine's fixed workspace; nothing on the round path allocates
- * afterwards. *out is owned by the caller; release it with ssb_free_model. */
+ * afterwards. *out is owned by the caller; release it with ssb_free_model.
+ * A bf16 model's packed copy holds the weights as fp16 (the matrix cores'
+ * operand type for its fp16 activations; exact for magnitudes in
+ * [2^-17, 65504]): SSB_EINVAL if a weight's magnitude exceeds 65504. */
 int ssb_init_model(const ssb_config* cfg, const ssb_weights* w, void* stream, ssb_model** out);
 void ssb_free_model(ssb_model* m);
 

@@ -104,8 +104,9 @@ __device__ __forceinline__ void mma_aa(f32x4_t& acc, uint4 a, uint4 b, float) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
-// mma_wa: A is a weight fragment (bf16, widened to fp16 here), B an activation fragment.
-__device__ __forceinline__ void mma_wa(f32x4_t& acc, uint4 w, uint4 x, bf16_t) { mma_aa(acc, bf8_to_h8(w), x, bf16_t()); }
+// mma_wa: A is a packed weight fragment (fp16 for a bf16 model: converted once when packed), B an
+// activation fragment.
+__device__ __forceinline__ void mma_wa(f32x4_t& acc, uint4 w, uint4 x, bf16_t) { mma_aa(acc, w, x, bf16_t()); }
 __device__ __forceinline__ void mma_wa(f32x4_t& acc, uint4 w, uint4 x, float) { mma_aa(acc, w, x, float()); }
 
 // Kernel timing stamps of one launch (measurement only), on the device's real-time counter:
@@ -295,8 +296,9 @@ extern hipEvent_t g_prof_ev[2];
 
 // Launchers (defined in ssb_kernels.hip).
 template <typename T>
+// bf16 weights are packed as fp16 (*range_err set to 1 if a value exceeds fp16's range)
 hipError_t launch_pack(uint4* dst, int n_tiles, int K, int mode, const void* s0, const void* s1, const void* s2,
-                       int n0, int n1, int hd, hipStream_t st);
+                       int n0, int n1, int hd, int* range_err, hipStream_t st);
 template <typename T> hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
 template <typename T> hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
 template <typename T> hipError_t launch_resid_reduce(const GemmArgs& a, hipStream_t st);

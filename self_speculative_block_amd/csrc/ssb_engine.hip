@@ -257,18 +257,28 @@ template <typename T>
 void pack_all(ssb_model* m, const ssb_weights* w, hipStream_t st) {
   const ssb_config& c = m->c;
   const int H = c.hidden, F = c.ffn, qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  // bf16 weights go into the packed copy as fp16: one flag word reports a value beyond fp16's range
+  int* range_err = nullptr;
+  if (hipMalloc(reinterpret_cast<void**>(&range_err), sizeof(int)) != hipSuccess)
+    fail(SSB_ENOMEM, "allocation of the packing flag failed");
+  std::unique_ptr<int, void (*)(int*)> hold(range_err, [](int* p) { (void)hipFree(p); });
+  hip_check(hipMemsetAsync(range_err, 0, sizeof(int), st), "clear packing flag");
   for (int l = 0; l < c.n_layers; ++l) {
     hip_check(launch_pack<T>(const_cast<uint4*>(m->qkv[l].W), (qd + 2 * kvd) / 16, H, 1, w->wq[l], w->wk[l],
-                             w->wv[l], qd, kvd, c.head_dim, st), "pack qkv");
-    hip_check(launch_pack<T>(const_cast<uint4*>(m->o[l].W), H / 16, qd, 0, w->wo[l], nullptr, nullptr, H, 0, 0, st),
-              "pack o");
+                             w->wv[l], qd, kvd, c.head_dim, range_err, st), "pack qkv");
+    hip_check(launch_pack<T>(const_cast<uint4*>(m->o[l].W), H / 16, qd, 0, w->wo[l], nullptr, nullptr, H, 0, 0,
+                             range_err, st), "pack o");
     hip_check(launch_pack<T>(const_cast<uint4*>(m->gu[l].W), 2 * F / 16, H, 2, w->wg[l], w->wu[l], nullptr, 0, 0, 0,
-                             st), "pack gate/up");
-    hip_check(launch_pack<T>(const_cast<uint4*>(m->d[l].W), H / 16, F, 0, w->wd[l], nullptr, nullptr, H, 0, 0, st),
-              "pack down");
+                             range_err, st), "pack gate/up");
+    hip_check(launch_pack<T>(const_cast<uint4*>(m->d[l].W), H / 16, F, 0, w->wd[l], nullptr, nullptr, H, 0, 0,
+                             range_err, st), "pack down");
   }
   hip_check(launch_pack<T>(const_cast<uint4*>(m->lm.W), m->lm.n_tiles, H, 0, w->lm_head, nullptr, nullptr,
-                           c.vocab, 0, 0, st), "pack lm_head");
+                           c.vocab, 0, 0, range_err, st), "pack lm_head");
+  int bad = 0;
+  hip_check(hipMemcpyAsync(&bad, range_err, sizeof(int), hipMemcpyDeviceToHost, st), "read packing flag");
+  hip_check(hipStreamSynchronize(st), "packing");
+  if (bad) fail(SSB_EINVAL, "a bf16 weight exceeds the fp16 range (|w| > 65504) of the packed copy");
 }
 
 void scratch_setup(int dev);   // the scratch array's device address (defined with the array)

@@ -44,7 +44,7 @@ hipEvent_t g_prof_ev[2] = {nullptr, nullptr};
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void k_pack(uint4* dst, int n_tiles, int K, int mode, const T* src0, const T* src1,
-                       const T* src2, int n0, int n1, int hd) {
+                       const T* src2, int n0, int n1, int hd, int* range_err) {
   constexpr int KS = Ty<T>::kStepK;
   constexpr int PER = Ty<T>::kPerFrag;
   const int ksteps = K / KS;
@@ -76,6 +76,17 @@ __global__ void k_pack(uint4* dst, int n_tiles, int K, int mode, const T* src0, 
     }
     uint4 v = make_uint4(0, 0, 0, 0);
     if (src) v = *reinterpret_cast<const uint4*>(src + (size_t)srow * K + k);
+    if constexpr (sizeof(T) == 2) {
+      // bf16 weights are stored as fp16, the matrix cores' operand type for fp16 activations (RNE;
+      // exact for magnitudes in [2^-17, 65504]); a value beyond fp16's range is reported
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      bool big = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        big |= fabsf(__uint_as_float(wv[i] << 16)) > 65504.f || fabsf(__uint_as_float(wv[i] & 0xffff0000u)) > 65504.f;
+      if (big) *range_err = 1;
+      v = bf8_to_h8(v);
+    }
     dst[f] = v;
   }
 }
@@ -2046,15 +2057,15 @@ __global__ __launch_bounds__(kThreads) void k_accept_sample(AcceptSampleArgs a) 
 // ---------------------------------------------------------------------------
 template <typename T>
 hipError_t launch_pack(uint4* dst, int n_tiles, int K, int mode, const void* s0, const void* s1,
-                       const void* s2, int n0, int n1, int hd, hipStream_t st) {
+                       const void* s2, int n0, int n1, int hd, int* range_err, hipStream_t st) {
   hipLaunchKernelGGL(k_pack<T>, dim3(1024), dim3(256), 0, st, dst, n_tiles, K, mode,
-                     (const T*)s0, (const T*)s1, (const T*)s2, n0, n1, hd);
+                     (const T*)s0, (const T*)s1, (const T*)s2, n0, n1, hd, range_err);
   return hipGetLastError();
 }
 template hipError_t launch_pack<bf16_t>(uint4*, int, int, int, const void*, const void*, const void*, int,
-                                        int, int, hipStream_t);
+                                        int, int, int*, hipStream_t);
 template hipError_t launch_pack<float>(uint4*, int, int, int, const void*, const void*, const void*, int,
-                                       int, int, hipStream_t);
+                                       int, int, int*, hipStream_t);
 
 template <typename T>
 hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
