@@ -731,6 +731,7 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
   constexpr int KS = Ty<T>::kStepK, PER = Ty<T>::kPerFrag, NTH = kGemmThreads;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float s_inv[48];
+  __shared__ uint32_t s_act[2 * 48 * 4];   // SwiGLU outputs, packed pairs [tile][row][pair]
   __shared__ int s_flag[2];
   __shared__ unsigned long long s_gen;
   stamp_begin(ta.stamp);
@@ -901,13 +902,22 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
       for (int i = 0; i < 4; ++i) dst[i] = v[i];
     }
     __syncthreads();
-    for (int e = lane; wave == kStoreWave && e < 2 * MB * 8; e += kWave) {
-      const int t = e / (MB * 8), r = (e / 8) % MB, c = e % 8;
-      if (r >= M) continue;
+    // SwiGLU of every (tile, row, column pair) by all waves into LDS, as packed pairs of outputs;
+    // the store wave then writes them coherently (the exponentials and divisions would take it
+    // about a microsecond alone)
+    for (int e = threadIdx.x; e < 2 * MB * 4; e += kTailThreads) {
+      const int t = e / (MB * 4), r = (e / 4) % MB, c = 2 * (e % 4);
       const float* ct = ctile + (t * MB + r) * 17;
-      const float g = ct[c] * s_inv[r];
-      const float u = ct[c + 8] * s_inv[r];
-      st_coh(reinterpret_cast<T*>(ag.act) + (size_t)r * ag.act_ld + (w * 2 + t) * 8 + c, Act<T>::from_f(silu_f(g) * u));
+      const float g0 = ct[c] * s_inv[r], u0 = ct[c + 8] * s_inv[r];
+      const float g1 = ct[c + 1] * s_inv[r], u1 = ct[c + 9] * s_inv[r];
+      s_act[e] = (uint32_t)Act<T>::from_f(silu_f(g0) * u0) | ((uint32_t)Act<T>::from_f(silu_f(g1) * u1) << 16);
+    }
+    __syncthreads();
+    for (int e = lane; wave == kStoreWave && e < 2 * MB * 4; e += kWave) {
+      const int t = e / (MB * 4), r = (e / 4) % MB;
+      if (r >= M) continue;
+      st_coh(reinterpret_cast<uint32_t*>(reinterpret_cast<T*>(ag.act) + (size_t)r * ag.act_ld + (w * 2 + t) * 8) + e % 4,
+             s_act[e]);
     }
   }
   if (!tail_barrier(ta.sync, 1, gen, ta.err, s_flag, &last)) return;
@@ -2345,7 +2355,7 @@ hipError_t launch_layer_tail(const TailArgs& a, hipStream_t st) {
                   a.gu.n_ssq / 4 <= 64 && ((a.gu.n_ssq / 4) & (a.gu.n_ssq / 4 - 1)) == 0 && a.sync && a.err;
   if (!ok) return hipErrorInvalidValue;
   const int shm = layer_tail_lds(a.gu.n_ssq);
-  if (shm > kGemmMaxLds) return hipErrorInvalidValue;
+  if (shm + 2048 > 160 * 1024) return hipErrorInvalidValue;   // the kernel's static arrays take < 2 KiB
   SSB_LAUNCH((k_layer_tail<4, 8, 16>), dim3(kTailWgs), dim3(kTailThreads), shm, st, a);
   return hipGetLastError();
 }
