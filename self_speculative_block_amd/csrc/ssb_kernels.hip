@@ -689,6 +689,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
 // second barrier advances the generation.  Waits are bounded: past kSpinMax polls a workgroup sets
 // *err and leaves (results are then invalid, and the argmax and accept kernels report it).
 // ---------------------------------------------------------------------------
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 constexpr int kTailParts = 8;
 constexpr int kSpinMax = 1 << 16;
 constexpr int kStoreWave = kGemmThreads / kWave;        // the ninth wave
@@ -732,6 +733,7 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float s_inv[48];
   __shared__ uint32_t s_act[2 * 48 * 4];   // SwiGLU outputs, packed pairs [tile][row][pair]
+  __shared__ __align__(16) float s_v[256];  // O stage: residual sums [16 rows][16 columns]
   __shared__ int s_flag[2];
   __shared__ unsigned long long s_gen;
   stamp_begin(ta.stamp);
@@ -803,24 +805,45 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
       for (int i = 0; i < 4; ++i) dst[i] = v[i];
     }
     __syncthreads();
+    // k_gemm's residual epilogue (v = h + tile, xg = v * gain, each row's 16 squares in order),
+    // computed by all waves into LDS; the store wave then writes h as 16-byte pieces, xg as packed
+    // pairs and the row sums, coherently
+    uint32_t* s_x = s_act;                                  // [16 rows][8 pairs]
+    float* s_q = reinterpret_cast<float*>(s_act + 128);     // [16 rows]
+    if (threadIdx.x < 256) s_v[threadIdx.x] = s_h[threadIdx.x] + ctile[(threadIdx.x / 16) * 17 + threadIdx.x % 16];
+    __syncthreads();
+    if (threadIdx.x < 128) {
+      const int r = threadIdx.x / 8, c = 2 * (threadIdx.x % 8);
+      s_x[threadIdx.x] = (uint32_t)Act<T>::from_f(s_v[r * 16 + c] * s_h[256 + c]) |
+                         ((uint32_t)Act<T>::from_f(s_v[r * 16 + c + 1] * s_h[256 + c + 1]) << 16);
+    } else if (threadIdx.x < 144) {
+      const int r = threadIdx.x - 128;
+      float sum = 0.f;
+      for (int n = 0; n < 16; ++n) {
+        const float v = s_v[r * 16 + n];
+        sum += v * v;
+      }
+      s_q[r] = sum;
+    }
+    __syncthreads();
     if (wave == kStoreWave) {
-      // k_gemm's residual epilogue: v = h + tile, xg = v * gain, each row's 16 squares in order
-      for (int e = lane; e < 256; e += kWave) {
-        const int r = e / 16, n = e % 16, m = mbase_o + r;
-        if (m >= mend_o) continue;
-        const float v = s_h[e] + ctile[r * 17 + n];
-        const int col = to * 16 + n;
-        st_coh(ao.h + (size_t)m * ao.hidden + col, v);
-        st_coh(reinterpret_cast<T*>(ao.xg_out) + (size_t)m * ao.hidden + col, Act<T>::from_f(v * s_h[256 + n]));
+      const int nr = mend_o - mbase_o;
+      const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(ao.h, (short)0, M * ao.hidden * 4, kBufWord3);
+      {
+        const int r = lane / 4, q = lane % 4;
+        if (r < nr)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4v, *reinterpret_cast<const float4*>(s_v + r * 16 + 4 * q)), hr,
+              ((mbase_o + r) * ao.hidden + to * 16 + 4 * q) * 4, 0, kCoh);
       }
-      if (lane < 16 && mbase_o + lane < mend_o) {
-        float sum = 0.f;
-        for (int n = 0; n < 16; ++n) {
-          const float v = s_h[lane * 16 + n] + ctile[lane * 17 + n];
-          sum += v * v;
-        }
-        st_coh(ao.ssq_out + (size_t)(mbase_o + lane) * ao.ssq_ld + to, sum);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = lane + k * kWave, r = e / 8;
+        if (r < nr)
+          st_coh(reinterpret_cast<uint32_t*>(reinterpret_cast<T*>(ao.xg_out) + (size_t)(mbase_o + r) * ao.hidden +
+                                             to * 16) + e % 8, s_x[e]);
       }
+      if (lane < nr) st_coh(ao.ssq_out + (size_t)(mbase_o + lane) * ao.ssq_ld + to, s_q[lane]);
     }
   }
   if (!tail_barrier(ta.sync, 0, gen, ta.err, s_flag, &last)) return;
@@ -2355,7 +2378,7 @@ hipError_t launch_layer_tail(const TailArgs& a, hipStream_t st) {
                   a.gu.n_ssq / 4 <= 64 && ((a.gu.n_ssq / 4) & (a.gu.n_ssq / 4 - 1)) == 0 && a.sync && a.err;
   if (!ok) return hipErrorInvalidValue;
   const int shm = layer_tail_lds(a.gu.n_ssq);
-  if (shm + 2048 > 160 * 1024) return hipErrorInvalidValue;   // the kernel's static arrays take < 2 KiB
+  if (shm + 4096 > 160 * 1024) return hipErrorInvalidValue;   // the kernel's static arrays take < 4 KiB
   SSB_LAUNCH((k_layer_tail<4, 8, 16>), dim3(kTailWgs), dim3(kTailThreads), shm, st, a);
   return hipGetLastError();
 }
