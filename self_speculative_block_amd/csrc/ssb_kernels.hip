@@ -486,15 +486,34 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (cwave) {
+    if constexpr (DIRECT) {
 #pragma unroll
-    for (int s = 0; s < KPW; ++s) {
-      const int kb = ((ksl * KPW + s) * KS + PER * (lane / 16)) * (int)sizeof(T);
+      for (int s = 0; s < KPW; ++s)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        uint4 b;
-        if constexpr (DIRECT) b = bx[s][mt];
-        else b = *reinterpret_cast<const uint4*>(slab + (mt * 16 + lane % 16) * XSTR + kb);
-        mma_wa(acc[mt], wf[s], b, T());
+        for (int mt = 0; mt < MT; ++mt) mma_wa(acc[mt], wf[s], bx[s][mt], T());
+    } else {
+      // activation fragments of step s + 1 are read from LDS while step s multiplies (a read
+      // awaited right before each product would expose the LDS latency on every step)
+      auto bfrag = [&](int s, int mt) {
+        const int kb = ((ksl * KPW + s) * KS + PER * (lane / 16)) * (int)sizeof(T);
+        return *reinterpret_cast<const uint4*>(slab + (mt * 16 + lane % 16) * XSTR + kb);
+      };
+      uint4 bc[MT], bn[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) bc[mt] = bfrag(0, mt);
+#pragma unroll
+      for (int s = 0; s < KPW; ++s) {
+        if (s + 1 < KPW) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) bn[mt] = bfrag(s + 1, mt);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of this step's products
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) mma_wa(acc[mt], wf[s], bc[mt], T());
+        if (s + 1 < KPW) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) bc[mt] = bn[mt];
+        }
       }
     }
   }
