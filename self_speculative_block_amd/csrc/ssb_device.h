@@ -282,7 +282,7 @@ struct AttnArgs {
 // Fused layer tail (O, gate|up, down) of decode forwards of at most 48 rows: one launch of
 // kTailWgs workgroups, one per CU, with two grid barriers (see k_layer_tail).
 constexpr int kTailWgs = 256;
-constexpr int kTailSyncWords = 16 * 35;   // generation word, 2 barriers x (global + 8 partitions + 8 release flags), 128 B apart
+constexpr int kTailSyncWords = 16 * 33;   // generation word, 2 barriers x (8 partition counters + 8 done flags), 128 B apart
 struct TailArgs {
   GemmArgs o, gu, d;                 // the three GEMMs as k_gemm runs them
   unsigned long long* sync;          // [kTailSyncWords] barrier counters, zero at model creation

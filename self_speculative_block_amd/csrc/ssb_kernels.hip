@@ -702,14 +702,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
 // store that crosses a barrier and loads nothing, so it alone waits for its stores before the
 // workgroup arrives, and the other waves keep their weight loads in flight across the barriers.
 //
-// Barriers: arrivals count on 8 partition counters (workgroup w in partition w % 8) whose last
-// arrival bumps a global counter; the arrival that completes the global count writes one release
-// flag per partition, and every other workgroup polls its partition's flag.  No word is both
-// polled and the target of arrivals: 256 pollers on the word the atomics land on delay the atomics
-// (polling the global counter itself measured 1778 against 1740 us per round at n = 1280; polling
-// all 8 partition counters without the global one, 1888).  Counters and flags grow monotonically,
-// a launch reading the generation word at entry and waiting for (generation + 1); the last
-// workgroup through the second barrier advances the generation.  Waits are bounded: past kSpinMax
+// Barriers: arrivals count on 8 partition counters (workgroup w in partition w % 8); the arrival
+// that completes a partition writes that partition's done flag, and every workgroup polls the 8
+// done flags (one lane each).  No polled word is the target of an atomic: 256 pollers on the word
+// that arrivals add to delay the adds.  (Measured per round at n = 1280: partition leaders adding
+// to a global counter that everyone polls, 1778 us; the same with the completing arrival writing
+// release flags, 1743 us; everyone polling the 8 partition counters themselves, 1888 us; done
+// flags, 1715 us.)  Counters and flags grow monotonically: a launch reads the generation word at
+// entry and waits for (generation + 1); workgroup 0 advances the generation once it has passed the
+// second barrier, by which time every workgroup has read it.  Waits are bounded: past kSpinMax
 // polls a workgroup sets *err and leaves (results are then invalid, and the argmax and accept
 // kernels report it).
 // ---------------------------------------------------------------------------
@@ -719,44 +720,37 @@ constexpr int kSpinMax = 1 << 16;
 constexpr int kStoreWave = kGemmThreads / kWave;        // the ninth wave
 constexpr int kTailThreads = kGemmThreads + kWave;
 
-// Arrival and polling are the store wave's: it holds no load that could delay its atomics (a
-// wave's memory operations complete in issue order, and the other waves have weight loads in
-// flight), and no other wave has a store in flight.  Returns whether every workgroup arrived;
-// *last tells the workgroup whose arrival completed the barrier.
+// Arrival and polling are the store wave's: it holds no load that could delay its atomic (a wave's
+// memory operations complete in issue order, and the other waves have weight loads in flight), and
+// no other wave has a store in flight.  Returns whether every workgroup arrived.
 __device__ __forceinline__ bool tail_barrier(unsigned long long* sync, int b, unsigned long long gen, int* err,
-                                             int* s_flag, bool* last) {
+                                             int* s_flag) {
   if ((int)threadIdx.x / kWave == kStoreWave) {
     const int lane = threadIdx.x % kWave;
     __builtin_amdgcn_s_waitcnt(0);   // this workgroup's coherent stores have completed
     const int p = blockIdx.x % kTailParts;
     const unsigned long long per = kTailWgs / kTailParts;
-    unsigned long long* gc = sync + 16 * (1 + 9 * b);
-    unsigned long long* pc = sync + 16 * (2 + 9 * b + p);
-    unsigned long long* rel = sync + 16 * (19 + 8 * b);   // release flags of this barrier, one per partition
-    int lst = 0;
+    unsigned long long* pc = sync + 16 * (1 + 16 * b + p);       // partition counters of barrier b
+    unsigned long long* done = sync + 16 * (9 + 16 * b);          // its done flags, one per partition
     if (lane == 0) {
       const unsigned long long old = __hip_atomic_fetch_add(pc, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old + 1 == (gen + 1) * per) {
-        const unsigned long long g = __hip_atomic_fetch_add(gc, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lst = g + 1 == (gen + 1) * kTailParts;
-      }
+      if (old + 1 == (gen + 1) * per) st_coh(done + 16 * p, gen + 1);
     }
-    lst = __builtin_amdgcn_readfirstlane(lst);
+    // lanes 0-7 each wait for one partition; a lane whose partition is done stops loading
+    bool ok = lane >= kTailParts;
     int spins = 0;
-    if (lst) {
-      if (lane < kTailParts) st_coh(rel + 16 * lane, gen + 1);
-    } else if (lane == 0) {
-      while (ld_coh(rel + 16 * p) < gen + 1 && ++spins < kSpinMax) __builtin_amdgcn_s_sleep(1);
+    for (;;) {
+      if (!ok) ok = ld_coh(done + 16 * (lane % kTailParts)) >= gen + 1;
+      if (__all(ok) || ++spins >= kSpinMax) break;
+      __builtin_amdgcn_s_sleep(1);
     }
     if (lane == 0) {
-      const bool ok = spins < kSpinMax;
-      if (!ok) st_coh(err, 1);
-      s_flag[0] = ok;
-      s_flag[1] = lst;
+      const bool passed = spins < kSpinMax;
+      if (!passed) st_coh(err, 1);
+      s_flag[0] = passed;
     }
   }
   __syncthreads();
-  *last = s_flag[1] != 0;
   return s_flag[0] != 0;
 }
 
@@ -769,7 +763,7 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
   __shared__ float s_inv[48];
   __shared__ uint32_t s_act[2 * 48 * 4];   // SwiGLU outputs, packed pairs [tile][row][pair]
   __shared__ __align__(16) float s_v[256];  // O stage: residual sums [16 rows][16 columns]
-  __shared__ int s_flag[2];
+  __shared__ int s_flag[1];
   __shared__ unsigned long long s_gen;
   stamp_begin(ta.stamp);
   const GemmArgs& ao = ta.o;
@@ -814,7 +808,6 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
   }
   __syncthreads();
   const unsigned long long gen = s_gen;
-  bool last = false;
 
   // ---- stage 1: O + residual (h, xg, norm partials written coherently by the store wave) ----
   if (has_o) {
@@ -881,7 +874,7 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
       if (lane < nr) st_coh(ao.ssq_out + (size_t)(mbase_o + lane) * ao.ssq_ld + to, s_q[lane]);
     }
   }
-  if (!tail_barrier(ta.sync, 0, gen, ta.err, s_flag, &last)) return;
+  if (!tail_barrier(ta.sync, 0, gen, ta.err, s_flag)) return;
 
   // ---- stage 2: gate|up + SwiGLU over all rows (one 48-row block; SwiGLU output coherent) ----
   {
@@ -978,7 +971,7 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
              s_act[e]);
     }
   }
-  if (!tail_barrier(ta.sync, 1, gen, ta.err, s_flag, &last)) return;
+  if (!tail_barrier(ta.sync, 1, gen, ta.err, s_flag)) return;
 
   // ---- stage 3: down + residual (16-row blocks; its outputs feed the next kernel) ----
   if (has_d) {
@@ -1035,9 +1028,9 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
     __syncthreads();
     resid_epilogue<T, 16, false>(ad, ctile, s_h, td, 1, m_base, m_end);
   }
-  // every workgroup has read the generation word and passed both barriers: the next launch may go
-  if (last && (int)threadIdx.x == kStoreWave * kWave)
-    __hip_atomic_fetch_add(ta.sync, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // every workgroup has read the generation word (each arrived at the second barrier after reading
+  // it): the next launch may use the next one
+  if (w == 0 && (int)threadIdx.x == kStoreWave * kWave) st_coh(ta.sync, gen + 1);
   stamp_end(ta.stamp);
 }
 
