@@ -696,9 +696,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
 // down: one 16-column tile, 8 K slices; gate|up: 2 tiles, 4 K slices; slice partial tiles added
 // in slice order, the same 1/rms butterfly and epilogues, no contraction), so rows stay
 // bit-identical to the unfused kernels whatever kernel computes them.  Waves 0-7 own the K slices
-// as in k_gemm.  A wave's memory operations complete in issue order, so every load is placed by
-// what it must not wait behind: the gate|up weights go out right after the O stage's own loads,
-// the down weights once the gate|up activations are in.  A ninth wave (kStoreWave) makes every
+// as in k_gemm.  A wave's memory operations complete in issue order, and issuing a load can stall
+// the wave while the CU's memory queue is full, so every load is placed by what it must not delay:
+// the gate|up weights go out once the O stage's products are done, the down weights once the
+// gate|up activations are in.  A ninth wave (kStoreWave) makes every
 // store that crosses a barrier and loads nothing, so it alone waits for its stores before the
 // workgroup arrives, and the other waves keep their weight loads in flight across the barriers.
 //
@@ -785,6 +786,16 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
   const int td = w % ad.n_tiles, mb_d = w / ad.n_tiles;
   uint4 wo[KPW_O], bxo[KPW_O], wgf[KPW_G], wdf[KPW_D];
   float pho = 0.f, pgo = 0.f;
+  // The gate|up weights go out once the O stage's own operands are in (workgroups without an O item:
+  // at entry).  Issuing a load can stall the wave until the CU's memory queue takes it, so 64 KB of
+  // gate|up weights issued at entry held back the O products behind them (round 1710 -> 1688 us
+  // with them issued after the products); they still land well before the first barrier ends.
+  auto issue_gu = [&]() {
+    asm volatile("" ::: "memory");
+    const uint4* gp = ag.W + ((size_t)(w * 2 + wave / 4) * (ag.K / KS) + (wave % 4) * KPW_G) * kWave + lane;
+#pragma unroll
+    for (int s = 0; s < KPW_G; ++s) wgf[s] = gp[(size_t)s * kWave];
+  };
   if (cw) {
     if (has_o) {
       const uint4* wp = ao.W + ((size_t)to * (ao.K / KS) + wave * KPW_O) * kWave + lane;
@@ -801,10 +812,7 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
       pho = ao.h[(size_t)min(mbase_o + r, m_last) * ao.hidden + to * 16 + n];
       pgo = ao.gain_next[to * 16 + min((int)threadIdx.x, 15)];
     }
-    asm volatile("" ::: "memory");   // the gate|up weights go out after the O stage's loads
-    const uint4* gp = ag.W + ((size_t)(w * 2 + wave / 4) * (ag.K / KS) + (wave % 4) * KPW_G) * kWave + lane;
-#pragma unroll
-    for (int s = 0; s < KPW_G; ++s) wgf[s] = gp[(size_t)s * kWave];
+    if (!has_o) issue_gu();
   }
   __syncthreads();
   const unsigned long long gen = s_gen;
@@ -822,6 +830,7 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
 #pragma unroll
       for (int s = 0; s < KPW_O; ++s) mma_wa(acc, wo[s], bxo[s], T());
       red[wave * kWave + lane] = acc;
+      issue_gu();
     }
     __syncthreads();
     if (threadIdx.x < kWave) {
