@@ -182,6 +182,15 @@ __device__ __forceinline__ Top2 merge_top2(Top2 a, Top2 b) {
   else { r.v1 = a.v1; r.i1 = a.i1; r.v2 = fmaxf(a.v2, b.v1); }
   return r;
 }
+// The record of another lane of the same 8-lane group, moved by DPP (CTRL: quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1] or row_half_mirror); merging with it three times, in that order, leaves the
+// merge of all 8 lanes in every lane (merge_top2 is associative and commutative).
+template <int CTRL>
+__device__ __forceinline__ Top2 dpp_top2(Top2 x) {
+  return Top2{__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x.v1), CTRL, 0xF, 0xF, false)),
+              __builtin_amdgcn_update_dpp(0, x.i1, CTRL, 0xF, 0xF, false),
+              __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x.v2), CTRL, 0xF, 0xF, false))};
+}
 
 // ---------------------------------------------------------------------------
 // GEMM with fused epilogues:  out[m][n] = sum_k X[m][k] W[n][k].
@@ -543,8 +552,21 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
     f32x4_t v = red[((t * KSL) * MT + mt) * kWave + l];
     for (int j = 1; j < KSL; ++j) v = v + red[((t * KSL + j) * MT + mt) * kWave + l];
     float* dst = ctile + (t * MB + mt * 16 + l % 16) * 17 + 4 * (l / 16);
+    if constexpr (EPI == EPI_LOGITS) {
+      // the logits z = product * 1/rms of the row, scaled here rather than in a pass of their own
+      const int r = mt * 16 + l % 16, m = m_base + r;
+      const float inv = s_inv[r];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = v[i];
+      for (int i = 0; i < 4; ++i) {
+        const float z = v[i] * inv;
+        dst[i] = z;
+        const int col = (tg * NT + t) * 16 + 4 * (l / 16) + i;
+        if (a.logits && m < m_end && col < a.vocab) a.logits[(size_t)m * a.vocab + col] = z;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = v[i];
+    }
   }
   __syncthreads();
 
@@ -602,42 +624,39 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       const float u = ct[c + 8] * s_inv[r];
       reinterpret_cast<T*>(a.act)[(size_t)m * a.act_ld + (tg * NT + t) * 8 + c] = Act<T>::from_f(silu_f(g) * u);
     }
-  } else {  // EPI_LOGITS
-    for (int e = threadIdx.x; e < NT * MB * 16; e += NTH) {
-      const int t = e / (MB * 16), r = (e / 16) % MB, n = e % 16;
-      const int m = m_base + r;
-      float* ct = ctile + (t * MB + r) * 17;
-      const float z = ct[n] * s_inv[r];
-      ct[n] = z;
-      const int col = (tg * NT + t) * 16 + n;
-      if (a.logits && m < m_end && col < a.vocab) a.logits[(size_t)m * a.vocab + col] = z;
-    }
-    __syncthreads();
-    // one (top1, id, top2) record per row over the workgroup's NT*16 columns:
-    // 8 lanes per row scan 2*NT columns each, then merge across the 8 lanes
-    const int groups = NTH / 8, cpl = 2 * NT;
+  } else {  // EPI_LOGITS (the reduction above left the scaled logits z in ctile)
+    // one (top1, id, top2) record per row over the workgroup's NT*16 columns: 8 lanes per row
+    // scan 2*NT columns each in column order (all reads first, then a branch-free scan), then
+    // merge across the 8 lanes by DPP moves
+    constexpr int kMaxCpl = 8;                        // 2 * NT columns per lane, NT <= 4
+    const int cpl = 2 * NT;
+    const int groups = NTH / 8;
     const int n_it = (MB + groups - 1) / groups;
     for (int it = 0; it < n_it; ++it) {
       const int r = it * groups + threadIdx.x / 8, sub = threadIdx.x % 8;
+      const int rr = min(r, MB - 1);
+      float zv[kMaxCpl];
+#pragma unroll
+      for (int k = 0; k < kMaxCpl; ++k) {
+        const int cc = sub * cpl + min(k, cpl - 1);   // column within the workgroup's span
+        zv[k] = ctile[((cc / 16) * MB + rr) * 17 + cc % 16];
+      }
       Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
       bool nan = false;
-      if (r < MB) {
-        for (int k = 0; k < cpl; ++k) {
-          const int cc = sub * cpl + k;               // column within the workgroup's span
-          const int col = tg * NT * 16 + cc;
-          if (col >= a.vocab || col == a.mask_id) continue;
-          const float z = ctile[((cc / 16) * MB + r) * 17 + cc % 16];
-          if (z != z) { nan = true; continue; }
-          if (z > best.v1) { best.v2 = best.v1; best.v1 = z; best.i1 = col; }
+#pragma unroll
+      for (int k = 0; k < kMaxCpl; ++k) {
+        const int col = tg * NT * 16 + sub * cpl + k;
+        const float z = zv[k];
+        if (k < cpl && r < MB && col < a.vocab && col != a.mask_id) {
+          if (z != z) nan = true;
+          else if (z > best.v1) { best.v2 = best.v1; best.v1 = z; best.i1 = col; }
           else if (z > best.v2) { best.v2 = z; }
         }
       }
       if (nan) best = Top2{NAN, -1, NAN};
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        const Top2 other{__shfl_xor(best.v1, o), __shfl_xor(best.i1, o), __shfl_xor(best.v2, o)};
-        best = merge_top2(best, other);
-      }
+      best = merge_top2(best, dpp_top2<0xB1>(best));    // quad_perm [1,0,3,2]
+      best = merge_top2(best, dpp_top2<0x4E>(best));    // quad_perm [2,3,0,1]
+      best = merge_top2(best, dpp_top2<0x141>(best));   // row_half_mirror
       const int m = m_base + r;
       if (sub == 0 && r < MB && m < m_end) {
         const size_t o = (size_t)m * a.am_ld + tg;
@@ -685,10 +704,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // Fused tail of one decoder layer for decode forwards of at most 48 rows: O + residual, gate|up
 // + SwiGLU and down + residual in one kernel of kTailWgs workgroups (one per CU), separated by
-// two grid barriers.  Every workgroup issues the loads of all three of its weight slices at
-// entry (O: 32 KB, gate|up: 64 KB, down: 128 KB), so the gate|up and down weights stream in from
-// HBM while the O stage and the first barrier run, instead of each GEMM starting cold after a
-// kernel boundary.  The data that crosses a barrier inside the kernel (the residual h, the next
+// two grid barriers.  Each workgroup issues the loads of its next weight slice well before the
+// barrier that precedes its use (gate|up: 64 KB behind the O products, down: 128 KB behind the
+// gate|up activations), so those weights stream in from HBM while the current stage and the
+// barrier run, instead of each GEMM starting cold after a kernel boundary.  The data that crosses a barrier inside the kernel (the residual h, the next
 // GEMM input xg and the norm partials from O; the SwiGLU output from gate|up) is written and read
 // device-coherently (write-through stores, sc1 loads), so the barrier needs no cache flush.
 //
@@ -2221,6 +2240,7 @@ static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t st) {
   for (int mt = 1; mt < cap; ++mt)
     if ((long)gx * a.S * ((a.M + 16 * mt - 1) / (16 * mt)) <= kGemmPersistentWgs) { MT = mt; break; }
   if (EPI == EPI_RESID && a.NT * MT * 16 * 16 > 2 * kGemmThreads) return hipErrorInvalidValue;
+  if (EPI == EPI_LOGITS && a.NT > 4) return hipErrorInvalidValue;   // the top-2 scan holds 2 * NT columns per lane
   if (EPI == EPI_PARTIAL && (a.S < 2 || a.S > 8)) return hipErrorInvalidValue;
   if (MT == 1) return launch_gemm_mt<T, EPI, 1>(a, st);
   if (MT == 2) return launch_gemm_mt<T, EPI, 2>(a, st);
