@@ -174,13 +174,14 @@ __global__ __launch_bounds__(64) void k_prep_embed(PrepArgs a) {
 
 struct Top2 { float v1; int i1; float v2; };
 
+// (written with selects only, so that it compiles to conditional moves rather than branches)
 __device__ __forceinline__ Top2 merge_top2(Top2 a, Top2 b) {
-  if (a.i1 == -1 || b.i1 == -1) return Top2{NAN, -1, NAN};
+  const bool nan = a.i1 == -1 || b.i1 == -1;
   const bool bw = b.v1 > a.v1 || (b.v1 == a.v1 && b.i1 < a.i1);
-  Top2 r;
-  if (bw) { r.v1 = b.v1; r.i1 = b.i1; r.v2 = fmaxf(a.v1, b.v2); }
-  else { r.v1 = a.v1; r.i1 = a.i1; r.v2 = fmaxf(a.v2, b.v1); }
-  return r;
+  const float v1 = bw ? b.v1 : a.v1;
+  const int i1 = bw ? b.i1 : a.i1;
+  const float v2 = bw ? fmaxf(a.v1, b.v2) : fmaxf(a.v2, b.v1);
+  return Top2{nan ? NAN : v1, nan ? -1 : i1, nan ? NAN : v2};
 }
 // The record of another lane of the same 8-lane group, moved by DPP (CTRL: quad_perm [1,0,3,2],
 // quad_perm [2,3,0,1] or row_half_mirror); merging with it three times, in that order, leaves the
@@ -647,11 +648,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs a) {
       for (int k = 0; k < kMaxCpl; ++k) {
         const int col = tg * NT * 16 + sub * cpl + k;
         const float z = zv[k];
-        if (k < cpl && r < MB && col < a.vocab && col != a.mask_id) {
-          if (z != z) nan = true;
-          else if (z > best.v1) { best.v2 = best.v1; best.v1 = z; best.i1 = col; }
-          else if (z > best.v2) { best.v2 = z; }
-        }
+        // the sequential update (a new maximum pushes the old one to second place; equal values
+        // keep the earlier, lower column) as selects
+        const bool ok = k < cpl && r < MB && col < a.vocab && col != a.mask_id;
+        const bool isnan = ok && z != z;
+        const bool gt1 = ok && !isnan && z > best.v1;
+        const bool gt2 = ok && !isnan && !gt1 && z > best.v2;
+        best.v2 = gt1 ? best.v1 : (gt2 ? z : best.v2);
+        best.v1 = gt1 ? z : best.v1;
+        best.i1 = gt1 ? col : best.i1;
+        nan = nan || isnan;
       }
       if (nan) best = Top2{NAN, -1, NAN};
       best = merge_top2(best, dpp_top2<0xB1>(best));    // quad_perm [1,0,3,2]
