@@ -919,7 +919,6 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
     const GemmLds L = gemm_lds(MT, KR * (int)sizeof(T), 2, 4, ag.n_ssq, EPI_SWIGLU);
     unsigned char* slab = smem;
     f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + L.red);
-    float* ctile = reinterpret_cast<float*>(smem + L.ctile);
     constexpr int NPASS = 3;
     const int G = ag.n_ssq / 4, gsh = 31 - __builtin_clz(G), RP = NTH >> gsh;
     float4 sv[NPASS];
@@ -978,24 +977,28 @@ __global__ __launch_bounds__(kTailThreads) void k_layer_tail(TailArgs ta) {
       for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * kWave + lane] = acc[mt];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 2 * MT * kWave; e += NTH) {
-      const int t = e / (MT * kWave), mt = (e / kWave) % MT, l = e % kWave;
-      f32x4_t v = red[((t * 4) * MT + mt) * kWave + l];
-      for (int j = 1; j < 4; ++j) v = v + red[((t * 4 + j) * MT + mt) * kWave + l];
-      float* dst = ctile + (t * MB + mt * 16 + l % 16) * 17 + 4 * (l / 16);
+    // The K-slice reduction and SwiGLU in one pass: thread (t, mt, row lane rl, q) adds, in slice
+    // order, the 4 partials of gate columns 4q .. 4q+3 and of up columns 8+4q .. 8+4q+3 of row
+    // 16mt + rl (lanes rl + 16q and rl + 16(q+2) of the partial tiles), scales them by 1/rms and
+    // forms two packed pairs of SwiGLU outputs (an exponential and a division each) into LDS; the
+    // store wave then writes them coherently
+    for (int e = threadIdx.x; e < 2 * MT * 32; e += kTailThreads) {
+      const int t = e / (MT * 32), mt = (e / 32) % MT, q = (e / 16) % 2, rl = e % 16;
+      const int lg = rl + 16 * q, lu = rl + 16 * (q + 2);
+      f32x4_t vg = red[((t * 4) * MT + mt) * kWave + lg], vu = red[((t * 4) * MT + mt) * kWave + lu];
+      for (int j = 1; j < 4; ++j) {
+        vg = vg + red[((t * 4 + j) * MT + mt) * kWave + lg];
+        vu = vu + red[((t * 4 + j) * MT + mt) * kWave + lu];
+      }
+      const int r = mt * 16 + rl;
+      const float inv = s_inv[r];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = v[i];
-    }
-    __syncthreads();
-    // SwiGLU of every (tile, row, column pair) by all waves into LDS, as packed pairs of outputs;
-    // the store wave then writes them coherently (the exponentials and divisions would take it
-    // about a microsecond alone)
-    for (int e = threadIdx.x; e < 2 * MB * 4; e += kTailThreads) {
-      const int t = e / (MB * 4), r = (e / 4) % MB, c = 2 * (e % 4);
-      const float* ct = ctile + (t * MB + r) * 17;
-      const float g0 = ct[c] * s_inv[r], u0 = ct[c + 8] * s_inv[r];
-      const float g1 = ct[c + 1] * s_inv[r], u1 = ct[c + 9] * s_inv[r];
-      s_act[e] = (uint32_t)Act<T>::from_f(silu_f(g0) * u0) | ((uint32_t)Act<T>::from_f(silu_f(g1) * u1) << 16);
+      for (int p = 0; p < 2; ++p) {
+        const float g0 = vg[2 * p] * inv, u0 = vu[2 * p] * inv;
+        const float g1 = vg[2 * p + 1] * inv, u1 = vu[2 * p + 1] * inv;
+        s_act[(t * MB + r) * 4 + 2 * q + p] =
+            (uint32_t)Act<T>::from_f(silu_f(g0) * u0) | ((uint32_t)Act<T>::from_f(silu_f(g1) * u1) << 16);
+      }
     }
     __syncthreads();
     for (int e = lane; wave == kStoreWave && e < 2 * MB * 4; e += kWave) {
