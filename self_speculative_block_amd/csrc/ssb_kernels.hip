@@ -234,13 +234,33 @@ __device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
   }
   return v + __int_as_float(moved);
 }
+// Lane l's value paired with lane l ^ 16 (resp. l ^ 32) by a VALU lane swap instead of an LDS
+// permute: v_permlane16_swap / v_permlane32_swap of v with itself leave each lane the pair
+// {v[l & ~16], v[l | 16]} (resp. 32), lower lane first.  A sum or max of the pair equals
+// v + v[l ^ 16] (max, and addition, are commutative).
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
 __device__ __forceinline__ float lane_group_sum(float v, int g) {
   if (g >= 2) v = dpp_add(v, 0);
   if (g >= 4) v = dpp_add(v, 1);
   if (g >= 8) v = dpp_add(v, 2);
   if (g >= 16) v = dpp_add(v, 3);
-  if (g >= 32) v += __shfl_xor(v, 16);
-  if (g >= 64) v += __shfl_xor(v, 32);
+  if (g >= 32) v = xor16_sum(v);
+  if (g >= 64) v = xor32_sum(v);
   return v;
 }
 
@@ -1382,8 +1402,8 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
               sq += v * v;
             }
         } else {
-          sq += __shfl_xor(sq, 16);
-          sq += __shfl_xor(sq, 32);
+          sq = xor16_sum(sq);
+          sq = xor32_sum(sq);
         }
         if (ok) {
 #pragma unroll
@@ -1679,8 +1699,8 @@ __global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 4 : 1) void k_attn(A
           s[kt][i] = z;
           mx = fmaxf(mx, z);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = xor16_max(mx);
+      mx = xor32_max(mx);
       // a row with no visible key in this chunk has mx = -inf and contributes nothing
       const float mref = mx == -INFINITY ? 0.f : mx;
       float lsum = 0.f;
@@ -1692,8 +1712,8 @@ __global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 4 : 1) void k_attn(A
           s[kt][i] = p;
           lsum += p;
         }
-      lsum = lsum + __shfl_xor(lsum, 16);
-      lsum = lsum + __shfl_xor(lsum, 32);
+      lsum = xor16_sum(lsum);
+      lsum = xor32_sum(lsum);
       // o^T = V^T P^T ; lane supplies keys pi(lane, j) for P^T and V^T alike
       f32x4_t o[DT];
 #pragma unroll
