@@ -205,7 +205,7 @@ __device__ __forceinline__ Top2 dpp_top2(Top2 x) {
 // needs before its first MFMA: the weight fragments of each wave, the
 // activation slab (rows x K range, staged once in LDS and shared by all
 // waves), the norm partials and the inputs of its epilogue.  The KSL partial
-// tiles of a tile are added in a fixed pairwise tree through LDS.
+// tiles of a tile are added one after another in slice order through LDS.
 // The decomposition depends only on K and the GEMM, never on M or MT, so a
 // row's value never depends on how many rows share the launch.
 // Workgroups stream disjoint weight slices spread over every CU (one CU
@@ -221,8 +221,8 @@ __device__ __forceinline__ float silu_f(float g) {
 
 // Sum over aligned groups of g lanes (g a power of two, 1..64), result in every lane of the
 // group.  Steps: swap within pairs, within quads (DPP quad permutes), mirror within 8 and 16
-// lanes (DPP row half-mirror and mirror), then xor 16 and 32 through ds_bpermute.  The
-// pattern is fixed, so the rounding of the sum is too.
+// lanes (DPP row half-mirror and mirror), then pairs 16 and 32 apart by lane swaps (xor16_sum,
+// xor32_sum).  The pattern is fixed, so the rounding of the sum is too.
 __device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
   int moved;
   const int iv = __float_as_int(v);

@@ -253,6 +253,38 @@ def _oracle_prefill_cached(full, wid, i, P, Bb):
     return _copy_state(cache[key])
 
 
+def _top2_of_logits(lg, mask_id):
+    """Per row of float32 logits, the mask id excluded: the largest value, the lowest id holding it,
+    and the largest value left once that id is removed (equal to the first when it occurs twice)."""
+    z = np.array(lg, dtype=np.float32, copy=True)
+    z[:, mask_id] = -np.inf
+    rows = np.arange(len(z))
+    i1 = np.argmax(z, axis=1)                 # first occurrence: the lowest id
+    v1 = z[rows, i1]
+    z[rows, i1] = -np.inf
+    return i1, v1, z.max(axis=1)
+
+
+def test_lm_head_records_equal_exact_top2_of_logits(full):
+    """The LM head's per-group records (each of 8 lanes scans 8 columns, merged across the lanes and
+    then across the vocabulary groups) give, row for row, exactly the top-1 value, its lowest id and
+    the runner-up value of the logits the same launch writes: a teacher-forced forward of 33 tokens
+    (the round's row count), compared with a plain sort of the returned logits."""
+    from self_speculative_block_amd.engine import KV
+    cfg, pool = full["cfg"], full["pool"]
+    kv = KV(pool, full["P"] + 64)
+    kv.prefill(full["pre_dev"])
+    am, t1, t2, lg = kv.forward_tokens(full["cont"][:B + 1], full["P"], want_logits=True)
+    kv.close()
+    i1, v1, v2 = _top2_of_logits(lg.cpu().numpy(), cfg.mask_id)
+    assert list(am) == [int(i) for i in i1]
+    assert np.array_equal(np.asarray(t1, dtype=np.float32), v1)
+    assert np.array_equal(np.asarray(t2, dtype=np.float32), v2)
+    kv = full["kv"]
+    kv.reset()
+    assert kv.prefill(full["pre_dev"]) == full["y1"]
+
+
 def test_teacher_forced_tokens_match_oracle(full):
     """GravityOCR review, Appendix B.3: a decoded sequence is judged position by position; a
     position where the GPU's token differs from the oracle's greedy prediction for it (given the

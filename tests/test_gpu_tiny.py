@@ -41,6 +41,27 @@ def _kv(pool, n=200):
     return KV(pool, n)
 
 
+def test_lm_head_records_equal_exact_top2_of_logits(tiny):
+    """The tiny model's LM-head records and vocabulary merge give exactly the top-1 value, its lowest
+    id (the mask id excluded) and the runner-up value of the logits the same launch writes."""
+    wl, cfg, w, model, pool, orc = tiny
+    pre = prefix_embeddings(wl.wid, 5, wl.prefix_len, cfg.hidden)
+    toks = ar_decode(orc, pre, 24)
+    kv = _kv(pool)
+    kv.prefill(model.prefix_tensor(pre))
+    am, t1, t2, lg = kv.forward_tokens(toks, wl.prefix_len, want_logits=True)
+    kv.close()
+    z = lg.cpu().numpy().astype(np.float32)
+    z[:, cfg.mask_id] = -np.inf
+    rows = np.arange(len(z))
+    i1 = np.argmax(z, axis=1)
+    v1 = z[rows, i1]
+    z[rows, i1] = -np.inf
+    assert list(am) == [int(i) for i in i1]
+    assert np.array_equal(np.asarray(t1, dtype=np.float32), v1)
+    assert np.array_equal(np.asarray(t2, dtype=np.float32), z.max(axis=1))
+
+
 def test_teacher_forced_logits_match_oracle(tiny):
     wl, cfg, w, model, pool, orc = tiny
     for s in (0, 1, 2):
