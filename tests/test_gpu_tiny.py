@@ -103,6 +103,38 @@ def test_round_logits_and_accept_match_oracle(tiny):
         kv.close()
 
 
+def test_degenerate_block_sizes_and_budgets_match_oracle(tiny):
+    """Rounds at block size 0 (a one-row draft and a one-row verify: two AR steps), 1 and 2, and
+    full-block rounds under commit budgets below A + 2, against the oracle round: draft and verify
+    logits, A, the committed tokens and the state the round leaves."""
+    wl, cfg, w, model, pool, orc = tiny
+    for s, B, budget, astar in [(20, 0, None, None), (21, 1, None, None), (22, 2, None, None),
+                                (23, wl.block, 1, None), (24, wl.block, 3, wl.block), (25, wl.block, 5, 2),
+                                (26, 0, 1, None)]:
+        pre = prefix_embeddings(wl.wid, s, wl.prefix_len, cfg.hidden)
+        # budget cases with planted drafts accept astar tokens: A + 2 above the budget (3), below it (5)
+        cont = ar_decode(orc, pre, 48) if astar is not None else None
+        kv = _kv(pool)
+        kv.prefill(model.prefix_tensor(pre))
+        st, _, _ = prefill(orc, pre, wl.prefix_len + 48)
+        for k in range(3):
+            plant = pl = None
+            if astar is not None:
+                plant = build_plant(cont, st.n - wl.prefix_len + 1, astar, B, cfg.vocab, cfg.mask_id)
+                pl = torch.tensor(plant, dtype=torch.int32, device=model.device)
+            committed, A, dl, vl = kv.round(B, max_commit=budget, planted_dev=pl, want_logits=True)
+            r = spec_round(orc, st, B, planted=plant, budget=budget, keep_logits=True)
+            if astar is not None:
+                assert A == astar and len(committed) == min(budget, astar + 2)
+            assert dl.shape == (B + 1, cfg.vocab) and vl.shape == (B + 1, cfg.vocab)
+            assert np.abs(dl.cpu().numpy() - r.draft_logits).max() < LOGIT_TOL
+            assert np.abs(vl.cpu().numpy() - r.verify_logits).max() < LOGIT_TOL
+            assert committed == r.committed and A == r.A, (s, B, budget, k)
+            n, x0, _ = kv.state()
+            assert (n, x0) == (st.n, st.x0)
+        kv.close()
+
+
 def test_free_running_identity_and_gpu_spec_equals_gpu_ar(tiny):
     wl, cfg, w, model, pool, orc = tiny
     same = 0
