@@ -144,6 +144,24 @@ __host__ __device__ __forceinline__ size_t kv_off(int layer, int n_pages, int pa
   return base * kPage * hd + (kv == 0 ? (size_t)tok * hd + dim : (size_t)dim * kPage + tok);
 }
 
+// Element offset of value (m, k) of a [rows][K] 16-bit activation matrix in fragment-major order,
+// the layout the large-tile GEMM reads its activations in when a forward is tall: rows in tiles of
+// 16 and K in steps of 32, each (row tile, K step) a 1 KiB block in matrix-core operand order (lane
+// l holds row l % 16 and the 8 values from k = 8 (l / 16)), so one operand fragment is one
+// contiguous 1 KiB load instead of 16 rows of 64 B.  Rows are padded to a multiple of 16.
+__host__ __device__ __forceinline__ size_t pk_off(int m, int k, int K) {
+  return ((size_t)((m >> 4) * (K >> 5) + (k >> 5)) * 64 + (m & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+}
+
+// Four 16-bit values to 8-byte-aligned memory in one store (a fragment-major group of four).
+template <typename T>
+__device__ __forceinline__ void st4h(T* p, const T (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                                              (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+  }
+}
+
 // Per-request launch arguments (passed by value).
 struct ReqArgs {
   int n;                              // requests in this launch
@@ -193,6 +211,7 @@ struct PrepArgs {
   const float2* rope; int half;   // rotary table [max_positions][hd/2]
   int32_t* fwd_pt; int pt_ld;     // page ids of this forward's requests [req][pt_ld] (0 past npg)
   float* h; void* xg; float* ssq; int ssq_ld;   // ssq: per-16-column sums of squares [M][ssq_ld]
+  int xpk;                     // xg in fragment-major order (pk_off) instead of [M][hidden]
   const ReqArgs* req;          // device request state
   ProfStamp* stamp;            // nullable timing stamps of this launch
 };
@@ -214,6 +233,7 @@ struct GemmArgs {
   float* am_v1; int32_t* am_i1; float* am_v2; int am_ld;   // LOGITS: records [M][am_ld]
   float* am_s;                                  // LOGITS, nullable: sum of exp((z - group max) / T) [M][am_ld]
   float am_scale;                               // log2(e) / T for am_s
+  int xpk, opk;                                 // large-tile GEMM: x, and xg_out / act, fragment-major (pk_off)
   ProfStamp* stamp;                             // nullable timing stamps of this launch
 };
 
@@ -274,6 +294,7 @@ struct AttnArgs {
   float* part; int max_chunks;             // records [row][head][chunk][hd+4]
   void* out; int out_ld;                   // fold: [rows][n_heads*hd]
   int fold;
+  int opk;                                 // fold: out in fragment-major order (pk_off, K = out_ld)
   float scale;
   ProfStamp* stamp;                        // nullable timing stamps of this launch
   AttnTasks tasks;

@@ -375,11 +375,13 @@ void init_model(const ssb_config* cfg, const ssb_weights* w, hipStream_t st, ssb
   m->max_chunks = (c.max_positions + kKeyChunk - 1) / kKeyChunk;
   off = 0;
   const size_t w_h = take((size_t)MR * H * 4);
-  const size_t w_xg = take((size_t)MR * H * E);
+  // activations that tall forwards keep fragment-major (whole 16-row tiles): rows rounded up to 16
+  const int MR16 = (MR + 15) / 16 * 16;
+  const size_t w_xg = take((size_t)MR16 * H * E);
   const size_t w_ssq = take((size_t)(H / 16) * MR * 4);
   const size_t w_q = take((size_t)MR * qd * E);
-  const size_t w_attn = take((size_t)MR * qd * E);
-  const size_t w_act = take((size_t)MR * F * E);
+  const size_t w_attn = take((size_t)MR16 * qd * E);
+  const size_t w_act = take((size_t)MR16 * F * E);
   const size_t w_meta = take((size_t)5 * MR * 4);
   const size_t w_cs = take((size_t)MR * (hd / 2) * sizeof(float2));
   m->pt_ld = m->max_chunks * (kKeyChunk / kPage);
@@ -488,6 +490,13 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   const ssb_config& c = m->c;
   const int H = c.hidden, qd = c.n_heads * c.head_dim, MR = c.max_rows;
   const int M = f.M;
+  const bool tall = f.mode == PREP_PREFILL || f.mode == PREP_TOKENS;
+  // tall bf16 forwards use the large-tile GEMM (no decode row is computed there); its activations
+  // (the GEMM inputs xg, attention output and SwiGLU output) are written and read fragment-major,
+  // one contiguous 1 KiB block per matrix-core operand fragment; the last layer's xg stays
+  // row-major for the LM head
+  const bool big = tall && m->elem == 2 && M >= 128;
+  const int pk = big ? 1 : 0;
   PrepArgs pa{};
   pa.mode = f.mode; pa.M = M; pa.hidden = H; pa.vocab = c.vocab; pa.mask_id = c.mask_id;
   pa.pos0 = f.pos0; pa.prefix = f.prefix; pa.tokens = m->tok_dev; pa.am_prev = m->am_tok;
@@ -495,7 +504,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   pa.row_tok = m->row_tok; pa.row_pos = m->row_pos; pa.row_lim = m->row_lim; pa.row_req = m->row_req;
   pa.row_slot = m->row_slot; pa.row_cs = m->row_cs; pa.rope = m->rope; pa.half = c.head_dim / 2;
   pa.fwd_pt = m->fwd_pt; pa.pt_ld = m->pt_ld;
-  pa.h = m->h; pa.xg = m->xg; pa.ssq = m->ssq; pa.ssq_ld = H / 16; pa.req = m->req_dev;
+  pa.h = m->h; pa.xg = m->xg; pa.ssq = m->ssq; pa.ssq_ld = H / 16; pa.req = m->req_dev; pa.xpk = pk;
   pa.stamp = prof_begin(m, kKindPrep, st);
   hip_check(launch_prep<T>(pa, st), "prep");
   prof_end(m, kKindPrep, st);
@@ -523,12 +532,10 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
   at.out = m->attn; at.out_ld = qd;
   // rows of a prefill or teacher-forced forward fold their key chunks in one workgroup (no
   // records, no combine launch); decode windows split keys over workgroups and combine
-  const bool tall = f.mode == PREP_PREFILL || f.mode == PREP_TOKENS;
   at.fold = (tall || M > m->max_decode_rows) ? 1 : 0;
-  // tall bf16 forwards use the large-tile GEMM (no decode row is computed there); decode
-  // forwards of many rows (batched rounds) use its exact form, which reproduces k_gemm's
-  // arithmetic bit for bit (k_gemm keeps the small-M shapes it is fast at)
-  const bool big = tall && m->elem == 2 && M >= 128;
+  at.opk = pk;
+  // decode forwards of many rows (batched rounds) use the large-tile GEMM's exact form, which
+  // reproduces k_gemm's arithmetic bit for bit (k_gemm keeps the small-M shapes it is fast at)
   const bool dec_big = !tall && m->elem == 2;
   const bool x_qkv = dec_big && M >= kExactRowsQkv, x_o = dec_big && M >= kExactRowsO;
   const bool x_gu = dec_big && M >= kExactRowsGateUp, x_down = dec_big && M >= kExactRowsDown;
@@ -560,7 +567,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     {  // RMSNorm -> QKV -> RoPE -> KV write (input xg = h * attn_norm[l])
       GemmArgs a = g;
       set_w(a, m->qkv[l]);
-      a.x = m->xg; a.ldx = H;
+      a.x = m->xg; a.ldx = H; a.xpk = pk;
       a.stamp = prof_begin(m, SSB_K_QKV, st);
       hip_check(big || x_qkv ? launch_gemm_big(a, EPI_QKV, x_qkv, st) : launch_gemm<T>(a, EPI_QKV, st), "qkv gemm");
       prof_end(m, SSB_K_QKV, st);
@@ -591,7 +598,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     {  // O + residual; next input xg = h * mlp_norm[l]
       GemmArgs a = g;
       set_w(a, m->o[l]);
-      a.x = m->attn; a.ldx = qd;
+      a.x = m->attn; a.ldx = qd; a.xpk = pk; a.opk = pk;
       a.gain_next = m->mlp_norm[l];
       a.stamp = prof_begin(m, SSB_K_O, st);
       hip_check(big || x_o ? launch_gemm_big(a, EPI_RESID, x_o, st) : launch_gemm<T>(a, EPI_RESID, st), "o gemm");
@@ -600,7 +607,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     {  // gate|up + SwiGLU
       GemmArgs a = g;
       set_w(a, m->gu[l]);
-      a.x = m->xg; a.ldx = H;
+      a.x = m->xg; a.ldx = H; a.xpk = pk; a.opk = pk;
       a.stamp = prof_begin(m, SSB_K_GATEUP, st);
       hip_check(big || x_gu ? launch_gemm_big(a, EPI_SWIGLU, x_gu, st) : launch_gemm<T>(a, EPI_SWIGLU, st),
                 "gate/up gemm");
@@ -609,7 +616,7 @@ void forward(ssb_model* m, ssb_pool* pool, const FwdSpec& f, hipStream_t st) {
     {  // down + residual; next input xg = h * (next attn_norm | final_norm)
       GemmArgs a = g;
       set_w(a, m->d[l]);
-      a.x = m->act; a.ldx = c.ffn;
+      a.x = m->act; a.ldx = c.ffn; a.xpk = pk; a.opk = l + 1 < c.n_layers ? pk : 0;
       a.gain_next = l + 1 < c.n_layers ? m->attn_norm[l + 1] : m->final_norm;
       a.stamp = prof_begin(m, SSB_K_DOWN, st);
       const bool dexact = x_down && a.S == 1;   // a K-split down projection stays on k_gemm

@@ -164,7 +164,8 @@ __global__ __launch_bounds__(64) void k_prep_embed(PrepArgs a) {
                           : reinterpret_cast<const T*>(a.prefix) + (size_t)pos * a.hidden;
   const float v = Ty<T>::to_f(src[col]);
   a.h[(size_t)m * a.hidden + col] = v;
-  reinterpret_cast<T*>(a.xg)[(size_t)m * a.hidden + col] = Act<T>::from_f(v * a.gain[col]);
+  reinterpret_cast<T*>(a.xg)[a.xpk ? pk_off(m, col, a.hidden) : (size_t)m * a.hidden + col] =
+      Act<T>::from_f(v * a.gain[col]);
   float s = v * v;
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
@@ -1156,6 +1157,12 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
     if (f < 2 * CT) {
       src[i] = a.W + (size_t)(tn0 + f) * ksteps * kWave + lane;
       stride[i] = kWave;
+    } else if (a.xpk) {
+      // fragment-major activations: the (row tile, K step) fragment is 1 KiB in lane order; row
+      // tiles past the last one (only in the block's padding) read the last
+      const int rt = min(m0 / 16 + (f - 2 * CT), (a.M + 15) / 16 - 1);
+      src[i] = reinterpret_cast<const uint4*>(a.x) + (size_t)rt * ksteps * kWave + lane;
+      stride[i] = kWave;
     } else {
       const int row = min(m0 + 16 * (f - 2 * CT) + lane % 16, a.M - 1);   // rows past M: any valid row
       src[i] = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.x) + (size_t)row * a.ldx +
@@ -1376,9 +1383,15 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) zo[i] = __shfl_xor(z[i], 32);   // up (columns 8..15) for gate lanes
         if (ok && q < 2) {
+          bf16_t v[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            reinterpret_cast<bf16_t*>(a.act)[(size_t)m * a.act_ld + tg * 8 + 4 * q + i] = f2h(silu_f(z[i]) * zo[i]);
+          for (int i = 0; i < 4; ++i) v[i] = f2h(silu_f(z[i]) * zo[i]);
+          if (a.opk) {
+            st4h(reinterpret_cast<bf16_t*>(a.act) + pk_off(m, tg * 8 + 4 * q, a.act_ld), v);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) reinterpret_cast<bf16_t*>(a.act)[(size_t)m * a.act_ld + tg * 8 + 4 * q + i] = v[i];
+          }
         }
       } else {  // EPI_RESID
         const int n0 = tg * 16 + 4 * q;
@@ -1406,10 +1419,17 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
           sq = xor32_sum(sq);
         }
         if (ok) {
+          bf16_t v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             a.h[(size_t)m * a.hidden + n0 + i] = z[i];
-            reinterpret_cast<bf16_t*>(a.xg_out)[(size_t)m * a.hidden + n0 + i] = f2h(z[i] * gv[i]);
+            v[i] = f2h(z[i] * gv[i]);
+          }
+          if (a.opk) {
+            st4h(reinterpret_cast<bf16_t*>(a.xg_out) + pk_off(m, n0, a.hidden), v);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) reinterpret_cast<bf16_t*>(a.xg_out)[(size_t)m * a.hidden + n0 + i] = v[i];
           }
           if (q == 0) a.ssq_out[(size_t)m * a.ssq_ld + tg] = sq;
         }
@@ -1771,11 +1791,20 @@ __global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 4 : 1) void k_attn(A
   }
 
   if (a.fold && active && row_local < task.nrows) {
-    T* dst = reinterpret_cast<T*>(a.out) + (size_t)(task.row0 + row_local) * a.out_ld + head * HD;
+    const int row = task.row0 + row_local;
+    T* dst = reinterpret_cast<T*>(a.out) + (size_t)row * a.out_ld + head * HD;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt) {
+      T v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[dt * 16 + 4 * (lane / 16) + i] = Act<T>::from_f(run_o[dt][i] / run_l);
+      for (int i = 0; i < 4; ++i) v[i] = Act<T>::from_f(run_o[dt][i] / run_l);
+      if (sizeof(T) == 2 && a.opk) {   // four consecutive values of one 8-value group: one 8-byte store
+        st4h(reinterpret_cast<T*>(a.out) + pk_off(row, head * HD + dt * 16 + 4 * (lane / 16), a.out_ld), v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[dt * 16 + 4 * (lane / 16) + i] = v[i];
+      }
+    }
   }
   stamp_end(a.stamp);
 }
