@@ -215,9 +215,11 @@ __device__ __forceinline__ Top2 dpp_top2(Top2 x) {
 // by 1/rms(h), rms from the per-16-column sums of squares added in column
 // order (review section 3.1: both modes share these layers).
 // ---------------------------------------------------------------------------
+// SiLU g / (1 + e^-g): e^-g as 2^(-g log2 e) from the hardware base-2 exponential and the quotient
+// as g times the hardware reciprocal (each within about 1 ulp); every kernel uses this one form.
 __device__ __forceinline__ float silu_f(float g) {
 #pragma clang fp contract(off)
-  return g / (1.0f + expf(-g));
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
 }
 
 // Sum over aligned groups of g lanes (g a power of two, 1..64), result in every lane of the
@@ -246,6 +248,11 @@ __device__ __forceinline__ float xor16_sum(float v) {
 __device__ __forceinline__ float xor32_sum(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// The value of lane l ^ 32 (the same swap, the half that is not the lane's own).
+__device__ __forceinline__ float xor32_get(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((int)(threadIdx.x % kWave) < 32 ? p[1] : p[0]);
 }
 __device__ __forceinline__ float xor16_max(float v) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -1129,8 +1136,15 @@ __device__ __forceinline__ void load_lds16(const void* gptr, unsigned lds_base) 
                : "memory", "m0");
 }
 
+// JIT (the wide non-exact tiles): the fragments of a step are read from LDS as the products use
+// them, with no register copy of the next step, so that the kernel fits two workgroups per CU;
+// each covers the other's LDS latency.  The copy of step s + NS - 1 then goes into the buffer of
+// step s - 1, which every wave has finished reading at step s's barrier.
+template <int RT, int CT, bool EXACT>
+constexpr bool big_jit() { return !EXACT && RT * CT >= 32; }
+
 template <int EPI, int RT, int CT, int NS, bool EXACT>
-__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
+__global__ __launch_bounds__(256, (big_jit<RT, CT, EXACT>() ? 2 : 1)) void k_gemm_big(GemmArgs a) {
 #pragma clang fp contract(off)
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
   static_assert(EPI != EPI_LOGITS || (EXACT && CT == 4), "LM head: exact form, one 4-tile group per wave");
@@ -1203,9 +1217,11 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
   }
 
   // NS steps in flight; step s+1's operands are read from LDS into registers while step s
-  // multiplies (register double buffer), one barrier per step
+  // multiplies (register double buffer), one barrier per step.  JIT: NS - 1 steps in flight
+  // beside the one being read.
+  constexpr bool JIT = big_jit<RT, CT, EXACT>();
 #pragma unroll
-  for (int s = 0; s < NS; ++s) issue(s);
+  for (int s = 0; s < (JIT ? NS - 1 : NS); ++s) issue(s);
   f32x4_t acc[CT][RT];
 #pragma unroll
   for (int c = 0; c < CT; ++c)
@@ -1224,6 +1240,22 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
   const int kpw = EXACT ? ksteps / a.KSL : ksteps;
   int left = kpw;
   bool first_slice = true;
+  if constexpr (JIT) {
+    for (int s = 0; s < ksteps; ++s) {
+      wait_vmcnt<FPW * (NS - 2)>();        // step s has landed (steps past the end reload the last)
+      __syncthreads();                     // for every wave, and every wave is done with step s - 1
+      issue(s + NS - 1);                   // into step s - 1's buffer
+      const unsigned char* buf = smem + (s % NS) * NF * 1024;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) xf[r] = *reinterpret_cast<const uint4*>(buf + (2 * CT + wr * RT + r) * 1024 + lane * 16);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const uint4 w = *reinterpret_cast<const uint4*>(buf + (wc * CT + c) * 1024 + lane * 16);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) mma_wa(acc[c][r], w, xf[r], bf16_t());
+      }
+    }
+  } else {
   wait_vmcnt<FPW * (NS - 1)>();            // step 0 has landed
   __syncthreads();
   rd(0, wf, xf);
@@ -1254,6 +1286,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
     for (int c = 0; c < CT; ++c) wf[c] = wn[c];
 #pragma unroll
     for (int r = 0; r < RT; ++r) xf[r] = xn[r];
+  }
   }
   wait_vmcnt<0>();
   if constexpr (EXACT) {
@@ -1350,7 +1383,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = acc[c][r][i] * s_inv[rl];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zo[i] = __shfl_xor(z[i], 32);   // the rotary partner column (c +- 8)
+        for (int i = 0; i < 4; ++i) zo[i] = xor32_get(z[i]);   // the rotary partner column (c +- 8)
         {
           // q row, or the K/V block of the row's slot (dim d at dst[d * dstr])
           bf16_t* dst;
@@ -1381,7 +1414,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = acc[c][r][i] * s_inv[rl];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zo[i] = __shfl_xor(z[i], 32);   // up (columns 8..15) for gate lanes
+        for (int i = 0; i < 4; ++i) zo[i] = xor32_get(z[i]);   // up (columns 8..15) for gate lanes
         if (ok && q < 2) {
           bf16_t v[4];
 #pragma unroll
@@ -2337,6 +2370,8 @@ static hipError_t launch_gemm_big_epi(const GemmArgs& a, hipStream_t st) {
     const int rb4 = (a.M + 127) / 128;
     // (LDS: 3 steps of 16 KiB, 4 of 12 KiB, 6 of 8 KiB: two or three workgroups per CU; deeper
     // pipelines with one workgroup per CU measured slower)
+    if (!EXACT && a.n_tiles % 16 == 0 && (a.n_tiles / 16) * rb4 >= 240)
+      return launch_gemm_big_cfg<EPI, 4, 8, 3, EXACT>(a, st);
     if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3, EXACT>(a, st);
     if (a.n_tiles % 4 == 0 && (a.n_tiles / 4) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 2, 4, EXACT>(a, st);
     if (a.n_tiles % 4 == 0) return launch_gemm_big_cfg<EPI, 2, 2, 6, EXACT>(a, st);
