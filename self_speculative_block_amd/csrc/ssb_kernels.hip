@@ -1600,8 +1600,9 @@ __device__ __forceinline__ float fold_val(float v, float al, float vc, float be)
 }
 
 // fp16 K/V: at most 128 VGPRs, so four workgroups share a CU (long contexts launch several per CU)
-template <typename T, int HD>
-__global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 4 : 1) void k_attn(AttnArgs a) {
+// (folded launches have about one workgroup per CU: their register budget is two waves per SIMD)
+template <typename T, int HD, bool FOLD>
+__global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)) void k_attn(AttnArgs a) {
 #pragma clang fp contract(off)
   constexpr int NTH = kAttnThreads;
   constexpr int KS = Ty<T>::kStepK;
@@ -1675,29 +1676,34 @@ __global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 4 : 1) void k_attn(A
 #pragma unroll
   for (int d = 0; d < DT; ++d) run_o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int c = cbeg; c < cend; ++c) {
-    if (c != cbeg) {
-#pragma unroll
-      for (int q = 0; q < KVF; ++q) {
-        const int f = (int)threadIdx.x + q * NTH;
-        pg[q] = pt[(c * kKeyChunk + frag_key(f)) / kPage];
-      }
-    }
-    uint4 kvv[KVF];
-    // ---- second round trip: K and V of keys [c*64, c*64+64) ----
-    // Unconditional loads: a conditional load makes the compiler wait for it inside its branch,
-    // which serialised the KVF round trips.  Every address is in the pool: the page list holds
-    // page 0 past the request's pages.  Keys past the task's limit are zeroed below (their
-    // scores are masked; a zero V keeps 0 * P finite).
+  // ---- second round trip: K and V of keys [c*64, c*64+64) ----
+  // Unconditional loads: a conditional load makes the compiler wait for it inside its branch,
+  // which serialised the KVF round trips.  Every address is in the pool: the page list holds
+  // page 0 past the request's pages.  Keys past the task's limit are zeroed below (their
+  // scores are masked; a zero V keeps 0 * P finite).
+  auto load_kv = [&](const int (&pgs)[KVF], uint4 (&dst)[KVF]) {
 #pragma unroll
     for (int q = 0; q < KVF; ++q) {
       const int f = threadIdx.x + q * NTH;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
       const int key = frag_key(f) % kPage, dim = kv == 0 ? (rem % FPK) * PER : rem % (HD * GPP) / GPP;
-      kvv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kv_pool) +
-                                               kv_off(a.layer, a.n_pages, pg[q], kv, a.n_kv, g, key, dim, HD));
+      dst[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.kv_pool) +
+                                               kv_off(a.layer, a.n_pages, pgs[q], kv, a.n_kv, g, key, dim, HD));
     }
+  };
+  auto load_pg = [&](int c, int (&dst)[KVF]) {
+#pragma unroll
+    for (int q = 0; q < KVF; ++q) dst[q] = pt[(c * kKeyChunk + frag_key((int)threadIdx.x + q * NTH)) / kPage];
+  };
+  // Folded rows walk their chunks with the next chunk's K and V and the page ids of the one after
+  // in flight while the current chunk is multiplied (the last chunks re-read the last one, never
+  // used), so a chunk costs its products rather than two dependent memory round trips.
+  uint4 kvv[KVF];
+  load_kv(pg, kvv);
+  if constexpr (FOLD) load_pg(min(cbeg + 1, cend - 1), pg);
+
+  for (int c = cbeg; c < cend; ++c) {
     // (the row limits are stored once the K/V loads are in flight)
     if (threadIdx.x < 16) s_lim[threadIdx.x] = lim_row < task.nrows ? lim_ld : -1;
 #pragma unroll
@@ -1727,6 +1733,10 @@ __global__ __launch_bounds__(kAttnThreads, sizeof(T) == 2 ? 4 : 1) void k_attn(A
       }
     }
     __syncthreads();
+    if constexpr (FOLD) {
+      load_kv(pg, kvv);                        // chunk c + 1 (its page ids landed a chunk ago)
+      load_pg(min(c + 2, cend - 1), pg);
+    }
 
     if (active) {
       // S^T tiles: element i of tile kt = score of key kt*16 + 4*(lane/16) + i for row_local
@@ -2446,8 +2456,13 @@ hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipSt
   if (a.n_heads / a.n_kv > kAttnThreads / kWave) return hipErrorInvalidValue;
   if (!a.fold && n_chunk_slots > a.max_chunks) return hipErrorInvalidValue;
   dim3 grid(a.fold ? 1 : n_chunk_slots, a.n_kv, a.tasks.n * (kTaskRows / 16));
-  if (head_dim == 64) SSB_LAUNCH((k_attn<T, 64>), grid, dim3(kAttnThreads), 0, st, a);
-  else SSB_LAUNCH((k_attn<T, 32>), grid, dim3(kAttnThreads), 0, st, a);
+  if (head_dim == 64) {
+    if (a.fold) SSB_LAUNCH((k_attn<T, 64, true>), grid, dim3(kAttnThreads), 0, st, a);
+    else SSB_LAUNCH((k_attn<T, 64, false>), grid, dim3(kAttnThreads), 0, st, a);
+  } else {
+    if (a.fold) SSB_LAUNCH((k_attn<T, 32, true>), grid, dim3(kAttnThreads), 0, st, a);
+    else SSB_LAUNCH((k_attn<T, 32, false>), grid, dim3(kAttnThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 template hipError_t launch_attn<bf16_t>(const AttnArgs&, int, int, hipStream_t);
