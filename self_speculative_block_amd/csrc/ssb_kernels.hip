@@ -1599,12 +1599,15 @@ __device__ __forceinline__ float fold_val(float v, float al, float vc, float be)
   return __fadd_rn(__fmul_rn(v, al), __fmul_rn(vc, be));
 }
 
-// fp16 K/V: at most 128 VGPRs, so four workgroups share a CU (long contexts launch several per CU)
-// (folded launches have about one workgroup per CU: their register budget is two waves per SIMD)
+// fp16 K/V: at most 128 VGPRs, so four workgroups share a CU (long contexts launch several per CU).
+// Folded rows (FOLD) run two chunk streams of four waves each, the even and the odd chunks of the
+// same rows and heads, and merge the two running states at the end: half the dependent chain per
+// workgroup and two waves per SIMD.
 template <typename T, int HD, bool FOLD>
-__global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__((FOLD ? 2 : 1) * kAttnThreads, (FOLD ? 2 : (sizeof(T) == 2 ? 4 : 1))) void k_attn(AttnArgs a) {
 #pragma clang fp contract(off)
-  constexpr int NTH = kAttnThreads;
+  constexpr int NTH = kAttnThreads;        // threads of one chunk stream
+  constexpr int NST = FOLD ? 2 : 1;        // chunk streams
   constexpr int KS = Ty<T>::kStepK;
   constexpr int PER = Ty<T>::kPerFrag;
   constexpr int DT = HD / 16;
@@ -1627,16 +1630,22 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
   };
   constexpr int KVF = NKF / NTH;
   static_assert(NKF % NTH == 0, "every thread loads the same number of K/V fragments");
-  __shared__ __align__(16) unsigned char ks[kKeyChunk * KSTR];
-  __shared__ __align__(16) unsigned char vts[HD * VSTR];
+  __shared__ __align__(16) unsigned char ks[NST * kKeyChunk * KSTR];
+  __shared__ __align__(16) unsigned char vts[NST * HD * VSTR];
   __shared__ int s_lim[16];
+  // the second stream's running state goes to the first through the K buffers after the loop
+  static_assert(!FOLD || NST * kKeyChunk * KSTR >= (kAttnThreads / kWave) * kWave * (4 * DT + 2) * 4, "state exchange");
 
   stamp_begin(a.stamp);
   const AttnTask task = a.tasks.t[blockIdx.z / TILES];
   const int mt = blockIdx.z % TILES;       // this workgroup's 16-row tile of the task
   if (mt * 16 >= task.nrows) return;
   const int g = blockIdx.y;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int sm = (int)threadIdx.x / NTH;   // chunk stream (0 unless FOLD)
+  const int tl = (int)threadIdx.x % NTH;   // thread within the stream
+  unsigned char* const ksm = ks + sm * kKeyChunk * KSTR;
+  unsigned char* const vtsm = vts + sm * HD * VSTR;
+  const int wave = tl / kWave, lane = tl % kWave;
   const int n_rep = a.n_heads / a.n_kv;
   const bool active = wave < n_rep;        // wave = query head within the KV group
   const int row_local = mt * 16 + lane % 16;
@@ -1647,12 +1656,12 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
 
   // ---- first memory round trip: page ids, limits, query fragments (loads complete in issue
   //      order, so the K/V addresses wait for the page ids only) ----
-  const int cbeg = a.fold ? 0 : blockIdx.x;
+  const int cbeg = FOLD ? 0 : blockIdx.x;
   int pg[KVF];
+  {
+    const int c1 = min(cbeg + sm, a.max_chunks - 1);   // this stream's first chunk (a junk one past the end)
 #pragma unroll
-  for (int q = 0; q < KVF; ++q) {
-    const int f = (int)threadIdx.x + q * NTH;
-    pg[q] = pt[(cbeg * kKeyChunk + frag_key(f)) / kPage];
+    for (int q = 0; q < KVF; ++q) pg[q] = pt[(c1 * kKeyChunk + frag_key(tl + q * NTH)) / kPage];
   }
   // Branch-free as well (clamped to the task's last row and the last head): rows past the task
   // and idle waves read real data that never reaches a written result (rows stay independent in
@@ -1668,7 +1677,7 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
   }
   // largest visibility limit of the task's rows
   const int maxlim = task.lim_mode == 0 ? task.max_lim : a.req->p[task.req] + a.req->B + (task.lim_mode == 2 ? 1 : 0);
-  const int cend = a.fold ? maxlim / kKeyChunk + 1 : cbeg + 1;
+  const int cend = FOLD ? maxlim / kKeyChunk + 1 : cbeg + 1;
   if (cbeg * kKeyChunk > maxlim) return;     // no visible key in this chunk slot
 
   float run_m = -INFINITY, run_l = 0.f;
@@ -1684,7 +1693,7 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
   auto load_kv = [&](const int (&pgs)[KVF], uint4 (&dst)[KVF]) {
 #pragma unroll
     for (int q = 0; q < KVF; ++q) {
-      const int f = threadIdx.x + q * NTH;
+      const int f = tl + q * NTH;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
       const int key = frag_key(f) % kPage, dim = kv == 0 ? (rem % FPK) * PER : rem % (HD * GPP) / GPP;
@@ -1694,27 +1703,29 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
   };
   auto load_pg = [&](int c, int (&dst)[KVF]) {
 #pragma unroll
-    for (int q = 0; q < KVF; ++q) dst[q] = pt[(c * kKeyChunk + frag_key((int)threadIdx.x + q * NTH)) / kPage];
+    for (int q = 0; q < KVF; ++q) dst[q] = pt[(c * kKeyChunk + frag_key(tl + q * NTH)) / kPage];
   };
   // Folded rows walk their chunks with the next chunk's K and V and the page ids of the one after
   // in flight while the current chunk is multiplied (the last chunks re-read the last one, never
   // used), so a chunk costs its products rather than two dependent memory round trips.
   uint4 kvv[KVF];
   load_kv(pg, kvv);
-  if constexpr (FOLD) load_pg(min(cbeg + 1, cend - 1), pg);
+  if constexpr (FOLD) load_pg(min(cbeg + sm + NST, cend - 1), pg);
 
-  for (int c = cbeg; c < cend; ++c) {
+  for (int c0 = cbeg; c0 < cend; c0 += NST) {
+    const int c = c0 + sm;                 // this stream's chunk
+    const bool cvalid = c < cend;          // (the odd stream may have none in the last pass)
     // (the row limits are stored once the K/V loads are in flight)
     if (threadIdx.x < 16) s_lim[threadIdx.x] = lim_row < task.nrows ? lim_ld : -1;
 #pragma unroll
     for (int q = 0; q < KVF; ++q) {
-      const int f = threadIdx.x + q * NTH;
+      const int f = tl + q * NTH;
       const int kv = f / (kKeyChunk * FPK);
       const int rem = f % (kKeyChunk * FPK);
       const int kk = frag_key(f);
       if (kv == 0) {
         if (c * kKeyChunk + kk > maxlim) kvv[q] = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(ks + kk * KSTR + (rem % FPK) * PER * (int)sizeof(T)) = kvv[q];
+        *reinterpret_cast<uint4*>(ksm + kk * KSTR + (rem % FPK) * PER * (int)sizeof(T)) = kvv[q];
       } else {
         // zero the values of keys past the limit (PER keys per fragment)
         const int nv = maxlim - (c * kKeyChunk + kk) + 1;
@@ -1729,16 +1740,16 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
           }
         }
         const int d = rem % (HD * GPP) / GPP;
-        *reinterpret_cast<uint4*>(vts + d * VSTR + kk * (int)sizeof(T)) = kvv[q];
+        *reinterpret_cast<uint4*>(vtsm + d * VSTR + kk * (int)sizeof(T)) = kvv[q];
       }
     }
     __syncthreads();
     if constexpr (FOLD) {
-      load_kv(pg, kvv);                        // chunk c + 1 (its page ids landed a chunk ago)
-      load_pg(min(c + 2, cend - 1), pg);
+      load_kv(pg, kvv);                        // chunk c + 2 (its page ids landed a pass ago)
+      load_pg(min(c + 2 * NST, cend - 1), pg);
     }
 
-    if (active) {
+    if (active && cvalid) {
       // S^T tiles: element i of tile kt = score of key kt*16 + 4*(lane/16) + i for row_local
       f32x4_t s[KT];
 #pragma unroll
@@ -1747,7 +1758,7 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
 #pragma unroll
         for (int st = 0; st < QKS; ++st) {
           const uint4 kf = *reinterpret_cast<const uint4*>(
-              ks + (kt * 16 + lane % 16) * KSTR + (st * KS + PER * (lane / 16)) * (int)sizeof(T));
+              ksm + (kt * 16 + lane % 16) * KSTR + (st * KS + PER * (lane / 16)) * (int)sizeof(T));
           mma_aa(s[kt], kf, qf[st], T());
         }
       }
@@ -1798,7 +1809,7 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const unsigned char* vrow = vts + (dt * 16 + lane % 16) * VSTR;
+          const unsigned char* vrow = vtsm + (dt * 16 + lane % 16) * VSTR;
           uint4 vf;
           if constexpr (sizeof(T) == 2) {
             const uint2 va = *reinterpret_cast<const uint2*>(vrow + (32 * st + 4 * (lane / 16)) * 2);
@@ -1811,7 +1822,7 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
         }
       }
       // o[dt][i] = o_c[d = dt*16 + 4*(lane/16) + i] of row_local; the record's max is mref
-      if (a.fold) {
+      if constexpr (FOLD) {
         if (mx != -INFINITY) {
           float mn, al, be;
           fold_coef(run_m, mref, mn, al, be);
@@ -1833,7 +1844,33 @@ __global__ __launch_bounds__(kAttnThreads, (sizeof(T) == 2 ? (FOLD ? 2 : 4) : 1)
     __syncthreads();
   }
 
-  if (a.fold && active && row_local < task.nrows) {
+  if constexpr (FOLD) {
+    // the odd-chunk stream's (m, l, o) into the even stream's, the same online merge
+    constexpr int XS = 4 * DT + 2;
+    float* xs = reinterpret_cast<float*>(ks) + (size_t)(wave * kWave + lane) * XS;
+    if (sm == 1) {
+      xs[0] = run_m;
+      xs[1] = run_l;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[2 + 4 * dt + i] = run_o[dt][i];
+    }
+    __syncthreads();
+    const float m1 = xs[0];
+    if (sm == 0 && m1 != -INFINITY) {
+      float mn, al, be;
+      fold_coef(run_m, m1, mn, al, be);
+      run_l = fold_val(run_l, al, xs[1], be);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) run_o[dt][i] = fold_val(run_o[dt][i], al, xs[2 + 4 * dt + i], be);
+      run_m = mn;
+    }
+  }
+
+  if (FOLD && sm == 0 && active && row_local < task.nrows) {
     const int row = task.row0 + row_local;
     T* dst = reinterpret_cast<T*>(a.out) + (size_t)row * a.out_ld + head * HD;
 #pragma unroll
@@ -2456,11 +2493,12 @@ hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipSt
   if (a.n_heads / a.n_kv > kAttnThreads / kWave) return hipErrorInvalidValue;
   if (!a.fold && n_chunk_slots > a.max_chunks) return hipErrorInvalidValue;
   dim3 grid(a.fold ? 1 : n_chunk_slots, a.n_kv, a.tasks.n * (kTaskRows / 16));
+  // folded rows: two chunk streams per workgroup
   if (head_dim == 64) {
-    if (a.fold) SSB_LAUNCH((k_attn<T, 64, true>), grid, dim3(kAttnThreads), 0, st, a);
+    if (a.fold) SSB_LAUNCH((k_attn<T, 64, true>), grid, dim3(2 * kAttnThreads), 0, st, a);
     else SSB_LAUNCH((k_attn<T, 64, false>), grid, dim3(kAttnThreads), 0, st, a);
   } else {
-    if (a.fold) SSB_LAUNCH((k_attn<T, 32, true>), grid, dim3(kAttnThreads), 0, st, a);
+    if (a.fold) SSB_LAUNCH((k_attn<T, 32, true>), grid, dim3(2 * kAttnThreads), 0, st, a);
     else SSB_LAUNCH((k_attn<T, 32, false>), grid, dim3(kAttnThreads), 0, st, a);
   }
   return hipGetLastError();
