@@ -1136,49 +1136,54 @@ __device__ __forceinline__ void load_lds16(const void* gptr, unsigned lds_base) 
                : "memory", "m0");
 }
 
-// JIT (the wide non-exact tiles): the fragments of a step are read from LDS as the products use
+// JIT (the wide non-exact blocks): the fragments of a step are read from LDS as the products use
 // them, with no register copy of the next step, so that the kernel fits two workgroups per CU;
 // each covers the other's LDS latency.  The copy of step s + NS - 1 then goes into the buffer of
 // step s - 1, which every wave has finished reading at step s's barrier.
-template <int RT, int CT, bool EXACT>
-constexpr bool big_jit() { return !EXACT && RT * CT >= 32; }
+template <int RT, int CT, bool EXACT, int WC>
+constexpr bool big_jit() { return !EXACT && RT * CT * WC >= 64; }
 
-template <int EPI, int RT, int CT, int NS, bool EXACT>
-__global__ __launch_bounds__(256, (big_jit<RT, CT, EXACT>() ? 2 : 1)) void k_gemm_big(GemmArgs a) {
+// Waves as 2 x WC, each RT row tiles x CT column tiles: a block of 32 RT rows x 16 WC CT columns.
+// WC = 4 (eight waves, two workgroups per CU: four waves per SIMD) for the widest non-exact GEMM:
+// one wave per SIMD left every LDS, matrix-core and barrier latency of a step exposed.
+template <int EPI, int RT, int CT, int NS, bool EXACT, int WC = 2>
+__global__ __launch_bounds__(2 * WC * kWave, (WC == 4 ? 4 : (big_jit<RT, CT, EXACT, WC>() ? 2 : 1))) void k_gemm_big(GemmArgs a) {
 #pragma clang fp contract(off)
   constexpr bool NORM = (EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_LOGITS);
-  static_assert(EPI != EPI_LOGITS || (EXACT && CT == 4), "LM head: exact form, one 4-tile group per wave");
-  constexpr int NF = 2 * CT + 2 * RT;      // 1 KiB fragments per step: weights first, then activations
-  constexpr int FPW = NF / 4;              // fragments each wave stages per step
+  static_assert(EPI != EPI_LOGITS || (EXACT && CT == 4 && WC == 2), "LM head: exact form, one 4-tile group per wave");
+  static_assert(!EXACT || WC == 2, "the exact form runs four waves");
+  constexpr int NW = 2 * WC;               // waves
+  constexpr int NF = WC * CT + 2 * RT;     // 1 KiB fragments per step: weights first, then activations
+  constexpr int FPW = NF / NW;             // fragments each wave stages per step
   constexpr int BM = 32 * RT;
-  static_assert(NF % 4 == 0 && NS >= 2, "tile shape");
+  static_assert(NF % NW == 0 && NS >= 2, "tile shape");
   extern __shared__ __align__(16) unsigned char smem[];   // [NS][NF][1 KiB], then 1/rms [BM]
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int wr = wave / 2, wc = wave % 2;
-  const int tn0 = blockIdx.x * 2 * CT;     // first 16-column tile of the block
+  const int wr = wave / WC, wc = wave % WC;
+  const int tn0 = blockIdx.x * WC * CT;    // first 16-column tile of the block
   const int m0 = blockIdx.y * BM;          // first row of the block
   const int ksteps = a.K / Ty<bf16_t>::kStepK;
   float* s_inv = reinterpret_cast<float*>(smem + NS * NF * 1024);
   const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)smem;   // LDS byte address of the staging area
   stamp_begin(a.stamp);
 
-  // this wave's fragments of a step: f = wave + 4i; weights for f < 2CT, activations after
+  // this wave's fragments of a step: f = wave + NW i; weights for f < WC CT, activations after
   const uint4* src[FPW];
   int stride[FPW];
 #pragma unroll
   for (int i = 0; i < FPW; ++i) {
-    const int f = wave + 4 * i;
-    if (f < 2 * CT) {
+    const int f = wave + NW * i;
+    if (f < WC * CT) {
       src[i] = a.W + (size_t)(tn0 + f) * ksteps * kWave + lane;
       stride[i] = kWave;
     } else if (a.xpk) {
       // fragment-major activations: the (row tile, K step) fragment is 1 KiB in lane order; row
       // tiles past the last one (only in the block's padding) read the last
-      const int rt = min(m0 / 16 + (f - 2 * CT), (a.M + 15) / 16 - 1);
+      const int rt = min(m0 / 16 + (f - WC * CT), (a.M + 15) / 16 - 1);
       src[i] = reinterpret_cast<const uint4*>(a.x) + (size_t)rt * ksteps * kWave + lane;
       stride[i] = kWave;
     } else {
-      const int row = min(m0 + 16 * (f - 2 * CT) + lane % 16, a.M - 1);   // rows past M: any valid row
+      const int row = min(m0 + 16 * (f - WC * CT) + lane % 16, a.M - 1);   // rows past M: any valid row
       src[i] = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.x) + (size_t)row * a.ldx +
                                               (lane / 16) * 8);
       stride[i] = Ty<bf16_t>::kStepK / 8;   // uint4 per 32 K
@@ -1188,7 +1193,7 @@ __global__ __launch_bounds__(256, (big_jit<RT, CT, EXACT>() ? 2 : 1)) void k_gem
     const int ss = min(s, ksteps - 1);      // steps past the end reload the last one (never read)
     const unsigned buf = lds0 + (s % NS) * NF * 1024;
 #pragma unroll
-    for (int i = 0; i < FPW; ++i) load_lds16(src[i] + (size_t)ss * stride[i], buf + (wave + 4 * i) * 1024);
+    for (int i = 0; i < FPW; ++i) load_lds16(src[i] + (size_t)ss * stride[i], buf + (wave + NW * i) * 1024);
   };
 
   if constexpr (NORM && EXACT) {
@@ -1219,7 +1224,7 @@ __global__ __launch_bounds__(256, (big_jit<RT, CT, EXACT>() ? 2 : 1)) void k_gem
   // NS steps in flight; step s+1's operands are read from LDS into registers while step s
   // multiplies (register double buffer), one barrier per step.  JIT: NS - 1 steps in flight
   // beside the one being read.
-  constexpr bool JIT = big_jit<RT, CT, EXACT>();
+  constexpr bool JIT = big_jit<RT, CT, EXACT, WC>();
 #pragma unroll
   for (int s = 0; s < (JIT ? NS - 1 : NS); ++s) issue(s);
   f32x4_t acc[CT][RT];
@@ -1232,7 +1237,7 @@ __global__ __launch_bounds__(256, (big_jit<RT, CT, EXACT>() ? 2 : 1)) void k_gem
 #pragma unroll
     for (int c = 0; c < CT; ++c) w[c] = *reinterpret_cast<const uint4*>(buf + (wc * CT + c) * 1024 + lane * 16);
 #pragma unroll
-    for (int r = 0; r < RT; ++r) x[r] = *reinterpret_cast<const uint4*>(buf + (2 * CT + wr * RT + r) * 1024 + lane * 16);
+    for (int r = 0; r < RT; ++r) x[r] = *reinterpret_cast<const uint4*>(buf + (WC * CT + wr * RT + r) * 1024 + lane * 16);
   };
   uint4 wf[CT], xf[RT];
   // EXACT: acc holds the current K slice's chain, tot the slices so far (added in slice order)
@@ -1247,9 +1252,9 @@ __global__ __launch_bounds__(256, (big_jit<RT, CT, EXACT>() ? 2 : 1)) void k_gem
       issue(s + NS - 1);                   // into step s - 1's buffer
       const unsigned char* buf = smem + (s % NS) * NF * 1024;
 #pragma unroll
-      for (int r = 0; r < RT; ++r) xf[r] = *reinterpret_cast<const uint4*>(buf + (2 * CT + wr * RT + r) * 1024 + lane * 16);
-      // a raised wave priority while the products issue (the other workgroup's loads and LDS reads
-      // wait): 43.6 -> 42.6 us for the 1088-row gate|up
+      for (int r = 0; r < RT; ++r) xf[r] = *reinterpret_cast<const uint4*>(buf + (WC * CT + wr * RT + r) * 1024 + lane * 16);
+      // a raised wave priority while the products issue (the other waves' loads and LDS reads wait;
+      // measured on four-wave blocks: 43.6 -> 42.6 us for the 1088-row gate|up)
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
@@ -2405,12 +2410,12 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
 template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
 template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
 
-template <int EPI, int RT, int CT, int NS, bool EXACT>
+template <int EPI, int RT, int CT, int NS, bool EXACT, int WC = 2>
 static hipError_t launch_gemm_big_cfg(const GemmArgs& a, hipStream_t st) {
-  constexpr int NF = 2 * CT + 2 * RT;
-  const dim3 grid(a.n_tiles / (2 * CT), (a.M + 32 * RT - 1) / (32 * RT));
+  constexpr int NF = WC * CT + 2 * RT;
+  const dim3 grid(a.n_tiles / (WC * CT), (a.M + 32 * RT - 1) / (32 * RT));
   const int shm = NS * NF * 1024 + 32 * RT * 4;
-  SSB_LAUNCH((k_gemm_big<EPI, RT, CT, NS, EXACT>), grid, dim3(256), shm, st, a);
+  SSB_LAUNCH((k_gemm_big<EPI, RT, CT, NS, EXACT, WC>), grid, dim3(2 * WC * kWave), shm, st, a);
   return hipGetLastError();
 }
 
@@ -2421,12 +2426,13 @@ static hipError_t launch_gemm_big_epi(const GemmArgs& a, hipStream_t st) {
     return a.n_tiles % 8 == 0 ? launch_gemm_big_cfg<EPI, 4, 4, 3, true>(a, st) : hipErrorInvalidValue;
   } else {
     // the largest tile that still gives about one workgroup per CU; non-exact (prefill) GEMMs wide
-    // enough take 128 x 256 tiles at two workgroups per CU (JIT fragment reads)
+    // enough take 128 x 256 blocks of eight waves at two workgroups per CU (JIT fragment reads;
+    // against four waves of 64 x 128: 41.0 -> 38.2 us for the 1088-row gate|up)
     const int rb4 = (a.M + 127) / 128;
     // (LDS: 3 steps of 16 KiB, 4 of 12 KiB, 6 of 8 KiB: two or three workgroups per CU; deeper
     // pipelines with one workgroup per CU measured slower)
     if constexpr (!EXACT) {
-      if (a.n_tiles % 16 == 0 && (a.n_tiles / 16) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 8, 3, false>(a, st);
+      if (a.n_tiles % 16 == 0 && (a.n_tiles / 16) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3, false, 4>(a, st);
     }
     if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3, EXACT>(a, st);
     if (a.n_tiles % 4 == 0 && (a.n_tiles / 4) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 2, 4, EXACT>(a, st);
