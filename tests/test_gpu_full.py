@@ -285,6 +285,29 @@ def test_lm_head_records_equal_exact_top2_of_logits(full):
     assert kv.prefill(full["pre_dev"]) == full["y1"]
 
 
+def test_tall_forward_logits_match_oracle(full):
+    """A teacher-forced forward of 200 rows after the prefill runs as a tall forward: the large-tile
+    GEMMs on fragment-major activations, the folded two-stream attention, the 128 x 256 gate|up
+    blocks. Its logits, every row and every id, against the oracle's forward of the same rows on
+    the same prefilled cache, at the logit bar."""
+    from oracle.decode import causal_visibility
+    from self_speculative_block_amd.engine import KV
+    cfg, pool, orc, P = full["cfg"], full["pool"], full["orc"], full["P"]
+    M = 200
+    toks = [int(t) for t in np.random.default_rng(17).integers(0, cfg.vocab - 2, M)]
+    kv = KV(pool, P + M + 8)
+    kv.prefill(full["pre_dev"])
+    _, _, _, lg = kv.forward_tokens(toks, P, want_logits=True)
+    kv.close()
+    st = _copy_state(full["st"])
+    pos = P + np.arange(M)
+    ref = orc.forward(st.cache, orc.embed_tokens(toks), pos, causal_visibility(pos, P + M))
+    err = float(np.abs(lg.cpu().numpy() - ref).max())
+    print(f"\n[{cfg.n_layers} layers] tall forward of {M} rows: logit max-abs error vs the oracle {err:.5f}",
+          flush=True)
+    assert err < LOGIT_TOL, err
+
+
 def test_teacher_forced_tokens_match_oracle(full):
     """GravityOCR review, Appendix B.3: a decoded sequence is judged position by position; a
     position where the GPU's token differs from the oracle's greedy prediction for it (given the
