@@ -1128,7 +1128,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane (lds_base is
 // wave-uniform; it goes through M0).  Issued as inline assembly so the compiler does not pair
 // every later LDS read with a wait for all outstanding loads; the caller waits with wait_vmcnt
-// and a barrier before reading the destination.
+// and a barrier before reading the destination.  The compiler does not preserve M0 across inline
+// assembly; in the built k_gemm_big kernels every M0 write and read is this block's own.
 __device__ __forceinline__ void load_lds16(const void* gptr, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :
