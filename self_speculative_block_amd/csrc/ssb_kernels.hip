@@ -1610,14 +1610,19 @@ __device__ __forceinline__ float fold_val(float v, float al, float vc, float be)
 }
 
 // fp16 K/V: at most 128 VGPRs, so four workgroups share a CU (long contexts launch several per CU).
-// Folded rows (FOLD) run two chunk streams of four waves each, the even and the odd chunks of the
-// same rows and heads, and merge the two running states at the end: half the dependent chain per
-// workgroup and two waves per SIMD.
+// Folded rows (FOLD) run fold_streams<T>() chunk streams of four waves each (stream k takes
+// chunks k, k + streams, ...) of the same rows and heads, and merge the running states into
+// stream 0's at the end, in stream order: a fraction of the dependent chain per workgroup and
+// several waves per SIMD (two streams: 28.6 -> 20.5 us per 1088-row prefill layer).  fp32 K/V
+// keeps two streams (four would spill).
+template <typename T>
+constexpr int fold_streams() { return sizeof(T) == 2 ? 4 : 2; }
 template <typename T, int HD, bool FOLD>
-__global__ __launch_bounds__((FOLD ? 2 : 1) * kAttnThreads, (FOLD ? 2 : (sizeof(T) == 2 ? 4 : 1))) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__((FOLD ? fold_streams<T>() : 1) * kAttnThreads,
+                             (FOLD ? fold_streams<T>() : (sizeof(T) == 2 ? 4 : 1))) void k_attn(AttnArgs a) {
 #pragma clang fp contract(off)
   constexpr int NTH = kAttnThreads;        // threads of one chunk stream
-  constexpr int NST = FOLD ? 2 : 1;        // chunk streams
+  constexpr int NST = FOLD ? fold_streams<T>() : 1;   // chunk streams
   constexpr int KS = Ty<T>::kStepK;
   constexpr int PER = Ty<T>::kPerFrag;
   constexpr int DT = HD / 16;
@@ -1858,28 +1863,31 @@ __global__ __launch_bounds__((FOLD ? 2 : 1) * kAttnThreads, (FOLD ? 2 : (sizeof(
   }
 
   if constexpr (FOLD) {
-    // the odd-chunk stream's (m, l, o) into the even stream's, the same online merge
+    // streams 1, 2, ... hand their (m, l, o) to stream 0 in turn, merged by the same online step
     constexpr int XS = 4 * DT + 2;
     float* xs = reinterpret_cast<float*>(ks) + (size_t)(wave * kWave + lane) * XS;
-    if (sm == 1) {
-      xs[0] = run_m;
-      xs[1] = run_l;
+    for (int k = 1; k < NST; ++k) {
+      if (sm == k) {
+        xs[0] = run_m;
+        xs[1] = run_l;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xs[2 + 4 * dt + i] = run_o[dt][i];
-    }
-    __syncthreads();
-    const float m1 = xs[0];
-    if (sm == 0 && m1 != -INFINITY) {
-      float mn, al, be;
-      fold_coef(run_m, m1, mn, al, be);
-      run_l = fold_val(run_l, al, xs[1], be);
+          for (int i = 0; i < 4; ++i) xs[2 + 4 * dt + i] = run_o[dt][i];
+      }
+      __syncthreads();
+      const float m1 = xs[0];
+      if (sm == 0 && m1 != -INFINITY) {
+        float mn, al, be;
+        fold_coef(run_m, m1, mn, al, be);
+        run_l = fold_val(run_l, al, xs[1], be);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) run_o[dt][i] = fold_val(run_o[dt][i], al, xs[2 + 4 * dt + i], be);
-      run_m = mn;
+          for (int i = 0; i < 4; ++i) run_o[dt][i] = fold_val(run_o[dt][i], al, xs[2 + 4 * dt + i], be);
+        run_m = mn;
+      }
+      __syncthreads();   // before the next stream overwrites the exchange area
     }
   }
 
@@ -2513,12 +2521,12 @@ hipError_t launch_attn(const AttnArgs& a, int n_chunk_slots, int head_dim, hipSt
   if (a.n_heads / a.n_kv > kAttnThreads / kWave) return hipErrorInvalidValue;
   if (!a.fold && n_chunk_slots > a.max_chunks) return hipErrorInvalidValue;
   dim3 grid(a.fold ? 1 : n_chunk_slots, a.n_kv, a.tasks.n * (kTaskRows / 16));
-  // folded rows: two chunk streams per workgroup
+  // folded rows: fold_streams<T>() chunk streams per workgroup
   if (head_dim == 64) {
-    if (a.fold) SSB_LAUNCH((k_attn<T, 64, true>), grid, dim3(2 * kAttnThreads), 0, st, a);
+    if (a.fold) SSB_LAUNCH((k_attn<T, 64, true>), grid, dim3(fold_streams<T>() * kAttnThreads), 0, st, a);
     else SSB_LAUNCH((k_attn<T, 64, false>), grid, dim3(kAttnThreads), 0, st, a);
   } else {
-    if (a.fold) SSB_LAUNCH((k_attn<T, 32, true>), grid, dim3(2 * kAttnThreads), 0, st, a);
+    if (a.fold) SSB_LAUNCH((k_attn<T, 32, true>), grid, dim3(fold_streams<T>() * kAttnThreads), 0, st, a);
     else SSB_LAUNCH((k_attn<T, 32, false>), grid, dim3(kAttnThreads), 0, st, a);
   }
   return hipGetLastError();
