@@ -2440,7 +2440,7 @@ static hipError_t launch_gemm_big_epi(const GemmArgs& a, hipStream_t st) {
     const int rb4 = (a.M + 127) / 128;
     // (LDS: 3 steps of 16 KiB, 4 of 12 KiB, 6 of 8 KiB: two or three workgroups per CU; deeper
     // pipelines with one workgroup per CU measured slower)
-    if constexpr (!EXACT) {
+    if constexpr (!EXACT && EPI == EPI_SWIGLU) {   // (the QKV epilogue would spill at 128 VGPRs)
       if (a.n_tiles % 16 == 0 && (a.n_tiles / 16) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3, false, 4>(a, st);
     }
     if (a.n_tiles % 8 == 0 && (a.n_tiles / 8) * rb4 >= 240) return launch_gemm_big_cfg<EPI, 4, 4, 3, EXACT>(a, st);
