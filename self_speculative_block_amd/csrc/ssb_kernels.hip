@@ -1648,7 +1648,7 @@ __global__ __launch_bounds__((FOLD ? fold_streams<T>() : 1) * kAttnThreads,
   __shared__ __align__(16) unsigned char ks[NST * kKeyChunk * KSTR];
   __shared__ __align__(16) unsigned char vts[NST * HD * VSTR];
   __shared__ int s_lim[16];
-  // the second stream's running state goes to the first through the K buffers after the loop
+  // the other streams' running states go to stream 0 through the K buffers after the loop
   static_assert(!FOLD || NST * kKeyChunk * KSTR >= (kAttnThreads / kWave) * kWave * (4 * DT + 2) * 4, "state exchange");
 
   stamp_begin(a.stamp);
@@ -1732,7 +1732,7 @@ __global__ __launch_bounds__((FOLD ? fold_streams<T>() : 1) * kAttnThreads,
 
   for (int c0 = cbeg; c0 < cend; c0 += NST) {
     const int c = c0 + sm;                 // this stream's chunk
-    const bool cvalid = c < cend;          // (the odd stream may have none in the last pass)
+    const bool cvalid = c < cend;          // (later streams may have none in the last pass)
     // (the row limits are stored once the K/V loads are in flight)
     if (threadIdx.x < 16) s_lim[threadIdx.x] = lim_row < task.nrows ? lim_ld : -1;
 #pragma unroll
@@ -1763,7 +1763,7 @@ __global__ __launch_bounds__((FOLD ? fold_streams<T>() : 1) * kAttnThreads,
     }
     __syncthreads();
     if constexpr (FOLD) {
-      load_kv(pg, kvv);                        // chunk c + 2 (its page ids landed a pass ago)
+      load_kv(pg, kvv);                        // chunk c + NST (its page ids landed a pass ago)
       load_pg(min(c + 2 * NST, cend - 1), pg);
     }
 
